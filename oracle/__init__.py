@@ -1,0 +1,131 @@
+"""fp64 CPU oracle for the block-causal linear-attention scan.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  It does not import, link or call the
+GPU library and the GPU library never calls it.
+
+The arithmetic lives in ``oracle.c`` (plain loops over frames and tokens in
+double precision, each function citing the passage it follows).  This module
+only builds that file with gcc, loads it with ctypes and marshals numpy arrays.
+
+Inputs are taken as float32 arrays (bf16 and fp32 values widen to float32
+exactly); states and outputs come back as float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O3, OpenMP) into oracle/liboracle.so."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i = ctypes.c_int
+    d = ctypes.c_double
+    lib.oracle_relu_block.argtypes = [i, i, i, i, i, i, d, P, P, P, P, P, P, P, P, i]
+    lib.oracle_relu_block.restype = i
+    lib.oracle_gdn_frame.argtypes = [i, i, i, i, i, d, P, P, P, P, P, P, P, P, i]
+    lib.oracle_gdn_frame.restype = i
+    lib.oracle_max_threads.restype = i
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f32(x, shape=None):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: widen on the CPU (exact for bf16/fp32)
+        x = x.detach().to("cpu").float().numpy()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if shape is not None and a.shape != tuple(shape):
+        a = a.reshape(shape)
+    return a
+
+
+def _f64(x, shape):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(shape))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def relu_block(q, k, v, state=None, norm=None, block_frames: int = 1, eps: float = 1e-6,
+               with_output: bool = True, nthreads: int = 0):
+    """ReLU block-causal linear attention, fp64.
+
+    q, k, v: [B, H, F, N, D].  state: [B, H, D, D] or None (zeros);
+    norm: [B, H, D] or None (zeros).  Returns (o or None, S, z) as float64.
+    """
+    k = _f32(k)
+    B, H, F, N, D = k.shape
+    v = _f32(v, k.shape)
+    q = _f32(q, k.shape) if with_output else None
+    S0 = _f64(state, (B, H, D, D))
+    z0 = _f64(norm, (B, H, D))
+    o = np.empty((B, H, F, N, D), np.float64) if with_output else None
+    S = np.empty((B, H, D, D), np.float64)
+    z = np.empty((B, H, D), np.float64)
+    rc = _load().oracle_relu_block(B, H, F, N, D, int(block_frames), float(eps),
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0),
+                                   _ptr(o), _ptr(S), _ptr(z), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_relu_block failed with code %d" % rc)
+    return o, S, z
+
+
+def gdn_frame(q, k, v, alpha, beta, state=None, key_scale=None, with_output: bool = True,
+              nthreads: int = 0):
+    """Frame-wise Gated DeltaNet, fp64.
+
+    q, k, v: [B, H, F, N, D]; alpha, beta: [B, H, F]; state: [B, H, D, D] or
+    None (zeros); key_scale None means 1/sqrt(D*N).  Returns (o or None, S).
+    """
+    k = _f32(k)
+    B, H, F, N, D = k.shape
+    v = _f32(v, k.shape)
+    q = _f32(q, k.shape) if with_output else None
+    a = _f32(alpha, (B, H, F))
+    b = _f32(beta, (B, H, F))
+    S0 = _f64(state, (B, H, D, D))
+    o = np.empty((B, H, F, N, D), np.float64) if with_output else None
+    S = np.empty((B, H, D, D), np.float64)
+    c = -1.0 if key_scale is None else float(key_scale)
+    rc = _load().oracle_gdn_frame(B, H, F, N, D, c, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                  _ptr(S0), _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_frame failed with code %d" % rc)
+    return o, S

@@ -1,0 +1,227 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the block-causal linear-attention
+ * scan.  TEST INFRASTRUCTURE: only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it.  It shares no code, header
+ * or constant with the GPU library and never calls into it.
+ *
+ * Everything here is a direct loop over frames and tokens in the order the
+ * pages describe, with double-precision arithmetic throughout.  Token
+ * tensors arrive as float32 (bf16 and fp32 inputs widen to float32 without
+ * rounding); states arrive and leave as float64.
+ *
+ * Layout: token tensors are [B][H][F][N][D] row-major (D fastest); the state
+ * S is [B][H][D][D] with S[i][j], i indexing value dimensions and j key
+ * dimensions, so a query reads out o = S q; the normaliser z is [B][H][D];
+ * the gates alpha, beta are [B][H][F].
+ *
+ * Sources:
+ *  - ReLU linear attention with a cumulative D x D state that is cached and
+ *    extended block by block: "SANA-Video: Efficient Video Generation with
+ *    Block Linear Diffusion Transformer" (ICLR 2026 oral, talk transcript),
+ *    the passage on the block KV cache of linear attention; feature map ReLU
+ *    per the "SANA-Video practical guide" (lpnh.cn), section on core
+ *    mechanisms (attn_type LiteLAReLURope), which also states that each block
+ *    attends to itself and the blocks before it.
+ *  - Frame-wise Gated DeltaNet with a D x D state updated once per latent
+ *    frame from all of that frame's spatial tokens, decay alpha and update
+ *    gate beta: "SANA-WM: Efficient Minute-Scale World Modeling with Hybrid
+ *    Linear Diffusion Transformer" (paperlayer.ai summary), section 3 Method,
+ *    item "Hybrid GDN/Softmax Attention"; key scaling by 1/sqrt(D*S) with S the
+ *    spatial tokens per frame: the SANA-WM digest (seosoyoung.eiaserinnys.me),
+ *    paragraph on stabilising the spatial explosion.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in
+ * the design notes of the repository):
+ *  - the ReLU normaliser is o = (S phi(q)) / (z . phi(q) + eps);
+ *  - outputs of a block read the state AFTER that block's own tokens were
+ *    added (a block sees itself);
+ *  - the GDN frame update is S <- alpha S (I - beta G) + beta U with
+ *    G = sum_n (c k_n)(c k_n)^T and U = sum_n v_n (c k_n)^T over the frame's
+ *    tokens, and the frame's outputs read the updated S;
+ *  - phi(x) = 0 when x carries a negative sign, else x (ReLU; -0 maps to 0).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+int oracle_version(void) { return 1; }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+static double relu(double x) { return signbit(x) ? 0.0 : x; }
+
+/* offset of token n of frame f of head (b*H + h) in a [B][H][F][N][D] tensor */
+static size_t tok(long bh, int f, int n, int F, int N, int D) {
+  return (((size_t)bh * F + f) * N + n) * (size_t)D;
+}
+
+/*
+ * ReLU block-causal linear attention.
+ * Frames are grouped into blocks of `block_frames` consecutive frames starting
+ * at frame 0 of this call.  For each block in order: every token of the block
+ * adds v phi(k)^T to S and phi(k) to z; then every token of the block reads
+ * o = S phi(q) / (z . phi(q) + eps).
+ * q, k, v: [B][H][F][N][D] float32.  S0, z0: initial state / normaliser or
+ * NULL for zeros.  o (may be NULL to skip outputs), S_out, z_out (may be NULL).
+ */
+int oracle_relu_block(int B, int H, int F, int N, int D, int block_frames, double eps,
+                      const float* q, const float* k, const float* v,
+                      const double* S0, const double* z0,
+                      double* o, double* S_out, double* z_out, int nthreads) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1 || block_frames < 1) return ORACLE_BAD_ARG;
+  if (!k || !v || (o && !q)) return ORACLE_BAD_ARG;
+  int status = ORACLE_OK;
+  long heads = (long)B * H;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (long bh = 0; bh < heads; ++bh) {
+    double* S = (double*)calloc((size_t)D * D, sizeof(double));
+    double* z = (double*)calloc((size_t)D, sizeof(double));
+    double* feat = (double*)malloc((size_t)D * sizeof(double));
+    if (!S || !z || !feat) {
+      status = ORACLE_NO_MEMORY;
+      free(S); free(z); free(feat);
+      continue;
+    }
+    if (S0) memcpy(S, S0 + (size_t)bh * D * D, (size_t)D * D * sizeof(double));
+    if (z0) memcpy(z, z0 + (size_t)bh * D, (size_t)D * sizeof(double));
+
+    for (int f0 = 0; f0 < F; f0 += block_frames) {
+      int f1 = f0 + block_frames < F ? f0 + block_frames : F;
+      /* 1. the block's keys and values extend the cached state */
+      for (int f = f0; f < f1; ++f) {
+        for (int n = 0; n < N; ++n) {
+          const float* kn = k + tok(bh, f, n, F, N, D);
+          const float* vn = v + tok(bh, f, n, F, N, D);
+          for (int j = 0; j < D; ++j) feat[j] = relu((double)kn[j]);
+          for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) S[(size_t)i * D + j] += (double)vn[i] * feat[j];
+          for (int j = 0; j < D; ++j) z[j] += feat[j];
+        }
+      }
+      /* 2. the block's queries read the state that now includes the block */
+      if (o) {
+        for (int f = f0; f < f1; ++f) {
+          for (int n = 0; n < N; ++n) {
+            const float* qn = q + tok(bh, f, n, F, N, D);
+            double* on = o + tok(bh, f, n, F, N, D);
+            for (int j = 0; j < D; ++j) feat[j] = relu((double)qn[j]);
+            double den = 0.0;
+            for (int j = 0; j < D; ++j) den += z[j] * feat[j];
+            den += eps;
+            for (int i = 0; i < D; ++i) {
+              double num = 0.0;
+              for (int j = 0; j < D; ++j) num += S[(size_t)i * D + j] * feat[j];
+              on[i] = num / den;
+            }
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * D * D, S, (size_t)D * D * sizeof(double));
+    if (z_out) memcpy(z_out + (size_t)bh * D, z, (size_t)D * sizeof(double));
+    free(S); free(z); free(feat);
+  }
+  return status;
+}
+
+/*
+ * Frame-wise Gated DeltaNet.
+ * c = key_scale if key_scale > 0, else 1/sqrt(D*N).  For each frame f in order:
+ *   G = sum_n (c k_n)(c k_n)^T,  U = sum_n v_n (c k_n)^T   (frame f's tokens)
+ *   M = I - beta_f G,  S <- alpha_f (S M) + beta_f U
+ *   o_n = S q_n for every token n of frame f.
+ * alpha, beta: [B][H][F] float32.  S0: [B][H][D][D] or NULL for zeros.
+ * o may be NULL (state only); S_out may be NULL.
+ */
+int oracle_gdn_frame(int B, int H, int F, int N, int D, double key_scale,
+                     const float* q, const float* k, const float* v,
+                     const float* alpha, const float* beta, const double* S0,
+                     double* o, double* S_out, int nthreads) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1) return ORACLE_BAD_ARG;
+  if (!k || !v || !alpha || !beta || (o && !q)) return ORACLE_BAD_ARG;
+  const double c = key_scale > 0.0 ? key_scale : 1.0 / sqrt((double)D * (double)N);
+  int status = ORACLE_OK;
+  long heads = (long)B * H;
+  size_t DD = (size_t)D * D;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (long bh = 0; bh < heads; ++bh) {
+    double* S = (double*)calloc(DD, sizeof(double));
+    double* G = (double*)malloc(DD * sizeof(double));
+    double* U = (double*)malloc(DD * sizeof(double));
+    double* M = (double*)malloc(DD * sizeof(double));
+    double* T = (double*)malloc(DD * sizeof(double));
+    double* kt = (double*)malloc((size_t)D * sizeof(double));
+    if (!S || !G || !U || !M || !T || !kt) {
+      status = ORACLE_NO_MEMORY;
+      free(S); free(G); free(U); free(M); free(T); free(kt);
+      continue;
+    }
+    if (S0) memcpy(S, S0 + (size_t)bh * DD, DD * sizeof(double));
+
+    for (int f = 0; f < F; ++f) {
+      const double a = (double)alpha[(size_t)bh * F + f];
+      const double b = (double)beta[(size_t)bh * F + f];
+      /* 1. the frame's key Gram matrix and value-key matrix, keys scaled by c */
+      memset(G, 0, DD * sizeof(double));
+      memset(U, 0, DD * sizeof(double));
+      for (int n = 0; n < N; ++n) {
+        const float* kn = k + tok(bh, f, n, F, N, D);
+        const float* vn = v + tok(bh, f, n, F, N, D);
+        for (int j = 0; j < D; ++j) kt[j] = c * (double)kn[j];
+        for (int i = 0; i < D; ++i) {
+          for (int j = 0; j < D; ++j) {
+            G[(size_t)i * D + j] += kt[i] * kt[j];
+            U[(size_t)i * D + j] += (double)vn[i] * kt[j];
+          }
+        }
+      }
+      /* 2. transition: S <- alpha S (I - beta G) + beta U */
+      for (int i = 0; i < D; ++i)
+        for (int j = 0; j < D; ++j)
+          M[(size_t)i * D + j] = (i == j ? 1.0 : 0.0) - b * G[(size_t)i * D + j];
+      for (int i = 0; i < D; ++i) {
+        for (int j = 0; j < D; ++j) {
+          double acc = 0.0;
+          for (int l = 0; l < D; ++l) acc += S[(size_t)i * D + l] * M[(size_t)l * D + j];
+          T[(size_t)i * D + j] = acc;
+        }
+      }
+      for (size_t e = 0; e < DD; ++e) S[e] = a * T[e] + b * U[e];
+      /* 3. the frame's queries read the updated state */
+      if (o) {
+        for (int n = 0; n < N; ++n) {
+          const float* qn = q + tok(bh, f, n, F, N, D);
+          double* on = o + tok(bh, f, n, F, N, D);
+          for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < D; ++j) acc += S[(size_t)i * D + j] * (double)qn[j];
+            on[i] = acc;
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * DD, S, DD * sizeof(double));
+    free(S); free(G); free(U); free(M); free(T); free(kt);
+  }
+  return status;
+}
