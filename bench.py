@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Scan tokens/s of liblinscan on one MI355X at the 720p minute-scale shapes.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  1. SANA-Video 720p minute-scale block-autoregressive rollout, ReLU linear
+     attention: B1 H70 D32, 45x80 = 3600 tokens per frame, 241 latent frames
+     in 25 calls (24 x 10 + 1) chained by ls_state_carry;
+  2. SANA-WM 720p 60 s frame-wise Gated DeltaNet: B1 H24 D128, 23x40 = 920
+     tokens per frame, 181 latent frames in one call.
+Inputs are drawn once on the GPU (seeded, N(0,1) bf16, L2-normalised GDN
+keys) and stay resident in HBM; the timed region holds only library calls.
+
+Prints one JSON line: the throughput (tokens = B*F*N summed over both parts,
+all heads of a token counted once), the roofline object of the dominant
+kernel (per-kernel HIP-event timing from the library's profiling session, over
+extra steps after the timed ones), and the fp64 CPU oracle timed on a sample
+of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scan tokens/sec (1 GPU) at 720p minute-scale; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads per part in the oracle sample (default: oracle threads)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the scan has no multi-GPU path in this build "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_causal_linear_attn_amd import binding as ls
+    from block_causal_linear_attn_amd import inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wv = inputs.WORKLOADS["sana_video_720p_minute"]
+    wg = inputs.WORKLOADS["sana_wm_720p_60s"]
+
+    # ---- resident inputs and outputs
+    calls = [inputs.workload_call_inputs(wv, i, device=dev) for i in range(len(wv.calls))]
+    outs = [torch.empty_like(c["q"]) for c in calls]
+    cache = torch.zeros((wv.B, wv.H, wv.D, wv.D), device=dev)
+    ncache = torch.zeros((wv.B, wv.H, wv.D), device=dev)
+    S_blk = torch.empty_like(cache)
+    z_blk = torch.empty_like(ncache)
+    g = inputs.workload_call_inputs(wg, 0, device=dev)
+    g_out = torch.empty_like(g["q"])
+    g_state = torch.empty((wg.B, wg.H, wg.D, wg.D), device=dev)
+    torch.cuda.synchronize()
+
+    def part_video():
+        for i, c in enumerate(calls):
+            first = i == 0  # each pass starts the rollout from the zero state
+            ls.ls_relu_block_forward(c["q"], c["k"], c["v"], None if first else cache,
+                                     None if first else ncache, out=outs[i], state_out=S_blk,
+                                     norm_out=z_blk)
+            ls.ls_state_carry(S_blk, cache, z_blk, ncache)
+
+    def part_wm():
+        ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], None, out=g_out,
+                                state_out=g_state)
+
+    for _ in range(args.warmup):
+        part_video()
+        part_wm()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        part_video()
+        e1.record()
+        part_wm()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_video = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    ms_wm = sorted(b.elapsed_time(c) for _, b, c in ev)
+    ms_step = sorted(a.elapsed_time(c) for a, _, c in ev)
+    gpu_total_s = sum(ms_step) / 1e3
+    print("timed %d steps: wall %.3f s, events %.3f s" % (args.steps, wall, gpu_total_s),
+          file=sys.stderr, flush=True)
+
+    tok_video = wv.B * wv.F * wv.N
+    tok_wm = wg.B * wg.F * wg.N
+    tokens = tok_video + tok_wm
+    elt = 2  # bf16 bytes
+    bytes_video = 4 * wv.B * wv.H * wv.F * wv.N * wv.D * elt
+    bytes_wm = 4 * wg.B * wg.H * wg.F * wg.N * wg.D * elt
+    value = tokens * args.steps / gpu_total_s
+    med = lambda xs: xs[len(xs) // 2]
+
+    # ---- per-kernel timing (library profiling session over extra steps)
+    ls.ls_profile_begin()
+    for _ in range(args.profile_steps):
+        part_video()
+        part_wm()
+    torch.cuda.synchronize()
+    kstats = ls.ls_profile_end()
+    # algorithmic HBM bytes per launch: the token tensors each kernel must move
+    half_video = 2 * wv.B * wv.H * wv.F * wv.N * wv.D * elt  # two of q, k, v, o over all calls
+    half_wm = 2 * wg.B * wg.H * wg.F * wg.N * wg.D * elt
+    n_calls = len(wv.calls)
+    alg = {
+        "relu_summary": half_video / n_calls,   # k, v in (per call, averaged over the 25 calls)
+        "relu_output": half_video / n_calls,    # q in, o out
+        "gdn_gram": half_wm,                    # k, v in
+        "gdn_output": half_wm,                  # q in, o out
+    }
+    kernels = {}
+    for name, (launches, total_ms) in kstats.items():
+        avg_us = 1e3 * total_ms / max(1, launches)
+        k = {"launches_per_step": launches / max(1, args.profile_steps), "avg_us": round(avg_us, 2),
+             "ms_per_step": round(total_ms / max(1, args.profile_steps), 4)}
+        if name in alg:
+            gbs = alg[name] / (avg_us * 1e-6) / 1e9
+            k["alg_bytes_per_launch"] = int(alg[name])
+            k["achieved_GBs"] = round(gbs, 1)
+            k["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+        kernels[name] = k
+    dom = max((n for n in kernels if n in alg), key=lambda n: kernels[n]["ms_per_step"])
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_GBs"],
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
+                "traffic": None}
+
+    # ---- CPU baseline: the fp64 oracle on a sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, inputs, wv, wg, tokens)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(gpu_total_s * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "720p minute-scale scan: SANA-Video ReLU block-AR rollout (B1 H70 D32 N3600, "
+                        "241 frames in 24x10+1 calls with state carry) + SANA-WM frame-wise GDN "
+                        "(B1 H24 D128 N920 F181)",
+            "global_batch": 1,
+            "tokens_per_step": tokens,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parts": {
+            "sana_video_720p_minute": {"ms_median": round(med(ms_video), 4), "tokens": tok_video,
+                                       "tokens_per_s": round(tok_video / (med(ms_video) / 1e3), 1),
+                                       "hbm_frac": round(bytes_video / (med(ms_video) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "sana_wm_720p_60s": {"ms_median": round(med(ms_wm), 4), "tokens": tok_wm,
+                                 "tokens_per_s": round(tok_wm / (med(ms_wm) / 1e3), 1),
+                                 "hbm_frac": round(bytes_wm / (med(ms_wm) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "step_ms_p10_p50_p90": [round(ms_step[int(0.1 * (len(ms_step) - 1))], 4), round(med(ms_step), 4),
+                                    round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
+            "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, inputs, wv, wg, tokens):
+    """Time the fp64 oracle on Hs heads of each part (all frames), scaled to the step."""
+    import oracle
+    threads = oracle.max_threads()
+    hs = args.cpu_heads or threads
+    hv, hg = min(hs, wv.H), min(hs, wg.H)
+    xv = inputs.relu_inputs(1, hv, wv.F, wv.N, wv.D, "bf16", seed=wv.seed, part=999)
+    xv = {k: t.float().numpy() for k, t in xv.items()}
+    t0 = time.perf_counter()
+    oracle.relu_block(xv["q"], xv["k"], xv["v"], nthreads=threads)
+    tv = time.perf_counter() - t0
+    del xv
+    xg = inputs.gdn_inputs(1, hg, wg.F, wg.N, wg.D, "bf16", seed=wg.seed, part=999, l2_keys=True)
+    xg = {k: t.float().numpy() for k, t in xg.items()}
+    t0 = time.perf_counter()
+    oracle.gdn_frame(xg["q"], xg["k"], xg["v"], xg["alpha"], xg["beta"], nthreads=threads)
+    tg = time.perf_counter() - t0
+    step_s = tv * wv.H / hv + tg * wg.H / hg
+    print("oracle: %d+%d heads in %.2f+%.2f s on %d threads" % (hv, hg, tv, tg, threads),
+          file=sys.stderr, flush=True)
+    return {"value": round(tokens / step_s, 1), "unit": "tokens/s", "cores": min(threads, max(hv, hg)),
+            "kind": "oracle",
+            "sample": "%d of %d heads of the ReLU rollout (all 241 frames) and %d of %d heads of the GDN "
+                      "scan (all 181 frames), same shapes and distributions, timed %.1f s + %.1f s and "
+                      "scaled by the head ratio" % (hv, wv.H, hg, wg.H, tv, tg)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+"""Thin ctypes binding of liblinscan with the C entry points' names.
+
+Only argument marshalling happens here: torch device tensors are checked for
+dtype, shape, contiguity and device, and their data pointers, the workspace
+and the current HIP stream are passed to the C ABI, where every step of the
+scan runs in HIP kernels.  If liblinscan.so has not been built this module
+raises on import: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinscan.so")
+
+LS_OK = 0
+LS_DTYPE_FP32 = 0
+LS_DTYPE_BF16 = 1
+_DT = {torch.float32: LS_DTYPE_FP32, torch.bfloat16: LS_DTYPE_BF16}
+
+
+class LinscanError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("liblinscan status %d: %s" % (status, message))
+        self.status = status
+
+
+class ls_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("F", ctypes.c_int),
+                ("N", ctypes.c_int), ("D", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+class ls_kernel_stat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblinscan.so is not built (%s); run "
+                          "`python -m block_causal_linear_attn_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    SP = ctypes.POINTER(ls_shape)
+    lib.ls_relu_block_workspace_size.argtypes = [SP, I]
+    lib.ls_relu_block_workspace_size.restype = Z
+    lib.ls_relu_block_forward.argtypes = [SP, I, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_relu_block_forward.restype = I
+    lib.ls_gdn_frame_workspace_size.argtypes = [SP]
+    lib.ls_gdn_frame_workspace_size.restype = Z
+    lib.ls_gdn_frame_forward.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_gdn_frame_forward.restype = I
+    lib.ls_state_carry.argtypes = [I, I, I, P, P, P, P, I, P]
+    lib.ls_state_carry.restype = I
+    lib.ls_status_string.argtypes = [I]
+    lib.ls_status_string.restype = ctypes.c_char_p
+    lib.ls_last_error.argtypes = []
+    lib.ls_last_error.restype = ctypes.c_char_p
+    lib.ls_version.argtypes = []
+    lib.ls_version.restype = I
+    lib.ls_profile_begin.argtypes = []
+    lib.ls_profile_begin.restype = I
+    lib.ls_profile_end.argtypes = [ctypes.POINTER(ls_kernel_stat), I]
+    lib.ls_profile_end.restype = I
+    return lib
+
+
+lib = _load()
+
+EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
+           "ls_gdn_frame_forward", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_version", "ls_profile_begin", "ls_profile_end")
+
+
+def _check(status: int):
+    if status != LS_OK:
+        detail = lib.ls_last_error().decode() or lib.ls_status_string(status).decode()
+        raise LinscanError(status, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _tokens(name, t, like=None):
+    if not isinstance(t, torch.Tensor) or t.dim() != 5:
+        raise ValueError("%s must be a 5-D [B, H, F, N, D] tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must live on a GPU (got %s)" % (name, t.device))
+    if t.dtype not in _DT:
+        raise ValueError("%s must be float32 or bfloat16 (got %s)" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError("%s must match q in shape, dtype and device" % name)
+    return t
+
+
+def _f32(name, t, shape, device):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or t.device != device \
+            or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor of shape %s on %s"
+                         % (name, tuple(shape), device))
+    return t
+
+
+_ws_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A cached uint8 device buffer of at least nbytes (per device and stream)."""
+    key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+        return buf
+
+
+def _shape(q) -> ls_shape:
+    B, H, F, N, D = q.shape
+    return ls_shape(B, H, F, N, D, _DT[q.dtype])
+
+
+def ls_relu_block_forward(q, k, v, state=None, norm=None, block_frames: int = 1, eps: float = 1e-6,
+                          out=None, state_out=None, norm_out=None, ws=None):
+    """ReLU block-causal linear attention; returns (o, state_out, norm_out).
+
+    q, k, v: [B, H, F, N, D] fp32 or bf16 on one GPU.  state [B, H, D, D] and
+    norm [B, H, D] (fp32) seed the scan (zeros when None).  New output
+    tensors are allocated unless given; pass state_out=state (and
+    norm_out=norm) for an in-place update.
+    """
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("state", state, (B, H, D, D), dev)
+    _f32("norm", norm, (B, H, D), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    no = norm_out if norm_out is not None else torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    _f32("norm_out", no, (B, H, D), dev)
+    shp = _shape(q)
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    w = ws if ws is not None else workspace(need, dev)
+    _check(lib.ls_relu_block_forward(ctypes.byref(shp), int(block_frames), float(eps), _ptr(q), _ptr(k),
+                                     _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so), _ptr(no),
+                                     _ptr(w), w.numel(), _stream(dev)))
+    return o, so, no
+
+
+def ls_gdn_frame_forward(q, k, v, alpha, beta, state=None, key_scale=None, out=None, state_out=None,
+                         ws=None):
+    """Frame-wise Gated DeltaNet; returns (o, state_out).
+
+    alpha, beta: [B, H, F] fp32.  key_scale None means 1/sqrt(D*N).
+    """
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F), dev)
+    _f32("state", state, (B, H, D, D), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    shp = _shape(q)
+    need = lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    w = ws if ws is not None else workspace(need, dev)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward(ctypes.byref(shp), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                    _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
+                                    _stream(dev)))
+    return o, so
+
+
+def ls_state_carry(state_src, state_dst, norm_src=None, norm_dst=None, reset: bool = False):
+    """Commit a finished block's state to the carried cache (or zero the cache)."""
+    B, H, D, _ = state_dst.shape
+    dev = state_dst.device
+    _f32("state_dst", state_dst, (B, H, D, D), dev)
+    _f32("state_src", state_src, (B, H, D, D), dev)
+    _f32("norm_src", norm_src, (B, H, D), dev)
+    _f32("norm_dst", norm_dst, (B, H, D), dev)
+    _check(lib.ls_state_carry(B, H, D, _ptr(state_src), _ptr(norm_src), _ptr(state_dst), _ptr(norm_dst),
+                              int(bool(reset)), _stream(dev)))
+    return state_dst
+
+
+def ls_profile_begin():
+    """Start timing every library kernel launch with HIP events."""
+    _check(lib.ls_profile_begin())
+
+
+def ls_profile_end():
+    """Stop timing; returns {kernel: (launches, total_ms)} in first-launch order."""
+    stats = (ls_kernel_stat * 64)()
+    n = lib.ls_profile_end(stats, 64)
+    if n < 0:
+        raise LinscanError(9, "profiling events failed")
+    return {stats[i].name.decode(): (stats[i].launches, stats[i].total_ms) for i in range(min(n, 64))}
+
+
+relu_block_forward = ls_relu_block_forward
+gdn_frame_forward = ls_gdn_frame_forward
+state_carry = ls_state_carry

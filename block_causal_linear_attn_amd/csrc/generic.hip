@@ -1,0 +1,211 @@
+// generic.hip -- fp32-accumulating VALU kernels of both scans for every
+// supported (dtype, head dim) pair.  They carry the fp32 token path (whose
+// outputs must track the fp64 reference to ~1e-5) and the bf16 head dims that
+// have no MFMA specialisation.  Straightforward LDS-tiled loops: a workgroup
+// owns one (frame, token chunk) and each thread owns fixed entries of the
+// D x D result.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace linscan {
+
+namespace {
+
+constexpr int GT = 32;  // tokens per LDS tile
+
+// dS = sum v phi(k)^T, dz = sum phi(k) over one token chunk (RELU), or
+// G = c2 sum k k^T, U = c sum v k^T (GDN).  Output row of `partial`.
+// Entries of the D x D result per thread; larger results are split over
+// gridDim.y workgroups that share the token chunk.
+template <int D>
+struct SummarySplit {
+  static constexpr int kEPT = (D * D + 255) / 256 < 16 ? (D * D + 255) / 256 : 16;
+  static constexpr int kParts = (D * D + 256 * kEPT - 1) / (256 * kEPT);
+};
+
+template <typename T, int D, bool RELU>
+__global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, const T* __restrict__ v,
+                                                   float* __restrict__ partial, float c, float c2,
+                                                   int N, int nc, int chunk) {
+  constexpr int EPT = SummarySplit<D>::kEPT;
+  __shared__ float ks[GT][D + 1];
+  __shared__ float vs[GT][D + 1];
+  const int tid = threadIdx.x;
+  const int e0 = blockIdx.y * 256 * EPT;  // first entry owned by this workgroup
+  const long wg = blockIdx.x;
+  const long bhf = wg / nc;
+  const int n0 = (int)(wg % nc) * chunk;
+  const int n1 = min(N, n0 + chunk);
+  const T* kf = k + (size_t)bhf * N * D;
+  const T* vf = v + (size_t)bhf * N * D;
+
+  float a1[EPT], a2[EPT];
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) a1[x] = a2[x] = 0.0f;
+  float az = 0.0f;
+
+  for (int t0 = n0; t0 < n1; t0 += GT) {
+    for (int e = tid; e < GT * D; e += 256) {
+      const int tok = e / D, d = e % D;
+      const int n = t0 + tok;
+      float kk = 0.0f, vv = 0.0f;
+      if (n < n1) {
+        kk = Elem<T>::load(kf, (size_t)n * D + d);
+        vv = Elem<T>::load(vf, (size_t)n * D + d);
+      }
+      ks[tok][d] = RELU ? relu_f32(kk) : kk;
+      vs[tok][d] = vv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int e = e0 + tid + 256 * x;
+      if (e < D * D) {
+        const int i = e / D, j = e % D;
+        for (int tok = 0; tok < GT; ++tok) {
+          const float kj = ks[tok][j];
+          a1[x] = fmaf(vs[tok][i], kj, a1[x]);
+          if (!RELU) a2[x] = fmaf(ks[tok][i], kj, a2[x]);
+        }
+      }
+    }
+    if (RELU && blockIdx.y == 0 && tid < D)
+      for (int tok = 0; tok < GT; ++tok) az += ks[tok][tid];
+    __syncthreads();
+  }
+
+  if (RELU) {
+    float* dst = partial + (size_t)wg * (D * D + D);
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int e = e0 + tid + 256 * x;
+      if (e < D * D) dst[e] = a1[x];
+    }
+    if (blockIdx.y == 0 && tid < D) dst[D * D + tid] = az;
+  } else {
+    float* Gd = partial + (size_t)wg * 2 * D * D;
+    float* Ud = Gd + D * D;
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int e = e0 + tid + 256 * x;
+      if (e < D * D) {
+        Gd[e] = c2 * a2[x];
+        Ud[e] = c * a1[x];
+      }
+    }
+  }
+}
+
+// o = S_f phi(q) / (z_f . phi(q) + eps) (RELU) or o = S_f q, one token per
+// group of D threads.  `state` points at S_f (fp32) followed, for RELU, by z_f.
+template <typename T, int D, bool RELU>
+__global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __restrict__ o,
+                                                  const float* __restrict__ states, size_t state_stride,
+                                                  float eps, int N, int nco, int chunk) {
+  constexpr int SLOTS = 256 / D;
+  __shared__ float Ss[D][D + 1];
+  __shared__ float zs[D];
+  __shared__ float qs[SLOTS][D];
+  const int tid = threadIdx.x;
+  const long wg = blockIdx.x;
+  const long bhf = wg / nco;
+  const int n0 = (int)(wg % nco) * chunk;
+  const int n1 = min(N, n0 + chunk);
+  const float* Sf = states + (size_t)bhf * state_stride;
+  for (int e = tid; e < D * D; e += 256) Ss[e / D][e % D] = Sf[e];
+  if (RELU && tid < D) zs[tid] = Sf[D * D + tid];
+  const int slot = tid / D, i = tid % D;
+  const T* qf = q + (size_t)bhf * N * D;
+  T* of = o + (size_t)bhf * N * D;
+  for (int t0 = n0; t0 < n1; t0 += SLOTS) {
+    __syncthreads();
+    if (slot < SLOTS) {
+      const int n = t0 + slot;
+      float x = (n < n1) ? Elem<T>::load(qf, (size_t)n * D + i) : 0.0f;
+      qs[slot][i] = RELU ? relu_f32(x) : x;
+    }
+    __syncthreads();
+    if (slot < SLOTS && t0 + slot < n1) {
+      float num = 0.0f, den = 0.0f;
+      for (int j = 0; j < D; ++j) {
+        const float qj = qs[slot][j];
+        num = fmaf(Ss[i][j], qj, num);
+        if (RELU) den = fmaf(zs[j], qj, den);
+      }
+      const float out = RELU ? num / (den + eps) : num;
+      Elem<T>::store(of, (size_t)(t0 + slot) * D + i, out);
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t summary_launch(bool relu, const void* k, const void* v, float* partial, float c, float c2,
+                          long bhf, int N, int nc, int chunk, hipStream_t st) {
+  dim3 grid((unsigned)(bhf * nc), SummarySplit<D>::kParts), block(256);
+  if (relu)
+    hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)k, (const T*)v,
+                       partial, c, c2, N, nc, chunk);
+  else
+    hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)k, (const T*)v,
+                       partial, c, c2, N, nc, chunk);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t output_launch(bool relu, const void* q, void* o, const float* states, size_t stride,
+                         float eps, long bhf, int N, int nco, int chunk, hipStream_t st) {
+  dim3 grid((unsigned)(bhf * nco)), block(256);
+  if (relu)
+    hipLaunchKernelGGL((gen_output<T, D, true>), grid, block, 0, st, (const T*)q, (T*)o, states,
+                       stride, eps, N, nco, chunk);
+  else
+    hipLaunchKernelGGL((gen_output<T, D, false>), grid, block, 0, st, (const T*)q, (T*)o, states,
+                       stride, eps, N, nco, chunk);
+  return hipGetLastError();
+}
+
+#define LINSCAN_FOR_EACH_D(X) X(16) X(32) X(48) X(64) X(80) X(96) X(112) X(128)
+
+template <typename T>
+hipError_t summary_dispatch(int D, bool relu, const void* k, const void* v, float* partial, float c,
+                            float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
+  switch (D) {
+#define CASE(d) \
+  case d: return summary_launch<T, d>(relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
+    LINSCAN_FOR_EACH_D(CASE)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+hipError_t output_dispatch(int D, bool relu, const void* q, void* o, const float* states, size_t stride,
+                           float eps, long bhf, int N, int nco, int chunk, hipStream_t st) {
+  switch (D) {
+#define CASE(d) \
+  case d: return output_launch<T, d>(relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
+    LINSCAN_FOR_EACH_D(CASE)
+#undef CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_summary_generic(int D, int dtype, bool relu, const void* k, const void* v,
+                                  float* partial, float c, float c2, long bhf, int N, int nc, int chunk,
+                                  hipStream_t st) {
+  if (dtype == DT_F32)
+    return summary_dispatch<float>(D, relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
+  return summary_dispatch<uint16_t>(D, relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
+}
+
+hipError_t launch_output_generic(int D, int dtype, bool relu, const void* q, void* o,
+                                 const float* states, size_t stride, float eps, long bhf, int N,
+                                 int nco, int chunk, hipStream_t st) {
+  if (dtype == DT_F32)
+    return output_dispatch<float>(D, relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
+  return output_dispatch<uint16_t>(D, relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
+}
+
+}  // namespace linscan

@@ -1,0 +1,436 @@
+// linscan_api.cpp -- the C ABI of liblinscan: argument checks, workspace
+// planning and kernel dispatch.  Every check runs before the first launch, so
+// a rejected call enqueues nothing and touches no output.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/linscan.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ls_status fail(ls_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ls_status ok() { return LS_OK; }
+
+bool supported_d(int D) {
+  return D == 16 || D == 32 || D == 48 || D == 64 || D == 80 || D == 96 || D == 112 || D == 128;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Dims {
+  long bh = 0;      // B*H
+  long bhf = 0;     // B*H*F
+  size_t elems = 0; // B*H*F*N*D
+  size_t esize = 0; // bytes per token element
+};
+
+ls_status check_shape(const ls_shape* s, Dims* d) {
+  if (!s) return fail(LS_ERR_NULL_POINTER, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->F < 0 || s->N < 0)
+    return fail(LS_ERR_BAD_SHAPE, "negative dimension (B=%d H=%d F=%d N=%d)", s->B, s->H, s->F, s->N);
+  if (!supported_d(s->D))
+    return fail(LS_ERR_UNSUPPORTED_HEAD_DIM, "head dim D=%d not in {16,32,48,64,80,96,112,128}", s->D);
+  if (s->dtype != LS_DTYPE_FP32 && s->dtype != LS_DTYPE_BF16)
+    return fail(LS_ERR_BAD_DTYPE, "dtype %d is neither LS_DTYPE_FP32 nor LS_DTYPE_BF16", s->dtype);
+  // sizes must stay well inside 2^62 elements and 2^31 workgroups
+  const double el = (double)s->B * s->H * s->F * s->N * s->D;
+  const double bhf = (double)s->B * s->H * s->F;
+  if (el > 4.0e18 || bhf > 1.0e9)
+    return fail(LS_ERR_BAD_SHAPE, "shape too large (B*H*F*N*D = %.3g)", el);
+  d->bh = (long)s->B * s->H;
+  d->bhf = d->bh * s->F;
+  d->elems = (size_t)d->bhf * s->N * s->D;
+  d->esize = s->dtype == LS_DTYPE_BF16 ? 2 : 4;
+  return LS_OK;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+// [a, a+na) and [b, b+nb) overlap (empty ranges never do)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Token chunking: enough workgroups to fill 256 CUs several times over, with
+// chunks of at least `min_chunk` tokens (a multiple of `quantum`).
+void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, int* nc, int* chunk) {
+  if (N <= 0 || frames <= 0) {
+    *nc = 1;
+    *chunk = N > 0 ? N : 1;
+    return;
+  }
+  long want = (target_wg + frames - 1) / frames;
+  long max_nc = N / min_chunk;
+  if (max_nc < 1) max_nc = 1;
+  if (want < 1) want = 1;
+  if (want > max_nc) want = max_nc;
+  int ch = (int)((N + want - 1) / want);
+  ch = (ch + quantum - 1) / quantum * quantum;
+  *chunk = ch;
+  *nc = (N + ch - 1) / ch;
+}
+
+struct ReluPlan {
+  bool mfma;
+  int nc, chunk, nco, chunko;
+  size_t partial_off, prefix_off, bytes;
+};
+
+ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
+  ReluPlan p;
+  p.mfma = linscan::relu_has_mfma(s->D, s->dtype);
+  plan_chunks(d.bhf, s->N, 2048, 512, 64, &p.nc, &p.chunk);
+  plan_chunks(d.bhf, s->N, 2048, 256, 128, &p.nco, &p.chunko);
+  const size_t out = (size_t)s->D * s->D + s->D;
+  p.partial_off = 0;
+  p.prefix_off = align_up((size_t)d.bhf * p.nc * out * sizeof(float), 256);
+  p.bytes = align_up(p.prefix_off + (size_t)d.bhf * out * sizeof(float), 256);
+  return p;
+}
+
+struct GdnPlan {
+  bool mfma;
+  int nc, chunk, nco, chunko;
+  size_t partial_off, states_off, bytes;
+};
+
+GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
+  GdnPlan p;
+  p.mfma = linscan::gdn_has_mfma(s->D, s->dtype);
+  // a chunk's G/U partials are 8 D^2 bytes: keep chunks long enough that they
+  // stay small next to the chunk's own key/value bytes
+  plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
+  plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
+  const size_t dd = (size_t)s->D * s->D;
+  p.partial_off = 0;
+  p.states_off = align_up((size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
+  p.bytes = align_up(p.states_off + (size_t)d.bhf * dd * sizeof(float), 256);
+  return p;
+}
+
+ls_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return LS_OK;
+}
+
+// ---- optional per-kernel event timing (diagnostics) ----------------------
+struct ProfRecord {
+  const char* name;
+  hipEvent_t start, stop;
+};
+constexpr size_t kMaxProfRecords = 65536;
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (which enqueues one kernel on `st`) between two events when
+// profiling is on.
+template <typename Fn>
+hipError_t timed(const char* name, hipStream_t st, Fn&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_prof_on && g_prof_records.size() < kMaxProfRecords) {
+      a = prof_event();
+      b = prof_event();
+    }
+  }
+  if (a && b) hipEventRecord(a, st);
+  hipError_t e = launch();
+  if (a && b) {
+    hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_records.push_back({name, a, b});
+  }
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ls_version(void) { return LINSCAN_VERSION; }
+
+ls_status ls_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = true;
+  return LS_OK;
+}
+
+int ls_profile_end(ls_kernel_stat* stats, int max_stats) {
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    recs.swap(g_prof_records);
+  }
+  std::vector<ls_kernel_stat> agg;
+  int rc = 0;
+  for (const ProfRecord& r : recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      rc = -1;
+    size_t i = 0;
+    while (i < agg.size() && strcmp(agg[i].name, r.name) != 0) ++i;
+    if (i == agg.size()) {
+      ls_kernel_stat s0;
+      memset(&s0, 0, sizeof(s0));
+      snprintf(s0.name, sizeof(s0.name), "%s", r.name);
+      agg.push_back(s0);
+    }
+    agg[i].launches += 1;
+    agg[i].total_ms += ms;
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (const ProfRecord& r : recs) {
+      g_prof_pool.push_back(r.start);
+      g_prof_pool.push_back(r.stop);
+    }
+  }
+  for (size_t i = 0; i < agg.size() && (int)i < max_stats; ++i) stats[i] = agg[i];
+  return rc < 0 ? -1 : (int)agg.size();
+}
+
+const char* ls_last_error(void) { return g_last_error.c_str(); }
+
+const char* ls_status_string(ls_status st) {
+  switch (st) {
+    case LS_OK: return "ok";
+    case LS_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case LS_ERR_BAD_SHAPE: return "invalid shape";
+    case LS_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension";
+    case LS_ERR_BAD_DTYPE: return "unsupported dtype";
+    case LS_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case LS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LS_ERR_BAD_PARAM: return "invalid scalar parameter";
+    case LS_ERR_ALIASING: return "output overlaps an input";
+    case LS_ERR_HIP: return "HIP runtime error";
+    case LS_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+size_t ls_relu_block_workspace_size(const ls_shape* s, int block_frames) {
+  Dims d;
+  if (check_shape(s, &d) != LS_OK || block_frames < 1) return 0;
+  return relu_plan(s, d).bytes;
+}
+
+size_t ls_gdn_frame_workspace_size(const ls_shape* s) {
+  Dims d;
+  if (check_shape(s, &d) != LS_OK) return 0;
+  return gdn_plan(s, d).bytes;
+}
+
+ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, const void* q,
+                                const void* k, const void* v, void* o, const float* state_in,
+                                const float* norm_in, float* state_out, float* norm_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  ls_status st = check_shape(s, &d);
+  if (st != LS_OK) return st;
+  if (block_frames < 1) return fail(LS_ERR_BAD_PARAM, "block_frames=%d < 1", block_frames);
+  if (!(eps > 0.0f) || !isfinite(eps)) return fail(LS_ERR_BAD_PARAM, "eps=%g must be finite and > 0", (double)eps);
+  const int D = s->D;
+  const size_t tok_bytes = d.elems * d.esize;
+  const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
+  const size_t norm_bytes = (size_t)d.bh * D * sizeof(float);
+  if (d.bh == 0) return ok();
+  if (tok_bytes > 0 && (!q || !k || !v || !o))
+    return fail(LS_ERR_NULL_POINTER, "q, k, v and o are required when F*N > 0");
+  if ((tok_bytes && (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o))) ||
+      misaligned(state_in) || misaligned(norm_in) || misaligned(state_out) || misaligned(norm_out) ||
+      misaligned(workspace))
+    return fail(LS_ERR_MISALIGNED, "token tensors, states and workspace must be 16-byte aligned");
+  // outputs may not overlap inputs, except the documented in-place state update
+  const void* ins[5] = {q, k, v, state_in, norm_in};
+  const size_t in_n[5] = {tok_bytes, tok_bytes, tok_bytes, state_in ? state_bytes : 0,
+                          norm_in ? norm_bytes : 0};
+  for (int i = 0; i < 5; ++i) {
+    if (overlap(o, tok_bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "o overlaps an input");
+    if (state_out && !(i == 3 && state_out == state_in) && overlap(state_out, state_bytes, ins[i], in_n[i]))
+      return fail(LS_ERR_ALIASING, "state_out overlaps an input other than state_in");
+    if (norm_out && !(i == 4 && norm_out == norm_in) && overlap(norm_out, norm_bytes, ins[i], in_n[i]))
+      return fail(LS_ERR_ALIASING, "norm_out overlaps an input other than norm_in");
+  }
+  if (overlap(o, tok_bytes, state_out, state_out ? state_bytes : 0) ||
+      overlap(o, tok_bytes, norm_out, norm_out ? norm_bytes : 0) ||
+      overlap(state_out, state_out ? state_bytes : 0, norm_out, norm_out ? norm_bytes : 0))
+    return fail(LS_ERR_ALIASING, "outputs overlap each other");
+
+  hipStream_t hs = (hipStream_t)stream;
+  if (s->F == 0 || s->N == 0) {
+    // no tokens: the state passes through unchanged
+    if (state_out && state_out != state_in)
+      if ((st = hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, state_in == nullptr, hs),
+                          "state copy")) != LS_OK)
+        return st;
+    if (norm_out && norm_out != norm_in)
+      if ((st = hip_check(linscan::launch_carry(norm_in, norm_out, norm_bytes / 4, norm_in == nullptr, hs),
+                          "norm copy")) != LS_OK)
+        return st;
+    return ok();
+  }
+  const ReluPlan p = relu_plan(s, d);
+  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", p.bytes);
+  if (workspace_bytes < p.bytes)
+    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  for (int i = 0; i < 5; ++i)
+    if (overlap(workspace, p.bytes, ins[i], in_n[i]))
+      return fail(LS_ERR_ALIASING, "workspace overlaps an input");
+  if (overlap(workspace, p.bytes, o, tok_bytes) || overlap(workspace, p.bytes, state_out, state_out ? state_bytes : 0) ||
+      overlap(workspace, p.bytes, norm_out, norm_out ? norm_bytes : 0))
+    return fail(LS_ERR_ALIASING, "workspace overlaps an output");
+
+  char* ws = (char*)workspace;
+  float* partial = (float*)(ws + p.partial_off);
+  float* prefix = (float*)(ws + p.prefix_off);
+  if ((st = hip_check(timed("relu_summary", hs, [&] { return linscan::launch_relu_summary(D, p.mfma, s->dtype, k, v, partial, d.bhf, s->N,
+                                                   p.nc, p.chunk, hs); }), "relu summary")) != LS_OK)
+    return st;
+  if ((st = hip_check(timed("relu_prefix", hs, [&] { return linscan::launch_relu_prefix(D, partial, state_in, norm_in, prefix, state_out, norm_out,
+                                                  d.bh, s->F, p.nc, block_frames, hs); }), "relu prefix")) != LS_OK)
+    return st;
+  if ((st = hip_check(timed("relu_output", hs, [&] { return linscan::launch_relu_output(D, p.mfma, s->dtype, q, o, prefix, eps, d.bhf, s->N,
+                                                  p.nco, p.chunko, hs); }), "relu output")) != LS_OK)
+    return st;
+  return ok();
+}
+
+ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta, void* o,
+                               const float* state_in, float* state_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  Dims d;
+  ls_status st = check_shape(s, &d);
+  if (st != LS_OK) return st;
+  if (!isfinite(key_scale)) return fail(LS_ERR_BAD_PARAM, "key_scale is not finite");
+  const int D = s->D;
+  const size_t tok_bytes = d.elems * d.esize;
+  const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
+  const size_t gate_bytes = (size_t)d.bhf * sizeof(float);
+  if (d.bh == 0) return ok();
+  if (tok_bytes > 0 && (!q || !k || !v || !o))
+    return fail(LS_ERR_NULL_POINTER, "q, k, v and o are required when F*N > 0");
+  if (s->F > 0 && (!alpha || !beta)) return fail(LS_ERR_NULL_POINTER, "alpha and beta are required when F > 0");
+  if ((tok_bytes && (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o))) ||
+      misaligned(state_in) || misaligned(state_out) || misaligned(workspace))
+    return fail(LS_ERR_MISALIGNED, "token tensors, states and workspace must be 16-byte aligned");
+  if (((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
+    return fail(LS_ERR_MISALIGNED, "alpha and beta must be 4-byte aligned");
+  const void* ins[6] = {q, k, v, alpha, beta, state_in};
+  const size_t in_n[6] = {tok_bytes, tok_bytes, tok_bytes, gate_bytes, gate_bytes,
+                          state_in ? state_bytes : 0};
+  for (int i = 0; i < 6; ++i) {
+    if (overlap(o, tok_bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "o overlaps an input");
+    if (state_out && !(i == 5 && state_out == state_in) && overlap(state_out, state_bytes, ins[i], in_n[i]))
+      return fail(LS_ERR_ALIASING, "state_out overlaps an input other than state_in");
+  }
+  if (overlap(o, tok_bytes, state_out, state_out ? state_bytes : 0))
+    return fail(LS_ERR_ALIASING, "outputs overlap each other");
+
+  hipStream_t hs = (hipStream_t)stream;
+  if (s->F == 0) {
+    if (state_out && state_out != state_in)
+      return hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, state_in == nullptr, hs),
+                       "state copy");
+    return ok();
+  }
+  const GdnPlan p = gdn_plan(s, d);
+  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", p.bytes);
+  if (workspace_bytes < p.bytes)
+    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  for (int i = 0; i < 6; ++i)
+    if (overlap(workspace, p.bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "workspace overlaps an input");
+  if (overlap(workspace, p.bytes, o, tok_bytes) || overlap(workspace, p.bytes, state_out, state_out ? state_bytes : 0))
+    return fail(LS_ERR_ALIASING, "workspace overlaps an output");
+
+  // keys are scaled by c = 1/sqrt(D*N) unless the caller gives a scale; with
+  // no tokens there is nothing to scale
+  double c = key_scale > 0.0f ? (double)key_scale : (s->N > 0 ? 1.0 / sqrt((double)D * s->N) : 0.0);
+  char* ws = (char*)workspace;
+  float* partial = (float*)(ws + p.partial_off);
+  void* states = ws + p.states_off;
+  if ((st = hip_check(timed("gdn_gram", hs, [&] { return linscan::launch_gdn_gram(D, p.mfma, s->dtype, k, v, partial, (float)c, (float)(c * c),
+                                               d.bhf, s->N, p.nc, p.chunk, hs); }), "gdn gram")) != LS_OK)
+    return st;
+  if ((st = hip_check(timed("gdn_scan", hs, [&] { return linscan::launch_gdn_scan(D, p.mfma, partial, alpha, beta, state_in, states, state_out,
+                                               d.bh, s->F, p.nc, hs); }), "gdn scan")) != LS_OK)
+    return st;
+  if (s->N > 0)
+    if ((st = hip_check(timed("gdn_output", hs, [&] { return linscan::launch_gdn_output(D, p.mfma, s->dtype, q, o, states, d.bhf, s->N, p.nco,
+                                                   p.chunko, hs); }), "gdn output")) != LS_OK)
+      return st;
+  return ok();
+}
+
+ls_status ls_state_carry(int B, int H, int D, const float* state_src, const float* norm_src,
+                         float* state_dst, float* norm_dst, int reset, void* stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0) return fail(LS_ERR_BAD_SHAPE, "negative dimension (B=%d H=%d)", B, H);
+  if (!supported_d(D)) return fail(LS_ERR_UNSUPPORTED_HEAD_DIM, "head dim D=%d unsupported", D);
+  const size_t bh = (size_t)B * H;
+  if (bh == 0) return ok();
+  if (!state_dst) return fail(LS_ERR_NULL_POINTER, "state_dst is NULL");
+  if (!reset && !state_src) return fail(LS_ERR_NULL_POINTER, "state_src is NULL (and reset == 0)");
+  if (misaligned(state_src) || misaligned(state_dst) || misaligned(norm_src) || misaligned(norm_dst))
+    return fail(LS_ERR_MISALIGNED, "states must be 16-byte aligned");
+  const size_t sb = bh * D * D * sizeof(float), nb = bh * D * sizeof(float);
+  const bool with_norm = norm_dst && (reset || norm_src);
+  if (!reset) {
+    if (state_src != state_dst && overlap(state_src, sb, state_dst, sb))
+      return fail(LS_ERR_ALIASING, "state_src and state_dst partially overlap");
+    if (with_norm && norm_src != norm_dst && overlap(norm_src, nb, norm_dst, nb))
+      return fail(LS_ERR_ALIASING, "norm_src and norm_dst partially overlap");
+  }
+  if (with_norm && overlap(state_dst, sb, norm_dst, nb))
+    return fail(LS_ERR_ALIASING, "state_dst and norm_dst overlap");
+  hipStream_t hs = (hipStream_t)stream;
+  ls_status st;
+  if (reset || state_src != state_dst)
+    if ((st = hip_check(timed("state_carry", hs, [&] { return linscan::launch_carry(state_src, state_dst, sb / 4, reset, hs); }), "state carry")) != LS_OK)
+      return st;
+  if (with_norm && (reset || norm_src != norm_dst))
+    if ((st = hip_check(timed("state_carry", hs, [&] { return linscan::launch_carry(norm_src, norm_dst, nb / 4, reset, hs); }), "norm carry")) != LS_OK)
+      return st;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+/*
+ * linscan.h -- C ABI of liblinscan, the block-causal linear-attention scan on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The scan keeps one fixed-size D x D state per (batch, head) and walks the
+ * latent frames of a video in order, so memory does not grow with video
+ * length.  Two update rules are provided:
+ *
+ *  - ReLU linear attention with a cumulative state and normaliser, extended
+ *    block by block and cached between blocks ("SANA-Video: Efficient Video
+ *    Generation with Block Linear Diffusion Transformer", ICLR 2026 oral talk
+ *    transcript, passage on the block KV cache of linear attention; feature
+ *    map ReLU and the rule that a block attends to itself and to earlier
+ *    blocks: the SANA-Video practical guide, section on core mechanisms);
+ *  - frame-wise Gated DeltaNet, one update per latent frame over all of the
+ *    frame's spatial tokens, with decay alpha and update gate beta
+ *    ("SANA-WM: Efficient Minute-Scale World Modeling with Hybrid Linear
+ *    Diffusion Transformer", section 3 Method, hybrid GDN/softmax attention),
+ *    keys scaled by 1/sqrt(D*N) with N the spatial tokens per frame (SANA-WM
+ *    digest, paragraph on stabilising the spatial explosion, which also
+ *    states that this scaling keeps the transition's spectral norm <= 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Token tensors q, k, v, o are contiguous [B][H][F][N][D], D fastest,
+ *    either fp32 or bf16 (ls_shape.dtype); o has the dtype of the inputs and
+ *    bf16 outputs are rounded to nearest even from fp32.
+ *  - The state S is fp32 [B][H][D][D] with S[i][j], i a value dimension and
+ *    j a key dimension, so that a query reads o = S q.  The ReLU normaliser
+ *    z is fp32 [B][H][D].  Gates alpha, beta are fp32 [B][H][F].
+ *  - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent) except
+ *    the ls_shape pointer, which is host memory read during the call.
+ *  - Token tensors, states and the workspace must be 16-byte aligned.
+ *  - Supported head dims: D in {16, 32, 48, 64, 80, 96, 112, 128}.
+ *  - A call only enqueues work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns; results are ready once the stream reaches that
+ *    point.  All argument checks run on the host before anything is
+ *    enqueued: on any error nothing is launched, no output is touched and
+ *    the status names the reason (ls_last_error() gives details).  A device
+ *    fault surfaces at the caller's next synchronisation.
+ *  - The caller owns every buffer, including the workspace.  The library
+ *    never allocates device memory and carries nothing from one call to the
+ *    next (the optional profiling session below only keeps HIP events).
+ *    Calls on different streams are safe when their outputs and workspaces
+ *    differ.
+ *  - A dimension of size zero is legal: B*H == 0 does nothing; F == 0 copies
+ *    the initial state to the output state; N == 0 gives frames without
+ *    tokens (the ReLU state is unchanged, the GDN state still decays).
+ */
+#ifndef LINSCAN_H
+#define LINSCAN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LINSCAN_VERSION 100 /* major*100 + minor */
+
+typedef enum {
+  LS_OK = 0,
+  LS_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+  LS_ERR_BAD_SHAPE = 2,           /* a negative dimension, or sizes overflow */
+  LS_ERR_UNSUPPORTED_HEAD_DIM = 3,
+  LS_ERR_BAD_DTYPE = 4,
+  LS_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned */
+  LS_ERR_WORKSPACE_TOO_SMALL = 6,
+  LS_ERR_BAD_PARAM = 7,           /* eps <= 0, block_frames < 1, non-finite scale ... */
+  LS_ERR_ALIASING = 8,            /* an output overlaps an input it must not overlap */
+  LS_ERR_HIP = 9,                 /* a HIP runtime call or kernel launch failed */
+  LS_ERR_INTERNAL = 10
+} ls_status;
+
+typedef enum { LS_DTYPE_FP32 = 0, LS_DTYPE_BF16 = 1 } ls_dtype;
+
+/* Shape of one call.  F is the number of frames handled by THIS call. */
+typedef struct {
+  int B, H, F, N, D;
+  int dtype; /* ls_dtype of q, k, v, o */
+} ls_shape;
+
+/*
+ * Workspace bytes ls_relu_block_forward needs for `shape` and `block_frames`
+ * (0 if the shape is invalid).  The size depends on the shape only.
+ */
+size_t ls_relu_block_workspace_size(const ls_shape* shape, int block_frames);
+
+/*
+ * ReLU block-causal linear attention over the F frames of one call.
+ *
+ * Frames are grouped into blocks of `block_frames` consecutive frames,
+ * counted from frame 0 of this call (1 = frame-causal).  With phi = ReLU
+ * (phi(x) = 0 when x has its sign bit set, else x), the state and normaliser
+ * start from (state_in, norm_in) (zeros when NULL).  For each block in
+ * order, every token of the block adds v phi(k)^T to S and phi(k) to z; then
+ * every token of the block reads
+ *     o = (S phi(q)) / (z . phi(q) + eps),
+ * i.e. a block sees itself and all earlier blocks.  The final (S, z) are
+ * written to (state_out, norm_out) when those are non-NULL; state_out may
+ * equal state_in and norm_out may equal norm_in (in place), other overlaps
+ * between outputs and inputs are rejected with LS_ERR_ALIASING.
+ *
+ *   q, k, v   [B][H][F][N][D] inputs (dtype of shape)
+ *   o         [B][H][F][N][D] output (may not be NULL unless N*F == 0)
+ *   eps       > 0 (1e-6 in the video workloads)
+ *   workspace >= ls_relu_block_workspace_size(shape, block_frames) bytes,
+ *             contents ignored on entry and undefined on return.
+ */
+ls_status ls_relu_block_forward(const ls_shape* shape, int block_frames, float eps,
+                                const void* q, const void* k, const void* v, void* o,
+                                const float* state_in, const float* norm_in,
+                                float* state_out, float* norm_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes ls_gdn_frame_forward needs for `shape` (0 if invalid). */
+size_t ls_gdn_frame_workspace_size(const ls_shape* shape);
+
+/*
+ * Frame-wise Gated DeltaNet over the F frames of one call.
+ *
+ * With c = key_scale when key_scale > 0, else c = 1/sqrt(D*N), and S starting
+ * from state_in (zeros when NULL), each frame f in order does
+ *     G = sum_n (c k_n)(c k_n)^T,   U = sum_n v_n (c k_n)^T   (frame f's tokens)
+ *     S <- alpha_f S (I - beta_f G) + beta_f U
+ *     o_n = S q_n   for every token n of frame f (the updated state).
+ * No feature map or normalisation is applied to q, k or v; callers that want
+ * unit-norm keys normalise them beforehand.  alpha and beta are not range
+ * checked on the device; their intended domain is [0, 1].
+ *
+ *   alpha, beta [B][H][F] fp32
+ *   o           [B][H][F][N][D] output
+ *   state_in    [B][H][D][D] or NULL (zeros)
+ *   state_out   [B][H][D][D] or NULL (not written); may equal state_in
+ *   workspace   >= ls_gdn_frame_workspace_size(shape) bytes
+ */
+ls_status ls_gdn_frame_forward(const ls_shape* shape, float key_scale,
+                               const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, void* o,
+                               const float* state_in, float* state_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-autoregressive hand-off of the carried state: the state a finished
+ * block leaves behind becomes the cache the next block starts from (SANA-Video
+ * talk, block KV cache passage: the state of block i is cached and block i+1
+ * adds its own contribution to it).
+ *
+ * reset == 0: copy state_src -> state_dst ([B][H][D][D] fp32) and, when both
+ *             norm pointers are non-NULL, norm_src -> norm_dst ([B][H][D]).
+ * reset != 0: zero state_dst (and norm_dst when non-NULL); the sources are
+ *             ignored and may be NULL.
+ * Source and destination may not partially overlap (identical is a no-op).
+ */
+ls_status ls_state_carry(int B, int H, int D, const float* state_src, const float* norm_src,
+                         float* state_dst, float* norm_dst, int reset, void* stream);
+
+/*
+ * Diagnostics: per-kernel timing with HIP events.
+ *
+ * Between ls_profile_begin() and ls_profile_end(), every kernel the library
+ * launches (from any thread, on any stream) is bracketed by two HIP events
+ * recorded on the stream it runs on.  ls_profile_end() waits for those
+ * events, fills up to `max_stats` entries (one per kernel kind, in first-
+ * launch order) with the launch count and the summed event-to-event time,
+ * and returns the number of kernel kinds seen (or -1 on a HIP error).  The
+ * event records add a few microseconds per launch, so time throughput with
+ * profiling off.  At most 65536 launches are recorded per session.
+ */
+typedef struct {
+  char name[32];
+  int launches;
+  double total_ms;
+} ls_kernel_stat;
+
+ls_status ls_profile_begin(void);
+int ls_profile_end(ls_kernel_stat* stats, int max_stats);
+
+/* Static description of a status code. */
+const char* ls_status_string(ls_status status);
+
+/* Details of the last non-OK status returned on the calling thread ("" if none). */
+const char* ls_last_error(void);
+
+/* LINSCAN_VERSION of the built library. */
+int ls_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINSCAN_H */

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/linscan.h declares, and rejects bad arguments on the host before any
+HIP call (fake, never-dereferenced device addresses are enough for that)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linscan.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_causal_linear_attn_amd import build as b
+    srcs = b.sources() + [HEADER]
+    if not os.path.exists(b.LIB) or os.path.getmtime(b.LIB) < max(os.path.getmtime(s) for s in srcs):
+        b.build()
+    from block_causal_linear_attn_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ls_relu_block_forward", "ls_gdn_frame_forward", "ls_state_carry",
+              "ls_relu_block_workspace_size", "ls_gdn_frame_workspace_size",
+              "ls_status_string", "ls_last_error", "ls_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(lib.EXPORTS) == set(declared_functions())
+    assert lib.lib.ls_version() == 100
+
+
+def _shape(lib, B=1, H=2, F=3, N=64, D=32, dtype=1):
+    return lib.ls_shape(B, H, F, N, D, dtype)
+
+
+A = 1 << 32  # fake 16-byte aligned device addresses, far apart
+P = [ctypes.c_void_p(A * (i + 1)) for i in range(16)]
+
+
+def _relu(lib, shp, eps=1e-6, bf=1, q=P[0], k=P[1], v=P[2], o=P[3], si=None, ni=None, so=P[4],
+          no=P[5], ws=P[6], wsb=1 << 40):
+    return lib.lib.ls_relu_block_forward(ctypes.byref(shp), bf, eps, q, k, v, o, si, ni, so, no, ws,
+                                         wsb, None)
+
+
+def _gdn(lib, shp, scale=0.0, q=P[0], k=P[1], v=P[2], a=P[7], b=P[8], o=P[3], si=None, so=P[4],
+         ws=P[6], wsb=1 << 40):
+    return lib.lib.ls_gdn_frame_forward(ctypes.byref(shp), scale, q, k, v, a, b, o, si, so, ws, wsb, None)
+
+
+def test_validation_errors_relu(lib):
+    assert _relu(lib, _shape(lib, D=24)) == 3
+    assert _relu(lib, _shape(lib, dtype=7)) == 4
+    assert _relu(lib, _shape(lib, N=-1)) == 2
+    assert _relu(lib, _shape(lib), eps=0.0) == 7
+    assert _relu(lib, _shape(lib), eps=float("nan")) == 7
+    assert _relu(lib, _shape(lib), bf=0) == 7
+    assert _relu(lib, _shape(lib), q=None) == 1
+    assert _relu(lib, _shape(lib), k=ctypes.c_void_p(A + 8)) == 5
+    assert _relu(lib, _shape(lib), o=P[0]) == 8                      # o aliases q
+    assert _relu(lib, _shape(lib), so=P[1]) == 8                     # state_out inside k
+    assert _relu(lib, _shape(lib), ws=None) == 1
+    shp = _shape(lib)
+    need = lib.lib.ls_relu_block_workspace_size(ctypes.byref(shp), 1)
+    assert need > 0
+    assert _relu(lib, shp, wsb=need - 1) == 6
+    assert "workspace" in lib.lib.ls_last_error().decode()
+    assert lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, D=24)), 1) == 0
+
+
+def test_validation_errors_gdn(lib):
+    assert _gdn(lib, _shape(lib, D=100)) == 3
+    assert _gdn(lib, _shape(lib), scale=float("inf")) == 7
+    assert _gdn(lib, _shape(lib), a=None) == 1
+    assert _gdn(lib, _shape(lib), b=ctypes.c_void_p(A * 9 + 2)) == 5
+    assert _gdn(lib, _shape(lib), o=P[2]) == 8
+    assert _gdn(lib, _shape(lib), so=P[7]) == 8                      # state_out over alpha
+    shp = _shape(lib, D=128)
+    need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    assert need > 0
+    assert _gdn(lib, shp, wsb=need - 1) == 6
+
+
+def test_in_place_state_is_not_an_aliasing_error(lib):
+    """state_out == state_in is allowed; the call then fails only on the workspace check."""
+    shp = _shape(lib)
+    assert _relu(lib, shp, si=P[9], ni=P[10], so=P[9], no=P[10], wsb=1) == 6
+    assert _gdn(lib, shp, si=P[9], so=P[9], wsb=1) == 6
+
+
+def test_carry_validation(lib):
+    c = lib.lib.ls_state_carry
+    assert c(1, 1, 24, P[0], None, P[1], None, 0, None) == 3
+    assert c(1, 1, 32, None, None, P[1], None, 0, None) == 1
+    assert c(1, 1, 32, P[0], None, None, None, 0, None) == 1
+    assert c(1, 1, 32, ctypes.c_void_p(A + 4), None, P[1], None, 0, None) == 5
+    assert c(1, 1, 32, ctypes.c_void_p(A), None, ctypes.c_void_p(A + 16), None, 0, None) == 8
+    assert c(0, 1, 32, None, None, None, None, 0, None) == 0           # nothing to do
+
+
+def test_status_strings(lib):
+    for st in range(11):
+        assert lib.lib.ls_status_string(st).decode()

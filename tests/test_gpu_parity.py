@@ -1,0 +1,260 @@
+"""GPU parity of liblinscan against the fp64 oracle (needs an MI355X).
+
+Bar (written here, applied per tensor with the floor-relative measure of
+tests/metrics.py):
+  bf16 tokens: outputs <= 2e-2, final state <= 1e-2 (floor 1e-3 * max|y|)
+  fp32 tokens: outputs and state <= 1e-5 (normwise: floor max|y|)
+Inputs come from block_causal_linear_attn_amd.inputs on the CPU (small cases)
+or on the GPU (full-size workloads); the oracle sees exactly the values the
+GPU library sees.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from metrics import FLOOR, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-2), "fp32": (1e-5, 1e-5)}
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def ls():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    from block_causal_linear_attn_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def gen():
+    from block_causal_linear_attn_amd import inputs
+    return inputs
+
+
+def _dev(x):
+    return {k: t.to(DEV) for k, t in x.items()}
+
+
+def _rand_state(B, H, D, seed, scale=1.0, norm=False):
+    g = torch.Generator().manual_seed(seed)
+    S = scale * torch.randn((B, H, D, D), generator=g)
+    if norm:
+        z = torch.rand((B, H, D), generator=g) * scale * D
+        return S, z
+    return S
+
+
+def check(name, got, want, tol, dt="bf16"):
+    err = max_rel_err(got, want, FLOOR[dt])
+    print("%-40s max rel err %.3e (tol %.0e, floor %g)" % (name, err, tol, FLOOR[dt]), flush=True)
+    assert err <= tol, (name, err)
+
+
+# --------------------------------------------------------------------------- ReLU
+RELU_CASES = [
+    # (B, H, F, N, D, dtype, block_frames, with_state)
+    (1, 2, 4, 16, 16, "fp32", 1, False),        # the tiny workload's shape
+    (1, 3, 5, 333, 32, "bf16", 1, True),        # MFMA path, ragged token count
+    (2, 2, 3, 700, 32, "bf16", 1, False),       # several token chunks per frame
+    (1, 2, 4, 200, 64, "bf16", 1, True),        # MFMA path, D = 64
+    (1, 2, 3, 97, 112, "bf16", 1, True),        # generic bf16 path at the pages' head dim
+    (1, 2, 3, 50, 16, "bf16", 1, False),        # generic bf16, D = 16
+    (1, 2, 7, 40, 32, "bf16", 3, True),         # blocks of 3 frames (ragged last block)
+    (1, 2, 3, 70, 48, "fp32", 2, True),         # generic fp32
+    (1, 1, 2, 33, 128, "fp32", 1, True),        # generic fp32, D = 128
+    (1, 2, 1, 1, 32, "bf16", 1, True),          # single token
+]
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,bf,with_state", RELU_CASES)
+def test_relu_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, bf, with_state):
+    x = gen.relu_inputs(B, H, F, N, D, dt, seed=11, part=N)
+    S0 = z0 = None
+    if with_state:
+        S0, z0 = _rand_state(B, H, D, 5, scale=4.0, norm=True)
+    xd = _dev(x)
+    o, S, z = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"],
+                                       None if S0 is None else S0.to(DEV),
+                                       None if z0 is None else z0.to(DEV), block_frames=bf)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], S0, z0, block_frames=bf)
+    to, ts = TOL[dt]
+    tag = "relu B%d H%d F%d N%d D%d %s bf%d" % (B, H, F, N, D, dt, bf)
+    check(tag + " o", o, ro, to, dt)
+    check(tag + " S", S, rS, ts, dt)
+    check(tag + " z", z, rz, ts, dt)
+
+
+# --------------------------------------------------------------------------- GDN
+GDN_CASES = [
+    # (B, H, F, N, D, dtype, l2_keys, with_state)
+    (1, 2, 4, 16, 16, "fp32", False, False),    # the tiny workload's shape
+    (1, 2, 6, 300, 128, "bf16", True, True),    # MFMA path, ragged token count
+    (2, 1, 3, 920, 128, "bf16", True, False),   # the 720p token count
+    (1, 2, 3, 97, 112, "bf16", True, True),     # generic bf16 at the pages' head dim
+    (1, 2, 4, 64, 64, "bf16", True, False),     # generic bf16, D = 64
+    (1, 2, 3, 40, 32, "fp32", False, True),     # generic fp32, raw keys
+    (1, 1, 2, 45, 128, "fp32", True, True),     # generic fp32, D = 128
+    (1, 2, 2, 1, 128, "bf16", True, True),      # single token per frame
+]
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,l2,with_state", GDN_CASES)
+def test_gdn_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, l2, with_state):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=13, part=N, alpha_mu=3.0 if l2 else 2.0, l2_keys=l2)
+    S0 = _rand_state(B, H, D, 6, scale=0.5) if with_state else None
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
+                                   None if S0 is None else S0.to(DEV))
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0)
+    to, ts = TOL[dt]
+    tag = "gdn B%d H%d F%d N%d D%d %s" % (B, H, F, N, D, dt)
+    check(tag + " o", o, ro, to, dt)
+    check(tag + " S", S, rS, ts, dt)
+
+
+def test_gdn_explicit_key_scale(ls, gen, oracle_mod):
+    x = gen.gdn_inputs(1, 2, 3, 64, 128, "bf16", seed=14, l2_keys=True)
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], key_scale=0.01)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"], key_scale=np.float32(0.01))
+    check("gdn key_scale=0.01 o", o, ro, 2e-2)
+    check("gdn key_scale=0.01 S", S, rS, 1e-2)
+
+
+# --------------------------------------------------------------------------- edge cases
+def test_zero_frames_copies_state(ls):
+    S0 = torch.randn(1, 2, 32, 32, device=DEV)
+    z0 = torch.rand(1, 2, 32, device=DEV)
+    q = torch.empty((1, 2, 0, 16, 32), dtype=torch.bfloat16, device=DEV)
+    o, S, z = ls.ls_relu_block_forward(q, q.clone(), q.clone(), S0, z0)
+    o2, S2 = ls.ls_gdn_frame_forward(q, q.clone(), q.clone(), torch.empty(1, 2, 0, device=DEV),
+                                     torch.empty(1, 2, 0, device=DEV), S0)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0) and torch.equal(z, z0) and torch.equal(S2, S0)
+    _, S3, z3 = ls.ls_relu_block_forward(q, q.clone(), q.clone())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S3) == 0 and torch.count_nonzero(z3) == 0
+
+
+def test_zero_tokens(ls, oracle_mod):
+    """N = 0: the ReLU state is unchanged, the GDN state only decays."""
+    S0 = torch.randn(1, 2, 128, 128)
+    a = torch.rand(1, 2, 3) * 0.5 + 0.5
+    b = torch.rand(1, 2, 3)
+    q = torch.empty((1, 2, 3, 0, 128), dtype=torch.bfloat16, device=DEV)
+    _, S = ls.ls_gdn_frame_forward(q, q.clone(), q.clone(), a.to(DEV), b.to(DEV), S0.to(DEV))
+    torch.cuda.synchronize()
+    want = S0.double() * torch.prod(a.double(), dim=2)[:, :, None, None]
+    check("gdn N=0 decay", S, want, 1e-5, "fp32")
+    q32 = torch.empty((1, 2, 3, 0, 32), dtype=torch.bfloat16, device=DEV)
+    S1 = torch.randn(1, 2, 32, 32, device=DEV)
+    _, S2, _ = ls.ls_relu_block_forward(q32, q32.clone(), q32.clone(), S1, None)
+    torch.cuda.synchronize()
+    assert torch.equal(S2, S1)
+
+
+def test_empty_batch_is_a_no_op(ls):
+    q = torch.empty((0, 2, 3, 16, 32), dtype=torch.bfloat16, device=DEV)
+    o, S, z = ls.ls_relu_block_forward(q, q.clone(), q.clone())
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and S.numel() == 0
+
+
+def test_in_place_state_and_poisoned_outputs(ls, gen, oracle_mod):
+    """state_out == state_in works, and outputs prefilled with NaN are fully overwritten."""
+    x = gen.relu_inputs(1, 2, 3, 130, 32, "bf16", seed=21)
+    S0, z0 = _rand_state(1, 2, 32, 7, norm=True)
+    xd = _dev(x)
+    S = S0.to(DEV).clone()
+    z = z0.to(DEV).clone()
+    o = torch.full_like(xd["q"], float("nan"))
+    ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], S, z, out=o, state_out=S, norm_out=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], S0, z0)
+    assert torch.isfinite(o).all()
+    check("relu in-place o", o, ro, 2e-2)
+    check("relu in-place S", S, rS, 1e-2)
+    check("relu in-place z", z, rz, 1e-2)
+
+    y = gen.gdn_inputs(1, 2, 3, 130, 128, "bf16", seed=22)
+    G0 = _rand_state(1, 2, 128, 8, scale=0.3)
+    yd = _dev(y)
+    G = G0.to(DEV).clone()
+    o = torch.full_like(yd["q"], float("nan"))
+    ls.ls_gdn_frame_forward(yd["q"], yd["k"], yd["v"], yd["alpha"], yd["beta"], G, out=o, state_out=G)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(y["q"], y["k"], y["v"], y["alpha"], y["beta"], G0)
+    assert torch.isfinite(o).all()
+    check("gdn in-place o", o, ro, 2e-2)
+    check("gdn in-place S", G, rS, 1e-2)
+
+
+def test_deterministic(ls, gen):
+    x = _dev(gen.relu_inputs(1, 4, 4, 1000, 32, "bf16", seed=23))
+    a = ls.ls_relu_block_forward(x["q"], x["k"], x["v"])
+    b = ls.ls_relu_block_forward(x["q"], x["k"], x["v"])
+    y = _dev(gen.gdn_inputs(1, 2, 5, 500, 128, "bf16", seed=24))
+    c = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    d = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    torch.cuda.synchronize()
+    for s, t in zip(a + c, b + d):
+        assert torch.equal(s, t)
+
+
+def test_head_isolation(ls, gen):
+    """A NaN in one head's values stays in that head."""
+    x = _dev(gen.relu_inputs(1, 3, 2, 100, 32, "bf16", seed=25))
+    x["v"][0, 1, 0, 5, 3] = float("nan")
+    o, S, z = ls.ls_relu_block_forward(x["q"], x["k"], x["v"])
+    y = _dev(gen.gdn_inputs(1, 3, 2, 100, 128, "bf16", seed=26))
+    y["v"][0, 1, 1, 7, 0] = float("nan")
+    o2, S2 = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    torch.cuda.synchronize()
+    for t in (o, S, o2, S2):
+        assert torch.isfinite(t[:, 0]).all() and torch.isfinite(t[:, 2]).all()
+        assert not torch.isfinite(t[:, 1]).all()
+
+
+# --------------------------------------------------------------------------- carry
+def test_state_carry_copy_and_reset(ls):
+    S = torch.randn(2, 3, 32, 32, device=DEV)
+    z = torch.randn(2, 3, 32, device=DEV)
+    S2 = torch.empty_like(S)
+    z2 = torch.empty_like(z)
+    ls.ls_state_carry(S, S2, z, z2)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S2) and torch.equal(z, z2)
+    ls.ls_state_carry(None, S2, None, z2, reset=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S2) == 0 and torch.count_nonzero(z2) == 0
+
+
+def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
+    """Block-autoregressive rollout (calls of 3 frames chained by ls_state_carry)."""
+    B, H, F, N, D = 1, 2, 8, 200, 32
+    x = gen.relu_inputs(B, H, F, N, D, "bf16", seed=27)
+    xd = _dev(x)
+    o1, S1, z1 = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"])
+    cache = torch.zeros((B, H, D, D), device=DEV)
+    ncache = torch.zeros((B, H, D), device=DEV)
+    outs = []
+    for f0 in range(0, F, 3):
+        sl = slice(f0, min(F, f0 + 3))
+        q, k, v = (xd[n][:, :, sl].contiguous() for n in "qkv")
+        o, S, z = ls.ls_relu_block_forward(q, k, v, cache, ncache)
+        ls.ls_state_carry(S, cache, z, ncache)
+        outs.append(o)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"])
+    check("rollout o", torch.cat(outs, dim=2), ro, 2e-2)
+    check("rollout S", cache, rS, 1e-2)
+    check("rollout z", ncache, rz, 1e-2)
+    check("rollout vs one call o", torch.cat(outs, dim=2).float(), o1.float().double().cpu().numpy(), 1e-2)
+    assert torch.allclose(cache, S1, rtol=1e-5, atol=1e-5 * S1.abs().max().item())
