@@ -6,6 +6,9 @@
 //   v_mfma_f32_32x32x16_bf16  A: lane l holds row (l & 31), 8 k-slots of group (l >> 5)
 //                             B: lane l holds col (l & 31), the same 8 k-slots
 //                             C: lane l, reg r holds C[8*(r>>2) + 4*(l>>5) + (r&3)][l & 31]
+//   v_mfma_f32_16x16x32_bf16  A: lane l holds row (l & 15), 8 k-slots of group (l >> 4)
+//                             B: lane l holds col (l & 15), the same 8 k-slots
+//                             C: lane l, reg r holds C[4*(l>>4) + r][l & 15]
 //   v_mfma_f32_16x16x4_f32    A: lane l holds A[l & 15][l >> 4]
 //                             B: lane l holds B[l >> 4][l & 15]
 //                             C: lane l, reg r holds C[4*(l>>4) + r][l & 15]
@@ -31,15 +34,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN of the same sign.
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32); NaN stays NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ReLU on two packed bf16 values: a value whose sign bit is set becomes +0.
@@ -58,11 +60,43 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   hi = f32_to_bf16(x);
   lo = f32_to_bf16(x - bf16_to_f32(hi));
 }
+// Two values at once, packed: .x = (bf16(x0), bf16(x1)) hi terms, .y the lo terms.
+__device__ __forceinline__ uint2 split_bf16x2(float x0, float x1) {
+  const uint32_t hi = pack_bf16x2(x0, x1);
+  return make_uint2(hi, pack_bf16x2(x0 - bf16lo_to_f32(hi), x1 - bf16hi_to_f32(hi)));
+}
+
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
+// lanes, output lane i, element r is 16-bit element (i % 4) of the 8 bytes
+// addressed by lane 4r + i/4 of the same group.  So if lane j of a group
+// points at row t0 + j/4, columns c0 + 4(j%4) .. +3 of a row-major bf16 tile,
+// lane i receives column c0 + i of rows t0 .. t0+3: four tokens of one
+// dimension, the layout an MFMA operand wants when tokens are contracted.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  shortx4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+// MFMA 32x32x16 operand of one 32-wide dimension block: lane l gets dimension
+// col0 + (l & 31) of tokens t0 + 8 (l >> 5) + e, e = 0..7, from a row-major
+// [token][pitch] bf16 LDS tile (pitch a multiple of 4 elements).
+template <int PITCH>
+__device__ __forceinline__ u32x4 gather_tokens_32(const uint16_t* tile, int t0, int col0, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const uint16_t* p = tile + (t0 + 8 * (q >> 1) + (j >> 2)) * PITCH + col0 + 16 * (q & 1) + 4 * (j & 3);
+  const uint2 a = lds_read_tr16(p);
+  const uint2 b = lds_read_tr16(p + 4 * PITCH);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -71,6 +105,59 @@ __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
 // 16-byte global load / store through 32-bit words.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// ReLU scan: the state (S_f, z_f) frame f reads, written to LDS by the whole
+// workgroup: the initial state of head bh plus the chunk partials of every
+// frame up to the end of f's block (blocks of `bfr` frames from frame 0; a
+// block reads the state after all of its own frames).  `partial` holds
+// [bh][frame][chunk] records of D*D + D floats, `init` [bh] records.
+// Partial loads are issued eight at a time so their latencies overlap.
+template <int D>
+__device__ __forceinline__ void relu_frame_state(const float* __restrict__ partial,
+                                                 const float* __restrict__ init, long bh, int f,
+                                                 int F, int nc, int bfr, float* Ss, int pitch,
+                                                 float* zs) {
+  constexpr int OUT = D * D + D;
+  const int fend = min(F, (f / bfr + 1) * bfr);
+  const int cnt = fend * nc;
+  const float* P = partial + (size_t)bh * F * nc * OUT;
+  for (int e = threadIdx.x; e < OUT; e += blockDim.x) {
+    float acc = init[(size_t)bh * OUT + e];
+    int i = 0;
+    for (; i + 8 <= cnt; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = P[(size_t)(i + j) * OUT + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+    for (; i < cnt; ++i) acc += P[(size_t)i * OUT + e];
+    if (e < D * D)
+      Ss[(e / D) * pitch + e % D] = acc;
+    else
+      zs[e - D * D] = acc;
+  }
+}
+
+// ReLU scan: workgroup (frame 0, chunk 0) of each head copies the initial
+// state (or zeros) into the workspace, so that later kernels never read
+// state_in and state_out may alias it.
+template <int D>
+__device__ __forceinline__ void relu_copy_init(const float* S0, const float* z0, float* init, long wg,
+                                               int F, int nc) {
+  constexpr int OUT = D * D + D;
+  if (wg % ((long)F * nc) != 0) return;
+  const long bh = wg / ((long)F * nc);
+  for (int e = threadIdx.x; e < OUT; e += blockDim.x) {
+    float x = 0.0f;
+    if (e < D * D) {
+      if (S0) x = S0[(size_t)bh * D * D + e];
+    } else if (z0) {
+      x = z0[(size_t)bh * D + e - D * D];
+    }
+    init[(size_t)bh * OUT + e] = x;
+  }
+}
 
 // Token-tensor element types.
 template <typename T> struct Elem;

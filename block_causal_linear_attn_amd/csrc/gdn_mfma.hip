@@ -7,7 +7,8 @@
 // needs all four key fragments and one value fragment per 16-token k-step.
 // The workgroup stages 64-token K and V tiles in LDS (double buffered, next
 // tile's HBM loads in flight while the current one is contracted) and each
-// lane gathers 8 tokens of one dimension per operand.  Inputs are exact bf16
+// lane gathers 8 tokens of one dimension per operand with two LDS transpose
+// reads.  Inputs are exact bf16
 // products accumulated in fp32; c and c^2 are applied once at the end.
 //
 // Output pass: o = S_f q.  Wave w computes output dims [32w, 32w + 32) from
@@ -21,10 +22,12 @@ namespace linscan {
 namespace {
 
 constexpr int GD = 128;
+// bytes of one (frame, token chunk) record: beta*G hi and lo planes (bf16) + beta*U (fp32)
+constexpr size_t kRecBytes = 8 * (size_t)GD * GD;
 
 __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
-    float c, float c2, int N, int nc, int chunk) {
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk) {
   constexpr int D = GD;
   constexpr int TILE = 64;
   constexpr int ROW = D + 4;  // 264-byte pitch: the two lane groups' gathers land 16 banks apart
@@ -91,23 +94,10 @@ __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     const uint16_t* vl = lds[buf][1];
 #pragma unroll
     for (int s = 0; s < TILE / 16; ++s) {
-      const int tb = s * 16 + g * 8;
-      u32x4 kfrag[4], vfrag;
+      u32x4 kfrag[4];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        const int d = J * 32 + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          kfrag[J][e] = (uint32_t)kl[(tb + 2 * e) * ROW + d] |
-                        ((uint32_t)kl[(tb + 2 * e + 1) * ROW + d] << 16);
-      }
-      {
-        const int d = wave * 32 + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vfrag[e] = (uint32_t)vl[(tb + 2 * e) * ROW + d] |
-                     ((uint32_t)vl[(tb + 2 * e + 1) * ROW + d] << 16);
-      }
+      for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32<ROW>(kl, s * 16, J * 32, lane);
+      const u32x4 vfrag = gather_tokens_32<ROW>(vl, s * 16, wave * 32, lane);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         accG[J] = mfma32x32x16(as_bf16x8(kfrag[wave]), as_bf16x8(kfrag[J]), accG[J]);
@@ -118,16 +108,207 @@ __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     __syncthreads();
   }
 
-  float* Gd = partial + (size_t)wg * 2 * D * D;
-  float* Ud = Gd + D * D;
+  // record of this (frame, chunk): beta*G as bf16 hi and lo planes (row-major),
+  // then beta*U in fp32 with each group of four rows interleaved, element
+  // (m, n) at ((m / 4) * D + n) * 4 + m % 4, so that the four rows a scan lane
+  // owns in one column are one 16-byte load
+  const float bf = beta[bhf];
+  const float gs = c2 * bf, us = c * bf;
+  uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)wg * kRecBytes);
+  uint16_t* Glo = Ghi + D * D;
+  float* Ud = reinterpret_cast<float*>(Glo + D * D);
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = wave * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-      Gd[m * D + J * 32 + col] = c2 * accG[J][r];
-      Ud[m * D + J * 32 + col] = c * accU[J][r];
+      uint16_t h, l;
+      split_bf16(gs * accG[J][r], h, l);
+      Ghi[m * D + J * 32 + col] = h;
+      Glo[m * D + J * 32 + col] = l;
     }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int m0 = wave * 32 + 8 * q4 + 4 * g;  // rows m0 .. m0 + 3 sit in regs 4 q4 .. 4 q4 + 3
+      float4 u4 = make_float4(us * accU[J][4 * q4], us * accU[J][4 * q4 + 1], us * accU[J][4 * q4 + 2],
+                              us * accU[J][4 * q4 + 3]);
+      *reinterpret_cast<float4*>(Ud + ((size_t)(m0 >> 2) * D + J * 32 + col) * 4) = u4;
+    }
+  }
+}
+
+// One workgroup per (batch*head, 16-row block of S); a head's eight row
+// blocks get block ids that are equal mod 8, so they run on one XCD and
+// share its L2 copy of each frame's record.  Per frame:
+//   S_rows <- alpha (S_rows - S_rows (beta G)) + beta U
+// The product runs as three bf16 MFMAs on hi/lo splits of S and beta G
+// (dropping only lo*lo), accumulated in fp32; S stays fp32 in registers (C
+// layout) and in a double-buffered LDS copy that feeds the next frame's A
+// operands.  G is symmetric, so the B operand (8 consecutive k of column n)
+// is read as 16 contiguous bytes of row n.
+//
+// The frame loop is a dependency chain, so it is kept free of branches and
+// light on memory instructions: records are fetched two frames ahead into a
+// register ring (always issued, with the frame index clamped at the end),
+// the decays of up to kAlphaWin frames sit in LDS, and each frame's state is
+// written back with two 16-byte stores per thread from the LDS copy.  MULTI
+// handles frames split into several token chunks (one record per chunk).
+constexpr int kAlphaWin = 2048;
+
+template <bool MULTI>
+__global__ __launch_bounds__(256) void gdn_scan_mfma128(
+    const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
+    uint16_t* __restrict__ states, float* S_out, long bh, int F, int nc) {
+  constexpr int D = GD, RB = 16, PITCH = D + 4;
+  __shared__ __align__(16) float Ss[2][RB][PITCH];
+  __shared__ float As[kAlphaWin];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const long b = blockIdx.x;
+  const long head = (b / 64) * 8 + (b % 8);
+  const int r0 = (int)((b / 8) % 8) * RB;
+  if (head >= bh) return;  // whole workgroup leaves together
+
+  float s[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+      s[nb][r] = S0 ? S0[(size_t)head * D * D + (size_t)(r0 + m) * D + n] : 0.0f;
+      Ss[0][m][n] = s[nb][r];
+    }
+
+  struct Rec {
+    u32x4 hi[2][4], lo[2][4];
+    float u[2][4];
+  };
+  const size_t hf0 = (size_t)head * F;
+  auto load_rec = [&](int f, int cidx, Rec& R) {
+    const uint8_t* base = rec + ((hf0 + f) * nc + cidx) * kRecBytes;
+    const uint16_t* gh = reinterpret_cast<const uint16_t*>(base);
+    const uint16_t* gl = gh + D * D;
+    const float* U = reinterpret_cast<const float*>(gl + D * D);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = 32 * wave + 16 * nb + lr;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const size_t off = (size_t)n * D + 32 * s4 + 8 * lg;
+        R.hi[nb][s4] = ld16(gh + off);
+        R.lo[nb][s4] = ld16(gl + off);
+      }
+      const float4 u4 = *reinterpret_cast<const float4*>(U + ((size_t)((r0 >> 2) + lg) * D + n) * 4);
+      R.u[nb][0] = u4.x;
+      R.u[nb][1] = u4.y;
+      R.u[nb][2] = u4.z;
+      R.u[nb][3] = u4.w;
+    }
+  };
+  // S_f leaves for the output pass from the LDS copy the next frame reads
+  // anyway: each thread splits 8 consecutive entries of one row and writes
+  // them to the hi and lo planes with two 16-byte stores
+  auto store_state = [&](int f, int buf) {
+    const int row = tid >> 4, c0 = 8 * (tid & 15);
+    const float* src = &Ss[buf][row][c0];
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+    const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+    uint16_t* hp = states + (hf0 + f) * 2 * D * D + (size_t)(r0 + row) * D + c0;
+    st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
+    st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+  };
+  // hi*hi, hi*lo and lo*hi go to three accumulators: independent MFMA
+  // chains overlap their latencies instead of queueing behind each other
+  auto mfma3 = [&](floatx4 (&acc)[3], const u32x4& ah, const u32x4& al, const u32x4& bh_, const u32x4& bl_) {
+    acc[0] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(bh_), acc[0]);
+    acc[1] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(bl_), acc[1]);
+    acc[2] = mfma16x16x32(as_bf16x8(al), as_bf16x8(bh_), acc[2]);
+  };
+
+  Rec R0, R1;
+  if (F > 0) {
+    load_rec(0, 0, R0);
+    load_rec(min(1, F - 1), 0, R1);
+  }
+
+  auto frame = [&](int f, Rec& R) {
+    const int cur = f & 1;
+    const float a = As[f % kAlphaWin];
+    // A operands: this workgroup's 16 rows of S_{f-1}, split into bf16 hi + lo
+    u32x4 ahi[4], alo[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float* src = &Ss[cur][lr][32 * s4 + 8 * lg];
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+      const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+      ahi[s4] = u32x4{p0.x, p1.x, p2.x, p3.x};
+      alo[s4] = u32x4{p0.y, p1.y, p2.y, p3.y};
+    }
+    floatx4 acc3[2][3];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc3[nb][t] = floatx4{};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mfma3(acc3[nb], ahi[s4], alo[s4], R.hi[nb][s4], R.lo[nb][s4]);
+    float uf[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) uf[nb][r] = R.u[nb][r];
+    if (MULTI) {
+      for (int cidx = 1; cidx < nc; ++cidx) {  // the frame's further token chunks
+        Rec T;
+        load_rec(f, cidx, T);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) mfma3(acc3[nb], ahi[s4], alo[s4], T.hi[nb][s4], T.lo[nb][s4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) uf[nb][r] += T.u[nb][r];
+        }
+      }
+    }
+    // refill this ring slot two frames ahead (the last record again at the end)
+    load_rec(min(f + 2, F - 1), 0, R);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+        const float prod = acc3[nb][0][r] + (acc3[nb][1][r] + acc3[nb][2][r]);
+        s[nb][r] = a * (s[nb][r] - prod) + uf[nb][r];
+        Ss[cur ^ 1][m][n] = s[nb][r];
+      }
+    __syncthreads();
+    store_state(f, cur ^ 1);
+  };
+
+  for (int w0 = 0; w0 < F; w0 += kAlphaWin) {
+    const int w1 = min(F, w0 + kAlphaWin);
+    for (int i = tid; i < w1 - w0; i += 256) As[i] = alpha[hf0 + w0 + i];
+    __syncthreads();
+    int f = w0;
+    for (; f + 2 <= w1; f += 2) {
+      frame(f, R0);
+      frame(f + 1, R1);
+    }
+    if (f < w1) frame(f, R0);  // window tail (kAlphaWin is even, so slot f % 2 == 0)
+    __syncthreads();  // As is rewritten for the next window
+  }
+  if (S_out) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S_out[(size_t)head * D * D + (size_t)(r0 + 4 * lg + r) * D + 32 * wave + 16 * nb + lr] = s[nb][r];
   }
 }
 
@@ -221,11 +402,24 @@ __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
 
 bool gdn_has_mfma(int D, int dtype) { return dtype == DT_BF16 && D == GD; }
 
-hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, float* partial, float c,
-                                float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
+hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
+                                float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
   if (D != GD) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gdn_gram_mfma128, dim3((unsigned)(bhf * nc)), dim3(256), 0, st,
-                     (const uint16_t*)k, (const uint16_t*)v, partial, c, c2, N, nc, chunk);
+                     (const uint16_t*)k, (const uint16_t*)v, beta, (uint8_t*)rec, c, c2, N, nc, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
+                                void* states, float* S_out, long bh, int F, int nc, hipStream_t st) {
+  if (D != GD) return hipErrorInvalidValue;
+  const long groups = (bh + 7) / 8;  // eight heads x eight row blocks per group of 64 workgroups
+  if (nc == 1)
+    hipLaunchKernelGGL(gdn_scan_mfma128<false>, dim3((unsigned)(groups * 64)), dim3(256), 0, st,
+                       (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
+  else
+    hipLaunchKernelGGL(gdn_scan_mfma128<true>, dim3((unsigned)(groups * 64)), dim3(256), 0, st,
+                       (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ struct SummarySplit {
 template <typename T, int D, bool RELU>
 __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, const T* __restrict__ v,
                                                    float* __restrict__ partial, float c, float c2,
-                                                   int N, int nc, int chunk) {
+                                                   const float* S0, const float* z0, float* init,
+                                                   int F, int N, int nc, int chunk) {
   constexpr int EPT = SummarySplit<D>::kEPT;
   __shared__ float ks[GT][D + 1];
   __shared__ float vs[GT][D + 1];
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       if (e < D * D) dst[e] = a1[x];
     }
     if (blockIdx.y == 0 && tid < D) dst[D * D + tid] = az;
+    if (blockIdx.y == 0) relu_copy_init<D>(S0, z0, init, wg, F, nc);
   } else {
     float* Gd = partial + (size_t)wg * 2 * D * D;
     float* Ud = Gd + D * D;
@@ -97,11 +99,15 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
 }
 
 // o = S_f phi(q) / (z_f . phi(q) + eps) (RELU) or o = S_f q, one token per
-// group of D threads.  `state` points at S_f (fp32) followed, for RELU, by z_f.
+// group of D threads.  RELU forms (S_f, z_f) from the initial state and the
+// summary partials (and writes the call's final state from the last frame);
+// otherwise S_f (fp32) is read from `states`.
 template <typename T, int D, bool RELU>
 __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __restrict__ o,
-                                                  const float* __restrict__ states, size_t state_stride,
-                                                  float eps, int N, int nco, int chunk) {
+                                                  const float* __restrict__ states,
+                                                  const float* __restrict__ init, float* S_out,
+                                                  float* z_out, float eps, int F, int N, int nc,
+                                                  int bfr, int nco, int chunk) {
   constexpr int SLOTS = 256 / D;
   __shared__ float Ss[D][D + 1];
   __shared__ float zs[D];
@@ -111,9 +117,20 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
   const long bhf = wg / nco;
   const int n0 = (int)(wg % nco) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const float* Sf = states + (size_t)bhf * state_stride;
-  for (int e = tid; e < D * D; e += 256) Ss[e / D][e % D] = Sf[e];
-  if (RELU && tid < D) zs[tid] = Sf[D * D + tid];
+  if (RELU) {
+    const long bh = bhf / F;
+    const int f = (int)(bhf % F);
+    relu_frame_state<D>(states, init, bh, f, F, nc, bfr, &Ss[0][0], D + 1, zs);
+    __syncthreads();
+    if (f == F - 1 && wg % nco == 0) {
+      for (int e = tid; e < D * D; e += 256)
+        if (S_out) S_out[(size_t)bh * D * D + e] = Ss[e / D][e % D];
+      if (z_out && tid < D) z_out[(size_t)bh * D + tid] = zs[tid];
+    }
+  } else {
+    const float* Sf = states + (size_t)bhf * D * D;
+    for (int e = tid; e < D * D; e += 256) Ss[e / D][e % D] = Sf[e];
+  }
   const int slot = tid / D, i = tid % D;
   const T* qf = q + (size_t)bhf * N * D;
   T* of = o + (size_t)bhf * N * D;
@@ -139,39 +156,36 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
 }
 
 template <typename T, int D>
-hipError_t summary_launch(bool relu, const void* k, const void* v, float* partial, float c, float c2,
-                          long bhf, int N, int nc, int chunk, hipStream_t st) {
-  dim3 grid((unsigned)(bhf * nc), SummarySplit<D>::kParts), block(256);
-  if (relu)
-    hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)k, (const T*)v,
-                       partial, c, c2, N, nc, chunk);
+hipError_t summary_launch(const GenArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.bhf * a.nc), SummarySplit<D>::kParts), block(256);
+  if (a.relu)
+    hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.F, a.N, a.nc, a.chunk);
   else
-    hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)k, (const T*)v,
-                       partial, c, c2, N, nc, chunk);
+    hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.F, a.N, a.nc, a.chunk);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t output_launch(bool relu, const void* q, void* o, const float* states, size_t stride,
-                         float eps, long bhf, int N, int nco, int chunk, hipStream_t st) {
-  dim3 grid((unsigned)(bhf * nco)), block(256);
-  if (relu)
-    hipLaunchKernelGGL((gen_output<T, D, true>), grid, block, 0, st, (const T*)q, (T*)o, states,
-                       stride, eps, N, nco, chunk);
+hipError_t output_launch(const GenArgs& a, hipStream_t st) {
+  dim3 grid((unsigned)(a.bhf * a.nco)), block(256);
+  if (a.relu)
+    hipLaunchKernelGGL((gen_output<T, D, true>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
+                       a.partial, a.init, a.S_out, a.z_out, a.eps, a.F, a.N, a.nc, a.bfr, a.nco, a.chunko);
   else
-    hipLaunchKernelGGL((gen_output<T, D, false>), grid, block, 0, st, (const T*)q, (T*)o, states,
-                       stride, eps, N, nco, chunk);
+    hipLaunchKernelGGL((gen_output<T, D, false>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
+                       (const float*)a.states, nullptr, nullptr, nullptr, 0.0f, a.F, a.N, 1, 1, a.nco, a.chunko);
   return hipGetLastError();
 }
 
 #define LINSCAN_FOR_EACH_D(X) X(16) X(32) X(48) X(64) X(80) X(96) X(112) X(128)
 
 template <typename T>
-hipError_t summary_dispatch(int D, bool relu, const void* k, const void* v, float* partial, float c,
-                            float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
-  switch (D) {
+hipError_t summary_dispatch(const GenArgs& a, hipStream_t st) {
+  switch (a.D) {
 #define CASE(d) \
-  case d: return summary_launch<T, d>(relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
+  case d: return summary_launch<T, d>(a, st);
     LINSCAN_FOR_EACH_D(CASE)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -179,11 +193,10 @@ hipError_t summary_dispatch(int D, bool relu, const void* k, const void* v, floa
 }
 
 template <typename T>
-hipError_t output_dispatch(int D, bool relu, const void* q, void* o, const float* states, size_t stride,
-                           float eps, long bhf, int N, int nco, int chunk, hipStream_t st) {
-  switch (D) {
+hipError_t output_dispatch(const GenArgs& a, hipStream_t st) {
+  switch (a.D) {
 #define CASE(d) \
-  case d: return output_launch<T, d>(relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
+  case d: return output_launch<T, d>(a, st);
     LINSCAN_FOR_EACH_D(CASE)
 #undef CASE
     default: return hipErrorInvalidValue;
@@ -192,20 +205,12 @@ hipError_t output_dispatch(int D, bool relu, const void* q, void* o, const float
 
 }  // namespace
 
-hipError_t launch_summary_generic(int D, int dtype, bool relu, const void* k, const void* v,
-                                  float* partial, float c, float c2, long bhf, int N, int nc, int chunk,
-                                  hipStream_t st) {
-  if (dtype == DT_F32)
-    return summary_dispatch<float>(D, relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
-  return summary_dispatch<uint16_t>(D, relu, k, v, partial, c, c2, bhf, N, nc, chunk, st);
+hipError_t launch_summary_generic(const GenArgs& a, hipStream_t st) {
+  return a.dtype == DT_F32 ? summary_dispatch<float>(a, st) : summary_dispatch<uint16_t>(a, st);
 }
 
-hipError_t launch_output_generic(int D, int dtype, bool relu, const void* q, void* o,
-                                 const float* states, size_t stride, float eps, long bhf, int N,
-                                 int nco, int chunk, hipStream_t st) {
-  if (dtype == DT_F32)
-    return output_dispatch<float>(D, relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
-  return output_dispatch<uint16_t>(D, relu, q, o, states, stride, eps, bhf, N, nco, chunk, st);
+hipError_t launch_output_generic(const GenArgs& a, hipStream_t st) {
+  return a.dtype == DT_F32 ? output_dispatch<float>(a, st) : output_dispatch<uint16_t>(a, st);
 }
 
 }  // namespace linscan

@@ -16,40 +16,64 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 bool relu_has_mfma(int D, int dtype);
 bool gdn_has_mfma(int D, int dtype);
 
+// Everything a launcher may need for one call (pointers are device pointers).
+struct ScanArgs {
+  int D = 0, dtype = 0;
+  bool relu = false, mfma = false;
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  void* o = nullptr;
+  const float* alpha = nullptr;
+  const float* beta = nullptr;
+  const float* S0 = nullptr;   // initial state (NULL = zeros)
+  const float* z0 = nullptr;   // initial ReLU normaliser (NULL = zeros)
+  float* S_out = nullptr;
+  float* z_out = nullptr;
+  float* partial = nullptr;    // per (frame, chunk) summaries (workspace)
+  float* init = nullptr;       // ReLU: copy of the initial state (workspace)
+  void* states = nullptr;      // GDN: state after every frame (workspace)
+  float c = 0.0f, c2 = 0.0f;   // GDN key scale and its square
+  float eps = 0.0f;            // ReLU normaliser epsilon
+  long bh = 0, bhf = 0;        // B*H, B*H*F
+  int F = 0, N = 0;
+  int nc = 1, chunk = 1;       // token chunks of the summary/gram pass
+  int nco = 1, chunko = 1;     // token chunks of the output pass
+  int bfr = 1;                 // ReLU frames per causal block
+};
+using GenArgs = ScanArgs;
+
 // ReLU path ---------------------------------------------------------------
-// Per (frame, token chunk): dS = sum v phi(k)^T and dz = sum phi(k) over the
-// chunk's tokens -> partial[(bhf * nc + chunk)][D*D + D].
-hipError_t launch_relu_summary(int D, bool mfma, int dtype, const void* k, const void* v,
-                               float* partial, long bhf, int N, int nc, int chunk,
-                               hipStream_t st);
-// Per (batch, head): block-causal inclusive prefix of the partials, starting
-// from (S0, z0) -> prefix[bhf][D*D + D]; final state -> (S_out, z_out).
-hipError_t launch_relu_prefix(int D, const float* partial, const float* S0, const float* z0,
-                              float* prefix, float* S_out, float* z_out, long bh, int F, int nc,
-                              int block_frames, hipStream_t st);
-// Per (frame, token chunk): o = S_f phi(q) / (z_f . phi(q) + eps).
-hipError_t launch_relu_output(int D, bool mfma, int dtype, const void* q, void* o,
-                              const float* prefix, float eps, long bhf, int N, int nco, int chunk,
-                              hipStream_t st);
+// Per (frame, token chunk): dS = sum v phi(k)^T, dz = sum phi(k) ->
+// partial[(bhf * nc + chunk)][D*D + D]; (frame 0, chunk 0) of each head also
+// copies (S0, z0) into init[bh].
+hipError_t launch_relu_summary(const ScanArgs& a, hipStream_t st);
+// Per (frame, token chunk): (S_f, z_f) = init + partials of every frame up to
+// the end of f's block; o = S_f phi(q) / (z_f . phi(q) + eps); the last
+// frame's state goes to (S_out, z_out).
+hipError_t launch_relu_output(const ScanArgs& a, hipStream_t st);
 
 // Gated DeltaNet path -----------------------------------------------------
 // Per (frame, token chunk): G = c2 * sum k k^T, U = c * sum v k^T
-// -> partial[(bhf * nc + chunk)][2][D*D].
-hipError_t launch_gdn_gram(int D, bool mfma, int dtype, const void* k, const void* v,
-                           float* partial, float c, float c2, long bhf, int N, int nc, int chunk,
-                           hipStream_t st);
+// -> partial[(bhf * nc + chunk)], 8 D^2 bytes each.  Generic kernels store
+// G and U in fp32; the MFMA kernels store beta*G as bf16 hi/lo planes and
+// beta*U in fp32 (beta of the frame folded in).
+hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st);
 // Per (batch, head, 16-row block of S): S <- alpha S (I - beta G) + beta U for
-// every frame in order; the state after each frame goes to `states` (fp32, or
-// split into bf16 hi/lo planes when `hilo`), the last one to S_out.
-hipError_t launch_gdn_scan(int D, bool hilo, const float* partial, const float* alpha,
-                           const float* beta, const float* S0, void* states, float* S_out,
-                           long bh, int F, int nc, hipStream_t st);
+// every frame in order; the state after each frame goes to `states` (fp32 for
+// the generic kernels, bf16 hi/lo planes for the MFMA kernels), the last one
+// to S_out.
+hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st);
 // Per (frame, token chunk): o = S_f q.
-hipError_t launch_gdn_output(int D, bool mfma, int dtype, const void* q, void* o,
-                             const void* states, long bhf, int N, int nco, int chunk,
-                             hipStream_t st);
+hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
 
-// Copy n floats src -> dst, or zero dst when `reset`.
-hipError_t launch_carry(const float* src, float* dst, size_t n, int reset, hipStream_t st);
+// Generic (VALU) summary and output kernels of either path.
+hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);
+hipError_t launch_output_generic(const ScanArgs& a, hipStream_t st);
+
+// Copy n0 floats src0 -> dst0 and n1 floats src1 -> dst1 (or zero both
+// destinations when `reset`) in one launch.
+hipError_t launch_carry(const float* src0, float* dst0, size_t n0, const float* src1, float* dst1,
+                        size_t n1, int reset, hipStream_t st);
 
 }  // namespace linscan

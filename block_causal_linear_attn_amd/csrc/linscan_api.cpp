@@ -95,18 +95,21 @@ void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, 
 struct ReluPlan {
   bool mfma;
   int nc, chunk, nco, chunko;
-  size_t partial_off, prefix_off, bytes;
+  size_t partial_off, init_off, bytes;
 };
 
 ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   ReluPlan p;
   p.mfma = linscan::relu_has_mfma(s->D, s->dtype);
-  plan_chunks(d.bhf, s->N, 2048, 512, 64, &p.nc, &p.chunk);
-  plan_chunks(d.bhf, s->N, 2048, 256, 128, &p.nco, &p.chunko);
+  // summary: whole frames per workgroup unless there are too few frames to
+  // fill the chip; each output workgroup sums the partials of its frame and
+  // all earlier ones, so fewer partials per frame keep that read small
+  plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
+  plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
   const size_t out = (size_t)s->D * s->D + s->D;
   p.partial_off = 0;
-  p.prefix_off = align_up((size_t)d.bhf * p.nc * out * sizeof(float), 256);
-  p.bytes = align_up(p.prefix_off + (size_t)d.bhf * out * sizeof(float), 256);
+  p.init_off = align_up((size_t)d.bhf * p.nc * out * sizeof(float), 256);
+  p.bytes = align_up(p.init_off + (size_t)d.bh * out * sizeof(float), 256);
   return p;
 }
 
@@ -297,14 +300,14 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   hipStream_t hs = (hipStream_t)stream;
   if (s->F == 0 || s->N == 0) {
     // no tokens: the state passes through unchanged
-    if (state_out && state_out != state_in)
-      if ((st = hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, state_in == nullptr, hs),
-                          "state copy")) != LS_OK)
-        return st;
-    if (norm_out && norm_out != norm_in)
-      if ((st = hip_check(linscan::launch_carry(norm_in, norm_out, norm_bytes / 4, norm_in == nullptr, hs),
-                          "norm copy")) != LS_OK)
-        return st;
+    // (a NULL source means zeros: each range is either all copied or all zeroed)
+    const bool cs = state_out && state_out != state_in, cn = norm_out && norm_out != norm_in;
+    if (cs && (st = hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, nullptr, nullptr, 0,
+                                                    state_in == nullptr, hs), "state copy")) != LS_OK)
+      return st;
+    if (cn && (st = hip_check(linscan::launch_carry(norm_in, norm_out, norm_bytes / 4, nullptr, nullptr, 0,
+                                                    norm_in == nullptr, hs), "norm copy")) != LS_OK)
+      return st;
     return ok();
   }
   const ReluPlan p = relu_plan(s, d);
@@ -319,16 +322,36 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
     return fail(LS_ERR_ALIASING, "workspace overlaps an output");
 
   char* ws = (char*)workspace;
-  float* partial = (float*)(ws + p.partial_off);
-  float* prefix = (float*)(ws + p.prefix_off);
-  if ((st = hip_check(timed("relu_summary", hs, [&] { return linscan::launch_relu_summary(D, p.mfma, s->dtype, k, v, partial, d.bhf, s->N,
-                                                   p.nc, p.chunk, hs); }), "relu summary")) != LS_OK)
+  linscan::ScanArgs a;
+  a.D = D;
+  a.dtype = s->dtype;
+  a.relu = true;
+  a.mfma = p.mfma;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.S0 = state_in;
+  a.z0 = norm_in;
+  a.S_out = state_out;
+  a.z_out = norm_out;
+  a.partial = (float*)(ws + p.partial_off);
+  a.init = (float*)(ws + p.init_off);
+  a.eps = eps;
+  a.bh = d.bh;
+  a.bhf = d.bhf;
+  a.F = s->F;
+  a.N = s->N;
+  a.nc = p.nc;
+  a.chunk = p.chunk;
+  a.nco = p.nco;
+  a.chunko = p.chunko;
+  a.bfr = block_frames;
+  if ((st = hip_check(timed("relu_summary", hs, [&] { return linscan::launch_relu_summary(a, hs); }),
+                      "relu summary")) != LS_OK)
     return st;
-  if ((st = hip_check(timed("relu_prefix", hs, [&] { return linscan::launch_relu_prefix(D, partial, state_in, norm_in, prefix, state_out, norm_out,
-                                                  d.bh, s->F, p.nc, block_frames, hs); }), "relu prefix")) != LS_OK)
-    return st;
-  if ((st = hip_check(timed("relu_output", hs, [&] { return linscan::launch_relu_output(D, p.mfma, s->dtype, q, o, prefix, eps, d.bhf, s->N,
-                                                  p.nco, p.chunko, hs); }), "relu output")) != LS_OK)
+  if ((st = hip_check(timed("relu_output", hs, [&] { return linscan::launch_relu_output(a, hs); }),
+                      "relu output")) != LS_OK)
     return st;
   return ok();
 }
@@ -369,8 +392,8 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   hipStream_t hs = (hipStream_t)stream;
   if (s->F == 0) {
     if (state_out && state_out != state_in)
-      return hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, state_in == nullptr, hs),
-                       "state copy");
+      return hip_check(linscan::launch_carry(state_in, state_out, state_bytes / 4, nullptr, nullptr, 0,
+                                             state_in == nullptr, hs), "state copy");
     return ok();
   }
   const GdnPlan p = gdn_plan(s, d);
@@ -386,17 +409,38 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   // no tokens there is nothing to scale
   double c = key_scale > 0.0f ? (double)key_scale : (s->N > 0 ? 1.0 / sqrt((double)D * s->N) : 0.0);
   char* ws = (char*)workspace;
-  float* partial = (float*)(ws + p.partial_off);
-  void* states = ws + p.states_off;
-  if ((st = hip_check(timed("gdn_gram", hs, [&] { return linscan::launch_gdn_gram(D, p.mfma, s->dtype, k, v, partial, (float)c, (float)(c * c),
-                                               d.bhf, s->N, p.nc, p.chunk, hs); }), "gdn gram")) != LS_OK)
+  linscan::ScanArgs a;
+  a.D = D;
+  a.dtype = s->dtype;
+  a.relu = false;
+  a.mfma = p.mfma;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.S0 = state_in;
+  a.S_out = state_out;
+  a.partial = (float*)(ws + p.partial_off);
+  a.states = ws + p.states_off;
+  a.c = (float)c;
+  a.c2 = (float)(c * c);
+  a.bh = d.bh;
+  a.bhf = d.bhf;
+  a.F = s->F;
+  a.N = s->N;
+  a.nc = p.nc;
+  a.chunk = p.chunk;
+  a.nco = p.nco;
+  a.chunko = p.chunko;
+  if ((st = hip_check(timed("gdn_gram", hs, [&] { return linscan::launch_gdn_gram(a, hs); }), "gdn gram")) != LS_OK)
     return st;
-  if ((st = hip_check(timed("gdn_scan", hs, [&] { return linscan::launch_gdn_scan(D, p.mfma, partial, alpha, beta, state_in, states, state_out,
-                                               d.bh, s->F, p.nc, hs); }), "gdn scan")) != LS_OK)
+  if ((st = hip_check(timed("gdn_scan", hs, [&] { return linscan::launch_gdn_scan(a, hs); }), "gdn scan")) != LS_OK)
     return st;
   if (s->N > 0)
-    if ((st = hip_check(timed("gdn_output", hs, [&] { return linscan::launch_gdn_output(D, p.mfma, s->dtype, q, o, states, d.bhf, s->N, p.nco,
-                                                   p.chunko, hs); }), "gdn output")) != LS_OK)
+    if ((st = hip_check(timed("gdn_output", hs, [&] { return linscan::launch_gdn_output(a, hs); }),
+                        "gdn output")) != LS_OK)
       return st;
   return ok();
 }
@@ -423,13 +467,15 @@ ls_status ls_state_carry(int B, int H, int D, const float* state_src, const floa
   if (with_norm && overlap(state_dst, sb, norm_dst, nb))
     return fail(LS_ERR_ALIASING, "state_dst and norm_dst overlap");
   hipStream_t hs = (hipStream_t)stream;
-  ls_status st;
-  if (reset || state_src != state_dst)
-    if ((st = hip_check(timed("state_carry", hs, [&] { return linscan::launch_carry(state_src, state_dst, sb / 4, reset, hs); }), "state carry")) != LS_OK)
-      return st;
-  if (with_norm && (reset || norm_src != norm_dst))
-    if ((st = hip_check(timed("state_carry", hs, [&] { return linscan::launch_carry(norm_src, norm_dst, nb / 4, reset, hs); }), "norm carry")) != LS_OK)
-      return st;
+  // state and normaliser move in one launch
+  const bool do_state = reset || state_src != state_dst;
+  const bool do_norm = with_norm && (reset || norm_src != norm_dst);
+  if (!do_state && !do_norm) return ok();
+  ls_status st = hip_check(timed("state_carry", hs, [&] {
+                             return linscan::launch_carry(state_src, state_dst, do_state ? sb / 4 : 0,
+                                                          norm_src, norm_dst, do_norm ? nb / 4 : 0, reset, hs);
+                           }), "state carry");
+  if (st != LS_OK) return st;
   return ok();
 }
 

@@ -5,14 +5,17 @@
 // Summary pass: the per-frame contributions dS = V^T phi(K), dz = 1^T phi(K)
 // contract over tokens, the strided axis of the [N][D] tiles, so each wave
 // stages its 64-token K and V tiles in its own LDS slice and gathers 8 tokens
-// of one dimension per lane as an MFMA operand.  The normaliser rides on the
-// same MFMA with an all-ones A operand.
+// of one dimension per lane as an MFMA operand with two LDS transpose reads
+// (ds_read_b64_tr_b16).  The next tile's HBM loads are in flight meanwhile.
+// The normaliser rides on the same MFMA with an all-ones A operand.
 //
-// Output pass: o = S phi(q) contracts over the key dimension, which is
-// contiguous in q, so each lane loads 16-byte query fragments straight from
-// HBM as the MFMA B operand; S is split once into bf16 hi + lo terms (16
-// significant bits) held in registers, giving fp32-grade numerators from two
-// bf16 MFMAs.  The denominator z . phi(q) is an fp32 dot product on the VALU.
+// Output pass: each workgroup first forms its frame's state from the initial
+// state and the summary partials (the block-causal prefix), then o = S phi(q)
+// contracts over the key dimension, which is contiguous in q, so each lane
+// loads 16-byte query fragments straight from HBM as the MFMA B operand; S is
+// split once into bf16 hi + lo terms (16 significant bits) held in registers,
+// giving fp32-grade numerators from two bf16 MFMAs.  The denominator
+// z . phi(q) is an fp32 dot product on the VALU.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,10 +26,10 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256, 2) void relu_summary_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
-    int N, int nc, int chunk) {
+    const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk) {
   constexpr int DB = D / 32;            // 32-wide dimension blocks
   constexpr int TILE = 64;              // tokens per wave per step
-  constexpr int ROW = D + 4;            // LDS row pitch (bf16): +8 bytes keeps gathers conflict-free
+  constexpr int ROW = D + 4;            // LDS row pitch (bf16)
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
   constexpr int LPT = TILE * CPR / 64;  // 16-byte loads per lane per tensor per tile
   constexpr int OUT = D * D + D;
@@ -53,43 +56,49 @@ __global__ __launch_bounds__(256, 2) void relu_summary_mfma(
   }
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-  for (int t0 = n0 + wave * TILE; t0 < n1; t0 += 4 * TILE) {
-    // stage this wave's tile: token rows of K (ReLU applied) and V
+  // the next tile's rows are loaded into registers while the current tile is contracted
+  u32x4 kr[LPT], vr[LPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 64 + lane;
+      const int n = t0 + ci / CPR, cb = ci % CPR;
+      if (n < n1) {
+        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
+        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
+      } else {
+        kr[r] = u32x4{0u, 0u, 0u, 0u};
+        vr[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  int t0 = n0 + wave * TILE;
+  if (t0 < n1) fetch(t0);
+  for (; t0 < n1; t0 += 4 * TILE) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 64 + lane;
       const int tok = ci / CPR, cb = ci % CPR;
-      const int n = t0 + tok;
-      u32x4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (n < n1) {
-        kk = ld16(kf + (size_t)n * D + cb * 8);
-        vv = ld16(vf + (size_t)n * D + cb * 8);
-      }
+      u32x4 kk = kr[r];
 #pragma unroll
       for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
       uint2* kd = reinterpret_cast<uint2*>(kl + tok * ROW + cb * 8);
       uint2* vd = reinterpret_cast<uint2*>(vl + tok * ROW + cb * 8);
       kd[0] = make_uint2(kk[0], kk[1]);
       kd[1] = make_uint2(kk[2], kk[3]);
-      vd[0] = make_uint2(vv[0], vv[1]);
-      vd[1] = make_uint2(vv[2], vv[3]);
+      vd[0] = make_uint2(vr[r][0], vr[r][1]);
+      vd[1] = make_uint2(vr[r][2], vr[r][3]);
     }
+    if (t0 + 4 * TILE < n1) fetch(t0 + 4 * TILE);
     __builtin_amdgcn_wave_barrier();
-    // 16 tokens per MFMA k-step; lane group g takes tokens 8g..8g+7 of the step
+    // 16 tokens per MFMA k-step
 #pragma unroll
     for (int s = 0; s < TILE / 16; ++s) {
-      const int tb = s * 16 + g * 8;
       u32x4 af[DB], bfr[DB];
 #pragma unroll
       for (int blk = 0; blk < DB; ++blk) {
-        const int d = blk * 32 + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          af[blk][e] = (uint32_t)vl[(tb + 2 * e) * ROW + d] |
-                       ((uint32_t)vl[(tb + 2 * e + 1) * ROW + d] << 16);
-          bfr[blk][e] = (uint32_t)kl[(tb + 2 * e) * ROW + d] |
-                        ((uint32_t)kl[(tb + 2 * e + 1) * ROW + d] << 16);
-        }
+        af[blk] = gather_tokens_32<ROW>(vl, s * 16, blk * 32, lane);
+        bfr[blk] = gather_tokens_32<ROW>(kl, s * 16, blk * 32, lane);
       }
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
@@ -125,24 +134,40 @@ __global__ __launch_bounds__(256, 2) void relu_summary_mfma(
   float* dst = partial + (size_t)wg * OUT;
   for (int e = threadIdx.x; e < OUT; e += 256)
     dst[e] = ((red[e] + red[OUT + e]) + red[2 * OUT + e]) + red[3 * OUT + e];
+  relu_copy_init<D>(S0, z0, init, wg, F, nc);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void relu_output_mfma(
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ prefix,
-    float eps, int N, int nco, int chunk) {
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
+    const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
+    int bfr, int nco, int chunk) {
   constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
   constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
-  constexpr int TILE = 32;    // tokens per wave per step
+  constexpr int U = 4;        // 32-token groups per wave per step
+  constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
+  constexpr int PITCH = D + 4;
+  __shared__ __align__(16) float Ss[D * PITCH];
+  __shared__ float zs[D];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, col = lane & 31;
   const long wg = blockIdx.x;
   const long bhf = wg / nco;
+  const long bh = bhf / F;
+  const int f = (int)(bhf % F);
   const int n0 = (int)(wg % nco) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const float* Sf = prefix + (size_t)bhf * (D * D + D);
-  const float* zf = Sf + D * D;
+
+  // the state this frame reads: initial state plus every frame of its block and before
+  relu_frame_state<D>(partial, init, bh, f, F, nc, bfr, Ss, PITCH, zs);
+  __syncthreads();
+  if (f == F - 1 && wg % nco == 0) {  // the last frame's state is the call's final state
+    for (int e = threadIdx.x; e < D * D; e += 256) {
+      if (S_out) S_out[(size_t)bh * D * D + e] = Ss[(e / D) * PITCH + e % D];
+    }
+    if (z_out && threadIdx.x < D) z_out[(size_t)bh * D + threadIdx.x] = zs[threadIdx.x];
+  }
 
   // A operands: S[32I + col][16s + 8g + e] as bf16 hi and lo terms
   u32x4 ahi[DB][KS], alo[DB][KS];
@@ -150,14 +175,12 @@ __global__ __launch_bounds__(256) void relu_output_mfma(
   for (int I = 0; I < DB; ++I) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const float* src = Sf + (size_t)(I * 32 + col) * D + s * 16 + g * 8;
+      const float* src = Ss + (I * 32 + col) * PITCH + s * 16 + g * 8;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        uint16_t h0, l0, h1, l1;
-        split_bf16(src[2 * e], h0, l0);
-        split_bf16(src[2 * e + 1], h1, l1);
-        ahi[I][s][e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        alo[I][s][e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        const uint2 hl = split_bf16x2(src[2 * e], src[2 * e + 1]);
+        ahi[I][s][e] = hl.x;
+        alo[I][s][e] = hl.y;
       }
     }
   }
@@ -165,49 +188,67 @@ __global__ __launch_bounds__(256) void relu_output_mfma(
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zr[s][e] = zf[s * 16 + g * 8 + e];
+    for (int e = 0; e < 8; ++e) zr[s][e] = zs[s * 16 + g * 8 + e];
 
-  for (int t0 = n0 + wave * TILE; t0 < n1; t0 += 4 * TILE) {
-    const int t = t0 + col;
-    const bool valid = t < n1;
-    const uint16_t* qrow = q + ((size_t)bhf * N + (valid ? t : n0)) * D;
-    u32x4 b[KS];
+  const uint16_t* qf = q + (size_t)bhf * N * D;
+  uint16_t* of = o + (size_t)bhf * N * D;
+  // U groups of 32 tokens per wave; the next step's query fragments are in
+  // flight while the current ones are contracted
+  auto load = [&](u32x4 (&b)[U][KS], int t0) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      b[s] = ld16(qrow + s * 16 + g * 8);
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 32 + col;
+      const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * D + g * 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) b[s][e] = relu_bf16x2(b[s][e]);
+      for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
     }
-    float den = 0.0f;
+  };
+  auto compute = [&](u32x4 (&b)[U][KS], int t0) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[s][e]), den);
-        den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[s][e]), den);
-      }
-    }
-    den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims
-    const float inv = 1.0f / (den + eps);
-    uint16_t* orow = o + ((size_t)bhf * N + t) * D;
-#pragma unroll
-    for (int I = 0; I < DB; ++I) {
-      floatx16 acc = {};
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 32 + col;
+      float den = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[s]), acc);
-        acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[s]), acc);
-      }
-      if (valid) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint2 w;
-          w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
-          w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + I * 32 + 8 * q4 + 4 * g) = w;
+        for (int e = 0; e < 4; ++e) {
+          b[u][s][e] = relu_bf16x2(b[u][s][e]);
+          den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
+          den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
+        }
+      }
+      den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims
+      const float inv = 1.0f / (den + eps);
+#pragma unroll
+      for (int I = 0; I < DB; ++I) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[u][s]), acc);
+          acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[u][s]), acc);
+        }
+        if (t < n1) {
+          uint16_t* orow = of + (size_t)t * D + I * 32 + 4 * g;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
+            w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
+          }
         }
       }
     }
+  };
+  u32x4 b0[U][KS], b1[U][KS];
+  int t0 = n0 + wave * U * 32;
+  if (t0 < n1) load(b0, t0);
+  for (; t0 < n1; t0 += 2 * STEP) {
+    if (t0 + STEP < n1) load(b1, t0 + STEP);
+    compute(b0, t0);
+    if (t0 + STEP >= n1) break;
+    if (t0 + 2 * STEP < n1) load(b0, t0 + 2 * STEP);
+    compute(b1, t0 + STEP);
   }
 }
 
@@ -215,29 +256,31 @@ __global__ __launch_bounds__(256) void relu_output_mfma(
 
 bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D == 64); }
 
-hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial, long bhf,
+hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
+                                    const float* S0, const float* z0, float* init, long bhf, int F,
                                     int N, int nc, int chunk, hipStream_t st) {
   dim3 grid((unsigned)(bhf * nc)), block(256);
   if (D == 32)
     hipLaunchKernelGGL(relu_summary_mfma<32>, grid, block, 0, st, (const uint16_t*)k,
-                       (const uint16_t*)v, partial, N, nc, chunk);
+                       (const uint16_t*)v, partial, S0, z0, init, F, N, nc, chunk);
   else if (D == 64)
     hipLaunchKernelGGL(relu_summary_mfma<64>, grid, block, 0, st, (const uint16_t*)k,
-                       (const uint16_t*)v, partial, N, nc, chunk);
+                       (const uint16_t*)v, partial, S0, z0, init, F, N, nc, chunk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* prefix, float eps,
-                                   long bhf, int N, int nco, int chunk, hipStream_t st) {
+hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* partial,
+                                   const float* init, float* S_out, float* z_out, float eps, long bhf,
+                                   int F, int N, int nc, int bfr, int nco, int chunk, hipStream_t st) {
   dim3 grid((unsigned)(bhf * nco)), block(256);
   if (D == 32)
     hipLaunchKernelGGL(relu_output_mfma<32>, grid, block, 0, st, (const uint16_t*)q, (uint16_t*)o,
-                       prefix, eps, N, nco, chunk);
+                       partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk);
   else if (D == 64)
     hipLaunchKernelGGL(relu_output_mfma<64>, grid, block, 0, st, (const uint16_t*)q, (uint16_t*)o,
-                       prefix, eps, N, nco, chunk);
+                       partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

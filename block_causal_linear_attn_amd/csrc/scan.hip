@@ -1,65 +1,31 @@
-// scan.hip -- the sequential-over-frames parts of both scans, the state carry,
-// and the dispatch between MFMA and generic kernels.
-//
-// ReLU prefix: the ReLU state is a plain running sum, so frame f's state is
-// the initial state plus the contributions of every frame in blocks up to and
-// including f's block (a block reads the state after all of its own frames;
-// SANA-Video practical guide, section on core mechanisms).
+// scan.hip -- the generic GDN frame scan, the state carry, and the dispatch
+// between MFMA and generic kernels.
 //
 // GDN scan: S_f = alpha_f S_{f-1} (I - beta_f G_f) + beta_f U_f.  Rows of S
 // evolve independently given G_f (row r of S_f needs only row r of S_{f-1}),
-// so each workgroup owns 16 rows of one head's state and walks all frames;
-// the D x D product S_rows G_f runs in fp32 on the VALU against G_f staged in
-// LDS.
+// so each workgroup owns 16 rows of one head's state and walks all frames.
+// The generic kernel here runs the D x D product S_rows G_f in fp32 on the
+// VALU against G_f staged in LDS (the fp32-token path); the bf16 head-dim-128
+// path uses the MFMA scan next to its gram kernel.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace linscan {
 
-hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial, long bhf,
+hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
+                                    const float* S0, const float* z0, float* init, long bhf, int F,
                                     int N, int nc, int chunk, hipStream_t st);
-hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* prefix, float eps,
-                                   long bhf, int N, int nco, int chunk, hipStream_t st);
-hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, float* partial, float c,
-                                float c2, long bhf, int N, int nc, int chunk, hipStream_t st);
+hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* partial,
+                                   const float* init, float* S_out, float* z_out, float eps, long bhf,
+                                   int F, int N, int nc, int bfr, int nco, int chunk, hipStream_t st);
+hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
+                                float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st);
+hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
+                                void* states, float* S_out, long bh, int F, int nc, hipStream_t st);
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
                                   int N, int nco, int chunk, hipStream_t st);
-hipError_t launch_summary_generic(int D, int dtype, bool relu, const void* k, const void* v,
-                                  float* partial, float c, float c2, long bhf, int N, int nc, int chunk,
-                                  hipStream_t st);
-hipError_t launch_output_generic(int D, int dtype, bool relu, const void* q, void* o,
-                                 const float* states, size_t stride, float eps, long bhf, int N,
-                                 int nco, int chunk, hipStream_t st);
 
 namespace {
-
-__global__ __launch_bounds__(256) void relu_prefix_kernel(const float* __restrict__ partial,
-                                                          const float* S0, const float* z0,
-                                                          float* __restrict__ prefix, float* S_out,
-                                                          float* z_out, int D, int F, int nc,
-                                                          int block_frames) {
-  const int OUT = D * D + D;
-  const long bh = blockIdx.x;
-  const int e = blockIdx.y * 256 + threadIdx.x;
-  if (e >= OUT) return;
-  float acc = 0.0f;
-  if (e < D * D) {
-    if (S0) acc = S0[(size_t)bh * D * D + e];
-  } else if (z0) {
-    acc = z0[(size_t)bh * D + (e - D * D)];
-  }
-  for (int f0 = 0; f0 < F; f0 += block_frames) {
-    const int f1 = min(F, f0 + block_frames);
-    for (int f = f0; f < f1; ++f)
-      for (int c = 0; c < nc; ++c) acc += partial[(((size_t)bh * F + f) * nc + c) * OUT + e];
-    for (int f = f0; f < f1; ++f) prefix[((size_t)bh * F + f) * OUT + e] = acc;
-  }
-  if (e < D * D) {
-    if (S_out) S_out[(size_t)bh * D * D + e] = acc;
-  } else if (z_out) {
-    z_out[(size_t)bh * D + (e - D * D)] = acc;
-  }
-}
 
 // One workgroup per (batch*head, 16-row block).  State rows live in LDS; G_f
 // is summed over token chunks into LDS each frame; every thread owns EPT
@@ -164,69 +130,64 @@ hipError_t scan_launch(bool hilo, const float* partial, const float* alpha, cons
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ src, float* __restrict__ dst,
-                                                    size_t n, int reset) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
-    dst[i] = reset ? 0.0f : src[i];
+// Copies (or zeroes) two ranges in one launch: the state and the normaliser.
+__global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ src0, float* __restrict__ dst0,
+                                                    size_t n0, const float* __restrict__ src1,
+                                                    float* __restrict__ dst1, size_t n1, int reset) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n0 + n1; i += stride) {
+    if (i < n0)
+      dst0[i] = reset ? 0.0f : src0[i];
+    else
+      dst1[i - n0] = reset ? 0.0f : src1[i - n0];
+  }
 }
 
 }  // namespace
 
-hipError_t launch_relu_summary(int D, bool mfma, int dtype, const void* k, const void* v,
-                               float* partial, long bhf, int N, int nc, int chunk, hipStream_t st) {
-  if (mfma) return launch_relu_summary_mfma(D, k, v, partial, bhf, N, nc, chunk, st);
-  return launch_summary_generic(D, dtype, true, k, v, partial, 1.0f, 1.0f, bhf, N, nc, chunk, st);
+hipError_t launch_relu_summary(const ScanArgs& a, hipStream_t st) {
+  if (a.mfma)
+    return launch_relu_summary_mfma(a.D, a.k, a.v, a.partial, a.S0, a.z0, a.init, a.bhf, a.F, a.N,
+                                    a.nc, a.chunk, st);
+  return launch_summary_generic(a, st);
 }
 
-hipError_t launch_relu_prefix(int D, const float* partial, const float* S0, const float* z0,
-                              float* prefix, float* S_out, float* z_out, long bh, int F, int nc,
-                              int block_frames, hipStream_t st) {
-  dim3 grid((unsigned)bh, (unsigned)((D * D + D + 255) / 256)), block(256);
-  hipLaunchKernelGGL(relu_prefix_kernel, grid, block, 0, st, partial, S0, z0, prefix, S_out, z_out,
-                     D, F, nc, block_frames);
-  return hipGetLastError();
+hipError_t launch_relu_output(const ScanArgs& a, hipStream_t st) {
+  if (a.mfma)
+    return launch_relu_output_mfma(a.D, a.q, a.o, a.partial, a.init, a.S_out, a.z_out, a.eps, a.bhf,
+                                   a.F, a.N, a.nc, a.bfr, a.nco, a.chunko, st);
+  return launch_output_generic(a, st);
 }
 
-hipError_t launch_relu_output(int D, bool mfma, int dtype, const void* q, void* o,
-                              const float* prefix, float eps, long bhf, int N, int nco, int chunk,
-                              hipStream_t st) {
-  if (mfma) return launch_relu_output_mfma(D, q, o, prefix, eps, bhf, N, nco, chunk, st);
-  return launch_output_generic(D, dtype, true, q, o, prefix, (size_t)D * D + D, eps, bhf, N, nco,
-                               chunk, st);
+hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st) {
+  if (a.mfma)
+    return launch_gdn_gram_mfma(a.D, a.k, a.v, a.beta, a.partial, a.c, a.c2, a.bhf, a.N, a.nc, a.chunk, st);
+  return launch_summary_generic(a, st);
 }
 
-hipError_t launch_gdn_gram(int D, bool mfma, int dtype, const void* k, const void* v,
-                           float* partial, float c, float c2, long bhf, int N, int nc, int chunk,
-                           hipStream_t st) {
-  if (mfma) return launch_gdn_gram_mfma(D, k, v, partial, c, c2, bhf, N, nc, chunk, st);
-  return launch_summary_generic(D, dtype, false, k, v, partial, c, c2, bhf, N, nc, chunk, st);
-}
-
-hipError_t launch_gdn_scan(int D, bool hilo, const float* partial, const float* alpha,
-                           const float* beta, const float* S0, void* states, float* S_out,
-                           long bh, int F, int nc, hipStream_t st) {
-  switch (D) {
+hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st) {
+  if (a.mfma) return launch_gdn_scan_mfma(a.D, a.partial, a.alpha, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
+  switch (a.D) {
 #define CASE(d) \
-  case d: return scan_launch<d>(hilo, partial, alpha, beta, S0, states, S_out, bh, F, nc, st);
+  case d: return scan_launch<d>(false, a.partial, a.alpha, a.beta, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
     CASE(16) CASE(32) CASE(48) CASE(64) CASE(80) CASE(96) CASE(112) CASE(128)
 #undef CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gdn_output(int D, bool mfma, int dtype, const void* q, void* o,
-                             const void* states, long bhf, int N, int nco, int chunk,
-                             hipStream_t st) {
-  if (mfma) return launch_gdn_output_mfma(D, q, o, states, bhf, N, nco, chunk, st);
-  return launch_output_generic(D, dtype, false, q, o, (const float*)states, (size_t)D * D, 0.0f,
-                               bhf, N, nco, chunk, st);
+hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st) {
+  if (a.mfma) return launch_gdn_output_mfma(a.D, a.q, a.o, a.states, a.bhf, a.N, a.nco, a.chunko, st);
+  return launch_output_generic(a, st);
 }
 
-hipError_t launch_carry(const float* src, float* dst, size_t n, int reset, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  size_t blocks = (n + 255) / 256;
+hipError_t launch_carry(const float* src0, float* dst0, size_t n0, const float* src1, float* dst1,
+                        size_t n1, int reset, hipStream_t st) {
+  if (n0 + n1 == 0) return hipSuccess;
+  size_t blocks = (n0 + n1 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, n, reset);
+  hipLaunchKernelGGL(carry_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src0, dst0, n0, src1,
+                     dst1, n1, reset);
   return hipGetLastError();
 }
 
