@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads per part in the oracle sample (default: oracle threads)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy three times (counter calibration)")
     return ap.parse_args()
 
 
@@ -55,6 +57,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calib_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch, for
+        # scaling hardware byte counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wv = inputs.WORKLOADS["sana_video_720p_minute"]
     wg = inputs.WORKLOADS["sana_wm_720p_60s"]
 
@@ -127,10 +138,12 @@ def main():
     half_wm = 2 * wg.B * wg.H * wg.F * wg.N * wg.D * elt
     n_calls = len(wv.calls)
     alg = {
-        "relu_summary": half_video / n_calls,   # k, v in (per call, averaged over the 25 calls)
-        "relu_output": half_video / n_calls,    # q in, o out
-        "gdn_gram": half_wm,                    # k, v in
-        "gdn_output": half_wm,                  # q in, o out
+        "relu_fused": 2 * half_video / n_calls,  # q, k, v in, o out (per call, averaged over the calls)
+        "relu_summary": half_video / n_calls,    # k, v in
+        "relu_output": half_video / n_calls,     # q in, o out
+        "gdn_fused": 2 * half_wm,                # q, k, v in, o out
+        "gdn_gram": half_wm,                     # k, v in
+        "gdn_output": half_wm,                   # q in, o out
     }
     kernels = {}
     for name, (launches, total_ms) in kstats.items():

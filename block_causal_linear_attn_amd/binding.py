@@ -8,7 +8,7 @@ raises on import: there is no fallback implementation.
 """
 from __future__ import annotations
 
-import ctypes
+import ctypes  # noqa: F401  (re-exported for callers building ls_shape)
 import os
 import threading
 

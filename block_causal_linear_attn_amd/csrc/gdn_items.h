@@ -1,0 +1,424 @@
+// gdn_items.h -- bf16 MFMA work items of the frame-wise Gated DeltaNet scan for
+// head dim 128 (SANA-WM's frame-wise GDN: one state update per latent frame
+// from all of its spatial tokens, keys scaled by 1/sqrt(D*N)).
+//
+// Gram pass: per frame, G = c^2 K^T K and U = c V^T K (each 128 x 128) are 16
+// blocks of 32 x 32 apiece.  Wave w owns block row w of both, so every wave
+// needs all four key fragments and one value fragment per 16-token k-step.
+// The workgroup stages 64-token K and V tiles in LDS (double buffered, next
+// tile's HBM loads in flight while the current one is contracted) and each
+// lane gathers 8 tokens of one dimension per operand with two LDS transpose
+// reads.  Inputs are exact bf16
+// products accumulated in fp32; c and c^2 are applied once at the end.
+//
+// Output pass: o = S_f q.  Wave w computes output dims [32w, 32w + 32) from
+// S_f's rows held in registers as bf16 hi + lo terms (written by the scan),
+// against 64-token query tiles staged once per workgroup in LDS.
+#pragma once
+
+#include "device_common.h"
+#include "sync.h"
+
+namespace linscan {
+
+constexpr int GD = 128;
+// bytes of one (frame, token chunk) record: beta*G hi and lo planes (bf16) + beta*U (fp32)
+constexpr size_t kRecBytes = 8 * (size_t)GD * GD;
+
+constexpr int kGramLds = 2 * 2 * 64 * (GD + 4) * 2;
+
+// Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
+// (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.
+__device__ __forceinline__ void gdn_gram_item(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw) {
+  constexpr int D = GD;
+  constexpr int TILE = 64;
+  constexpr int ROW = D + 4;  // 264-byte pitch: the two lane groups' gathers land 16 banks apart
+  constexpr int LPT = TILE * (D / 8) / 256;  // 16-byte loads per thread per tensor per tile (4)
+  typedef uint16_t TileT[2][TILE * ROW];
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][K, V][TILE * ROW]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = wg / nc;
+  const int n0 = (int)(wg % nc) * chunk;
+  const int n1 = min(N, n0 + chunk);
+  const uint16_t* kf = k + (size_t)bhf * N * D;
+  const uint16_t* vf = v + (size_t)bhf * N * D;
+
+  floatx16 accG[4], accU[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    accG[j] = floatx16{};
+    accU[j] = floatx16{};
+  }
+
+  u32x4 kr[LPT], vr[LPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const int n = t0 + tok;
+      if (n < n1) {
+        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
+        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
+      } else {
+        kr[r] = u32x4{0u, 0u, 0u, 0u};
+        vr[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][tok * ROW + cb * 8]);
+      uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][tok * ROW + cb * 8]);
+      kd[0] = make_uint2(kr[r][0], kr[r][1]);
+      kd[1] = make_uint2(kr[r][2], kr[r][3]);
+      vd[0] = make_uint2(vr[r][0], vr[r][1]);
+      vd[1] = make_uint2(vr[r][2], vr[r][3]);
+    }
+  };
+
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+  if (ntiles > 0) {
+    fetch(n0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) fetch(n0 + (it + 1) * TILE);
+    const uint16_t* kl = lds[buf][0];
+    const uint16_t* vl = lds[buf][1];
+#pragma unroll
+    for (int s = 0; s < TILE / 16; ++s) {
+      u32x4 kfrag[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32<ROW>(kl, s * 16, J * 32, lane);
+      const u32x4 vfrag = gather_tokens_32<ROW>(vl, s * 16, wave * 32, lane);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        accG[J] = mfma32x32x16(as_bf16x8(kfrag[wave]), as_bf16x8(kfrag[J]), accG[J]);
+        accU[J] = mfma32x32x16(as_bf16x8(vfrag), as_bf16x8(kfrag[J]), accU[J]);
+      }
+    }
+    if (it + 1 < ntiles) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // record of this (frame, chunk): beta*G as bf16 hi and lo planes (row-major),
+  // then beta*U in fp32 with each group of four rows interleaved, element
+  // (m, n) at ((m / 4) * D + n) * 4 + m % 4, so that the four rows a scan lane
+  // owns in one column are one 16-byte load
+  const float bf = beta[bhf];
+  const float gs = c2 * bf, us = c * bf;
+  uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)wg * kRecBytes);
+  uint16_t* Glo = Ghi + D * D;
+  float* Ud = reinterpret_cast<float*>(Glo + D * D);
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = wave * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      uint16_t h, l;
+      split_bf16(gs * accG[J][r], h, l);
+      Ghi[m * D + J * 32 + col] = h;
+      Glo[m * D + J * 32 + col] = l;
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int m0 = wave * 32 + 8 * q4 + 4 * g;  // rows m0 .. m0 + 3 sit in regs 4 q4 .. 4 q4 + 3
+      float4 u4 = make_float4(us * accU[J][4 * q4], us * accU[J][4 * q4 + 1], us * accU[J][4 * q4 + 2],
+                              us * accU[J][4 * q4 + 3]);
+      *reinterpret_cast<float4*>(Ud + ((size_t)(m0 >> 2) * D + J * 32 + col) * 4) = u4;
+    }
+  }
+}
+
+// One workgroup per (batch*head, 16-row block of S); a head's eight row
+// blocks get block ids that are equal mod 8, so they run on one XCD and
+// share its L2 copy of each frame's record.  Per frame:
+//   S_rows <- alpha (S_rows - S_rows (beta G)) + beta U
+// The product runs as three bf16 MFMAs on hi/lo splits of S and beta G
+// (dropping only lo*lo), accumulated in fp32; S stays fp32 in registers (C
+// layout) and in a double-buffered LDS copy that feeds the next frame's A
+// operands.  G is symmetric, so the B operand (8 consecutive k of column n)
+// is read as 16 contiguous bytes of row n.
+//
+// The frame loop is a dependency chain, so it is kept free of branches and
+// light on memory instructions: records are fetched two frames ahead into a
+// register ring (always issued, with the frame index clamped at the end;
+// fused into one launch with the gram items, a frame's record is loaded once
+// its flag is up, straight from the XCD's L2),
+// the decays of up to kAlphaWin frames sit in LDS, and each frame's state is
+// written back with two 16-byte stores per thread from the LDS copy.  MULTI
+// handles frames split into several token chunks (one record per chunk).
+constexpr int kAlphaWin = 2048;
+constexpr int kScanRB = 16, kScanPitch = GD + 4;
+constexpr int kScanLds = 2 * kScanRB * kScanPitch * 4 + kAlphaWin * 4;
+
+// Scan item of rows [r0, r0 + 16) of head `head`'s state over all F frames.
+// FUSED: records come from gram items of the same launch (wait for gflags
+// before each frame, one flag per token chunk) and each frame's state is
+// announced on sflags[(head * F + f) * 8 + r0 / 16] for the output items.
+template <bool MULTI, bool FUSED>
+__device__ __forceinline__ void gdn_scan_item(
+    const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
+    uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, int nc, uint8_t* lds_raw,
+    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err) {
+  constexpr int D = GD, RB = kScanRB, PITCH = kScanPitch;
+  typedef float RowsT[RB][PITCH];
+  RowsT* Ss = reinterpret_cast<RowsT*>(lds_raw);                         // [2][RB][PITCH]
+  float* As = reinterpret_cast<float*>(lds_raw + 2 * RB * PITCH * 4);    // [kAlphaWin]
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  float s[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+      s[nb][r] = S0 ? S0[(size_t)head * D * D + (size_t)(r0 + m) * D + n] : 0.0f;
+      Ss[0][m][n] = s[nb][r];
+    }
+
+  struct Rec {
+    u32x4 hi[2][4], lo[2][4];
+    float u[2][4];
+  };
+  const size_t hf0 = (size_t)head * F;
+  auto load_rec = [&](int f, int cidx, Rec& R) {
+    const uint8_t* base = rec + ((hf0 + f) * nc + cidx) * kRecBytes;
+    const uint16_t* gh = reinterpret_cast<const uint16_t*>(base);
+    const uint16_t* gl = gh + D * D;
+    const float* U = reinterpret_cast<const float*>(gl + D * D);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int n = 32 * wave + 16 * nb + lr;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const size_t off = (size_t)n * D + 32 * s4 + 8 * lg;
+        R.hi[nb][s4] = ld16(gh + off);
+        R.lo[nb][s4] = ld16(gl + off);
+      }
+      const float4 u4 = *reinterpret_cast<const float4*>(U + ((size_t)((r0 >> 2) + lg) * D + n) * 4);
+      R.u[nb][0] = u4.x;
+      R.u[nb][1] = u4.y;
+      R.u[nb][2] = u4.z;
+      R.u[nb][3] = u4.w;
+    }
+  };
+  // S_f leaves for the output pass from the LDS copy the next frame reads
+  // anyway: each thread splits 8 consecutive entries of one row and writes
+  // them to the hi and lo planes with two 16-byte stores
+  auto store_state = [&](int f, int buf) {
+    const int row = tid >> 4, c0 = 8 * (tid & 15);
+    const float* src = &Ss[buf][row][c0];
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+    const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+    uint16_t* hp = states + (hf0 + f) * 2 * D * D + (size_t)(r0 + row) * D + c0;
+    st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
+    st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+  };
+  // hi*hi, hi*lo and lo*hi go to three accumulators: independent MFMA
+  // chains overlap their latencies instead of queueing behind each other
+  auto mfma3 = [&](floatx4 (&acc)[3], const u32x4& ah, const u32x4& al, const u32x4& bh_, const u32x4& bl_) {
+    acc[0] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(bh_), acc[0]);
+    acc[1] = mfma16x16x32(as_bf16x8(ah), as_bf16x8(bl_), acc[1]);
+    acc[2] = mfma16x16x32(as_bf16x8(al), as_bf16x8(bh_), acc[2]);
+  };
+
+  Rec R0, R1;
+  if (!FUSED && F > 0) {
+    load_rec(0, 0, R0);
+    load_rec(min(1, F - 1), 0, R1);
+  }
+
+  auto frame = [&](int f, Rec& R) {
+    const int cur = f & 1;
+    if (FUSED) {
+      // this frame's records are published by gram items; the previous
+      // frame's state (stored by every thread) is announced once all are done
+      __builtin_amdgcn_s_waitcnt(0);
+      wait_all(&gflags[(hf0 + f) * nc], nc, epoch, err);
+      if (f > 0 && tid == 0)
+        __hip_atomic_store(&sflags[(hf0 + f - 1) * 8 + r0 / RB], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      load_rec(f, 0, R);
+    }
+    const float a = As[f % kAlphaWin];
+    // A operands: this workgroup's 16 rows of S_{f-1}, split into bf16 hi + lo
+    u32x4 ahi[4], alo[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float* src = &Ss[cur][lr][32 * s4 + 8 * lg];
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+      const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+      ahi[s4] = u32x4{p0.x, p1.x, p2.x, p3.x};
+      alo[s4] = u32x4{p0.y, p1.y, p2.y, p3.y};
+    }
+    floatx4 acc3[2][3];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int t = 0; t < 3; ++t) acc3[nb][t] = floatx4{};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) mfma3(acc3[nb], ahi[s4], alo[s4], R.hi[nb][s4], R.lo[nb][s4]);
+    float uf[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) uf[nb][r] = R.u[nb][r];
+    if (MULTI) {
+      for (int cidx = 1; cidx < nc; ++cidx) {  // the frame's further token chunks
+        Rec T;
+        load_rec(f, cidx, T);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) mfma3(acc3[nb], ahi[s4], alo[s4], T.hi[nb][s4], T.lo[nb][s4]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) uf[nb][r] += T.u[nb][r];
+        }
+      }
+    }
+    // refill this ring slot two frames ahead (the last record again at the end)
+    if (!FUSED) load_rec(min(f + 2, F - 1), 0, R);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+        const float prod = acc3[nb][0][r] + (acc3[nb][1][r] + acc3[nb][2][r]);
+        s[nb][r] = a * (s[nb][r] - prod) + uf[nb][r];
+        Ss[cur ^ 1][m][n] = s[nb][r];
+      }
+    __syncthreads();
+    store_state(f, cur ^ 1);
+  };
+
+  for (int w0 = 0; w0 < F; w0 += kAlphaWin) {
+    const int w1 = min(F, w0 + kAlphaWin);
+    for (int i = tid; i < w1 - w0; i += 256) As[i] = alpha[hf0 + w0 + i];
+    __syncthreads();
+    int f = w0;
+    for (; f + 2 <= w1; f += 2) {
+      frame(f, R0);
+      frame(f + 1, R1);
+    }
+    if (f < w1) frame(f, R0);  // window tail (kAlphaWin is even, so slot f % 2 == 0)
+    __syncthreads();  // As is rewritten for the next window
+  }
+  if (FUSED && F > 0) publish(&sflags[(hf0 + F - 1) * 8 + r0 / RB], epoch);
+  if (S_out) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S_out[(size_t)head * D * D + (size_t)(r0 + 4 * lg + r) * D + 32 * wave + 16 * nb + lr] = s[nb][r];
+  }
+}
+
+constexpr int kOutLds = 2 * 64 * (GD + 8) * 2;
+
+// Work item `wg` = (frame of one head) * nco + token chunk: o = S_f q.
+__device__ __forceinline__ void gdn_output_item(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
+    int N, int nco, int chunk, long wg, uint8_t* lds_raw) {
+  constexpr int D = GD;
+  constexpr int TILE = 64;
+  constexpr int ROW = D + 8;  // 272-byte pitch: 16-byte fragment reads spread over all banks
+  constexpr int LPT = TILE * (D / 8) / 256;  // 4
+  typedef uint16_t TileT[TILE * ROW];
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][TILE * ROW]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = wg / nco;
+  const int n0 = (int)(wg % nco) * chunk;
+  const int n1 = min(N, n0 + chunk);
+
+  // A operands: rows 32*wave + col of S_f, dims 16s + 8g .. +7, hi and lo planes
+  const uint16_t* hi = states + (size_t)bhf * 2 * D * D;
+  const uint16_t* lo = hi + D * D;
+  u32x4 ahi[8], alo[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const size_t off = (size_t)(wave * 32 + col) * D + s * 16 + g * 8;
+    ahi[s] = ld16(hi + off);
+    alo[s] = ld16(lo + off);
+  }
+
+  const uint16_t* qf = q + (size_t)bhf * N * D;
+  uint16_t* of = o + (size_t)bhf * N * D;
+  u32x4 qr[LPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const int n = t0 + tok;
+      qr[r] = (n < n1) ? ld16(qf + (size_t)n * D + cb * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qr[r];
+    }
+  };
+
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+  if (ntiles > 0) {
+    fetch(n0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = n0 + it * TILE;
+    if (it + 1 < ntiles) fetch(t0 + TILE);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx16 acc = {};
+      const uint16_t* qrow = &lds[buf][(half * 32 + col) * ROW + g * 8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(qrow + s * 16);
+        acc = mfma32x32x16(as_bf16x8(ahi[s]), as_bf16x8(b), acc);
+        acc = mfma32x32x16(as_bf16x8(alo[s]), as_bf16x8(b), acc);
+      }
+      const int t = t0 + half * 32 + col;
+      if (t < n1) {
+        uint16_t* orow = of + (size_t)t * D + wave * 32 + 4 * g;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 w;
+          w.x = pack_bf16x2(acc[4 * q4 + 0], acc[4 * q4 + 1]);
+          w.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+          *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
+        }
+      }
+    }
+    if (it + 1 < ntiles) stage(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace linscan

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace linscan {
 
@@ -66,6 +67,17 @@ hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st);
 hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st);
 // Per (frame, token chunk): o = S_f q.
 hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
+
+// One launch for a whole call (MFMA paths): work items exchange partials,
+// records and states through flags set to `epoch`; `err` is set if a bounded
+// wait timed out.  bhp = B*H rounded up to a multiple of 8.
+//  ReLU: flags[B*H*F]; summary with one chunk per frame (nc = 1).
+hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
+                                  uint32_t* err, hipStream_t st);
+//  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states);
+//  only for B*H*8 <= 256 so that scan items never fill the chip.
+hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
+                                 uint64_t epoch, uint32_t* err, hipStream_t st);
 
 // Generic (VALU) summary and output kernels of either path.
 hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);

@@ -8,7 +8,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 #include <string>
 #include <vector>
 
@@ -36,6 +39,23 @@ bool supported_d(int D) {
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspaces start with a 256-byte header whose first word is the fault word.
+constexpr size_t kHeaderBytes = 256;
+
+// Epochs tag the flags of one launch: a 64-bit sequence that starts from a
+// random value per process, so flags left in a reused workspace never match.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{0};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    counter.store(((((uint64_t)rd()) << 32) ^ rd() ^ (t * 0x9e3779b97f4a7c15ull)) | 1ull);
+  });
+  uint64_t e = counter.fetch_add(1);
+  return e ? e : counter.fetch_add(1);
+}
 
 struct Dims {
   long bh = 0;      // B*H
@@ -93,43 +113,56 @@ void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, 
 }
 
 struct ReluPlan {
-  bool mfma;
+  bool mfma, fused;
   int nc, chunk, nco, chunko;
-  size_t partial_off, init_off, bytes;
+  size_t partial_off, init_off, flags_off, bytes;
 };
 
 ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   ReluPlan p;
   p.mfma = linscan::relu_has_mfma(s->D, s->dtype);
-  // summary: whole frames per workgroup unless there are too few frames to
-  // fill the chip; each output workgroup sums the partials of its frame and
-  // all earlier ones, so fewer partials per frame keep that read small
-  plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
+  p.fused = p.mfma;  // one launch: summary items then output items
+  // summary: whole frames per item unless there are too few frames to fill
+  // the chip (the fused launch always uses whole frames); each output item
+  // sums the partials of its frame and all earlier ones, so fewer partials
+  // per frame keep that read small
+  if (p.fused) {
+    p.nc = 1;
+    p.chunk = s->N > 0 ? s->N : 1;
+  } else {
+    plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
+  }
   plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
   const size_t out = (size_t)s->D * s->D + s->D;
-  p.partial_off = 0;
-  p.init_off = align_up((size_t)d.bhf * p.nc * out * sizeof(float), 256);
-  p.bytes = align_up(p.init_off + (size_t)d.bh * out * sizeof(float), 256);
+  p.partial_off = kHeaderBytes;
+  p.init_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * out * sizeof(float), 256);
+  p.flags_off = align_up(p.init_off + (size_t)d.bh * out * sizeof(float), 256);
+  p.bytes = align_up(p.flags_off + (p.fused ? (size_t)d.bhf * sizeof(uint64_t) : 0), 256);
   return p;
 }
 
 struct GdnPlan {
-  bool mfma;
+  bool mfma, fused;
   int nc, chunk, nco, chunko;
-  size_t partial_off, states_off, bytes;
+  size_t partial_off, states_off, gflags_off, sflags_off, bytes;
 };
 
 GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   GdnPlan p;
   p.mfma = linscan::gdn_has_mfma(s->D, s->dtype);
+  // one launch (scan items alongside the streaming items) when the scan items
+  // fill at most one slot per CU and there are frames to overlap
+  p.fused = p.mfma && d.bh * 8 <= 256 && s->F >= 2 && s->N > 0;
   // a chunk's G/U partials are 8 D^2 bytes: keep chunks long enough that they
   // stay small next to the chunk's own key/value bytes
   plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
   plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
   const size_t dd = (size_t)s->D * s->D;
-  p.partial_off = 0;
-  p.states_off = align_up((size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
-  p.bytes = align_up(p.states_off + (size_t)d.bhf * dd * sizeof(float), 256);
+  p.partial_off = kHeaderBytes;
+  p.states_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
+  p.gflags_off = align_up(p.states_off + (size_t)d.bhf * dd * sizeof(float), 256);
+  p.sflags_off = align_up(p.gflags_off + (p.fused ? (size_t)d.bhf * p.nc * sizeof(uint64_t) : 0), 256);
+  p.bytes = align_up(p.sflags_off + (p.fused ? (size_t)d.bhf * 8 * sizeof(uint64_t) : 0), 256);
   return p;
 }
 
@@ -347,6 +380,14 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   a.nco = p.nco;
   a.chunko = p.chunko;
   a.bfr = block_frames;
+  if (p.fused) {
+    const long bhp = (d.bh + 7) / 8 * 8;
+    uint64_t* flags = (uint64_t*)(ws + p.flags_off);
+    uint32_t* err = (uint32_t*)ws;
+    const uint64_t epoch = next_epoch();
+    return hip_check(timed("relu_fused", hs, [&] { return linscan::launch_relu_fused_mfma(a, bhp, flags, epoch, err, hs); }),
+                     "relu fused");
+  }
   if ((st = hip_check(timed("relu_summary", hs, [&] { return linscan::launch_relu_summary(a, hs); }),
                       "relu summary")) != LS_OK)
     return st;
@@ -434,6 +475,16 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   a.chunk = p.chunk;
   a.nco = p.nco;
   a.chunko = p.chunko;
+  if (p.fused) {
+    const long bhp = (d.bh + 7) / 8 * 8;
+    uint64_t* gflags = (uint64_t*)(ws + p.gflags_off);
+    uint64_t* sflags = (uint64_t*)(ws + p.sflags_off);
+    uint32_t* err = (uint32_t*)ws;
+    const uint64_t epoch = next_epoch();
+    return hip_check(timed("gdn_fused", hs, [&] {
+                       return linscan::launch_gdn_fused_mfma(a, bhp, gflags, sflags, epoch, err, hs);
+                     }), "gdn fused");
+  }
   if ((st = hip_check(timed("gdn_gram", hs, [&] { return linscan::launch_gdn_gram(a, hs); }), "gdn gram")) != LS_OK)
     return st;
   if ((st = hip_check(timed("gdn_scan", hs, [&] { return linscan::launch_gdn_scan(a, hs); }), "gdn scan")) != LS_OK)

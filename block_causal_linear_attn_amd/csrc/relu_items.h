@@ -1,0 +1,268 @@
+// relu_items.h -- bf16 MFMA work items of the ReLU block-causal linear-attention
+// scan for head dims 32 and 64 (SANA-Video's linear attention: ReLU feature map,
+// cumulative D x D state plus normaliser, extended frame block by frame block).
+//
+// Summary pass: the per-frame contributions dS = V^T phi(K), dz = 1^T phi(K)
+// contract over tokens, the strided axis of the [N][D] tiles, so each wave
+// stages its 64-token K and V tiles in its own LDS slice and gathers 8 tokens
+// of one dimension per lane as an MFMA operand with two LDS transpose reads
+// (ds_read_b64_tr_b16).  The next tile's HBM loads are in flight meanwhile.
+// The normaliser rides on the same MFMA with an all-ones A operand.
+//
+// Output pass: each workgroup first forms its frame's state from the initial
+// state and the summary partials (the block-causal prefix), then o = S phi(q)
+// contracts over the key dimension, which is contiguous in q, so each lane
+// loads 16-byte query fragments straight from HBM as the MFMA B operand; S is
+// split once into bf16 hi + lo terms (16 significant bits) held in registers,
+// giving fp32-grade numerators from two bf16 MFMAs.  The denominator
+// z . phi(q) is an fp32 dot product on the VALU.
+#pragma once
+
+#include "device_common.h"
+
+namespace linscan {
+
+// LDS bytes the summary item needs.
+template <int D>
+constexpr int relu_summary_lds_bytes() { return 4 * 2 * 64 * (D + 4) * 2; }
+
+// Work item `wg` = (frame of one head) * nc + token chunk: dS, dz partials of
+// the chunk -> partial[wg]; item (frame 0, chunk 0) of each head also copies
+// (S0, z0) into init[head].
+template <int D>
+__device__ __forceinline__ void relu_summary_item(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
+    const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk,
+    long wg, uint8_t* lds_raw) {
+  constexpr int DB = D / 32;            // 32-wide dimension blocks
+  constexpr int TILE = 64;              // tokens per wave per step
+  constexpr int ROW = D + 4;            // LDS row pitch (bf16)
+  constexpr int CPR = D / 8;            // 16-byte chunks per token row
+  constexpr int LPT = TILE * CPR / 64;  // 16-byte loads per lane per tensor per tile
+  constexpr int OUT = D * D + D;
+  typedef uint16_t TileT[2][TILE * ROW];
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [4 waves][K, V][TILE * ROW]
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = wg / nc;
+  const int n0 = (int)(wg % nc) * chunk;
+  const int n1 = min(N, n0 + chunk);
+  const uint16_t* kf = k + (size_t)bhf * N * D;
+  const uint16_t* vf = v + (size_t)bhf * N * D;
+  uint16_t* kl = lds[wave][0];
+  uint16_t* vl = lds[wave][1];
+
+  floatx16 acc[DB][DB];
+  floatx16 accz[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    accz[i] = floatx16{};
+#pragma unroll
+    for (int j = 0; j < DB; ++j) acc[i][j] = floatx16{};
+  }
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+  // the next tile's rows are loaded into registers while the current tile is contracted
+  u32x4 kr[LPT], vr[LPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 64 + lane;
+      const int n = t0 + ci / CPR, cb = ci % CPR;
+      if (n < n1) {
+        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
+        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
+      } else {
+        kr[r] = u32x4{0u, 0u, 0u, 0u};
+        vr[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  int t0 = n0 + wave * TILE;
+  if (t0 < n1) fetch(t0);
+  for (; t0 < n1; t0 += 4 * TILE) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 64 + lane;
+      const int tok = ci / CPR, cb = ci % CPR;
+      u32x4 kk = kr[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
+      uint2* kd = reinterpret_cast<uint2*>(kl + tok * ROW + cb * 8);
+      uint2* vd = reinterpret_cast<uint2*>(vl + tok * ROW + cb * 8);
+      kd[0] = make_uint2(kk[0], kk[1]);
+      kd[1] = make_uint2(kk[2], kk[3]);
+      vd[0] = make_uint2(vr[r][0], vr[r][1]);
+      vd[1] = make_uint2(vr[r][2], vr[r][3]);
+    }
+    if (t0 + 4 * TILE < n1) fetch(t0 + 4 * TILE);
+    __builtin_amdgcn_wave_barrier();
+    // 16 tokens per MFMA k-step
+#pragma unroll
+    for (int s = 0; s < TILE / 16; ++s) {
+      u32x4 af[DB], bfr[DB];
+#pragma unroll
+      for (int blk = 0; blk < DB; ++blk) {
+        af[blk] = gather_tokens_32<ROW>(vl, s * 16, blk * 32, lane);
+        bfr[blk] = gather_tokens_32<ROW>(kl, s * 16, blk * 32, lane);
+      }
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
+        accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // fixed-order reduction of the four waves' partial sums through LDS
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(lds_raw);
+  static_assert(4 * OUT * 4 <= relu_summary_lds_bytes<D>(), "reduction buffer exceeds LDS tile space");
+  float* mine = red + wave * OUT;
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        mine[m * D + j * 32 + col] = acc[i][j][r];
+      }
+    }
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int j = 0; j < DB; ++j) mine[D * D + j * 32 + col] = accz[j][0];
+  }
+  __syncthreads();
+  float* dst = partial + (size_t)wg * OUT;
+  for (int e = threadIdx.x; e < OUT; e += 256)
+    dst[e] = ((red[e] + red[OUT + e]) + red[2 * OUT + e]) + red[3 * OUT + e];
+  relu_copy_init<D>(S0, z0, init, wg, F, nc);
+}
+
+// LDS bytes the output item needs.
+template <int D>
+constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4; }
+
+// Work item `wg` = (frame of one head) * nco + token chunk: the frame's state
+// from init + partials, then o = S phi(q) / (z . phi(q) + eps) for the chunk;
+// the last frame's chunk-0 item writes the final state.
+template <int D>
+__device__ __forceinline__ void relu_output_item(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
+    const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
+    int bfr, int nco, int chunk, long wg, uint8_t* lds_raw) {
+  constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
+  constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
+  constexpr int U = 4;        // 32-token groups per wave per step
+  constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
+  constexpr int PITCH = D + 4;
+  float* Ss = reinterpret_cast<float*>(lds_raw);  // [D][PITCH]
+  float* zs = Ss + D * PITCH;                      // [D]
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = wg / nco;
+  const long bh = bhf / F;
+  const int f = (int)(bhf % F);
+  const int n0 = (int)(wg % nco) * chunk;
+  const int n1 = min(N, n0 + chunk);
+
+  // the state this frame reads: initial state plus every frame of its block and before
+  relu_frame_state<D>(partial, init, bh, f, F, nc, bfr, Ss, PITCH, zs);
+  __syncthreads();
+  if (f == F - 1 && wg % nco == 0) {  // the last frame's state is the call's final state
+    for (int e = threadIdx.x; e < D * D; e += 256) {
+      if (S_out) S_out[(size_t)bh * D * D + e] = Ss[(e / D) * PITCH + e % D];
+    }
+    if (z_out && threadIdx.x < D) z_out[(size_t)bh * D + threadIdx.x] = zs[threadIdx.x];
+  }
+
+  // A operands: S[32I + col][16s + 8g + e] as bf16 hi and lo terms
+  u32x4 ahi[DB][KS], alo[DB][KS];
+#pragma unroll
+  for (int I = 0; I < DB; ++I) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float* src = Ss + (I * 32 + col) * PITCH + s * 16 + g * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 hl = split_bf16x2(src[2 * e], src[2 * e + 1]);
+        ahi[I][s][e] = hl.x;
+        alo[I][s][e] = hl.y;
+      }
+    }
+  }
+  float zr[KS][8];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zr[s][e] = zs[s * 16 + g * 8 + e];
+
+  const uint16_t* qf = q + (size_t)bhf * N * D;
+  uint16_t* of = o + (size_t)bhf * N * D;
+  // U groups of 32 tokens per wave; the next step's query fragments are in
+  // flight while the current ones are contracted
+  auto load = [&](u32x4 (&b)[U][KS], int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 32 + col;
+      const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * D + g * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
+    }
+  };
+  auto compute = [&](u32x4 (&b)[U][KS], int t0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * 32 + col;
+      float den = 0.0f;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b[u][s][e] = relu_bf16x2(b[u][s][e]);
+          den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
+          den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
+        }
+      }
+      den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims
+      const float inv = 1.0f / (den + eps);
+#pragma unroll
+      for (int I = 0; I < DB; ++I) {
+        floatx16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[u][s]), acc);
+          acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[u][s]), acc);
+        }
+        if (t < n1) {
+          uint16_t* orow = of + (size_t)t * D + I * 32 + 4 * g;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
+            w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
+          }
+        }
+      }
+    }
+  };
+  u32x4 b0[U][KS], b1[U][KS];
+  int t0 = n0 + wave * U * 32;
+  if (t0 < n1) load(b0, t0);
+  for (; t0 < n1; t0 += 2 * STEP) {
+    if (t0 + STEP < n1) load(b1, t0 + STEP);
+    compute(b0, t0);
+    if (t0 + STEP >= n1) break;
+    if (t0 + 2 * STEP < n1) load(b0, t0 + 2 * STEP);
+    compute(b1, t0 + STEP);
+  }
+}
+
+}  // namespace linscan

@@ -1,140 +1,31 @@
-// relu_mfma.hip -- bf16 MFMA kernels of the ReLU block-causal linear-attention
-// scan for head dims 32 and 64 (SANA-Video's linear attention: ReLU feature map,
-// cumulative D x D state plus normaliser, extended frame block by frame block).
+// relu_mfma.hip -- kernels and launchers of the bf16 MFMA ReLU linear-attention
+// scan (head dims 32 and 64), built from the work items in relu_items.h.
 //
-// Summary pass: the per-frame contributions dS = V^T phi(K), dz = 1^T phi(K)
-// contract over tokens, the strided axis of the [N][D] tiles, so each wave
-// stages its 64-token K and V tiles in its own LDS slice and gathers 8 tokens
-// of one dimension per lane as an MFMA operand with two LDS transpose reads
-// (ds_read_b64_tr_b16).  The next tile's HBM loads are in flight meanwhile.
-// The normaliser rides on the same MFMA with an all-ones A operand.
-//
-// Output pass: each workgroup first forms its frame's state from the initial
-// state and the summary partials (the block-causal prefix), then o = S phi(q)
-// contracts over the key dimension, which is contiguous in q, so each lane
-// loads 16-byte query fragments straight from HBM as the MFMA B operand; S is
-// split once into bf16 hi + lo terms (16 significant bits) held in registers,
-// giving fp32-grade numerators from two bf16 MFMAs.  The denominator
-// z . phi(q) is an fp32 dot product on the VALU.
-#include "device_common.h"
+// relu_fused_mfma runs one call in a single launch: summary items of each
+// frame interleaved with output items of earlier frames.  An output item waits (bounded spin)
+// until the summaries of its frame's block and every earlier frame of its
+// head are published; since every item it waits on has a lower block id and
+// block ids dispatch in order, those items are running or done, so the wait
+// ends.  Every item of a head gets block ids equal to the head modulo 8, so
+// they share one XCD and exchange partials through its L2.  The separate
+// summary and output kernels remain for shapes where a single launch does not
+// apply.
+#include "relu_items.h"
 #include "kernels.h"
+#include "sync.h"
 
 namespace linscan {
 
 namespace {
 
+constexpr int kReluLag = 1;  // frames the output items trail the summary items
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void relu_summary_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
     const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk) {
-  constexpr int DB = D / 32;            // 32-wide dimension blocks
-  constexpr int TILE = 64;              // tokens per wave per step
-  constexpr int ROW = D + 4;            // LDS row pitch (bf16)
-  constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  constexpr int LPT = TILE * CPR / 64;  // 16-byte loads per lane per tensor per tile
-  constexpr int OUT = D * D + D;
-  __shared__ __align__(16) uint16_t lds[4][2][TILE * ROW];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 5, col = lane & 31;
-  const long wg = blockIdx.x;
-  const long bhf = wg / nc;
-  const int n0 = (int)(wg % nc) * chunk;
-  const int n1 = min(N, n0 + chunk);
-  const uint16_t* kf = k + (size_t)bhf * N * D;
-  const uint16_t* vf = v + (size_t)bhf * N * D;
-  uint16_t* kl = lds[wave][0];
-  uint16_t* vl = lds[wave][1];
-
-  floatx16 acc[DB][DB];
-  floatx16 accz[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    accz[i] = floatx16{};
-#pragma unroll
-    for (int j = 0; j < DB; ++j) acc[i][j] = floatx16{};
-  }
-  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-
-  // the next tile's rows are loaded into registers while the current tile is contracted
-  u32x4 kr[LPT], vr[LPT];
-  auto fetch = [&](int t0) {
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int ci = r * 64 + lane;
-      const int n = t0 + ci / CPR, cb = ci % CPR;
-      if (n < n1) {
-        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
-        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
-      } else {
-        kr[r] = u32x4{0u, 0u, 0u, 0u};
-        vr[r] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  int t0 = n0 + wave * TILE;
-  if (t0 < n1) fetch(t0);
-  for (; t0 < n1; t0 += 4 * TILE) {
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int ci = r * 64 + lane;
-      const int tok = ci / CPR, cb = ci % CPR;
-      u32x4 kk = kr[r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
-      uint2* kd = reinterpret_cast<uint2*>(kl + tok * ROW + cb * 8);
-      uint2* vd = reinterpret_cast<uint2*>(vl + tok * ROW + cb * 8);
-      kd[0] = make_uint2(kk[0], kk[1]);
-      kd[1] = make_uint2(kk[2], kk[3]);
-      vd[0] = make_uint2(vr[r][0], vr[r][1]);
-      vd[1] = make_uint2(vr[r][2], vr[r][3]);
-    }
-    if (t0 + 4 * TILE < n1) fetch(t0 + 4 * TILE);
-    __builtin_amdgcn_wave_barrier();
-    // 16 tokens per MFMA k-step
-#pragma unroll
-    for (int s = 0; s < TILE / 16; ++s) {
-      u32x4 af[DB], bfr[DB];
-#pragma unroll
-      for (int blk = 0; blk < DB; ++blk) {
-        af[blk] = gather_tokens_32<ROW>(vl, s * 16, blk * 32, lane);
-        bfr[blk] = gather_tokens_32<ROW>(kl, s * 16, blk * 32, lane);
-      }
-#pragma unroll
-      for (int j = 0; j < DB; ++j) {
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
-        accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // fixed-order reduction of the four waves' partial sums through LDS
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&lds[0][0][0]);
-  static_assert(4 * OUT * 4 <= (int)sizeof(lds), "reduction buffer exceeds LDS tile space");
-  float* mine = red + wave * OUT;
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-#pragma unroll
-    for (int j = 0; j < DB; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        mine[m * D + j * 32 + col] = acc[i][j][r];
-      }
-    }
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int j = 0; j < DB; ++j) mine[D * D + j * 32 + col] = accz[j][0];
-  }
-  __syncthreads();
-  float* dst = partial + (size_t)wg * OUT;
-  for (int e = threadIdx.x; e < OUT; e += 256)
-    dst[e] = ((red[e] + red[OUT + e]) + red[2 * OUT + e]) + red[3 * OUT + e];
-  relu_copy_init<D>(S0, z0, init, wg, F, nc);
+  __shared__ __align__(16) uint8_t lds[relu_summary_lds_bytes<D>()];
+  relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, nc, chunk, blockIdx.x, lds);
 }
 
 template <int D>
@@ -142,118 +33,59 @@ __global__ __launch_bounds__(256) void relu_output_mfma(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
     const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
     int bfr, int nco, int chunk) {
-  constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
-  constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
-  constexpr int U = 4;        // 32-token groups per wave per step
-  constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
-  constexpr int PITCH = D + 4;
-  __shared__ __align__(16) float Ss[D * PITCH];
-  __shared__ float zs[D];
+  __shared__ __align__(16) uint8_t lds[relu_output_lds_bytes<D>()];
+  relu_output_item<D>(q, o, partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk, blockIdx.x, lds);
+}
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 5, col = lane & 31;
-  const long wg = blockIdx.x;
-  const long bhf = wg / nco;
-  const long bh = bhf / F;
-  const int f = (int)(bhf % F);
-  const int n0 = (int)(wg % nco) * chunk;
-  const int n1 = min(N, n0 + chunk);
-
-  // the state this frame reads: initial state plus every frame of its block and before
-  relu_frame_state<D>(partial, init, bh, f, F, nc, bfr, Ss, PITCH, zs);
-  __syncthreads();
-  if (f == F - 1 && wg % nco == 0) {  // the last frame's state is the call's final state
-    for (int e = threadIdx.x; e < D * D; e += 256) {
-      if (S_out) S_out[(size_t)bh * D * D + e] = Ss[(e / D) * PITCH + e % D];
-    }
-    if (z_out && threadIdx.x < D) z_out[(size_t)bh * D + threadIdx.x] = zs[threadIdx.x];
+// Block ids run over steps j = 0, 1, ...: step j holds the summary items of
+// frame j (one per head, whole frame) and then the output items of frame
+// j - lag (one per head and token chunk), so summaries of later frames
+// stream while earlier frames' outputs are written.  lag >= block_frames
+// keeps every summary an output item waits for at a lower block id.  Within
+// a step items are head-minor with B*H padded to BHp (a multiple of 8);
+// padding items leave at once.
+template <int D>
+__global__ __launch_bounds__(256, 2) void relu_fused_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
+    const float* z0, float* S_out, float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr,
+    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err) {
+  constexpr int LDS = relu_summary_lds_bytes<D>() > relu_output_lds_bytes<D>() ? relu_summary_lds_bytes<D>()
+                                                                                : relu_output_lds_bytes<D>();
+  __shared__ __align__(16) uint8_t lds[LDS];
+  const long b = blockIdx.x;
+  const long bh = b % bhp;
+  const long u = b / bhp;  // unit: one item per head
+  if (bh >= bh_n) return;
+  const long head_units = lag, mid_units = (long)(F - lag) * (1 + nco);
+  bool summary;
+  int f, c = 0;
+  if (u < head_units) {
+    summary = true;
+    f = (int)u;
+  } else if (u < head_units + mid_units) {
+    const long j = lag + (u - head_units) / (1 + nco), r = (u - head_units) % (1 + nco);
+    summary = r == 0;
+    f = summary ? (int)j : (int)(j - lag);
+    c = summary ? 0 : (int)(r - 1);
+  } else {
+    const long r = u - head_units - mid_units;
+    summary = false;
+    f = F - lag + (int)(r / nco);
+    c = (int)(r % nco);
   }
-
-  // A operands: S[32I + col][16s + 8g + e] as bf16 hi and lo terms
-  u32x4 ahi[DB][KS], alo[DB][KS];
-#pragma unroll
-  for (int I = 0; I < DB; ++I) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const float* src = Ss + (I * 32 + col) * PITCH + s * 16 + g * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint2 hl = split_bf16x2(src[2 * e], src[2 * e + 1]);
-        ahi[I][s][e] = hl.x;
-        alo[I][s][e] = hl.y;
-      }
-    }
+  if (summary) {
+    relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds);
+    publish(&flags[bh * F + f], epoch);
+    return;
   }
-  float zr[KS][8];
-#pragma unroll
-  for (int s = 0; s < KS; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) zr[s][e] = zs[s * 16 + g * 8 + e];
-
-  const uint16_t* qf = q + (size_t)bhf * N * D;
-  uint16_t* of = o + (size_t)bhf * N * D;
-  // U groups of 32 tokens per wave; the next step's query fragments are in
-  // flight while the current ones are contracted
-  auto load = [&](u32x4 (&b)[U][KS], int t0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * 32 + col;
-      const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * D + g * 8;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
-    }
-  };
-  auto compute = [&](u32x4 (&b)[U][KS], int t0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * 32 + col;
-      float den = 0.0f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          b[u][s][e] = relu_bf16x2(b[u][s][e]);
-          den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
-          den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
-        }
-      }
-      den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims
-      const float inv = 1.0f / (den + eps);
-#pragma unroll
-      for (int I = 0; I < DB; ++I) {
-        floatx16 acc = {};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[u][s]), acc);
-          acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[u][s]), acc);
-        }
-        if (t < n1) {
-          uint16_t* orow = of + (size_t)t * D + I * 32 + 4 * g;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 w;
-            w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
-            w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
-          }
-        }
-      }
-    }
-  };
-  u32x4 b0[U][KS], b1[U][KS];
-  int t0 = n0 + wave * U * 32;
-  if (t0 < n1) load(b0, t0);
-  for (; t0 < n1; t0 += 2 * STEP) {
-    if (t0 + STEP < n1) load(b1, t0 + STEP);
-    compute(b0, t0);
-    if (t0 + STEP >= n1) break;
-    if (t0 + 2 * STEP < n1) load(b0, t0 + 2 * STEP);
-    compute(b1, t0 + STEP);
-  }
+  const int fend = min(F, (f / bfr + 1) * bfr);
+  wait_all(&flags[bh * F], fend, epoch, err);
+  relu_output_item<D>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
+                      (bh * F + f) * nco + c, lds);
 }
 
 }  // namespace
-
 bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D == 64); }
 
 hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
@@ -281,6 +113,25 @@ hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* p
   else if (D == 64)
     hipLaunchKernelGGL(relu_output_mfma<64>, grid, block, 0, st, (const uint16_t*)q, (uint16_t*)o,
                        partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
+                                  uint32_t* err, hipStream_t st) {
+  const long grid = (long)a.F * bhp * (1 + a.nco);
+  const int lag = a.bfr > kReluLag ? (a.bfr < a.F ? a.bfr : a.F) : (kReluLag < a.F ? kReluLag : a.F);
+  if (a.D == 32)
+    hipLaunchKernelGGL(relu_fused_mfma<32>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
+                       a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
+                       epoch, err);
+  else if (a.D == 64)
+    hipLaunchKernelGGL(relu_fused_mfma<64>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
+                       a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
+                       epoch, err);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -38,6 +38,12 @@
  *    enqueued: on any error nothing is launched, no output is touched and
  *    the status names the reason (ls_last_error() gives details).  A device
  *    fault surfaces at the caller's next synchronisation.
+ *  - The first 4 bytes of a workspace are its fault word.  Calls that run
+ *    as a single launch (bf16 at head dims 32/64 for the ReLU scan, head dim
+ *    128 for the GDN scan when B*H <= 32 and F >= 2) hand data between their
+ *    work items through flags with bounded waits; if a wait ever gave up,
+ *    the call's results are invalid and the fault word becomes nonzero.  The
+ *    library never clears it; callers that check it zero it beforehand.
  *  - The caller owns every buffer, including the workspace.  The library
  *    never allocates device memory and carries nothing from one call to the
  *    next (the optional profiling session below only keeps HIP events).

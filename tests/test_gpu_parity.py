@@ -258,3 +258,35 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
     check("rollout z", ncache, rz, 1e-2)
     check("rollout vs one call o", torch.cat(outs, dim=2).float(), o1.float().double().cpu().numpy(), 1e-2)
     assert torch.allclose(cache, S1, rtol=1e-5, atol=1e-5 * S1.abs().max().item())
+
+
+# --------------------------------------------------------------------------- single-launch paths
+@pytest.mark.parametrize("op", ["relu", "gdn"])
+def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
+    """The one-launch paths hand data between work items through flags with
+    bounded waits; the workspace's fault word must stay zero and results match."""
+    if op == "relu":
+        x = gen.relu_inputs(1, 11, 9, 777, 32, "bf16", seed=31)   # B*H not a multiple of 8
+        shp = ls.ls_shape(1, 11, 9, 777, 32, 1)
+        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
+    else:
+        x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=32)
+        shp = ls.ls_shape(1, 5, 9, 333, 128, 1)
+        need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    xd = _dev(x)
+    for rep in range(3):  # reuse of a workspace across calls (fresh epochs)
+        if op == "relu":
+            o, S, z = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], block_frames=2, ws=ws)
+        else:
+            o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+    if op == "relu":
+        ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], block_frames=2)
+        check("single-launch relu o", o, ro, 2e-2)
+        check("single-launch relu S", S, rS, 1e-2)
+    else:
+        ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+        check("single-launch gdn o", o, ro, 2e-2)
+        check("single-launch gdn S", S, rS, 1e-2)
