@@ -332,7 +332,9 @@ __device__ __forceinline__ void gdn_scan_item(
   }
 }
 
-constexpr int kOutLds = 2 * 64 * (GD + 8) * 2;
+constexpr int kOutPitch = GD + 8;
+// Q tiles (double buffered) and output staging tiles (double buffered), bf16
+constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;
 
 // Work item `wg` = (frame of one head) * nco + token chunk: o = S_f q.
 __device__ __forceinline__ void gdn_output_item(
@@ -343,7 +345,8 @@ __device__ __forceinline__ void gdn_output_item(
   constexpr int ROW = D + 8;  // 272-byte pitch: 16-byte fragment reads spread over all banks
   constexpr int LPT = TILE * (D / 8) / 256;  // 4
   typedef uint16_t TileT[TILE * ROW];
-  TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][TILE * ROW]
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);               // [buffer][TILE * ROW] query tiles
+  TileT* ost = reinterpret_cast<TileT*>(lds_raw + 2 * TILE * ROW * 2);  // [buffer][TILE * ROW] outputs
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -390,10 +393,21 @@ __device__ __forceinline__ void gdn_output_item(
     stage(0);
   }
   __syncthreads();
+  // the previous tile's outputs leave as whole 256-byte rows (16 lanes per
+  // token, 16 bytes each) from its staging buffer
+  auto drain = [&](int it) {
+    const int t0 = n0 + it * TILE;
+#pragma unroll
+    for (int r = 0; r < TILE * (D / 8) / 256; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
+      if (t0 + tok < n1) st16(of + (size_t)(t0 + tok) * D + cb * 8, w);
+    }
+  };
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    const int t0 = n0 + it * TILE;
-    if (it + 1 < ntiles) fetch(t0 + TILE);
+    if (it + 1 < ntiles) fetch(n0 + (it + 1) * TILE);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       floatx16 acc = {};
@@ -404,20 +418,19 @@ __device__ __forceinline__ void gdn_output_item(
         acc = mfma32x32x16(as_bf16x8(ahi[s]), as_bf16x8(b), acc);
         acc = mfma32x32x16(as_bf16x8(alo[s]), as_bf16x8(b), acc);
       }
-      const int t = t0 + half * 32 + col;
-      if (t < n1) {
-        uint16_t* orow = of + (size_t)t * D + wave * 32 + 4 * g;
+      // lane (col, g) of wave w holds token half*32 + col, dims 32 w + 8 q4 + 4 g + 0..3
+      uint16_t* srow = &ost[buf][(half * 32 + col) * ROW + wave * 32 + 4 * g];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint2 w;
-          w.x = pack_bf16x2(acc[4 * q4 + 0], acc[4 * q4 + 1]);
-          w.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
-          *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[4 * q4 + 0], acc[4 * q4 + 1]);
+        w.y = pack_bf16x2(acc[4 * q4 + 2], acc[4 * q4 + 3]);
+        *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
       }
     }
     if (it + 1 < ntiles) stage(buf ^ 1);
     __syncthreads();
+    drain(it);
   }
 }
 

@@ -144,9 +144,13 @@ __device__ __forceinline__ void relu_summary_item(
   relu_copy_init<D>(S0, z0, init, wg, F, nc);
 }
 
-// LDS bytes the output item needs.
+// Row pitch (bf16) of the per-wave output staging tile [32 tokens][D + 8].
 template <int D>
-constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4; }
+constexpr int relu_ostage_pitch() { return D + 8; }
+// LDS bytes the output item needs: the frame state (fp32) and four per-wave
+// output staging tiles.
+template <int D>
+constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4 + 4 * 32 * relu_ostage_pitch<D>() * 2; }
 
 // Work item `wg` = (frame of one head) * nco + token chunk: the frame's state
 // from init + partials, then o = S phi(q) / (z . phi(q) + eps) for the chunk;
@@ -163,6 +167,10 @@ __device__ __forceinline__ void relu_output_item(
   constexpr int PITCH = D + 4;
   float* Ss = reinterpret_cast<float*>(lds_raw);  // [D][PITCH]
   float* zs = Ss + D * PITCH;                      // [D]
+  constexpr int OP = relu_ostage_pitch<D>();
+  // this wave's [32][OP] bf16 staging tile: MFMA results are scattered over
+  // lanes by dimension, so they pass through LDS to leave as whole rows
+  uint16_t* ost = reinterpret_cast<uint16_t*>(lds_raw + (D * PITCH + D) * 4) + (threadIdx.x >> 6) * 32 * OP;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 5, col = lane & 31;
@@ -240,17 +248,29 @@ __device__ __forceinline__ void relu_output_item(
           acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[u][s]), acc);
           acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[u][s]), acc);
         }
-        if (t < n1) {
-          uint16_t* orow = of + (size_t)t * D + I * 32 + 4 * g;
+        // lane (col, g) holds token col's dims I*32 + 8 q4 + 4 g + 0..3
+        uint16_t* srow = ost + col * OP + I * 32 + 4 * g;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            uint2 w;
-            w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
-            w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + 8 * q4) = w;
-          }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 w;
+          w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
+          w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      // whole rows out: D/8 lanes per token, 16 bytes each, consecutive lanes
+      // on consecutive bytes
+      constexpr int LPR = D / 8;        // lanes per token row
+      constexpr int TPI = 64 / LPR;     // tokens per store instruction
+#pragma unroll
+      for (int i = 0; i < 32 / TPI; ++i) {
+        const int tl = i * TPI + lane / LPR, cb = lane % LPR;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(ost + tl * OP + cb * 8);
+        const int tt = t0 + u * 32 + tl;
+        if (tt < n1) st16(of + (size_t)tt * D + cb * 8, w);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   };
   u32x4 b0[U][KS], b1[U][KS];
