@@ -12,11 +12,20 @@ keys) and stay resident in HBM; the timed region holds only library calls.
 
 Prints one JSON line: the throughput (tokens = B*F*N summed over both parts,
 all heads of a token counted once), the roofline object of the dominant
-kernel (per-kernel HIP-event timing from the library's profiling session, over
-extra steps after the timed ones), and the fp64 CPU oracle timed on a sample
-of the same workload.
+kernel, and the fp64 CPU oracle timed on a sample of the same workload.
+
+The headline pass times K steps with one event pair per step.  Per-kernel
+durations come from a second pass over the same K steps in which the library
+records an event pair around each of its launches, on the stream it launches
+on; those per-launch events cost about 8% of a step, so they stay out of the
+headline pass.
+
+The roofline's `traffic` (HBM bytes per launch) comes from the hardware
+counter summary in profiles/hbm_traffic_720p_minute.md, and only while the
+kernel's sources still hash to the ones that summary was taken from.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +36,39 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scan tokens/sec (1 GPU) at 720p minute-scale; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_720p_minute.md")
+# sources each fused kernel is built from: counters taken on other sources are stale
+KERNEL_SOURCES = {
+    "relu_fused": ["device_common.h", "sync.h", "relu_items.h", "relu_mfma.hip"],
+    "gdn_fused": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
+}
+
+
+def kernel_sources_sha(name):
+    """sha256 over a kernel's HIP sources and the build flags."""
+    pkg = os.path.join(ROOT, "block_causal_linear_attn_amd")
+    h = hashlib.sha256()
+    for f in [os.path.join(pkg, "csrc", x) for x in KERNEL_SOURCES[name]] + [os.path.join(pkg, "build.py")]:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) or None if absent or stale."""
+    if name not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("traffic-json:"):
+                rec = json.loads(line.split(":", 1)[1]).get(name)
+                if rec is None:
+                    return None, "kernel not in counter summary"
+                if rec["sources_sha256"] != kernel_sources_sha(name):
+                    return None, "kernel changed since the counters were taken"
+                return rec["fetch_bytes"] + rec["write_bytes"], "FETCH_SIZE %.0f + WRITE_SIZE %.0f bytes" % (
+                    rec["fetch_bytes"], rec["write_bytes"])
+    return None, "no traffic line in counter summary"
 
 
 def parse():
@@ -34,10 +76,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--profile-steps", type=int, default=3)
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="skip the per-launch timing pass (no roofline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="heads per part in the oracle sample (default: oracle threads)")
+                    help="heads per part in the oracle sample (default: 2 per oracle thread for "
+                         "the ReLU part, all for the GDN part)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times (counter calibration)")
     return ap.parse_args()
@@ -110,6 +154,16 @@ def main():
         e2.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # second pass over the same steps: the library records an event pair
+    # around each of its launches, on the stream it launches on
+    kstats = {}
+    if not args.no_kernel_events:
+        ls.ls_profile_begin()
+        for _ in range(args.steps):
+            part_video()
+            part_wm()
+        torch.cuda.synchronize()
+        kstats = ls.ls_profile_end()
     ms_video = sorted(a.elapsed_time(b) for a, b, _ in ev)
     ms_wm = sorted(b.elapsed_time(c) for _, b, c in ev)
     ms_step = sorted(a.elapsed_time(c) for a, _, c in ev)
@@ -126,13 +180,7 @@ def main():
     value = tokens * args.steps / gpu_total_s
     med = lambda xs: xs[len(xs) // 2]
 
-    # ---- per-kernel timing (library profiling session over extra steps)
-    ls.ls_profile_begin()
-    for _ in range(args.profile_steps):
-        part_video()
-        part_wm()
-    torch.cuda.synchronize()
-    kstats = ls.ls_profile_end()
+    # ---- per-kernel timing over the timed steps
     # algorithmic HBM bytes per launch: the token tensors each kernel must move
     half_video = 2 * wv.B * wv.H * wv.F * wv.N * wv.D * elt  # two of q, k, v, o over all calls
     half_wm = 2 * wg.B * wg.H * wg.F * wg.N * wg.D * elt
@@ -148,18 +196,22 @@ def main():
     kernels = {}
     for name, (launches, total_ms) in kstats.items():
         avg_us = 1e3 * total_ms / max(1, launches)
-        k = {"launches_per_step": launches / max(1, args.profile_steps), "avg_us": round(avg_us, 2),
-             "ms_per_step": round(total_ms / max(1, args.profile_steps), 4)}
+        k = {"launches_per_step": launches / args.steps, "avg_us": round(avg_us, 2),
+             "ms_per_step": round(total_ms / args.steps, 4)}
         if name in alg:
             gbs = alg[name] / (avg_us * 1e-6) / 1e9
             k["alg_bytes_per_launch"] = int(alg[name])
             k["achieved_GBs"] = round(gbs, 1)
             k["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
         kernels[name] = k
-    dom = max((n for n in kernels if n in alg), key=lambda n: kernels[n]["ms_per_step"])
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_GBs"],
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
-                "traffic": None}
+    roofline = None
+    if kernels:
+        dom = max((n for n in kernels if n in alg), key=lambda n: kernels[n]["ms_per_step"])
+        traffic, note = measured_traffic(dom)
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_GBs"],
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
+                    "traffic": None if traffic is None else int(traffic),
+                    "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note}
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -209,8 +261,10 @@ def cpu_baseline(args, inputs, wv, wg, tokens):
     """Time the fp64 oracle on Hs heads of each part (all frames), scaled to the step."""
     import oracle
     threads = oracle.max_threads()
-    hs = args.cpu_heads or threads
-    hv, hg = min(hs, wv.H), min(hs, wg.H)
+    # about 10 s of oracle work on a 16-core host: two heads per thread for
+    # the ReLU rollout, every head of the GDN scan
+    hv = min(args.cpu_heads or 2 * threads, wv.H)
+    hg = min(args.cpu_heads or wg.H, wg.H)
     xv = inputs.relu_inputs(1, hv, wv.F, wv.N, wv.D, "bf16", seed=wv.seed, part=999)
     xv = {k: t.float().numpy() for k, t in xv.items()}
     t0 = time.perf_counter()
