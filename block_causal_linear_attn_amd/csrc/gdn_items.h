@@ -161,18 +161,24 @@ __device__ __forceinline__ void gdn_gram_item(
 // handles frames split into several token chunks (one record per chunk).
 constexpr int kAlphaWin = 2048;
 constexpr int kScanRB = 16, kScanPitch = GD + 4;
-constexpr int kScanLds = 2 * kScanRB * kScanPitch * 4 + kAlphaWin * 4;
+// LDS bytes of a scan item over RB rows
+template <int RB>
+constexpr int scan_lds_bytes() { return 2 * RB * kScanPitch * 4 + kAlphaWin * 4; }
+constexpr int kScanLds = scan_lds_bytes<kScanRB>();
 
-// Scan item of rows [r0, r0 + 16) of head `head`'s state over all F frames.
+// Scan item of rows [r0, r0 + RB) of head `head`'s state over all F frames
+// (RB = 16 or 32: one or two 16-row sub-blocks per wave).
 // FUSED: records come from gram items of the same launch (wait for gflags
 // before each frame, one flag per token chunk) and each frame's state is
-// announced on sflags[(head * F + f) * 8 + r0 / 16] for the output items.
-template <bool MULTI, bool FUSED>
+// announced on sflags[(head * F + f) * 8 + r0 / RB] for the output items.
+template <bool MULTI, bool FUSED, int RB = kScanRB>
 __device__ __forceinline__ void gdn_scan_item(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
     uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, int nc, uint8_t* lds_raw,
     const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err) {
-  constexpr int D = GD, RB = kScanRB, PITCH = kScanPitch;
+  constexpr int D = GD, PITCH = kScanPitch;
+  constexpr int SB = RB / 16;  // 16-row sub-blocks
+  static_assert(RB == 16 || RB == 32, "scan items cover 16 or 32 rows");
   typedef float RowsT[RB][PITCH];
   RowsT* Ss = reinterpret_cast<RowsT*>(lds_raw);                         // [2][RB][PITCH]
   float* As = reinterpret_cast<float*>(lds_raw + 2 * RB * PITCH * 4);    // [kAlphaWin]
@@ -180,19 +186,21 @@ __device__ __forceinline__ void gdn_scan_item(
   const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
 
-  float s[2][4];
+  float s[SB][2][4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
-      s[nb][r] = S0 ? S0[(size_t)head * D * D + (size_t)(r0 + m) * D + n] : 0.0f;
-      Ss[0][m][n] = s[nb][r];
-    }
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * sb + 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+        s[sb][nb][r] = S0 ? S0[(size_t)head * D * D + (size_t)(r0 + m) * D + n] : 0.0f;
+        Ss[0][m][n] = s[sb][nb][r];
+      }
 
   struct Rec {
     u32x4 hi[2][4], lo[2][4];
-    float u[2][4];
+    float u[SB][2][4];
   };
   const size_t hf0 = (size_t)head * F;
   auto load_rec = [&](int f, int cidx, Rec& R) {
@@ -209,26 +217,33 @@ __device__ __forceinline__ void gdn_scan_item(
         R.hi[nb][s4] = ld16(gh + off);
         R.lo[nb][s4] = ld16(gl + off);
       }
-      const float4 u4 = *reinterpret_cast<const float4*>(U + ((size_t)((r0 >> 2) + lg) * D + n) * 4);
-      R.u[nb][0] = u4.x;
-      R.u[nb][1] = u4.y;
-      R.u[nb][2] = u4.z;
-      R.u[nb][3] = u4.w;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const float4 u4 =
+            *reinterpret_cast<const float4*>(U + ((size_t)(((r0 + 16 * sb) >> 2) + lg) * D + n) * 4);
+        R.u[sb][nb][0] = u4.x;
+        R.u[sb][nb][1] = u4.y;
+        R.u[sb][nb][2] = u4.z;
+        R.u[sb][nb][3] = u4.w;
+      }
     }
   };
   // S_f leaves for the output pass from the LDS copy the next frame reads
-  // anyway: each thread splits 8 consecutive entries of one row and writes
-  // them to the hi and lo planes with two 16-byte stores
+  // anyway: each thread splits 8 consecutive entries of a row and writes
+  // them to the hi and lo planes with two 16-byte stores (per 16 rows)
   auto store_state = [&](int f, int buf) {
-    const int row = tid >> 4, c0 = 8 * (tid & 15);
-    const float* src = &Ss[buf][row][c0];
-    const float4 x0 = *reinterpret_cast<const float4*>(src);
-    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-    const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
-    const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
-    uint16_t* hp = states + (hf0 + f) * 2 * D * D + (size_t)(r0 + row) * D + c0;
-    st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
-    st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const int row = 16 * sb + (tid >> 4), c0 = 8 * (tid & 15);
+      const float* src = &Ss[buf][row][c0];
+      const float4 x0 = *reinterpret_cast<const float4*>(src);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+      const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+      const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+      uint16_t* hp = states + (hf0 + f) * 2 * D * D + (size_t)(r0 + row) * D + c0;
+      st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
+      st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+    }
   };
   // hi*hi, hi*lo and lo*hi go to three accumulators: independent MFMA
   // chains overlap their latencies instead of queueing behind each other
@@ -256,56 +271,70 @@ __device__ __forceinline__ void gdn_scan_item(
       load_rec(f, 0, R);
     }
     const float a = As[f % kAlphaWin];
-    // A operands: this workgroup's 16 rows of S_{f-1}, split into bf16 hi + lo
-    u32x4 ahi[4], alo[4];
+    // A operands: this workgroup's rows of S_{f-1}, split into bf16 hi + lo
+    u32x4 ahi[SB][4], alo[SB][4];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const float* src = &Ss[cur][lr][32 * s4 + 8 * lg];
-      const float4 x0 = *reinterpret_cast<const float4*>(src);
-      const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
-      const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
-      const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
-      ahi[s4] = u32x4{p0.x, p1.x, p2.x, p3.x};
-      alo[s4] = u32x4{p0.y, p1.y, p2.y, p3.y};
-    }
-    floatx4 acc3[2][3];
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float* src = &Ss[cur][16 * sb + lr][32 * s4 + 8 * lg];
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+        const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+        ahi[sb][s4] = u32x4{p0.x, p1.x, p2.x, p3.x};
+        alo[sb][s4] = u32x4{p0.y, p1.y, p2.y, p3.y};
+      }
+    floatx4 acc3[SB][2][3];
 #pragma unroll
-      for (int t = 0; t < 3; ++t) acc3[nb][t] = floatx4{};
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int t = 0; t < 3; ++t) acc3[sb][nb][t] = floatx4{};
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) mfma3(acc3[nb], ahi[s4], alo[s4], R.hi[nb][s4], R.lo[nb][s4]);
-    float uf[2][4];
+      for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
+          mfma3(acc3[sb][nb], ahi[sb][s4], alo[sb][s4], R.hi[nb][s4], R.lo[nb][s4]);
+    float uf[SB][2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) uf[nb][r] = R.u[nb][r];
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uf[sb][nb][r] = R.u[sb][nb][r];
     if (MULTI) {
       for (int cidx = 1; cidx < nc; ++cidx) {  // the frame's further token chunks
         Rec T;
         load_rec(f, cidx, T);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4) mfma3(acc3[nb], ahi[s4], alo[s4], T.hi[nb][s4], T.lo[nb][s4]);
+          for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) uf[nb][r] += T.u[nb][r];
-        }
+            for (int s4 = 0; s4 < 4; ++s4)
+              mfma3(acc3[sb][nb], ahi[sb][s4], alo[sb][s4], T.hi[nb][s4], T.lo[nb][s4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) uf[sb][nb][r] += T.u[sb][nb][r];
+          }
       }
     }
     // refill this ring slot two frames ahead (the last record again at the end)
     if (!FUSED) load_rec(min(f + 2, F - 1), 0, R);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * lg + r, n = 32 * wave + 16 * nb + lr;
-        const float prod = acc3[nb][0][r] + (acc3[nb][1][r] + acc3[nb][2][r]);
-        s[nb][r] = a * (s[nb][r] - prod) + uf[nb][r];
-        Ss[cur ^ 1][m][n] = s[nb][r];
-      }
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * sb + 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+          const float prod = acc3[sb][nb][0][r] + (acc3[sb][nb][1][r] + acc3[sb][nb][2][r]);
+          s[sb][nb][r] = a * (s[sb][nb][r] - prod) + uf[sb][nb][r];
+          Ss[cur ^ 1][m][n] = s[sb][nb][r];
+        }
     __syncthreads();
     store_state(f, cur ^ 1);
   };
@@ -325,10 +354,13 @@ __device__ __forceinline__ void gdn_scan_item(
   if (FUSED && F > 0) publish(&sflags[(hf0 + F - 1) * 8 + r0 / RB], epoch);
   if (S_out) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S_out[(size_t)head * D * D + (size_t)(r0 + 4 * lg + r) * D + 32 * wave + 16 * nb + lr] = s[nb][r];
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S_out[(size_t)head * D * D + (size_t)(r0 + 16 * sb + 4 * lg + r) * D + 32 * wave + 16 * nb + lr] =
+              s[sb][nb][r];
   }
 }
 

@@ -2,17 +2,19 @@
 // DeltaNet scan (head dim 128), built from the work items in gdn_items.h.
 //
 // gdn_fused_mfma runs one call in a single launch.  Block ids start with the
-// scan items (eight 16-row blocks per head), followed by the streaming items
+// scan items (four 32-row blocks per head), followed by the streaming items
 // in frame order: for each step j the gram items of frame j and the output
-// items of frame j - L (L = kLag).  Scan items wait for the gram records of
-// each frame, output items wait for the eight row blocks of their frame's
-// state.  Every item a wait depends on is either dispatched earlier or, for
-// the scan items, a gram item that can still find a free slot because scan
-// items fill at most one slot per CU; the launcher only picks this kernel
-// when that holds (B*H*8 <= 256).  All items of a head share one XCD (block
-// id equal to the head modulo 8) and exchange records and states through its
-// L2, so the scan's frame-to-frame chain overlaps the HBM streaming and
-// neither records nor per-frame states need to leave the caches.
+// items of frame j - L, with L chosen so that output items arrive about when
+// their frame's state is ready instead of holding slots while they wait.
+// Scan items wait for the gram records of each frame, output items wait for
+// the four row blocks of their frame's state.  Every item a wait depends on
+// is either dispatched earlier or, for the scan items, a gram item that can
+// still find a free slot because scan items fill at most one slot per CU;
+// the launcher only picks this kernel when that holds (B*H*4 <= 256).  All
+// items of a head share one XCD (block id equal to the head modulo 8), so
+// records and per-frame states are read back from that XCD's L2 shortly
+// after they are written, and the scan's frame-to-frame chain overlaps the
+// HBM streaming.
 #include "gdn_items.h"
 #include "kernels.h"
 
@@ -46,7 +48,7 @@ __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
   gdn_output_item(q, o, states, N, nco, chunk, blockIdx.x, lds);
 }
 
-constexpr int kLag = 4;  // frames the output items trail the gram items
+constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan item
 
 template <bool MULTI>
 __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
@@ -55,16 +57,18 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
     uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
-  constexpr int LDS = kGramLds > kScanLds ? (kGramLds > kOutLds ? kGramLds : kOutLds)
-                                          : (kScanLds > kOutLds ? kScanLds : kOutLds);
+  constexpr int kSL = scan_lds_bytes<kFusedRB>();
+  constexpr int LDS = kGramLds > kSL ? (kGramLds > kOutLds ? kGramLds : kOutLds) : (kSL > kOutLds ? kSL : kOutLds);
+  constexpr int NRB = kGdnFusedRowBlocks;
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
-  const long nscan = (bhp / 8) * 64;
+  const long nscan = (bhp / 8) * 8 * NRB;
   if (b < nscan) {
-    const long head = (b / 64) * 8 + (b % 8);
+    // eight heads x NRB row blocks per group; a head's row blocks keep its XCD
+    const long head = (b / (8 * NRB)) * 8 + (b % 8);
     if (head >= bh_n) return;
-    gdn_scan_item<MULTI, true>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % 8) * kScanRB, F, nc,
-                               lds, gflags, sflags, epoch, err);
+    gdn_scan_item<MULTI, true, kFusedRB>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
+                                         F, nc, lds, gflags, sflags, epoch, err);
     return;
   }
   const long s = b - nscan;
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     gdn_gram_item(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
     publish(&gflags[(bh * F + f) * nc + cidx], epoch);
   } else {
-    wait_all(&sflags[(bh * F + f) * 8], 8, epoch, err);
+    wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
     gdn_output_item(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds);
   }
 }
@@ -137,8 +141,9 @@ hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* sta
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st) {
   if (a.D != GD) return hipErrorInvalidValue;
-  const int lag = a.F < kLag ? a.F : kLag;
-  const long grid = (bhp / 8) * 64 + bhp * a.F * (a.nc + a.nco);
+  const long grid = bhp * kGdnFusedRowBlocks + bhp * a.F * (a.nc + a.nco);
+  const void* kern = a.nc == 1 ? (const void*)gdn_fused_mfma128<false> : (const void*)gdn_fused_mfma128<true>;
+  const int lag = fused_lag(device_slots(kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1, a.F);
   if (a.nc == 1)
     hipLaunchKernelGGL(gdn_fused_mfma128<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta, (uint16_t*)a.o,

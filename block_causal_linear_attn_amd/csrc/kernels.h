@@ -74,10 +74,24 @@ hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
 //  ReLU: flags[B*H*F]; summary with one chunk per frame (nc = 1).
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st);
-//  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states);
-//  only for B*H*8 <= 256 so that scan items never fill the chip.
+//  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states,
+//  kGdnFusedRowBlocks of the 8 used); only for B*H*kGdnFusedRowBlocks <= 256
+//  so that scan items never take more than one slot per CU.
+constexpr int kGdnFusedRowBlocks = 4;
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st);
+
+// Workgroups of 256 threads of `kernel` that the current device holds at
+// once (occupancy per CU x CUs), cached per (kernel, device); 512 if the
+// runtime cannot tell.
+int device_slots(const void* kernel);
+
+// Frames by which the consumer items of a fused launch trail their producers
+// so that a consumer is dispatched about when its inputs become ready: the
+// producers of one frame take about as long as the slots need to turn over
+// once, i.e. slots / items_per_step steps of dispatch, with a margin of 1/4
+// and one step.  At least `min_lag`, at most F.
+int fused_lag(long slots, long items_per_step, int min_lag, int F);
 
 // Generic (VALU) summary and output kernels of either path.
 hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);

@@ -152,7 +152,7 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   p.mfma = linscan::gdn_has_mfma(s->D, s->dtype);
   // one launch (scan items alongside the streaming items) when the scan items
   // fill at most one slot per CU and there are frames to overlap
-  p.fused = p.mfma && d.bh * 8 <= 256 && s->F >= 2 && s->N > 0;
+  p.fused = p.mfma && d.bh * linscan::kGdnFusedRowBlocks <= 256 && s->F >= 2 && s->N > 0;
   // a chunk's G/U partials are 8 D^2 bytes: keep chunks long enough that they
   // stay small next to the chunk's own key/value bytes
   plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);

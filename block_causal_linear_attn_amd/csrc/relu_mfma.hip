@@ -18,8 +18,6 @@ namespace linscan {
 
 namespace {
 
-constexpr int kReluLag = 1;  // frames the output items trail the summary items
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void relu_summary_mfma(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
@@ -121,7 +119,8 @@ hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* p
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
   const long grid = (long)a.F * bhp * (1 + a.nco);
-  const int lag = a.bfr > kReluLag ? (a.bfr < a.F ? a.bfr : a.F) : (kReluLag < a.F ? kReluLag : a.F);
+  const void* kern = a.D == 32 ? (const void*)relu_fused_mfma<32> : (const void*)relu_fused_mfma<64>;
+  const int lag = fused_lag(device_slots(kern), bhp * (1 + a.nco), a.bfr, a.F);
   if (a.D == 32)
     hipLaunchKernelGGL(relu_fused_mfma<32>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,

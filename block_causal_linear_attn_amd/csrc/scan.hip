@@ -10,6 +10,10 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace linscan {
 
 hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
@@ -144,6 +148,31 @@ __global__ __launch_bounds__(256) void carry_kernel(const float* __restrict__ sr
 }
 
 }  // namespace
+
+int device_slots(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 512;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find({kernel, dev});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  int slots = 512;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
+      cus > 0)
+    slots = per_cu * cus;
+  cache[{kernel, dev}] = slots;
+  return slots;
+}
+
+int fused_lag(long slots, long items_per_step, int min_lag, int F) {
+  long lag = items_per_step > 0 ? (5 * slots + 4 * items_per_step - 1) / (4 * items_per_step) + 1 : 1;
+  if (lag < min_lag) lag = min_lag;
+  if (lag > F) lag = F;
+  return lag < 1 ? 1 : (int)lag;
+}
 
 hipError_t launch_relu_summary(const ScanArgs& a, hipStream_t st) {
   if (a.mfma)

@@ -40,7 +40,7 @@
  *    fault surfaces at the caller's next synchronisation.
  *  - The first 4 bytes of a workspace are its fault word.  Calls that run
  *    as a single launch (bf16 at head dims 32/64 for the ReLU scan, head dim
- *    128 for the GDN scan when B*H <= 32 and F >= 2) hand data between their
+ *    128 for the GDN scan when B*H <= 64 and F >= 2) hand data between their
  *    work items through flags with bounded waits; if a wait ever gave up,
  *    the call's results are invalid and the fault word becomes nonzero.  The
  *    library never clears it; callers that check it zero it beforehand.
