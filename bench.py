@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads per part in the oracle sample (default: 2 per oracle thread for "
                          "the ReLU part, all for the GDN part)")
+    ap.add_argument("--no-chunk-step", action="store_true",
+                    help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times (counter calibration)")
     return ap.parse_args()
@@ -213,6 +215,8 @@ def main():
                     "traffic": None if traffic is None else int(traffic),
                     "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note}
 
+    chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
+
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -252,9 +256,51 @@ def main():
                                     round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
+        "side": {"sana_wm_chunk_step": chunk_step},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_chunk_step(torch, ls, inputs):
+    """Latency of single-frame GDN calls (B4 H24 D128 N920) re-reading one carried state.
+
+    Not part of the step: the 50 denoising-step calls of the chunk-causal
+    workload, each on its own resident input set, timed one by one after a
+    warm-up pass over all of them.
+    """
+    w = inputs.WORKLOADS["sana_wm_chunk_step"]
+    dev = torch.device("cuda:0")
+    calls = [inputs.workload_call_inputs(w, i, device=dev) for i in range(w.steps)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    state = 0.05 * torch.randn((w.B, w.H, w.D, w.D), generator=g, device=dev)  # any carried state
+    outs = [torch.empty_like(c["q"]) for c in calls]
+    s_out = torch.empty_like(state)
+
+    def call(i):
+        c = calls[i]
+        ls.ls_gdn_frame_forward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], state, out=outs[i],
+                                state_out=s_out)
+
+    for i in range(w.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(w.steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+    med_us = us[len(us) // 2]
+    tokens = w.B * w.N
+    alg = 4 * w.B * w.H * w.N * w.D * 2 + 2 * w.B * w.H * w.D * w.D * 4  # q, k, v, o + state in/out
+    del calls, outs
+    return {"calls": w.steps, "us_median": round(med_us, 2), "us_p10": round(us[len(us) // 10], 2),
+            "us_p90": round(us[(9 * len(us)) // 10], 2), "tokens_per_s": round(tokens / (med_us * 1e-6), 1),
+            "hbm_frac": round(alg / (med_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "B4 H24 D128 N920, F=1 per call, 50 distinct input sets, one carried state"}
 
 
 def cpu_baseline(args, inputs, wv, wg, tokens):

@@ -90,6 +90,33 @@ __device__ __forceinline__ u32x4 gather_tokens_32(const uint16_t* tile, int t0, 
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
+// Unpadded token-major LDS tiles of C 16-byte chunks per token row, with the
+// chunk index XOR-swizzled by token so that the four tokens one half-wave of
+// a transpose read touches (64 bytes each) fall on distinct LDS banks:
+// 256-byte rows (C = 16) swizzle by token % 4, 128-byte rows (C = 8) by
+// (token / 2) % 2; 64-byte rows (C = 4) tile the 64 banks unswizzled.
+template <int C>
+__device__ __forceinline__ int chunk_swizzle(int token) {
+  static_assert(C == 4 || C == 8 || C == 16, "rows of 4, 8 or 16 chunks");
+  return C == 16 ? (token & 3) << 2 : C == 8 ? ((token >> 1) & 1) << 2 : 0;
+}
+// element offset of (token, 16-byte chunk) in such a tile
+template <int C>
+__device__ __forceinline__ int swz_offset(int token, int chunk) {
+  return token * C * 8 + ((chunk ^ chunk_swizzle<C>(token)) << 3);
+}
+// gather_tokens_32 on a swizzled tile of C chunks per row (col0 a multiple of 32)
+template <int C>
+__device__ __forceinline__ u32x4 gather_tokens_32_swz(const uint16_t* tile, int t0, int col0, int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const int token = t0 + 8 * (q >> 1) + (j >> 2);
+  const int d = col0 + 16 * (q & 1) + 4 * (j & 3);
+  const uint16_t* p = tile + swz_offset<C>(token, d >> 3) + (d & 7);
+  const uint2 a = lds_read_tr16(p);
+  const uint2 b = lds_read_tr16(p + 4 * C * 8);  // token + 4: same swizzle
+  return u32x4{a.x, a.y, b.x, b.y};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 
 __device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
@@ -105,6 +132,15 @@ __device__ __forceinline__ floatx4 mfma16x16x4f32(float a, float b, floatx4 c) {
 // 16-byte global load / store through 32-bit words.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// The same for data touched once (token tensors): non-temporal, so that the
+// stream does not push out of the caches what other work items of the launch
+// still have to read.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 // ReLU scan: the state (S_f, z_f) frame f reads, written to LDS by the whole
 // workgroup: the initial state of head bh plus the chunk partials of every

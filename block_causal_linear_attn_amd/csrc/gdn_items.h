@@ -6,9 +6,9 @@
 // blocks of 32 x 32 apiece.  Wave w owns block row w of both, so every wave
 // needs all four key fragments and one value fragment per 16-token k-step.
 // The workgroup stages 64-token K and V tiles in LDS (double buffered, next
-// tile's HBM loads in flight while the current one is contracted) and each
-// lane gathers 8 tokens of one dimension per operand with two LDS transpose
-// reads.  Inputs are exact bf16
+// tile's HBM loads in flight while the current one is contracted; rows
+// unpadded with their 16-byte chunks swizzled by token) and each lane gathers
+// 8 tokens of one dimension per operand with two LDS transpose reads.  Inputs are exact bf16
 // products accumulated in fp32; c and c^2 are applied once at the end.
 //
 // Output pass: o = S_f q.  Wave w computes output dims [32w, 32w + 32) from
@@ -25,7 +25,7 @@ constexpr int GD = 128;
 // bytes of one (frame, token chunk) record: beta*G hi and lo planes (bf16) + beta*U (fp32)
 constexpr size_t kRecBytes = 8 * (size_t)GD * GD;
 
-constexpr int kGramLds = 2 * 2 * 64 * (GD + 4) * 2;
+constexpr int kGramLds = 2 * 2 * 64 * GD * 2;
 
 // Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
 // (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.
@@ -34,7 +34,8 @@ __device__ __forceinline__ void gdn_gram_item(
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw) {
   constexpr int D = GD;
   constexpr int TILE = 64;
-  constexpr int ROW = D + 4;  // 264-byte pitch: the two lane groups' gathers land 16 banks apart
+  constexpr int ROW = D;  // unpadded rows, chunks swizzled by token (conflict-free transpose reads)
+  constexpr int C = D / 8;
   constexpr int LPT = TILE * (D / 8) / 256;  // 16-byte loads per thread per tensor per tile (4)
   typedef uint16_t TileT[2][TILE * ROW];
   TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][K, V][TILE * ROW]
@@ -55,6 +56,9 @@ __device__ __forceinline__ void gdn_gram_item(
     accU[j] = floatx16{};
   }
 
+  // every load is issued (rows past the chunk re-read its first token) and
+  // such rows are zeroed when staged: loads under a lane condition would make
+  // the compiler wait for every load in flight before staging
   u32x4 kr[LPT], vr[LPT];
   auto fetch = [&](int t0) {
 #pragma unroll
@@ -62,33 +66,32 @@ __device__ __forceinline__ void gdn_gram_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      if (n < n1) {
-        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
-        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
-      } else {
-        kr[r] = u32x4{0u, 0u, 0u, 0u};
-        vr[r] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const size_t off = (size_t)(n < n1 ? n : n0) * D + cb * 8;
+      kr[r] = ld16_stream(kf + off);
+      vr[r] = ld16_stream(vf + off);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][tok * ROW + cb * 8]);
-      uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][tok * ROW + cb * 8]);
-      kd[0] = make_uint2(kr[r][0], kr[r][1]);
-      kd[1] = make_uint2(kr[r][2], kr[r][3]);
-      vd[0] = make_uint2(vr[r][0], vr[r][1]);
-      vd[1] = make_uint2(vr[r][2], vr[r][3]);
+      const bool live = t0 + tok < n1;
+      const u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+      uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
+      uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
+      kd[0] = make_uint2(kk[0], kk[1]);
+      kd[1] = make_uint2(kk[2], kk[3]);
+      vd[0] = make_uint2(vv[0], vv[1]);
+      vd[1] = make_uint2(vv[2], vv[3]);
     }
   };
 
   const int ntiles = (n1 - n0 + TILE - 1) / TILE;
   if (ntiles > 0) {
     fetch(n0);
-    stage(0);
+    stage(0, n0);
   }
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
@@ -100,15 +103,15 @@ __device__ __forceinline__ void gdn_gram_item(
     for (int s = 0; s < TILE / 16; ++s) {
       u32x4 kfrag[4];
 #pragma unroll
-      for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32<ROW>(kl, s * 16, J * 32, lane);
-      const u32x4 vfrag = gather_tokens_32<ROW>(vl, s * 16, wave * 32, lane);
+      for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32_swz<C>(kl, s * 16, J * 32, lane);
+      const u32x4 vfrag = gather_tokens_32_swz<C>(vl, s * 16, wave * 32, lane);
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         accG[J] = mfma32x32x16(as_bf16x8(kfrag[wave]), as_bf16x8(kfrag[J]), accG[J]);
         accU[J] = mfma32x32x16(as_bf16x8(vfrag), as_bf16x8(kfrag[J]), accU[J]);
       }
     }
-    if (it + 1 < ntiles) stage(buf ^ 1);
+    if (it + 1 < ntiles) stage(buf ^ 1, n0 + (it + 1) * TILE);
     __syncthreads();
   }
 
@@ -138,6 +141,134 @@ __device__ __forceinline__ void gdn_gram_item(
                               us * accU[J][4 * q4 + 3]);
       *reinterpret_cast<float4*>(Ud + ((size_t)(m0 >> 2) * D + J * 32 + col) * 4) = u4;
     }
+  }
+}
+
+// Row-split gram pass, for calls with few frames: work item `item` =
+// (frame of one head) * 4 + w computes block row w (rows 32w .. 32w + 31) of
+// beta*G and beta*U over all of the frame's tokens, so the four items of a
+// frame write disjoint parts of one record and no partial records need to be
+// summed.  Each 64-token tile stages K (all dims) and the w-th 32 dims of V
+// in LDS; wave j accumulates G(w, j) = sum k_w k_j^T and U(w, j) = sum v_w k_j^T
+// (two accumulators), which leaves registers for several tiles in flight.  The
+// four items of a frame read K four times, from HBM once and otherwise from
+// their XCD's L2.
+constexpr int kGramRowsKRow = GD, kGramRowsVRow = 32;  // unpadded; K chunks swizzled by token
+constexpr int kGramRowsDepth = 4;  // tiles in flight per workgroup
+constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;
+
+__device__ __forceinline__ void gdn_gram_rows_item(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw) {
+  constexpr int D = GD;
+  constexpr int TILE = 64;
+  constexpr int KROW = kGramRowsKRow, VROW = kGramRowsVRow;
+  constexpr int KLPT = TILE * (D / 8) / 256;  // 16-byte K loads per thread per tile (4)
+  uint16_t* kl[2] = {reinterpret_cast<uint16_t*>(lds_raw),
+                     reinterpret_cast<uint16_t*>(lds_raw) + TILE * KROW};
+  uint16_t* vl[2] = {reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW,
+                     reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW + TILE * VROW};
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = item >> 2;
+  const int w = (int)(item & 3);
+  const uint16_t* kf = k + (size_t)bhf * N * D;
+  const uint16_t* vf = v + (size_t)bhf * N * D + 32 * w;
+
+  floatx16 accG = {}, accU = {};
+  struct Regs {
+    u32x4 k[KLPT], v;
+  };
+  constexpr int DEPTH = kGramRowsDepth;
+  Regs R[DEPTH];
+  // K: token ci >> 4, 16-byte chunk ci & 15; V: token tid >> 2, chunk tid & 3
+  // of the w-th 32 dims.  Every load is issued (rows past the frame re-read
+  // token 0) and such rows are zeroed when staged, so that the compiler can
+  // count the loads in flight instead of waiting for all of them.
+  auto fetch = [&](Regs& R, int t0) {
+#pragma unroll
+    for (int r = 0; r < KLPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int n = t0 + (ci >> 4);
+      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * D + (ci & 15) * 8);
+    }
+    const int n = t0 + (tid >> 2);
+    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * D + (tid & 3) * 8);
+  };
+  auto stage = [&](const Regs& R, int buf, int t0) {
+#pragma unroll
+    for (int r = 0; r < KLPT; ++r) {
+      const int ci = r * 256 + tid;
+      const u32x4 kk = t0 + (ci >> 4) < N ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
+      uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
+      kd[0] = make_uint2(kk[0], kk[1]);
+      kd[1] = make_uint2(kk[2], kk[3]);
+    }
+    const u32x4 vv = t0 + (tid >> 2) < N ? R.v : u32x4{0u, 0u, 0u, 0u};
+    uint2* vd = reinterpret_cast<uint2*>(vl[buf] + swz_offset<VROW / 8>(tid >> 2, tid & 3));
+    vd[0] = make_uint2(vv[0], vv[1]);
+    vd[1] = make_uint2(vv[2], vv[3]);
+  };
+  auto contract = [&](int buf) {
+#pragma unroll
+    for (int s = 0; s < TILE / 16; ++s) {
+      const u32x4 kw = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * w, lane);
+      const u32x4 kj = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * wave, lane);
+      const u32x4 vw = gather_tokens_32_swz<VROW / 8>(vl[buf], s * 16, 0, lane);
+      accG = mfma32x32x16(as_bf16x8(kw), as_bf16x8(kj), accG);
+      accU = mfma32x32x16(as_bf16x8(vw), as_bf16x8(kj), accU);
+    }
+  };
+
+  // tile t sits in register set t % DEPTH from its fetch until it is staged,
+  // so DEPTH tiles stay in flight while one is contracted from LDS (the loop
+  // runs DEPTH tiles per pass so that every set index is a constant).  The
+  // loop body has no branch: it runs a whole number of passes, tiles past the
+  // end are staged as zeros (every row fails the token check) and add
+  // nothing, and fetches past the end re-read the last tile (from L2).  A
+  // fetch or stage under a branch would leave the compiler unable to count
+  // the loads in flight, and it would wait for all of them at every stage.
+  const int ntiles = (N + TILE - 1) / TILE;  // >= 1: callers have N > 0
+  const int tlast = (ntiles - 1) * TILE;
+  const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) fetch(R[d], min(d * TILE, tlast));
+  stage(R[0], 0, 0);
+  fetch(R[0], min(DEPTH * TILE, tlast));
+  __syncthreads();
+  for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+      const int it = it0 + u;
+      contract(it & 1);
+      Regs& nxt = R[(u + 1) % DEPTH];  // holds tile it + 1
+      stage(nxt, (it + 1) & 1, (it + 1) * TILE);
+      fetch(nxt, min((it + 1 + DEPTH) * TILE, tlast));
+      __syncthreads();
+    }
+  }
+
+  // block (w, wave) of the record: beta*G hi/lo planes and beta*U (layout as in gdn_gram_item)
+  const float bf = beta[bhf];
+  const float gs = c2 * bf, us = c * bf;
+  uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)bhf * kRecBytes);
+  uint16_t* Glo = Ghi + D * D;
+  float* Ud = reinterpret_cast<float*>(Glo + D * D);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = w * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    uint16_t h, l;
+    split_bf16(gs * accG[r], h, l);
+    Ghi[m * D + wave * 32 + col] = h;
+    Glo[m * D + wave * 32 + col] = l;
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int m0 = w * 32 + 8 * q4 + 4 * g;
+    float4 u4 = make_float4(us * accU[4 * q4], us * accU[4 * q4 + 1], us * accU[4 * q4 + 2], us * accU[4 * q4 + 3]);
+    *reinterpret_cast<float4*>(Ud + ((size_t)(m0 >> 2) * D + wave * 32 + col) * 4) = u4;
   }
 }
 
@@ -175,7 +306,10 @@ template <bool MULTI, bool FUSED, int RB = kScanRB>
 __device__ __forceinline__ void gdn_scan_item(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
     uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, int nc, uint8_t* lds_raw,
-    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err) {
+    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err, int gpf = 0) {
+  // gram flags per frame: one per record chunk, or gpf when the frame's record
+  // is written in gpf disjoint parts
+  const int nfl = gpf > 0 ? gpf : nc;
   constexpr int D = GD, PITCH = kScanPitch;
   constexpr int SB = RB / 16;  // 16-row sub-blocks
   static_assert(RB == 16 || RB == 32, "scan items cover 16 or 32 rows");
@@ -265,7 +399,7 @@ __device__ __forceinline__ void gdn_scan_item(
       // this frame's records are published by gram items; the previous
       // frame's state (stored by every thread) is announced once all are done
       __builtin_amdgcn_s_waitcnt(0);
-      wait_all(&gflags[(hf0 + f) * nc], nc, epoch, err);
+      wait_all(&gflags[(hf0 + f) * nfl], nfl, epoch, err);
       if (f > 0 && tid == 0)
         __hip_atomic_store(&sflags[(hf0 + f - 1) * 8 + r0 / RB], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       load_rec(f, 0, R);
@@ -407,7 +541,8 @@ __device__ __forceinline__ void gdn_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      qr[r] = (n < n1) ? ld16(qf + (size_t)n * D + cb * 8) : u32x4{0u, 0u, 0u, 0u};
+      // rows past the chunk re-read its first token: their outputs are never stored
+      qr[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * D + cb * 8);
     }
   };
   auto stage = [&](int buf) {
@@ -434,7 +569,7 @@ __device__ __forceinline__ void gdn_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
-      if (t0 + tok < n1) st16(of + (size_t)(t0 + tok) * D + cb * 8, w);
+      if (t0 + tok < n1) st16_stream(of + (size_t)(t0 + tok) * D + cb * 8, w);
     }
   };
   for (int it = 0; it < ntiles; ++it) {

@@ -106,8 +106,65 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
   }
 }
 
+// One call in a single launch for any number of heads: block ids run over
+// the row-split gram items of every (frame, head, row block), then the scan
+// items (four 32-row blocks per head), then the output items of every
+// (frame, chunk, head), each phase head-minor with B*H padded to BHp (a
+// multiple of 8) so that a head's items share one XCD.  Every wait is for
+// items with lower block ids, which dispatch first, so the waits end
+// whatever the number of heads.  For single-frame calls the scan has no
+// frame chain and the phases overlap across heads; longer calls run the
+// chain once all records are in.
+__global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
+    uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
+    float c2, long bh_n, long bhp, int F, int N, int nco, int chunko, uint64_t* __restrict__ gflags,
+    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
+  constexpr int RB = 32, NRB = GD / RB;
+  constexpr int kSL = scan_lds_bytes<RB>();
+  constexpr int LDS = kGramRowsLds > kSL ? (kGramRowsLds > kOutLds ? kGramRowsLds : kOutLds)
+                                         : (kSL > kOutLds ? kSL : kOutLds);
+  __shared__ __align__(16) uint8_t lds[LDS];
+  const long b = blockIdx.x;
+  const long ngram = bhp * F * 4, nscan = bhp * NRB;
+  if (b < ngram) {
+    const long bh = b % bhp, r = b / bhp;  // r = f * 4 + row block
+    if (bh >= bh_n) return;
+    const long item = (bh * F + r / 4) * 4 + r % 4;
+    gdn_gram_rows_item(k, v, beta, rec, c, c2, N, item, lds);
+    publish(&gflags[item], epoch);
+    return;
+  }
+  if (b < ngram + nscan) {
+    const long bs = b - ngram;
+    const long head = bs % bhp;
+    if (head >= bh_n) return;
+    gdn_scan_item<false, true, RB>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
+                                   sflags, epoch, err, 4);
+    return;
+  }
+  const long bo = b - ngram - nscan;
+  const long bh = bo % bhp, r = bo / bhp;  // r = f * nco + chunk
+  if (bh >= bh_n) return;
+  const int f = (int)(r / nco);
+  wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
+  gdn_output_item(q, o, states, N, nco, chunko, bh * F * nco + r, lds);
+}
+
 }  // namespace
 bool gdn_has_mfma(int D, int dtype) { return dtype == DT_BF16 && D == GD; }
+
+hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags, uint64_t epoch,
+                                  uint32_t* err, hipStream_t st) {
+  if (a.D != GD) return hipErrorInvalidValue;
+  const long grid = bhp * (long)a.F * 4 + bhp * (GD / 32) + bhp * (long)a.F * a.nco;
+  hipLaunchKernelGGL(gdn_phased_mfma128, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta, (uint16_t*)a.o, (uint8_t*)a.partial,
+                     (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
+                     sflags, epoch, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {

@@ -93,6 +93,12 @@ int device_slots(const void* kernel);
 // and one step.  At least `min_lag`, at most F.
 int fused_lag(long slots, long items_per_step, int min_lag, int F);
 
+//  GDN, any B*H (N > 0): row-split gram items of all frames (four per frame,
+//  one record per frame: nc must be 1), then scan items, then output items,
+//  in one launch; gflags[B*H*F*4], sflags[B*H*F*8].
+hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
+                                  uint64_t epoch, uint32_t* err, hipStream_t st);
+
 // Generic (VALU) summary and output kernels of either path.
 hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);
 hipError_t launch_output_generic(const ScanArgs& a, hipStream_t st);

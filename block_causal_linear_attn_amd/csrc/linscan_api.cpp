@@ -142,7 +142,7 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
 }
 
 struct GdnPlan {
-  bool mfma, fused;
+  bool mfma, fused, phased;
   int nc, chunk, nco, chunko;
   size_t partial_off, states_off, gflags_off, sflags_off, bytes;
 };
@@ -153,16 +153,26 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   // one launch (scan items alongside the streaming items) when the scan items
   // fill at most one slot per CU and there are frames to overlap
   p.fused = p.mfma && d.bh * linscan::kGdnFusedRowBlocks <= 256 && s->F >= 2 && s->N > 0;
+  // every other MFMA call with tokens: gram, scan and output phases in one
+  // launch
+  p.phased = p.mfma && !p.fused && s->N > 0;
   // a chunk's G/U partials are 8 D^2 bytes: keep chunks long enough that they
   // stay small next to the chunk's own key/value bytes
-  plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
+  if (p.phased) {  // row-split gram items: one record per frame
+    p.nc = 1;
+    p.chunk = s->N;
+  } else {
+    plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
+  }
   plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
   const size_t dd = (size_t)s->D * s->D;
   p.partial_off = kHeaderBytes;
   p.states_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
+  const bool flags = p.fused || p.phased;
   p.gflags_off = align_up(p.states_off + (size_t)d.bhf * dd * sizeof(float), 256);
-  p.sflags_off = align_up(p.gflags_off + (p.fused ? (size_t)d.bhf * p.nc * sizeof(uint64_t) : 0), 256);
-  p.bytes = align_up(p.sflags_off + (p.fused ? (size_t)d.bhf * 8 * sizeof(uint64_t) : 0), 256);
+  const size_t gflags_per_frame = p.phased ? 4 : (size_t)p.nc;
+  p.sflags_off = align_up(p.gflags_off + (flags ? (size_t)d.bhf * gflags_per_frame * sizeof(uint64_t) : 0), 256);
+  p.bytes = align_up(p.sflags_off + (flags ? (size_t)d.bhf * 8 * sizeof(uint64_t) : 0), 256);
   return p;
 }
 
@@ -475,15 +485,19 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   a.chunk = p.chunk;
   a.nco = p.nco;
   a.chunko = p.chunko;
-  if (p.fused) {
+  if (p.fused || p.phased) {
     const long bhp = (d.bh + 7) / 8 * 8;
     uint64_t* gflags = (uint64_t*)(ws + p.gflags_off);
     uint64_t* sflags = (uint64_t*)(ws + p.sflags_off);
     uint32_t* err = (uint32_t*)ws;
     const uint64_t epoch = next_epoch();
-    return hip_check(timed("gdn_fused", hs, [&] {
-                       return linscan::launch_gdn_fused_mfma(a, bhp, gflags, sflags, epoch, err, hs);
-                     }), "gdn fused");
+    if (p.fused)
+      return hip_check(timed("gdn_fused", hs, [&] {
+                         return linscan::launch_gdn_fused_mfma(a, bhp, gflags, sflags, epoch, err, hs);
+                       }), "gdn fused");
+    return hip_check(timed("gdn_phased", hs, [&] {
+                       return linscan::launch_gdn_phased_mfma(a, bhp, gflags, sflags, epoch, err, hs);
+                     }), "gdn phased");
   }
   if ((st = hip_check(timed("gdn_gram", hs, [&] { return linscan::launch_gdn_gram(a, hs); }), "gdn gram")) != LS_OK)
     return st;

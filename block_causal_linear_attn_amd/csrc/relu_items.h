@@ -22,9 +22,12 @@
 
 namespace linscan {
 
-// LDS bytes the summary item needs.
+// LDS bytes the summary item needs: four waves' K and V tiles, or the
+// reduction of their partial sums if that is larger.
 template <int D>
-constexpr int relu_summary_lds_bytes() { return 4 * 2 * 64 * (D + 4) * 2; }
+constexpr int relu_summary_lds_bytes() {
+  return 4 * 2 * 64 * D * 2 > 4 * (D * D + D) * 4 ? 4 * 2 * 64 * D * 2 : 4 * (D * D + D) * 4;
+}
 
 // Work item `wg` = (frame of one head) * nc + token chunk: dS, dz partials of
 // the chunk -> partial[wg]; item (frame 0, chunk 0) of each head also copies
@@ -36,7 +39,7 @@ __device__ __forceinline__ void relu_summary_item(
     long wg, uint8_t* lds_raw) {
   constexpr int DB = D / 32;            // 32-wide dimension blocks
   constexpr int TILE = 64;              // tokens per wave per step
-  constexpr int ROW = D + 4;            // LDS row pitch (bf16)
+  constexpr int ROW = D;                // unpadded rows, chunks swizzled by token
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
   constexpr int LPT = TILE * CPR / 64;  // 16-byte loads per lane per tensor per tile
   constexpr int OUT = D * D + D;
@@ -63,20 +66,19 @@ __device__ __forceinline__ void relu_summary_item(
   }
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
-  // the next tile's rows are loaded into registers while the current tile is contracted
+  // the next tile's rows are loaded into registers while the current tile is
+  // contracted.  Every load is issued (rows past the chunk re-read its first
+  // token) and such rows are zeroed when staged: loads under a lane condition
+  // would make the compiler wait for every load in flight before staging.
   u32x4 kr[LPT], vr[LPT];
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 64 + lane;
       const int n = t0 + ci / CPR, cb = ci % CPR;
-      if (n < n1) {
-        kr[r] = ld16(kf + (size_t)n * D + cb * 8);
-        vr[r] = ld16(vf + (size_t)n * D + cb * 8);
-      } else {
-        kr[r] = u32x4{0u, 0u, 0u, 0u};
-        vr[r] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const size_t off = (size_t)(n < n1 ? n : n0) * D + cb * 8;
+      kr[r] = ld16(kf + off);
+      vr[r] = ld16(vf + off);
     }
   };
   int t0 = n0 + wave * TILE;
@@ -86,15 +88,17 @@ __device__ __forceinline__ void relu_summary_item(
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 64 + lane;
       const int tok = ci / CPR, cb = ci % CPR;
-      u32x4 kk = kr[r];
+      const bool live = t0 + tok < n1;
+      u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
-      uint2* kd = reinterpret_cast<uint2*>(kl + tok * ROW + cb * 8);
-      uint2* vd = reinterpret_cast<uint2*>(vl + tok * ROW + cb * 8);
+      uint2* kd = reinterpret_cast<uint2*>(kl + swz_offset<CPR>(tok, cb));
+      uint2* vd = reinterpret_cast<uint2*>(vl + swz_offset<CPR>(tok, cb));
       kd[0] = make_uint2(kk[0], kk[1]);
       kd[1] = make_uint2(kk[2], kk[3]);
-      vd[0] = make_uint2(vr[r][0], vr[r][1]);
-      vd[1] = make_uint2(vr[r][2], vr[r][3]);
+      vd[0] = make_uint2(vv[0], vv[1]);
+      vd[1] = make_uint2(vv[2], vv[3]);
     }
     if (t0 + 4 * TILE < n1) fetch(t0 + 4 * TILE);
     __builtin_amdgcn_wave_barrier();
@@ -104,8 +108,8 @@ __device__ __forceinline__ void relu_summary_item(
       u32x4 af[DB], bfr[DB];
 #pragma unroll
       for (int blk = 0; blk < DB; ++blk) {
-        af[blk] = gather_tokens_32<ROW>(vl, s * 16, blk * 32, lane);
-        bfr[blk] = gather_tokens_32<ROW>(kl, s * 16, blk * 32, lane);
+        af[blk] = gather_tokens_32_swz<CPR>(vl, s * 16, blk * 32, lane);
+        bfr[blk] = gather_tokens_32_swz<CPR>(kl, s * 16, blk * 32, lane);
       }
 #pragma unroll
       for (int j = 0; j < DB; ++j) {

@@ -100,6 +100,12 @@ GDN_CASES = [
     (1, 2, 3, 40, 32, "fp32", False, True),     # generic fp32, raw keys
     (1, 1, 2, 45, 128, "fp32", True, True),     # generic fp32, D = 128
     (1, 2, 2, 1, 128, "bf16", True, True),      # single token per frame
+    # single-launch phased path (gram, scan, output phases): one frame, or more heads than
+    # the frame-interleaved launch takes
+    (3, 24, 1, 920, 128, "bf16", True, True),   # the chunk-step shape at B = 3: chunked frames
+    (1, 2, 1, 300, 128, "bf16", True, True),    # one frame, two token chunks
+    (1, 70, 3, 130, 128, "bf16", True, True),   # 70 heads, a three-frame chain
+    (1, 1, 1, 1, 128, "bf16", True, True),      # one token, one frame
 ]
 
 
@@ -261,7 +267,7 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
 
 
 # --------------------------------------------------------------------------- single-launch paths
-@pytest.mark.parametrize("op", ["relu", "gdn"])
+@pytest.mark.parametrize("op", ["relu", "gdn", "gdn_phased"])
 def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     """The one-launch paths hand data between work items through flags with
     bounded waits; the workspace's fault word must stay zero and results match."""
@@ -269,9 +275,13 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         x = gen.relu_inputs(1, 11, 9, 777, 32, "bf16", seed=31)   # B*H not a multiple of 8
         shp = ls.ls_shape(1, 11, 9, 777, 32, 1)
         need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
-    else:
+    elif op == "gdn":
         x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=32)
         shp = ls.ls_shape(1, 5, 9, 333, 128, 1)
+        need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+    else:  # 80 heads: the phased launch
+        x = gen.gdn_inputs(2, 40, 2, 200, 128, "bf16", seed=33)
+        shp = ls.ls_shape(2, 40, 2, 200, 128, 1)
         need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     xd = _dev(x)
