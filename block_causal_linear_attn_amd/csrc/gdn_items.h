@@ -13,7 +13,9 @@
 //
 // Output pass: o = S_f q.  Wave w computes output dims [32w, 32w + 32) from
 // S_f's rows held in registers as bf16 hi + lo terms (written by the scan),
-// against 64-token query tiles staged once per workgroup in LDS.
+// against 64-token query tiles staged once per workgroup in LDS.  The lo term
+// matters: o sums 128 products that often cancel, and S rounded to bf16
+// alone would leave an error of 2^-9 of the products' size in such outputs.
 #pragma once
 
 #include "device_common.h"
@@ -554,27 +556,32 @@ __device__ __forceinline__ void gdn_output_item(
     }
   };
 
+  // full tiles run without any branch in the loop body (a load or store
+  // under a condition would make the compiler wait for every memory
+  // operation in flight); fetches past the end re-read the last tile and the
+  // last, partial tile stores under a token check
+  if (n0 >= n1) return;
   const int ntiles = (n1 - n0 + TILE - 1) / TILE;
-  if (ntiles > 0) {
-    fetch(n0);
-    stage(0);
-  }
+  const int nfull = (n1 - n0) / TILE;
+  const int tlast = n0 + (ntiles - 1) * TILE;
+  fetch(n0);
+  stage(0);
   __syncthreads();
-  // the previous tile's outputs leave as whole 256-byte rows (16 lanes per
-  // token, 16 bytes each) from its staging buffer
-  auto drain = [&](int it) {
+  // a tile's outputs leave as whole 256-byte rows (16 lanes per token, 16
+  // bytes each) from its staging buffer
+  auto drain = [&](int it, const bool full) {
     const int t0 = n0 + it * TILE;
 #pragma unroll
     for (int r = 0; r < TILE * (D / 8) / 256; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
-      if (t0 + tok < n1) st16_stream(of + (size_t)(t0 + tok) * D + cb * 8, w);
+      if (full || t0 + tok < n1) st16_stream(of + (size_t)(t0 + tok) * D + cb * 8, w);
     }
   };
-  for (int it = 0; it < ntiles; ++it) {
+  auto tile = [&](int it, const bool full) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) fetch(n0 + (it + 1) * TILE);
+    fetch(min(n0 + (it + 1) * TILE, tlast));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       floatx16 acc = {};
@@ -595,10 +602,12 @@ __device__ __forceinline__ void gdn_output_item(
         *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
       }
     }
-    if (it + 1 < ntiles) stage(buf ^ 1);
+    stage(buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
     __syncthreads();
-    drain(it);
-  }
+    drain(it, full);
+  };
+  for (int it = 0; it < nfull; ++it) tile(it, true);
+  if (nfull < ntiles) tile(nfull, false);
 }
 
 }  // namespace linscan

@@ -169,6 +169,7 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   p.partial_off = kHeaderBytes;
   p.states_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
   const bool flags = p.fused || p.phased;
+  // per-frame states: fp32 for the generic kernels, bf16 hi + lo for the MFMA ones
   p.gflags_off = align_up(p.states_off + (size_t)d.bhf * dd * sizeof(float), 256);
   const size_t gflags_per_frame = p.phased ? 4 : (size_t)p.nc;
   p.sflags_off = align_up(p.gflags_off + (flags ? (size_t)d.bhf * gflags_per_frame * sizeof(uint64_t) : 0), 256);

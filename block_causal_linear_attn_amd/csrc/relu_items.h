@@ -228,10 +228,13 @@ __device__ __forceinline__ void relu_output_item(
       for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
     }
   };
-  auto compute = [&](u32x4 (&b)[U][KS], int t0) {
+  // FULL: every token of the group step is inside the chunk, so the stores
+  // need no lane condition (a store under a condition would make the
+  // compiler wait for every memory operation in flight before the next
+  // group's loads are used)
+  auto compute = [&](u32x4 (&b)[U][KS], int t0, const bool full) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * 32 + col;
       float den = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -272,20 +275,35 @@ __device__ __forceinline__ void relu_output_item(
         const int tl = i * TPI + lane / LPR, cb = lane % LPR;
         const u32x4 w = *reinterpret_cast<const u32x4*>(ost + tl * OP + cb * 8);
         const int tt = t0 + u * 32 + tl;
-        if (tt < n1) st16(of + (size_t)tt * D + cb * 8, w);
+        if (full || tt < n1) st16(of + (size_t)tt * D + cb * 8, w);
       }
       __builtin_amdgcn_wave_barrier();
     }
   };
+  // This wave's steps of U * 32 tokens start at n0 + wave * U * 32 and every
+  // STEP after; the first nfull of them lie inside the chunk, at most one
+  // more is partial.  Loads past the chunk re-read its first token, so every
+  // load is issued unconditionally; the main loop has no branch.
+  if (n0 >= n1) return;
+  const int first = n0 + wave * U * 32;
+  const int nfull = first + U * 32 <= n1 ? (n1 - first - U * 32) / STEP + 1 : 0;
   u32x4 b0[U][KS], b1[U][KS];
-  int t0 = n0 + wave * U * 32;
-  if (t0 < n1) load(b0, t0);
-  for (; t0 < n1; t0 += 2 * STEP) {
-    if (t0 + STEP < n1) load(b1, t0 + STEP);
-    compute(b0, t0);
-    if (t0 + STEP >= n1) break;
-    if (t0 + 2 * STEP < n1) load(b0, t0 + 2 * STEP);
-    compute(b1, t0 + STEP);
+  int t0 = first;
+  load(b0, t0);
+  int k = 0;
+  for (; k + 2 <= nfull; k += 2, t0 += 2 * STEP) {
+    load(b1, t0 + STEP);
+    compute(b0, t0, true);
+    load(b0, t0 + 2 * STEP);
+    compute(b1, t0 + STEP, true);
+  }
+  // b0 holds step k: one more full step and/or a partial one
+  if (k < nfull) {
+    load(b1, t0 + STEP);
+    compute(b0, t0, true);
+    if (t0 + STEP < n1) compute(b1, t0 + STEP, false);
+  } else if (t0 < n1) {
+    compute(b0, t0, false);
   }
 }
 

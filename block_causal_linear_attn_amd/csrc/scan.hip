@@ -33,8 +33,8 @@ namespace {
 
 // One workgroup per (batch*head, 16-row block).  State rows live in LDS; G_f
 // is summed over token chunks into LDS each frame; every thread owns EPT
-// (row, col) entries.  HILO stores each frame's state as bf16 hi/lo planes.
-template <int D, bool HILO>
+// (row, col) entries.  Each frame's state goes to `states` in fp32.
+template <int D>
 __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__ partial,
                                                        const float* __restrict__ alpha,
                                                        const float* __restrict__ beta,
@@ -98,16 +98,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
       if (e < RB * D) {
         const int r = e / D, j = e % D;
         Ss[r][j] = s[x];
-        const size_t idx = (size_t)(r0 + r) * D + j;
-        if (HILO) {
-          uint16_t h, lo;
-          split_bf16(s[x], h, lo);
-          uint16_t* dst = reinterpret_cast<uint16_t*>(states) + bhf * 2 * D * D;
-          dst[idx] = h;
-          dst[(size_t)D * D + idx] = lo;
-        } else {
-          reinterpret_cast<float*>(states)[bhf * D * D + idx] = s[x];
-        }
+        reinterpret_cast<float*>(states)[bhf * D * D + (size_t)(r0 + r) * D + j] = s[x];
       }
     }
   }
@@ -121,16 +112,10 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
 }
 
 template <int D>
-hipError_t scan_launch(bool hilo, const float* partial, const float* alpha, const float* beta,
-                       const float* S0, void* states, float* S_out, long bh, int F, int nc,
-                       hipStream_t st) {
+hipError_t scan_launch(const float* partial, const float* alpha, const float* beta, const float* S0,
+                       void* states, float* S_out, long bh, int F, int nc, hipStream_t st) {
   dim3 grid((unsigned)(bh * (D / 16))), block(256);
-  if (hilo)
-    hipLaunchKernelGGL((gdn_scan_kernel<D, true>), grid, block, 0, st, partial, alpha, beta, S0,
-                       states, S_out, F, nc);
-  else
-    hipLaunchKernelGGL((gdn_scan_kernel<D, false>), grid, block, 0, st, partial, alpha, beta, S0,
-                       states, S_out, F, nc);
+  hipLaunchKernelGGL(gdn_scan_kernel<D>, grid, block, 0, st, partial, alpha, beta, S0, states, S_out, F, nc);
   return hipGetLastError();
 }
 
@@ -198,7 +183,7 @@ hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st) {
   if (a.mfma) return launch_gdn_scan_mfma(a.D, a.partial, a.alpha, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
   switch (a.D) {
 #define CASE(d) \
-  case d: return scan_launch<d>(false, a.partial, a.alpha, a.beta, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
+  case d: return scan_launch<d>(a.partial, a.alpha, a.beta, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
     CASE(16) CASE(32) CASE(48) CASE(64) CASE(80) CASE(96) CASE(112) CASE(128)
 #undef CASE
     default: return hipErrorInvalidValue;
