@@ -41,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_720p_minute.md")
 KERNEL_SOURCES = {
     "relu_fused": ["device_common.h", "sync.h", "relu_items.h", "relu_mfma.hip"],
     "gdn_fused": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
+    "gdn_phased": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
 }
 
 
