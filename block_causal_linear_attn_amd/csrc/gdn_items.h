@@ -28,6 +28,7 @@ constexpr int GD = 128;
 constexpr size_t kRecBytes = 8 * (size_t)GD * GD;
 
 constexpr int kGramLds = 2 * 2 * 64 * GD * 2;
+constexpr int kGramDepth = 2;  // tiles in flight per gram item
 
 // Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
 // (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.
@@ -58,29 +59,37 @@ __device__ __forceinline__ void gdn_gram_item(
     accU[j] = floatx16{};
   }
 
-  // every load is issued (rows past the chunk re-read its first token) and
-  // such rows are zeroed when staged: loads under a lane condition would make
-  // the compiler wait for every load in flight before staging
-  u32x4 kr[LPT], vr[LPT];
-  auto fetch = [&](int t0) {
+  // Tiles of the chunk are fetched into a ring of kGramDepth register sets
+  // (tile t in set t % kGramDepth until staged), so that many tiles are in
+  // flight while one is contracted from LDS.  The loop body has no branch: it
+  // runs a whole number of ring passes, tiles past the chunk are staged as
+  // zeros (every row fails the token check) and add nothing, and fetches past
+  // the chunk re-read its last tile.  A load or stage under a condition would
+  // make the compiler wait for every load in flight at every stage.
+  constexpr int DEPTH = kGramDepth;
+  struct Regs {
+    u32x4 k[LPT], v[LPT];
+  };
+  Regs R[DEPTH];
+  auto fetch = [&](Regs& X, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
       const size_t off = (size_t)(n < n1 ? n : n0) * D + cb * 8;
-      kr[r] = ld16_stream(kf + off);
-      vr[r] = ld16_stream(vf + off);
+      X.k[r] = ld16_stream(kf + off);
+      X.v[r] = ld16_stream(vf + off);
     }
   };
-  auto stage = [&](int buf, int t0) {
+  auto stage = [&](const Regs& X, int buf, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const bool live = t0 + tok < n1;
-      const u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -89,16 +98,7 @@ __device__ __forceinline__ void gdn_gram_item(
       vd[1] = make_uint2(vv[2], vv[3]);
     }
   };
-
-  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
-  if (ntiles > 0) {
-    fetch(n0);
-    stage(0, n0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) fetch(n0 + (it + 1) * TILE);
+  auto contract = [&](int buf) {
     const uint16_t* kl = lds[buf][0];
     const uint16_t* vl = lds[buf][1];
 #pragma unroll
@@ -113,8 +113,28 @@ __device__ __forceinline__ void gdn_gram_item(
         accU[J] = mfma32x32x16(as_bf16x8(vfrag), as_bf16x8(kfrag[J]), accU[J]);
       }
     }
-    if (it + 1 < ntiles) stage(buf ^ 1, n0 + (it + 1) * TILE);
+  };
+
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+  if (ntiles > 0) {
+    const int tlast = n0 + (ntiles - 1) * TILE;
+    const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) fetch(R[d], min(n0 + d * TILE, tlast));
+    stage(R[0], 0, n0);
+    fetch(R[0], min(n0 + DEPTH * TILE, tlast));
     __syncthreads();
+    for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int it = it0 + u;
+        contract(it & 1);
+        Regs& nxt = R[(u + 1) % DEPTH];  // holds tile it + 1
+        stage(nxt, (it + 1) & 1, n0 + (it + 1) * TILE);
+        fetch(nxt, min(n0 + (it + 1 + DEPTH) * TILE, tlast));
+        __syncthreads();
+      }
+    }
   }
 
   // record of this (frame, chunk): beta*G as bf16 hi and lo planes (row-major),
@@ -536,36 +556,43 @@ __device__ __forceinline__ void gdn_output_item(
 
   const uint16_t* qf = q + (size_t)bhf * N * D;
   uint16_t* of = o + (size_t)bhf * N * D;
-  u32x4 qr[LPT];
-  auto fetch = [&](int t0) {
+  // query tiles come in through two register sets (tile t in set t % 2
+  // until staged), so two tiles are in flight while one is contracted
+  struct Regs {
+    u32x4 q[LPT];
+  };
+  auto fetch = [&](Regs& X, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
       // rows past the chunk re-read its first token: their outputs are never stored
-      qr[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * D + cb * 8);
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * D + cb * 8);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](const Regs& X, int buf) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qr[r];
+      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = X.q[r];
     }
   };
 
-  // full tiles run without any branch in the loop body (a load or store
-  // under a condition would make the compiler wait for every memory
-  // operation in flight); fetches past the end re-read the last tile and the
-  // last, partial tile stores under a token check
+  // Full tiles run in pairs without any branch in the loop body (a load or
+  // store under a condition would make the compiler wait for every memory
+  // operation in flight); fetches past the end re-read the last tile, and a
+  // last, partial tile stores under a token check after the loop.
   if (n0 >= n1) return;
   const int ntiles = (n1 - n0 + TILE - 1) / TILE;
   const int nfull = (n1 - n0) / TILE;
   const int tlast = n0 + (ntiles - 1) * TILE;
-  fetch(n0);
-  stage(0);
+  Regs R0, R1;
+  fetch(R0, n0);
+  fetch(R1, min(n0 + TILE, tlast));
+  stage(R0, 0);
+  fetch(R0, min(n0 + 2 * TILE, tlast));
   __syncthreads();
   // a tile's outputs leave as whole 256-byte rows (16 lanes per token, 16
   // bytes each) from its staging buffer
@@ -579,9 +606,9 @@ __device__ __forceinline__ void gdn_output_item(
       if (full || t0 + tok < n1) st16_stream(of + (size_t)(t0 + tok) * D + cb * 8, w);
     }
   };
-  auto tile = [&](int it, const bool full) {
+  // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3
+  auto tile = [&](int it, Regs& nxt, const bool full) {
     const int buf = it & 1;
-    fetch(min(n0 + (it + 1) * TILE, tlast));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       floatx16 acc = {};
@@ -602,12 +629,23 @@ __device__ __forceinline__ void gdn_output_item(
         *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
       }
     }
-    stage(buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
+    stage(nxt, buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
+    fetch(nxt, min(n0 + (it + 3) * TILE, tlast));
     __syncthreads();
     drain(it, full);
   };
-  for (int it = 0; it < nfull; ++it) tile(it, true);
-  if (nfull < ntiles) tile(nfull, false);
+  int it = 0;
+  for (; it + 2 <= nfull; it += 2) {
+    tile(it, R1, true);
+    tile(it + 1, R0, true);
+  }
+  // R1 holds tile it + 1: at most one more full tile, then at most one partial one
+  if (it < nfull) {
+    tile(it, R1, true);
+    if (it + 1 < ntiles) tile(it + 1, R0, false);
+  } else if (it < ntiles) {
+    tile(it, R1, false);
+  }
 }
 
 }  // namespace linscan
