@@ -9,8 +9,9 @@
 // Scan items wait for the gram records of each frame, output items wait for
 // the four row blocks of their frame's state.  Every item a wait depends on
 // is either dispatched earlier or, for the scan items, a gram item that can
-// still find a free slot because scan items fill at most one slot per CU;
-// the launcher only picks this kernel when that holds (B*H*4 <= 256).  All
+// still find a free slot because scan items fill at most a quarter of the
+// device's slots; the library only picks this kernel when that holds
+// (B*H*4 <= 128), which leaves room for other launches running alongside.  All
 // items of a head share one XCD (block id equal to the head modulo 8), so
 // records and per-frame states are read back from that XCD's L2 shortly
 // after they are written, and the scan's frame-to-frame chain overlaps the

@@ -75,8 +75,8 @@ hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st);
 //  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states,
-//  kGdnFusedRowBlocks of the 8 used); only for B*H*kGdnFusedRowBlocks <= 256
-//  so that scan items never take more than one slot per CU.
+//  kGdnFusedRowBlocks of the 8 used); only for B*H*kGdnFusedRowBlocks <= 128
+//  so that scan items never take more than a quarter of the device's slots.
 constexpr int kGdnFusedRowBlocks = 4;
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st);

@@ -150,9 +150,12 @@ struct GdnPlan {
 GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   GdnPlan p;
   p.mfma = linscan::gdn_has_mfma(s->D, s->dtype);
-  // one launch (scan items alongside the streaming items) when the scan items
-  // fill at most one slot per CU and there are frames to overlap
-  p.fused = p.mfma && d.bh * linscan::kGdnFusedRowBlocks <= 256 && s->F >= 2 && s->N > 0;
+  // one launch with the scan items alongside the streaming items when there
+  // are frames to overlap and the scan items take at most a quarter of the
+  // device's workgroup slots: they stay resident waiting for gram items that
+  // come later in dispatch order, which need free slots even if calls on
+  // other streams occupy the rest (see the header)
+  p.fused = p.mfma && d.bh * linscan::kGdnFusedRowBlocks <= 128 && s->F >= 2 && s->N > 0;
   // every other MFMA call with tokens: gram, scan and output phases in one
   // launch
   p.phased = p.mfma && !p.fused && s->N > 0;

@@ -39,16 +39,24 @@
  *    the status names the reason (ls_last_error() gives details).  A device
  *    fault surfaces at the caller's next synchronisation.
  *  - The first 4 bytes of a workspace are its fault word.  Calls that run
- *    as a single launch (bf16 at head dims 32/64 for the ReLU scan, head dim
- *    128 for the GDN scan when B*H <= 64 and F >= 2) hand data between their
- *    work items through flags with bounded waits; if a wait ever gave up,
- *    the call's results are invalid and the fault word becomes nonzero.  The
- *    library never clears it; callers that check it zero it beforehand.
+ *    as a single launch (bf16 at head dims 32/64 for the ReLU scan, bf16 at
+ *    head dim 128 for the GDN scan whenever it has tokens) hand data between
+ *    their work items through flags with bounded waits; if a wait ever gave
+ *    up, the call's results are invalid and the fault word becomes nonzero.
+ *    The library never clears it; callers that check it zero it beforehand.
+ *  - Concurrency: every wait of these launches is for work dispatched
+ *    earlier in the same launch, with one exception.  A GDN call with
+ *    B*H <= 32 and F >= 2 keeps 4*B*H scan work-groups resident for its
+ *    whole run, waiting for work-groups of the same launch that still need
+ *    free slots; at most a quarter of an MI355X's slots at this kernel's
+ *    occupancy.  Up to three such calls may run concurrently on different
+ *    streams whatever else runs; a fourth could find every slot taken by
+ *    waiting work, and its waits would time out (fault word set).
  *  - The caller owns every buffer, including the workspace.  The library
  *    never allocates device memory and carries nothing from one call to the
  *    next (the optional profiling session below only keeps HIP events).
  *    Calls on different streams are safe when their outputs and workspaces
- *    differ.
+ *    differ (within the concurrency limit above).
  *  - A dimension of size zero is legal: B*H == 0 does nothing; F == 0 copies
  *    the initial state to the output state; N == 0 gives frames without
  *    tokens (the ReLU state is unchanged, the GDN state still decays).
