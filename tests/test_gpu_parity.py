@@ -300,3 +300,44 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
         check("single-launch gdn o", o, ro, 2e-2)
         check("single-launch gdn S", S, rS, 1e-2)
+
+
+def test_concurrent_streams_match_sequential(ls, gen):
+    """Single-launch calls running at the same time on separate streams (three
+    frame-interleaved GDN calls, one phased GDN call, two ReLU calls) give the
+    same bits as when run one after another, and no wait times out."""
+    jobs = []
+    for i in range(3):  # frame-interleaved GDN launches (B*H <= 32)
+        jobs.append(("gdn", _dev(gen.gdn_inputs(1, 8, 6, 300, 128, "bf16", seed=40 + i))))
+    jobs.append(("gdn", _dev(gen.gdn_inputs(1, 40, 3, 200, 128, "bf16", seed=44))))  # phased launch
+    for i in range(2):
+        jobs.append(("relu", _dev(gen.relu_inputs(1, 12, 5, 700, 32, "bf16", seed=45 + i))))
+
+    def run(kind, x, ws):
+        if kind == "gdn":
+            return ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], ws=ws)
+        return ls.ls_relu_block_forward(x["q"], x["k"], x["v"], ws=ws)
+
+    def workspace(kind, x):
+        B, H, F, N, D = x["q"].shape
+        shp = ls.ls_shape(B, H, F, N, D, 1)
+        if kind == "gdn":
+            need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+        else:
+            need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 1)
+        return torch.zeros(need, dtype=torch.uint8, device=DEV)
+
+    ref = [run(kind, x, workspace(kind, x)) for kind, x in jobs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in jobs]
+    wss = [workspace(kind, x) for kind, x in jobs]
+    torch.cuda.synchronize()
+    out = []
+    for (kind, x), st, ws in zip(jobs, streams, wss):
+        with torch.cuda.stream(st):
+            out.append(run(kind, x, ws))
+    torch.cuda.synchronize()
+    for i, (r, o, ws) in enumerate(zip(ref, out, wss)):
+        assert int(ws[:4].view(torch.int32).item()) == 0, i
+        for a, b in zip(r, o):
+            assert torch.equal(a, b), i
