@@ -31,11 +31,15 @@ constexpr int kGramLds = 2 * 2 * 64 * GD * 2;
 constexpr int kGramDepth = 2;  // tiles in flight per gram item
 
 // Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
-// (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.
+// (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.  DI is the head dim
+// of the tensors (112 or 128); the items work on 128 dims, the dims past DI
+// being zero.
+template <int DI = GD>
 __device__ __forceinline__ void gdn_gram_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw) {
   constexpr int D = GD;
+  constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
   constexpr int ROW = D;  // unpadded rows, chunks swizzled by token (conflict-free transpose reads)
   constexpr int C = D / 8;
@@ -49,8 +53,8 @@ __device__ __forceinline__ void gdn_gram_item(
   const long bhf = wg / nc;
   const int n0 = (int)(wg % nc) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const uint16_t* kf = k + (size_t)bhf * N * D;
-  const uint16_t* vf = v + (size_t)bhf * N * D;
+  const uint16_t* kf = k + (size_t)bhf * N * DI;
+  const uint16_t* vf = v + (size_t)bhf * N * DI;
 
   floatx16 accG[4], accU[4];
 #pragma unroll
@@ -77,7 +81,7 @@ __device__ __forceinline__ void gdn_gram_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      const size_t off = (size_t)(n < n1 ? n : n0) * D + cb * 8;
+      const size_t off = (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8;
       X.k[r] = ld16_stream(kf + off);
       X.v[r] = ld16_stream(vf + off);
     }
@@ -87,7 +91,7 @@ __device__ __forceinline__ void gdn_gram_item(
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      const bool live = t0 + tok < n1;
+      const bool live = t0 + tok < n1 && cb < CI;
       const u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
@@ -179,10 +183,12 @@ constexpr int kGramRowsKRow = GD, kGramRowsVRow = 32;  // unpadded; K chunks swi
 constexpr int kGramRowsDepth = 4;  // tiles in flight per workgroup
 constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;
 
+template <int DI = GD>
 __device__ __forceinline__ void gdn_gram_rows_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw) {
   constexpr int D = GD;
+  constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
   constexpr int KROW = kGramRowsKRow, VROW = kGramRowsVRow;
   constexpr int KLPT = TILE * (D / 8) / 256;  // 16-byte K loads per thread per tile (4)
@@ -196,8 +202,9 @@ __device__ __forceinline__ void gdn_gram_rows_item(
   const int g = lane >> 5, col = lane & 31;
   const long bhf = item >> 2;
   const int w = (int)(item & 3);
-  const uint16_t* kf = k + (size_t)bhf * N * D;
-  const uint16_t* vf = v + (size_t)bhf * N * D + 32 * w;
+  const uint16_t* kf = k + (size_t)bhf * N * DI;
+  const uint16_t* vf = v + (size_t)bhf * N * DI;
+  const int vchunk = 4 * w + (tid & 3);  // this thread's 16-byte chunk of the V rows
 
   floatx16 accG = {}, accU = {};
   struct Regs {
@@ -214,21 +221,21 @@ __device__ __forceinline__ void gdn_gram_rows_item(
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
       const int n = t0 + (ci >> 4);
-      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * D + (ci & 15) * 8);
+      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * DI + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
     }
     const int n = t0 + (tid >> 2);
-    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * D + (tid & 3) * 8);
+    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * DI + (vchunk < CI ? vchunk : CI - 1) * 8);
   };
   auto stage = [&](const Regs& R, int buf, int t0) {
 #pragma unroll
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
-      const u32x4 kk = t0 + (ci >> 4) < N ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 kk = t0 + (ci >> 4) < N && (ci & 15) < CI ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
       uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
       kd[0] = make_uint2(kk[0], kk[1]);
       kd[1] = make_uint2(kk[2], kk[3]);
     }
-    const u32x4 vv = t0 + (tid >> 2) < N ? R.v : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 vv = t0 + (tid >> 2) < N && vchunk < CI ? R.v : u32x4{0u, 0u, 0u, 0u};
     uint2* vd = reinterpret_cast<uint2*>(vl[buf] + swz_offset<VROW / 8>(tid >> 2, tid & 3));
     vd[0] = make_uint2(vv[0], vv[1]);
     vd[1] = make_uint2(vv[2], vv[3]);
@@ -324,7 +331,7 @@ constexpr int kScanLds = scan_lds_bytes<kScanRB>();
 // FUSED: records come from gram items of the same launch (wait for gflags
 // before each frame, one flag per token chunk) and each frame's state is
 // announced on sflags[(head * F + f) * 8 + r0 / RB] for the output items.
-template <bool MULTI, bool FUSED, int RB = kScanRB>
+template <bool MULTI, bool FUSED, int RB = kScanRB, int DI = GD>
 __device__ __forceinline__ void gdn_scan_item(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
     uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, int nc, uint8_t* lds_raw,
@@ -350,7 +357,7 @@ __device__ __forceinline__ void gdn_scan_item(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 16 * sb + 4 * lg + r, n = 32 * wave + 16 * nb + lr;
-        s[sb][nb][r] = S0 ? S0[(size_t)head * D * D + (size_t)(r0 + m) * D + n] : 0.0f;
+        s[sb][nb][r] = S0 && r0 + m < DI && n < DI ? S0[(size_t)head * DI * DI + (size_t)(r0 + m) * DI + n] : 0.0f;
         Ss[0][m][n] = s[sb][nb][r];
       }
 
@@ -514,9 +521,10 @@ __device__ __forceinline__ void gdn_scan_item(
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S_out[(size_t)head * D * D + (size_t)(r0 + 16 * sb + 4 * lg + r) * D + 32 * wave + 16 * nb + lr] =
-              s[sb][nb][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + 16 * sb + 4 * lg + r, cl = 32 * wave + 16 * nb + lr;
+          if (row < DI && cl < DI) S_out[(size_t)head * DI * DI + (size_t)row * DI + cl] = s[sb][nb][r];
+        }
   }
 }
 
@@ -525,10 +533,12 @@ constexpr int kOutPitch = GD + 8;
 constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;
 
 // Work item `wg` = (frame of one head) * nco + token chunk: o = S_f q.
+template <int DI = GD>
 __device__ __forceinline__ void gdn_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
     int N, int nco, int chunk, long wg, uint8_t* lds_raw) {
   constexpr int D = GD;
+  constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
   constexpr int ROW = D + 8;  // 272-byte pitch: 16-byte fragment reads spread over all banks
   constexpr int LPT = TILE * (D / 8) / 256;  // 4
@@ -554,8 +564,8 @@ __device__ __forceinline__ void gdn_output_item(
     alo[s] = ld16(lo + off);
   }
 
-  const uint16_t* qf = q + (size_t)bhf * N * D;
-  uint16_t* of = o + (size_t)bhf * N * D;
+  const uint16_t* qf = q + (size_t)bhf * N * DI;
+  uint16_t* of = o + (size_t)bhf * N * DI;
   // query tiles come in through two register sets (tile t in set t % 2
   // until staged), so two tiles are in flight while one is contracted
   struct Regs {
@@ -568,7 +578,8 @@ __device__ __forceinline__ void gdn_output_item(
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
       // rows past the chunk re-read its first token: their outputs are never stored
-      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * D + cb * 8);
+      // (dims past DI re-read a real chunk: S_f is zero in those columns)
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8);
     }
   };
   auto stage = [&](const Regs& X, int buf) {
@@ -603,7 +614,7 @@ __device__ __forceinline__ void gdn_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
-      if (full || t0 + tok < n1) st16_stream(of + (size_t)(t0 + tok) * D + cb * 8, w);
+      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * DI + cb * 8, w);
     }
   };
   // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3

@@ -19,18 +19,21 @@
 #include "gdn_items.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace linscan {
 
 namespace {
 
+template <int DI>
 __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk) {
   __shared__ __align__(16) uint8_t lds[kGramLds];
-  gdn_gram_item(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds);
+  gdn_gram_item<DI>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds);
 }
 
-template <bool MULTI>
+template <bool MULTI, int DI>
 __global__ __launch_bounds__(256) void gdn_scan_mfma128(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
     uint16_t* __restrict__ states, float* S_out, long bh, int F, int nc) {
@@ -38,20 +41,21 @@ __global__ __launch_bounds__(256) void gdn_scan_mfma128(
   const long b = blockIdx.x;
   const long head = (b / 64) * 8 + (b % 8);
   if (head >= bh) return;  // whole workgroup leaves together
-  gdn_scan_item<MULTI, false>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % 8) * kScanRB, F, nc,
+  gdn_scan_item<MULTI, false, kScanRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % 8) * kScanRB, F, nc,
                               lds, nullptr, nullptr, 0, nullptr);
 }
 
+template <int DI>
 __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
     int N, int nco, int chunk) {
   __shared__ __align__(16) uint8_t lds[kOutLds];
-  gdn_output_item(q, o, states, N, nco, chunk, blockIdx.x, lds);
+  gdn_output_item<DI>(q, o, states, N, nco, chunk, blockIdx.x, lds);
 }
 
 constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan item
 
-template <bool MULTI>
+template <bool MULTI, int DI>
 __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     // eight heads x NRB row blocks per group; a head's row blocks keep its XCD
     const long head = (b / (8 * NRB)) * 8 + (b % 8);
     if (head >= bh_n) return;
-    gdn_scan_item<MULTI, true, kFusedRB>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
+    gdn_scan_item<MULTI, true, kFusedRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
                                          F, nc, lds, gflags, sflags, epoch, err);
     return;
   }
@@ -99,11 +103,11 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     cidx = (int)(r % nco);
   }
   if (gram) {
-    gdn_gram_item(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
+    gdn_gram_item<DI>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
     publish(&gflags[(bh * F + f) * nc + cidx], epoch);
   } else {
     wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-    gdn_output_item(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds);
+    gdn_output_item<DI>(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds);
   }
 }
 
@@ -116,6 +120,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
 // whatever the number of heads.  For single-frame calls the scan has no
 // frame chain and the phases overlap across heads; longer calls run the
 // chain once all records are in.
+template <int DI>
 __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long bh = b % bhp, r = b / bhp;  // r = f * 4 + row block
     if (bh >= bh_n) return;
     const long item = (bh * F + r / 4) * 4 + r % 4;
-    gdn_gram_rows_item(k, v, beta, rec, c, c2, N, item, lds);
+    gdn_gram_rows_item<DI>(k, v, beta, rec, c, c2, N, item, lds);
     publish(&gflags[item], epoch);
     return;
   }
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long bs = b - ngram;
     const long head = bs % bhp;
     if (head >= bh_n) return;
-    gdn_scan_item<false, true, RB>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
+    gdn_scan_item<false, true, RB, DI>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
                                    sflags, epoch, err, 4);
     return;
   }
@@ -150,69 +155,87 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
   if (bh >= bh_n) return;
   const int f = (int)(r / nco);
   wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-  gdn_output_item(q, o, states, N, nco, chunko, bh * F * nco + r, lds);
+  gdn_output_item<DI>(q, o, states, N, nco, chunko, bh * F * nco + r, lds);
 }
 
 }  // namespace
-bool gdn_has_mfma(int D, int dtype) { return dtype == DT_BF16 && D == GD; }
+// Head dims with an MFMA path: 128, and 112 (the items run on 128 dims with
+// the last 16 zero).
+bool gdn_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == GD || D == 112); }
+
+// Instantiate `body` with the head dim as a compile-time constant.
+template <typename Body>
+hipError_t with_head_dim(int D, Body body) {
+  if (D == GD) return body(std::integral_constant<int, GD>());
+  if (D == 112) return body(std::integral_constant<int, 112>());
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
-  if (a.D != GD) return hipErrorInvalidValue;
   const long grid = bhp * (long)a.F * 4 + bhp * (GD / 32) + bhp * (long)a.F * a.nco;
-  hipLaunchKernelGGL(gdn_phased_mfma128, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta, (uint16_t*)a.o, (uint8_t*)a.partial,
-                     (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
-                     sflags, epoch, err);
-  return hipGetLastError();
+  return with_head_dim(a.D, [&](auto di) {
+    hipLaunchKernelGGL((gdn_phased_mfma128<decltype(di)::value>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
+                       (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
+                       bhp, a.F, a.N, a.nco, a.chunko, gflags, sflags, epoch, err);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
-  if (D != GD) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdn_gram_mfma128, dim3((unsigned)(bhf * nc)), dim3(256), 0, st,
-                     (const uint16_t*)k, (const uint16_t*)v, beta, (uint8_t*)rec, c, c2, N, nc, chunk);
-  return hipGetLastError();
+  return with_head_dim(D, [&](auto di) {
+    hipLaunchKernelGGL((gdn_gram_mfma128<decltype(di)::value>), dim3((unsigned)(bhf * nc)), dim3(256), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, beta, (uint8_t*)rec, c, c2, N, nc, chunk);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
                                 void* states, float* S_out, long bh, int F, int nc, hipStream_t st) {
-  if (D != GD) return hipErrorInvalidValue;
   const long groups = (bh + 7) / 8;  // eight heads x eight row blocks per group of 64 workgroups
-  if (nc == 1)
-    hipLaunchKernelGGL(gdn_scan_mfma128<false>, dim3((unsigned)(groups * 64)), dim3(256), 0, st,
-                       (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
-  else
-    hipLaunchKernelGGL(gdn_scan_mfma128<true>, dim3((unsigned)(groups * 64)), dim3(256), 0, st,
-                       (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
-  return hipGetLastError();
+  return with_head_dim(D, [&](auto di) {
+    constexpr int DI = decltype(di)::value;
+    if (nc == 1)
+      hipLaunchKernelGGL((gdn_scan_mfma128<false, DI>), dim3((unsigned)(groups * 64)), dim3(256), 0, st,
+                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
+    else
+      hipLaunchKernelGGL((gdn_scan_mfma128<true, DI>), dim3((unsigned)(groups * 64)), dim3(256), 0, st,
+                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
                                   int N, int nco, int chunk, hipStream_t st) {
-  if (D != GD) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gdn_output_mfma128, dim3((unsigned)(bhf * nco)), dim3(256), 0, st,
-                     (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk);
-  return hipGetLastError();
+  return with_head_dim(D, [&](auto di) {
+    hipLaunchKernelGGL((gdn_output_mfma128<decltype(di)::value>), dim3((unsigned)(bhf * nco)), dim3(256), 0, st,
+                       (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st) {
-  if (a.D != GD) return hipErrorInvalidValue;
   const long grid = bhp * kGdnFusedRowBlocks + bhp * a.F * (a.nc + a.nco);
-  const void* kern = a.nc == 1 ? (const void*)gdn_fused_mfma128<false> : (const void*)gdn_fused_mfma128<true>;
-  const int lag = fused_lag(device_slots(kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1, a.F);
-  if (a.nc == 1)
-    hipLaunchKernelGGL(gdn_fused_mfma128<false>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta, (uint16_t*)a.o,
-                       (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N,
-                       a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
-  else
-    hipLaunchKernelGGL(gdn_fused_mfma128<true>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta, (uint16_t*)a.o,
-                       (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N,
-                       a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
-  return hipGetLastError();
+  return with_head_dim(a.D, [&](auto di) {
+    constexpr int DI = decltype(di)::value;
+    const void* kern =
+        a.nc == 1 ? (const void*)gdn_fused_mfma128<false, DI> : (const void*)gdn_fused_mfma128<true, DI>;
+    const int lag = fused_lag(device_slots(kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1, a.F);
+    if (a.nc == 1)
+      hipLaunchKernelGGL((gdn_fused_mfma128<false, DI>), dim3((unsigned)grid), dim3(256), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
+                         (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
+                         bhp, a.F, a.N, a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
+    else
+      hipLaunchKernelGGL((gdn_fused_mfma128<true, DI>), dim3((unsigned)grid), dim3(256), 0, st,
+                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
+                         (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
+                         bhp, a.F, a.N, a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace linscan

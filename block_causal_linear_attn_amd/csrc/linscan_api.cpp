@@ -168,7 +168,9 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
     plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
   }
   plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
-  const size_t dd = (size_t)s->D * s->D;
+  // records and per-frame states of the MFMA kernels always cover 128 dims
+  const size_t Dw = p.mfma ? 128 : (size_t)s->D;
+  const size_t dd = Dw * Dw;
   p.partial_off = kHeaderBytes;
   p.states_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * 2 * dd * sizeof(float), 256);
   const bool flags = p.fused || p.phased;

@@ -95,7 +95,11 @@ GDN_CASES = [
     (1, 2, 4, 16, 16, "fp32", False, False),    # the tiny workload's shape
     (1, 2, 6, 300, 128, "bf16", True, True),    # MFMA path, ragged token count
     (2, 1, 3, 920, 128, "bf16", True, False),   # the 720p token count
-    (1, 2, 3, 97, 112, "bf16", True, True),     # generic bf16 at the pages' head dim
+    (1, 2, 3, 97, 112, "bf16", True, True),     # the pages' head dim (MFMA path, 128 dims zero-padded)
+    (2, 3, 5, 920, 112, "bf16", True, True),    # head dim 112, frame-interleaved launch
+    (1, 2, 1, 300, 112, "bf16", True, True),    # head dim 112, phased launch, one frame
+    (1, 40, 3, 130, 112, "bf16", True, True),   # head dim 112, phased launch, 40 heads
+    (1, 2, 3, 80, 96, "bf16", True, True),      # generic bf16 kernels at a head dim without MFMA path
     (1, 2, 4, 64, 64, "bf16", True, False),     # generic bf16, D = 64
     (1, 2, 3, 40, 32, "fp32", False, True),     # generic fp32, raw keys
     (1, 1, 2, 45, 128, "fp32", True, True),     # generic fp32, D = 128
