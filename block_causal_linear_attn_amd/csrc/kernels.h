@@ -16,6 +16,8 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 // supported pair runs the generic kernels.
 bool relu_has_mfma(int D, int dtype);
 bool gdn_has_mfma(int D, int dtype);
+// The ReLU MFMA pairs served by the wide (head dims 112, 128) items.
+bool relu_wide_mfma(int D, int dtype);
 
 // Everything a launcher may need for one call (pointers are device pointers).
 struct ScanArgs {
@@ -74,6 +76,11 @@ hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
 //  ReLU: flags[B*H*F]; summary with one chunk per frame (nc = 1).
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st);
+//  ReLU, wide heads: `partial` holds the cumulative state of every frame,
+//  [B*H*F][128*128 + 128] floats (S row-major, then z; 128 dims wide, zero
+//  past D); flags[B*H*F] mark them complete.  `init` is unused.
+hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
+                                       uint32_t* err, hipStream_t st);
 //  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states,
 //  kGdnFusedRowBlocks of the 8 used); only for B*H*kGdnFusedRowBlocks <= 128
 //  so that scan items never take more than a quarter of the device's slots.

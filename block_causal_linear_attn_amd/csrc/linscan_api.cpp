@@ -113,7 +113,7 @@ void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, 
 }
 
 struct ReluPlan {
-  bool mfma, fused;
+  bool mfma, fused, wide;
   int nc, chunk, nco, chunko;
   size_t partial_off, init_off, flags_off, bytes;
 };
@@ -122,6 +122,7 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   ReluPlan p;
   p.mfma = linscan::relu_has_mfma(s->D, s->dtype);
   p.fused = p.mfma;  // one launch: summary items then output items
+  p.wide = linscan::relu_wide_mfma(s->D, s->dtype);
   // summary: whole frames per item unless there are too few frames to fill
   // the chip (the fused launch always uses whole frames); each output item
   // sums the partials of its frame and all earlier ones, so fewer partials
@@ -132,11 +133,18 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   } else {
     plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
   }
-  plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
-  const size_t out = (size_t)s->D * s->D + s->D;
+  if (p.wide) {
+    // wide heads: every output item reads one 66 KB cumulative state, so
+    // chunks are longer to keep that read small next to the query tiles
+    plan_chunks(d.bhf, s->N, 1024, 768, 128, &p.nco, &p.chunko);
+  } else {
+    plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
+  }
+  // wide heads keep one cumulative record per frame, 128 dims wide, and no init copy
+  const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;
   p.partial_off = kHeaderBytes;
   p.init_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * out * sizeof(float), 256);
-  p.flags_off = align_up(p.init_off + (size_t)d.bh * out * sizeof(float), 256);
+  p.flags_off = align_up(p.init_off + (p.wide ? 0 : (size_t)d.bh * out * sizeof(float)), 256);
   p.bytes = align_up(p.flags_off + (p.fused ? (size_t)d.bhf * sizeof(uint64_t) : 0), 256);
   return p;
 }
@@ -401,6 +409,10 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
     uint64_t* flags = (uint64_t*)(ws + p.flags_off);
     uint32_t* err = (uint32_t*)ws;
     const uint64_t epoch = next_epoch();
+    if (p.wide)
+      return hip_check(
+          timed("relu_wide_fused", hs, [&] { return linscan::launch_relu_wide_fused_mfma(a, bhp, flags, epoch, err, hs); }),
+          "relu wide fused");
     return hip_check(timed("relu_fused", hs, [&] { return linscan::launch_relu_fused_mfma(a, bhp, flags, epoch, err, hs); }),
                      "relu fused");
   }

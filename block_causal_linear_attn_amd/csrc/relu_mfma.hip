@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
 }
 
 }  // namespace
-bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D == 64); }
+bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D == 64 || relu_wide_mfma(D, dtype)); }
 
 hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
                                     const float* S0, const float* z0, float* init, long bhf, int F,

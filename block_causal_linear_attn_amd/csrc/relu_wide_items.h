@@ -1,0 +1,375 @@
+// relu_wide_items.h -- bf16 MFMA work items of the ReLU block-causal
+// linear-attention scan for wide heads (head dims 112 and 128; SANA-Video's
+// linear attention: ReLU feature map, cumulative D x D state plus normaliser).
+//
+// At these widths a D x D partial per wave (the layout of the narrow items)
+// no longer fits in registers, so the work is split by rows of the state:
+// tensors are taken as 128 dims wide, the dims past the head dim being zero
+// (they add nothing to any sum), and wave w owns rows [32w, 32w + 32).
+//
+// Summary item, one per (head, frame): dS = V^T phi(K) over all of the
+// frame's tokens.  The workgroup stages 64-token K and V tiles in LDS (ring of
+// register sets in flight, rows unpadded with their 16-byte chunks swizzled
+// by token; phi applied to K when staged) and each lane gathers 8 tokens of
+// one dimension per MFMA operand with two LDS transpose reads.  dz = 1^T phi(K)
+// comes from a padding row (head dim 112: value dim 112 is set to 1, so row
+// 112 of dS is dz) or, at head dim 128, from one more MFMA with an all-ones
+// A operand.  The item then adds the
+// cumulative state of the previous frame (the initial state for frame 0) and
+// writes the cumulative state of its own frame: the frames of a head form a
+// chain of short hand-offs, and no later reader has to sum partials.
+//
+// Output item, one per (head, frame, token chunk): reads the one cumulative
+// state its frame sees (the last frame of its block), splits S into bf16 hi +
+// lo terms (16 significant bits) held as MFMA A operands, and contracts
+// 64-token query tiles staged in LDS.  The denominator z . phi(q) is formed
+// when a tile is staged: each thread holds 8 dims of a token, and 16 lanes
+// finish the sum with DPP row reductions.
+#pragma once
+
+#include "device_common.h"
+#include "sync.h"
+
+namespace linscan {
+
+constexpr int kReluWide = 128;                                   // padded head dim
+constexpr int kReluWideRec = kReluWide * kReluWide + kReluWide;  // floats per cumulative record
+constexpr int kReluWideDepth = 2;                                // tiles in flight per summary item
+constexpr int kReluWideSumLds = 2 * 2 * 64 * kReluWide * 2;      // K, V tiles, double buffered
+constexpr int kReluWideOutPitch = kReluWide + 8;
+// query tiles and output staging tiles (double buffered, bf16) + per-token denominators
+constexpr int kReluWideOutLds = 4 * 64 * kReluWideOutPitch * 2 + 2 * 64 * 4;
+
+// Sum over the 16 lanes of a DPP row (every lane of the row gets the sum).
+__device__ __forceinline__ float row16_sum(float x) {
+  auto step = [](float v, int ctrl) {
+    int s;
+    switch (ctrl) {  // the DPP control must be a constant
+      case 0: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false); break;   // lanes ^1
+      case 1: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false); break;   // lanes ^2
+      case 2: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); break;  // half-row mirror
+      default: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); break; // row mirror
+    }
+    return v + __int_as_float(s);
+  };
+  x = step(x, 0);  // pairs
+  x = step(x, 1);  // quads
+  x = step(x, 2);  // lane i + lane 7 - i within 8: both quads of the half-row
+  return step(x, 3);  // lane i + lane 15 - i: both half-rows
+}
+
+// Summary item of frame f of head bh: cum[bh][f] = cum[bh][f - 1] + (dS, dz),
+// with cum[bh][-1] the initial state (S0, z0; zero where NULL).  The last
+// frame's item also writes the final state to (S_out, z_out), which may alias
+// (S0, z0).  flags[bh * F + f] is published when cum[bh][f] is complete;
+// the item waits for flags[bh * F + f - 1] before reading the previous one.
+template <int DI>
+__device__ __forceinline__ void relu_wide_summary_item(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ cum,
+    const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f,
+    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw) {
+  constexpr int D = kReluWide;
+  constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
+  constexpr int TILE = 64;
+  constexpr int C = D / 8;                   // chunks per (padded) LDS row
+  constexpr int LPT = TILE * (D / 8) / 256;  // 16-byte loads per thread per tensor per tile (4)
+  typedef uint16_t TileT[2][TILE * D];
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][K, V][TILE * D]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = bh * F + f;
+  const uint16_t* kf = k + (size_t)bhf * N * DI;
+  const uint16_t* vf = v + (size_t)bhf * N * DI;
+
+  // z: with DI < 128, value dim DI (zero padding) is set to 1 for every live
+  // token, so row DI of dS is dz at no cost; at DI = 128 an MFMA with an
+  // all-ones A operand forms it (register 0 of accz holds z[32 wave + col])
+  constexpr bool ZROW = DI < D;
+  floatx16 acc[4], accz = {};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = floatx16{};
+  const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+
+  // Tile t sits in register set t % DEPTH from its fetch until it is staged.
+  // The loop runs a whole number of ring passes with no branch: tiles past
+  // the frame are staged as zeros and add nothing, fetches past the frame
+  // re-read its last tile, and dims past DI re-read a real chunk and are
+  // zeroed when staged.  (A load or stage under a condition would make the
+  // compiler wait for every load in flight at each stage.)
+  constexpr int DEPTH = kReluWideDepth;
+  struct Regs {
+    u32x4 k[LPT], v[LPT];
+  };
+  Regs R[DEPTH];
+  auto fetch = [&](Regs& X, int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const int n = t0 + tok;
+      const size_t off = (size_t)(n < N ? n : 0) * DI + (cb < CI ? cb : CI - 1) * 8;
+      X.k[r] = ld16_stream(kf + off);
+      X.v[r] = ld16_stream(vf + off);
+    }
+  };
+  auto stage = [&](const Regs& X, int buf, int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const bool live = t0 + tok < N && cb < CI;
+      u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
+      if (ZROW) vv[0] = t0 + tok < N && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
+      uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
+      uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
+      kd[0] = make_uint2(kk[0], kk[1]);
+      kd[1] = make_uint2(kk[2], kk[3]);
+      vd[0] = make_uint2(vv[0], vv[1]);
+      vd[1] = make_uint2(vv[2], vv[3]);
+    }
+  };
+  auto contract = [&](int buf) {
+    const uint16_t* kl = lds[buf][0];
+    const uint16_t* vl = lds[buf][1];
+#pragma unroll
+    for (int s = 0; s < TILE / 16; ++s) {
+      u32x4 kfrag[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32_swz<C>(kl, s * 16, J * 32, lane);
+      const u32x4 vfrag = gather_tokens_32_swz<C>(vl, s * 16, wave * 32, lane);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) acc[J] = mfma32x32x16(as_bf16x8(vfrag), as_bf16x8(kfrag[J]), acc[J]);
+      if (!ZROW) accz = mfma32x32x16(as_bf16x8(ones), as_bf16x8(kfrag[wave]), accz);
+    }
+  };
+
+  const int ntiles = (N + TILE - 1) / TILE;
+  if (ntiles > 0) {
+    const int tlast = (ntiles - 1) * TILE;
+    const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) fetch(R[d], min(d * TILE, tlast));
+    stage(R[0], 0, 0);
+    fetch(R[0], min(DEPTH * TILE, tlast));
+    __syncthreads();
+    for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int it = it0 + u;
+        contract(it & 1);
+        Regs& nxt = R[(u + 1) % DEPTH];  // holds tile it + 1
+        stage(nxt, (it + 1) & 1, (it + 1) * TILE);
+        fetch(nxt, min((it + 1 + DEPTH) * TILE, tlast));
+        __syncthreads();
+      }
+    }
+  }
+
+  // Add the previous cumulative state.  Lane (col, g), register r of acc[J]
+  // holds S[32 wave + 8 (r / 4) + 4 g + r % 4][32 J + col]; z[n] sits in row
+  // DI, column n (ZROW; the record keeps that row, and a copy of it as its z
+  // part) or in register 0 of accz at n = 32 wave + col.
+  auto row_of = [&](int r) { return wave * 32 + 8 * (r >> 2) + 4 * g + (r & 3); };
+  if (f > 0) {
+    wait_all(&flags[bhf - 1], 1, epoch, err);
+    const float* prv = cum + (size_t)(bhf - 1) * kReluWideRec;
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[J][r] += prv[row_of(r) * D + J * 32 + col];
+    if (!ZROW) accz[0] += prv[D * D + wave * 32 + col];
+  } else {
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(r), n = J * 32 + col;
+        if (S0 && m < DI && n < DI) acc[J][r] += S0[(size_t)bh * DI * DI + m * DI + n];
+        if (ZROW && z0 && m == DI && n < DI) acc[J][r] += z0[(size_t)bh * DI + n];
+      }
+    if (!ZROW && z0) accz[0] += z0[(size_t)bh * DI + wave * 32 + col];
+  }
+  float* cur = cum + (size_t)bhf * kReluWideRec;
+#pragma unroll
+  for (int J = 0; J < 4; ++J)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      cur[row_of(r) * D + J * 32 + col] = acc[J][r];
+      if (ZROW && row_of(r) == DI) cur[D * D + J * 32 + col] = acc[J][r];
+    }
+  if (!ZROW && g == 0) cur[D * D + wave * 32 + col] = accz[0];
+  if (f == F - 1) {
+    // every element of S_out / z_out is written by the lane that read the
+    // same element of S0 / z0 (frame 0 of this head is this item when F = 1)
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = row_of(r), n = J * 32 + col;
+        if (S_out && m < DI && n < DI) S_out[(size_t)bh * DI * DI + m * DI + n] = acc[J][r];
+        if (ZROW && z_out && m == DI && n < DI) z_out[(size_t)bh * DI + n] = acc[J][r];
+      }
+    if (!ZROW && z_out && g == 0) z_out[(size_t)bh * DI + wave * 32 + col] = accz[0];
+  }
+  publish(&flags[bhf], epoch);
+}
+
+// Output item `wg` = (frame of one head) * nco + token chunk:
+// o = S phi(q) / (z . phi(q) + eps) with (S, z) = cum[bh][fend - 1], fend the
+// end of the frame's block of bfr frames.  The caller has waited for that
+// record.
+template <int DI>
+__device__ __forceinline__ void relu_wide_output_item(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ cum, float eps,
+    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw) {
+  constexpr int D = kReluWide;
+  constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
+  constexpr int TILE = 64;
+  constexpr int ROW = kReluWideOutPitch;     // 272-byte pitch: 16-byte fragment reads spread over all banks
+  constexpr int LPT = TILE * (D / 8) / 256;  // 4
+  typedef uint16_t TileT[TILE * ROW];
+  TileT* lds = reinterpret_cast<TileT*>(lds_raw);                       // [buffer] phi(q) tiles
+  TileT* ost = reinterpret_cast<TileT*>(lds_raw + 2 * TILE * ROW * 2);  // [buffer] output tiles
+  float(*den)[TILE] = reinterpret_cast<float(*)[TILE]>(lds_raw + 4 * TILE * ROW * 2);  // [buffer][token]
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = wg / nco;
+  const long bh = bhf / F;
+  const int f = (int)(bhf % F);
+  const int fend = min(F, (f / bfr + 1) * bfr);
+  const int n0 = (int)(wg % nco) * chunk;
+  const int n1 = min(N, n0 + chunk);
+  if (n0 >= n1) return;
+
+  // A operands: S[32 wave + col][16 s + 8 g + e] as bf16 hi and lo terms
+  const float* rec = cum + ((size_t)bh * F + fend - 1) * kReluWideRec;
+  u32x4 ahi[8], alo[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float* src = rec + (wave * 32 + col) * D + s * 16 + g * 8;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+    const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+    ahi[s] = u32x4{p0.x, p1.x, p2.x, p3.x};
+    alo[s] = u32x4{p0.y, p1.y, p2.y, p3.y};
+  }
+  // the 8 normaliser entries of the dims this thread stages (chunk tid % 16)
+  float zr[8];
+  {
+    const float4 z0 = *reinterpret_cast<const float4*>(rec + D * D + (tid & 15) * 8);
+    const float4 z1 = *reinterpret_cast<const float4*>(rec + D * D + (tid & 15) * 8 + 4);
+    zr[0] = z0.x, zr[1] = z0.y, zr[2] = z0.z, zr[3] = z0.w;
+    zr[4] = z1.x, zr[5] = z1.y, zr[6] = z1.z, zr[7] = z1.w;
+  }
+
+  const uint16_t* qf = q + (size_t)bhf * N * DI;
+  uint16_t* of = o + (size_t)bhf * N * DI;
+  struct Regs {
+    u32x4 q[LPT];
+  };
+  auto fetch = [&](Regs& X, int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const int n = t0 + tok;
+      // rows past the chunk re-read its first token: their outputs are never
+      // stored; dims past DI re-read a real chunk and are zeroed when staged
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8);
+    }
+  };
+  // phi(q) into LDS buffer buf, and each token's denominator into den[buf]
+  auto stage = [&](const Regs& X, int buf) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      u32x4 w = cb < CI ? X.q[r] : u32x4{0u, 0u, 0u, 0u};
+      float d = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[e] = relu_bf16x2(w[e]);
+        d = fmaf(zr[2 * e], bf16lo_to_f32(w[e]), d);
+        d = fmaf(zr[2 * e + 1], bf16hi_to_f32(w[e]), d);
+      }
+      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = w;
+      d = row16_sum(d);  // the 16 lanes of a DPP row hold the 16 chunks of this token
+      if (cb == 0) den[buf][tok] = d;
+    }
+  };
+
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+  const int nfull = (n1 - n0) / TILE;
+  const int tlast = n0 + (ntiles - 1) * TILE;
+  Regs R0, R1;
+  fetch(R0, n0);
+  fetch(R1, min(n0 + TILE, tlast));
+  stage(R0, 0);
+  fetch(R0, min(n0 + 2 * TILE, tlast));
+  __syncthreads();
+  // a tile's outputs leave as whole rows (16-byte chunks, consecutive lanes on
+  // consecutive bytes) from its staging buffer
+  auto drain = [&](int it, const bool full) {
+    const int t0 = n0 + it * TILE;
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
+      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * DI + cb * 8, w);
+    }
+  };
+  // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3
+  auto tile = [&](int it, Regs& nxt, const bool full) {
+    const int buf = it & 1;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      floatx16 acc = {};
+      const uint16_t* qrow = &lds[buf][(half * 32 + col) * ROW + g * 8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(qrow + s * 16);
+        acc = mfma32x32x16(as_bf16x8(ahi[s]), as_bf16x8(b), acc);
+        acc = mfma32x32x16(as_bf16x8(alo[s]), as_bf16x8(b), acc);
+      }
+      const float inv = 1.0f / (den[buf][half * 32 + col] + eps);
+      // lane (col, g) of wave w holds token half*32 + col, dims 32 w + 8 q4 + 4 g + 0..3
+      uint16_t* srow = &ost[buf][(half * 32 + col) * ROW + wave * 32 + 4 * g];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[4 * q4 + 0] * inv, acc[4 * q4 + 1] * inv);
+        w.y = pack_bf16x2(acc[4 * q4 + 2] * inv, acc[4 * q4 + 3] * inv);
+        *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
+      }
+    }
+    stage(nxt, buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
+    fetch(nxt, min(n0 + (it + 3) * TILE, tlast));
+    __syncthreads();
+    drain(it, full);
+  };
+  // Full tiles run in pairs with no branch in the loop body; a last,
+  // partial tile stores under a token check after the loop.
+  int it = 0;
+  for (; it + 2 <= nfull; it += 2) {
+    tile(it, R1, true);
+    tile(it + 1, R0, true);
+  }
+  // R1 holds tile it + 1: at most one more full tile, then at most one partial one
+  if (it < nfull) {
+    tile(it, R1, true);
+    if (it + 1 < ntiles) tile(it + 1, R0, false);
+  } else if (it < ntiles) {
+    tile(it, R1, false);
+  }
+}
+
+}  // namespace linscan

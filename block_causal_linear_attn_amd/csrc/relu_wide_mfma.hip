@@ -1,0 +1,86 @@
+// relu_wide_mfma.hip -- the single-launch bf16 MFMA ReLU linear-attention scan
+// for wide heads (head dims 112 and 128), built from relu_wide_items.h.
+//
+// Block ids run over steps j = 0, 1, ...: step j holds the summary item of
+// frame j of every head and then the output items of frame j - lag (one per
+// head and token chunk).  A summary item waits for the previous frame's
+// summary of its head (one step earlier); an output item waits for the
+// summary of the last frame of its block (lag >= block_frames puts it at an
+// earlier step).  Every item waited on has a lower block id, and block ids
+// dispatch in order, so it is running or done and every wait ends.  Within a
+// step, items are head-minor with B*H padded to a multiple of 8, so all items
+// of a head share one XCD and hand off through its L2; padding items leave at
+// once.
+#include "relu_wide_items.h"
+#include "kernels.h"
+
+#include <type_traits>
+
+namespace linscan {
+
+namespace {
+
+constexpr int kReluWideLds = kReluWideSumLds > kReluWideOutLds ? kReluWideSumLds : kReluWideOutLds;
+
+template <int DI>
+__global__ __launch_bounds__(256, 2) void relu_wide_fused_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ cum, const float* S0, const float* z0, float* S_out,
+    float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr, int nco, int chunko, int lag,
+    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err) {
+  __shared__ __align__(16) uint8_t lds[kReluWideLds];
+  const long b = blockIdx.x;
+  const long bh = b % bhp;
+  const long u = b / bhp;  // unit: one item per head
+  if (bh >= bh_n) return;
+  const long head_units = lag, mid_units = (long)(F - lag) * (1 + nco);
+  bool summary;
+  int f, c = 0;
+  if (u < head_units) {
+    summary = true;
+    f = (int)u;
+  } else if (u < head_units + mid_units) {
+    const long j = lag + (u - head_units) / (1 + nco), r = (u - head_units) % (1 + nco);
+    summary = r == 0;
+    f = summary ? (int)j : (int)(j - lag);
+    c = summary ? 0 : (int)(r - 1);
+  } else {
+    const long r = u - head_units - mid_units;
+    summary = false;
+    f = F - lag + (int)(r / nco);
+    c = (int)(r % nco);
+  }
+  if (summary) {
+    relu_wide_summary_item<DI>(k, v, cum, S0, z0, S_out, z_out, F, N, bh, f, flags, epoch, err, lds);
+    return;
+  }
+  const int fend = min(F, (f / bfr + 1) * bfr);
+  wait_all(&flags[bh * F + fend - 1], 1, epoch, err);
+  relu_wide_output_item<DI>(q, o, cum, eps, F, N, bfr, nco, chunko, (bh * F + f) * nco + c, lds);
+}
+
+template <typename Body>
+hipError_t with_wide_dim(int D, Body body) {
+  if (D == 128) return body(std::integral_constant<int, 128>{});
+  if (D == 112) return body(std::integral_constant<int, 112>{});
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool relu_wide_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 112 || D == 128); }
+
+hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
+                                       uint32_t* err, hipStream_t st) {
+  return with_wide_dim(a.D, [&](auto di) {
+    constexpr int DI = decltype(di)::value;
+    const long grid = (long)a.F * bhp * (1 + a.nco);
+    const int lag = fused_lag(device_slots((const void*)relu_wide_fused_mfma<DI>), bhp * (1 + a.nco), a.bfr, a.F);
+    hipLaunchKernelGGL(relu_wide_fused_mfma<DI>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.S0, a.z0, a.S_out,
+                       a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace linscan

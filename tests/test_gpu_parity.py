@@ -61,7 +61,11 @@ RELU_CASES = [
     (1, 3, 5, 333, 32, "bf16", 1, True),        # MFMA path, ragged token count
     (2, 2, 3, 700, 32, "bf16", 1, False),       # several token chunks per frame
     (1, 2, 4, 200, 64, "bf16", 1, True),        # MFMA path, D = 64
-    (1, 2, 3, 97, 112, "bf16", 1, True),        # generic bf16 path at the pages' head dim
+    (1, 2, 3, 97, 112, "bf16", 1, True),        # wide MFMA path at the pages' head dim (128 dims, zero-padded)
+    (1, 2, 4, 2000, 112, "bf16", 1, False),     # wide path, two output chunks per frame, ragged tail
+    (2, 10, 3, 200, 112, "bf16", 2, True),      # wide path, B*H = 20 (padding items), blocks of 2 frames
+    (1, 2, 1, 1, 112, "bf16", 1, True),         # wide path, single token, single frame
+    (1, 2, 5, 300, 128, "bf16", 3, True),       # wide path at D = 128 (normaliser by MFMA), ragged block
     (1, 2, 3, 50, 16, "bf16", 1, False),        # generic bf16, D = 16
     (1, 2, 7, 40, 32, "bf16", 3, True),         # blocks of 3 frames (ragged last block)
     (1, 2, 3, 70, 48, "fp32", 2, True),         # generic fp32
@@ -206,6 +210,24 @@ def test_in_place_state_and_poisoned_outputs(ls, gen, oracle_mod):
     check("gdn in-place S", G, rS, 1e-2)
 
 
+@pytest.mark.parametrize("F,D", [(1, 112), (3, 112), (1, 128)])
+def test_relu_wide_in_place_state(ls, gen, oracle_mod, F, D):
+    """Wide heads: state_out == state_in, also when one work item reads and writes it (F = 1)."""
+    x = gen.relu_inputs(1, 2, F, 150, D, "bf16", seed=28)
+    S0, z0 = _rand_state(1, 2, D, 9, norm=True)
+    xd = _dev(x)
+    S = S0.to(DEV).clone()
+    z = z0.to(DEV).clone()
+    o = torch.full_like(xd["q"], float("nan"))
+    ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], S, z, out=o, state_out=S, norm_out=z)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], S0, z0)
+    assert torch.isfinite(o).all()
+    check("relu wide in-place o", o, ro, 2e-2)
+    check("relu wide in-place S", S, rS, 1e-2)
+    check("relu wide in-place z", z, rz, 1e-2)
+
+
 def test_deterministic(ls, gen):
     x = _dev(gen.relu_inputs(1, 4, 4, 1000, 32, "bf16", seed=23))
     a = ls.ls_relu_block_forward(x["q"], x["k"], x["v"])
@@ -271,13 +293,17 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
 
 
 # --------------------------------------------------------------------------- single-launch paths
-@pytest.mark.parametrize("op", ["relu", "gdn", "gdn_phased"])
+@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased"])
 def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     """The one-launch paths hand data between work items through flags with
     bounded waits; the workspace's fault word must stay zero and results match."""
     if op == "relu":
         x = gen.relu_inputs(1, 11, 9, 777, 32, "bf16", seed=31)   # B*H not a multiple of 8
         shp = ls.ls_shape(1, 11, 9, 777, 32, 1)
+        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
+    elif op == "relu_wide":  # head dim 112: chained cumulative states
+        x = gen.relu_inputs(1, 11, 9, 777, 112, "bf16", seed=34)
+        shp = ls.ls_shape(1, 11, 9, 777, 112, 1)
         need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
     elif op == "gdn":
         x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=32)
@@ -290,13 +316,13 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     xd = _dev(x)
     for rep in range(3):  # reuse of a workspace across calls (fresh epochs)
-        if op == "relu":
+        if op.startswith("relu"):
             o, S, z = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], block_frames=2, ws=ws)
         else:
             o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], ws=ws)
         torch.cuda.synchronize()
         assert int(ws[:4].view(torch.int32).item()) == 0
-    if op == "relu":
+    if op.startswith("relu"):
         ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], block_frames=2)
         check("single-launch relu o", o, ro, 2e-2)
         check("single-launch relu S", S, rS, 1e-2)
