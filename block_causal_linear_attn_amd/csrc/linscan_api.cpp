@@ -133,13 +133,7 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   } else {
     plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
   }
-  if (p.wide) {
-    // wide heads: every output item reads one 66 KB cumulative state, so
-    // chunks are longer to keep that read small next to the query tiles
-    plan_chunks(d.bhf, s->N, 1024, 768, 128, &p.nco, &p.chunko);
-  } else {
-    plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
-  }
+  plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
   // wide heads keep one cumulative record per frame, 128 dims wide, and no init copy
   const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;
   p.partial_off = kHeaderBytes;
