@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads per part in the oracle sample (default: 2 per oracle thread for "
                          "the ReLU part, all for the GDN part)")
+    ap.add_argument("--no-head-dim-112", action="store_true",
+                    help="skip the side measurement of both workloads at head dim 112")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -217,6 +219,7 @@ def main():
                     "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note}
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
+    d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -257,10 +260,58 @@ def main():
                                     round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "side": {"sana_wm_chunk_step": chunk_step},
+        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_head_dim_112(torch, ls, inputs, reps=3):
+    """Both parts of the step at head dim 112 (not part of the step).
+
+    The ReLU rollout (B1 H20 D112 N3600, 25 calls with state carry) and the
+    GDN call (B1 H28 D112 N920 F181), each timed over `reps` passes after one
+    warm-up pass; tokens/s and the HBM fraction of the token tensors' bytes.
+    """
+    dev = torch.device("cuda:0")
+    res = {}
+    wv = inputs.WORKLOADS["sana_video_720p_minute_d112"]
+    calls = [inputs.workload_call_inputs(wv, i, device=dev) for i in range(len(wv.calls))]
+    outs = [torch.empty_like(c["q"]) for c in calls]
+    cache = torch.zeros((wv.B, wv.H, wv.D, wv.D), device=dev)
+    ncache = torch.zeros((wv.B, wv.H, wv.D), device=dev)
+    S_blk, z_blk = torch.empty_like(cache), torch.empty_like(ncache)
+
+    def video():
+        for i, c in enumerate(calls):
+            ls.ls_relu_block_forward(c["q"], c["k"], c["v"], None if i == 0 else cache,
+                                     None if i == 0 else ncache, out=outs[i], state_out=S_blk, norm_out=z_blk)
+            ls.ls_state_carry(S_blk, cache, z_blk, ncache)
+
+    wg = inputs.WORKLOADS["sana_wm_720p_60s_d112"]
+    g = inputs.workload_call_inputs(wg, 0, device=dev)
+    g_out = torch.empty_like(g["q"])
+    g_state = torch.empty((wg.B, wg.H, wg.D, wg.D), device=dev)
+
+    def wm():
+        ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], None, out=g_out, state_out=g_state)
+
+    for name, w, fn in (("sana_video_720p_minute_d112", wv, video), ("sana_wm_720p_60s_d112", wg, wm)):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        tokens = w.B * w.F * w.N
+        nbytes = 4 * w.B * w.H * w.F * w.N * w.D * 2
+        res[name] = {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+                     "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "workload": w.note}
+    del calls, outs, g, g_out
+    return res
 
 
 def time_chunk_step(torch, ls, inputs):

@@ -79,6 +79,15 @@ WORKLOADS = {
     "sana_wm_720p_60s": Workload("sana_wm_720p_60s", "gdn", 1, 24, 181, 920, 128, "bf16", 3,
                                  alpha_mu=3.0, l2_keys=True,
                                  note="B1 H24 D128 F181 N920 bf16, L2-normalised keys"),
+    # the same two workloads at the pages' linear-attention head dim, 112, with
+    # the hidden size kept (SANA-Video 20 x 112 = 2240) or the token bytes
+    # kept within 2% (SANA-WM 28 x 112 = 3136 against 24 x 128 = 3072)
+    "sana_video_720p_minute_d112": Workload("sana_video_720p_minute_d112", "relu", 1, 20, 241, 3600, 112,
+                                            "bf16", 2, call_frames=10,
+                                            note="B1 H20 D112 N3600, 241 frames as 24x10 + 1 calls"),
+    "sana_wm_720p_60s_d112": Workload("sana_wm_720p_60s_d112", "gdn", 1, 28, 181, 920, 112, "bf16", 3,
+                                      alpha_mu=3.0, l2_keys=True,
+                                      note="B1 H28 D112 F181 N920 bf16, L2-normalised keys"),
     # SANA-WM chunk-causal inference: 50 single-frame calls re-reading one carried state
     "sana_wm_chunk_step": Workload("sana_wm_chunk_step", "gdn", 4, 24, 1, 920, 128, "bf16", 4,
                                    alpha_mu=3.0, l2_keys=True, steps=50, prefix_frames=60,

@@ -78,6 +78,42 @@ def test_sana_video_720p_minute_rollout(ls, gen, oracle_mod):
     check("720p-minute relu z", _heads(ncache, hs), rz, 1e-2)
 
 
+def test_sana_video_720p_minute_rollout_d112(ls, gen, oracle_mod):
+    """The rollout at head dim 112 (wide MFMA path), one sampled head over all 241 frames."""
+    w = gen.WORKLOADS["sana_video_720p_minute_d112"]
+    hs = [13]
+    cache = torch.zeros((w.B, w.H, w.D, w.D), device=DEV)
+    ncache = torch.zeros((w.B, w.H, w.D), device=DEV)
+    S_blk = torch.empty_like(cache)
+    z_blk = torch.empty_like(ncache)
+    qs, ks, vs, os_ = [], [], [], []
+    for call in range(len(w.calls)):
+        x = gen.workload_call_inputs(w, call, device=DEV)
+        o, _, _ = ls.ls_relu_block_forward(x["q"], x["k"], x["v"], cache, ncache,
+                                           state_out=S_blk, norm_out=z_blk)
+        ls.ls_state_carry(S_blk, cache, z_blk, ncache)
+        for lst, t in ((qs, x["q"]), (ks, x["k"]), (vs, x["v"]), (os_, o)):
+            lst.append(_heads(t, hs))
+        del x, o
+    torch.cuda.synchronize()
+    q, k, v, o = (torch.cat(l, dim=2) for l in (qs, ks, vs, os_))
+    ro, rS, rz = oracle_mod.relu_block(q, k, v)
+    check("720p-minute D112 relu o (1 head, 241 frames)", o, ro, 2e-2)
+    check("720p-minute D112 relu S", _heads(cache, hs), rS, 1e-2)
+    check("720p-minute D112 relu z", _heads(ncache, hs), rz, 1e-2)
+
+
+def test_sana_wm_720p_60s_d112(ls, gen, oracle_mod):
+    w = gen.WORKLOADS["sana_wm_720p_60s_d112"]
+    x = gen.workload_call_inputs(w, 0, device=DEV)
+    o, S = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    torch.cuda.synchronize()
+    hs = [0, 27]
+    ro, rS = oracle_mod.gdn_frame(*(_heads(x[n], hs) for n in ("q", "k", "v", "alpha", "beta")))
+    check("wm-60s D112 gdn o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
+    check("wm-60s D112 gdn S", _heads(S, hs), rS, 1e-2)
+
+
 def test_sana_wm_720p_60s(ls, gen, oracle_mod):
     w = gen.WORKLOADS["sana_wm_720p_60s"]
     x = gen.workload_call_inputs(w, 0, device=DEV)
