@@ -51,6 +51,8 @@ def _load():
     lib.oracle_relu_block.restype = i
     lib.oracle_gdn_frame.argtypes = [i, i, i, i, i, d, P, P, P, P, P, P, P, P, i]
     lib.oracle_gdn_frame.restype = i
+    lib.oracle_gdn_frame_token_gate.argtypes = [i, i, i, i, i, d, P, P, P, P, P, P, P, P, i]
+    lib.oracle_gdn_frame_token_gate.restype = i
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -128,4 +130,28 @@ def gdn_frame(q, k, v, alpha, beta, state=None, key_scale=None, with_output: boo
                                   _ptr(S0), _ptr(o), _ptr(S), int(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_gdn_frame failed with code %d" % rc)
+    return o, S
+
+
+def gdn_frame_token_gate(q, k, v, alpha, beta, state=None, key_scale=None, with_output: bool = True,
+                         nthreads: int = 0):
+    """Frame-wise Gated DeltaNet with a per-token update gate, fp64.
+
+    As gdn_frame, but beta is [B, H, F, N]: token n's gate weights its terms
+    of the frame's G and U (the transition is S <- alpha S (I - G) + U).
+    """
+    k = _f32(k)
+    B, H, F, N, D = k.shape
+    v = _f32(v, k.shape)
+    q = _f32(q, k.shape) if with_output else None
+    a = _f32(alpha, (B, H, F))
+    b = _f32(beta, (B, H, F, N))
+    S0 = _f64(state, (B, H, D, D))
+    o = np.empty((B, H, F, N, D), np.float64) if with_output else None
+    S = np.empty((B, H, D, D), np.float64)
+    c = -1.0 if key_scale is None else float(key_scale)
+    rc = _load().oracle_gdn_frame_token_gate(B, H, F, N, D, c, _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                             _ptr(S0), _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_frame_token_gate failed with code %d" % rc)
     return o, S

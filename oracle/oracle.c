@@ -225,3 +225,85 @@ int oracle_gdn_frame(int B, int H, int F, int N, int D, double key_scale,
   }
   return status;
 }
+
+/*
+ * Frame-wise Gated DeltaNet with a per-token update gate.  The SANA-WM
+ * summary (paperlayer.ai), section 3 Method, item "Hybrid GDN/Softmax
+ * Attention", names a decay and a per-token update gate; with one update per
+ * frame the gate of token n weights that token's contribution:
+ *   G = sum_n beta_n (c k_n)(c k_n)^T,  U = sum_n beta_n v_n (c k_n)^T
+ *   S <- alpha_f S (I - G) + U ;  o_n = S q_n for the frame's tokens.
+ * With beta_n equal to beta_f for every token this is oracle_gdn_frame.
+ * alpha: [B][H][F]; beta: [B][H][F][N] float32.  Other arguments as there.
+ */
+int oracle_gdn_frame_token_gate(int B, int H, int F, int N, int D, double key_scale,
+                                const float* q, const float* k, const float* v,
+                                const float* alpha, const float* beta, const double* S0,
+                                double* o, double* S_out, int nthreads) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1) return ORACLE_BAD_ARG;
+  if (!k || !v || !alpha || !beta || (o && !q)) return ORACLE_BAD_ARG;
+  const double c = key_scale > 0.0 ? key_scale : 1.0 / sqrt((double)D * (double)N);
+  int status = ORACLE_OK;
+  long heads = (long)B * H;
+  size_t DD = (size_t)D * D;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (long bh = 0; bh < heads; ++bh) {
+    double* S = (double*)calloc(DD, sizeof(double));
+    double* G = (double*)malloc(DD * sizeof(double));
+    double* U = (double*)malloc(DD * sizeof(double));
+    double* T = (double*)malloc(DD * sizeof(double));
+    double* kt = (double*)malloc((size_t)D * sizeof(double));
+    if (!S || !G || !U || !T || !kt) {
+      status = ORACLE_NO_MEMORY;
+      free(S); free(G); free(U); free(T); free(kt);
+      continue;
+    }
+    if (S0) memcpy(S, S0 + (size_t)bh * DD, DD * sizeof(double));
+
+    for (int f = 0; f < F; ++f) {
+      const double a = (double)alpha[(size_t)bh * F + f];
+      /* 1. gate-weighted Gram and value-key matrices of the frame, keys scaled by c */
+      memset(G, 0, DD * sizeof(double));
+      memset(U, 0, DD * sizeof(double));
+      for (int n = 0; n < N; ++n) {
+        const double bn = (double)beta[((size_t)bh * F + f) * N + n];
+        const float* kn = k + tok(bh, f, n, F, N, D);
+        const float* vn = v + tok(bh, f, n, F, N, D);
+        for (int j = 0; j < D; ++j) kt[j] = c * (double)kn[j];
+        for (int i = 0; i < D; ++i) {
+          for (int j = 0; j < D; ++j) {
+            G[(size_t)i * D + j] += bn * kt[i] * kt[j];
+            U[(size_t)i * D + j] += bn * (double)vn[i] * kt[j];
+          }
+        }
+      }
+      /* 2. transition: S <- alpha (S - S G) + U */
+      for (int i = 0; i < D; ++i) {
+        for (int j = 0; j < D; ++j) {
+          double acc = 0.0;
+          for (int l = 0; l < D; ++l) acc += S[(size_t)i * D + l] * G[(size_t)l * D + j];
+          T[(size_t)i * D + j] = S[(size_t)i * D + j] - acc;
+        }
+      }
+      for (size_t e = 0; e < DD; ++e) S[e] = a * T[e] + U[e];
+      /* 3. the frame's queries read the updated state */
+      if (o) {
+        for (int n = 0; n < N; ++n) {
+          const float* qn = q + tok(bh, f, n, F, N, D);
+          double* on = o + tok(bh, f, n, F, N, D);
+          for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < D; ++j) acc += S[(size_t)i * D + j] * (double)qn[j];
+            on[i] = acc;
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * DD, S, DD * sizeof(double));
+    free(S); free(G); free(U); free(T); free(kt);
+  }
+  return status;
+}
