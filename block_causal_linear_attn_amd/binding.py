@@ -53,6 +53,8 @@ def _load():
     lib.ls_gdn_frame_workspace_size.restype = Z
     lib.ls_gdn_frame_forward.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward.restype = I
+    lib.ls_gdn_frame_forward_token_gate.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_gdn_frame_forward_token_gate.restype = I
     lib.ls_state_carry.argtypes = [I, I, I, P, P, P, P, I, P]
     lib.ls_state_carry.restype = I
     lib.ls_status_string.argtypes = [I]
@@ -71,7 +73,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
-           "ls_gdn_frame_forward", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate", "ls_state_carry", "ls_status_string", "ls_last_error",
            "ls_version", "ls_profile_begin", "ls_profile_end")
 
 
@@ -189,6 +191,34 @@ def ls_gdn_frame_forward(q, k, v, alpha, beta, state=None, key_scale=None, out=N
     _check(lib.ls_gdn_frame_forward(ctypes.byref(shp), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                     _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
                                     _stream(dev)))
+    return o, so
+
+
+def ls_gdn_frame_forward_token_gate(q, k, v, alpha, beta, state=None, key_scale=None, out=None,
+                                    state_out=None, ws=None):
+    """Frame-wise Gated DeltaNet with per-token update gates; returns (o, state_out).
+
+    alpha: [B, H, F] fp32; beta: [B, H, F, N] fp32 (one gate per token).
+    """
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F, N), dev)
+    _f32("state", state, (B, H, D, D), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    shp = _shape(q)
+    need = lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    w = ws if ws is not None else workspace(need, dev)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward_token_gate(ctypes.byref(shp), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                               _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
+                                               _stream(dev)))
     return o, so
 
 

@@ -66,6 +66,19 @@ __device__ __forceinline__ uint2 split_bf16x2(float x0, float x1) {
   return make_uint2(hi, pack_bf16x2(x0 - bf16lo_to_f32(hi), x1 - bf16hi_to_f32(hi)));
 }
 
+// The 8 bf16 values of an MFMA operand fragment (element e in half e % 2 of
+// word e / 2) times 8 fp32 factors, as bf16 hi + lo terms (16 significant
+// bits), so that MFMAs on hi and on lo together take products with the
+// scaled values to about fp32 accuracy.
+__device__ __forceinline__ void scale_split_bf16x8(u32x4 w, float4 s0, float4 s1, u32x4& hi, u32x4& lo) {
+  const uint2 p0 = split_bf16x2(bf16lo_to_f32(w[0]) * s0.x, bf16hi_to_f32(w[0]) * s0.y);
+  const uint2 p1 = split_bf16x2(bf16lo_to_f32(w[1]) * s0.z, bf16hi_to_f32(w[1]) * s0.w);
+  const uint2 p2 = split_bf16x2(bf16lo_to_f32(w[2]) * s1.x, bf16hi_to_f32(w[2]) * s1.y);
+  const uint2 p3 = split_bf16x2(bf16lo_to_f32(w[3]) * s1.z, bf16hi_to_f32(w[3]) * s1.w);
+  hi = u32x4{p0.x, p1.x, p2.x, p3.x};
+  lo = u32x4{p0.y, p1.y, p2.y, p3.y};
+}
+
 // ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
 // lanes, output lane i, element r is 16-bit element (i % 4) of the 8 bytes
 // addressed by lane 4r + i/4 of the same group.  So if lane j of a group

@@ -29,12 +29,25 @@ constexpr size_t kRecBytes = 8 * (size_t)GD * GD;
 
 constexpr int kGramLds = 2 * 2 * 64 * GD * 2;
 constexpr int kGramDepth = 2;  // tiles in flight per gram item
+// per-token gates of the two staged tiles, after the tiles (gated items only)
+constexpr int kGateLds = 2 * 64 * 4;
 
 // Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
 // (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.  DI is the head dim
 // of the tensors (112 or 128); the items work on 128 dims, the dims past DI
 // being zero.
-template <int DI = GD>
+//
+// TG (per-token update gate): `beta` holds one gate per token, [B*H*F][N],
+// and token n's terms of G and U carry its gate: G = sum_n b_n k_n k_n^T,
+// U = sum_n b_n v_n k_n^T (times c^2 and c).  The gates of a tile go to LDS
+// with it, and each MFMA's A operands (this wave's key and value fragments,
+// 8 tokens per lane) are scaled by their tokens' gates and split into bf16
+// hi + lo terms, each contracted against the exact B operand: twice the
+// MFMAs, products to ~2^-17.  (Rounding the scaled operand to bf16 alone
+// leaves errors of 2^-9 of single products, which outputs that cancel, such
+// as a query nearly orthogonal to the keys, turn into large relative errors.)
+// The record then carries no further gate factor.
+template <int DI = GD, bool TG = false>
 __device__ __forceinline__ void gdn_gram_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw) {
@@ -46,6 +59,7 @@ __device__ __forceinline__ void gdn_gram_item(
   constexpr int LPT = TILE * (D / 8) / 256;  // 16-byte loads per thread per tensor per tile (4)
   typedef uint16_t TileT[2][TILE * ROW];
   TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [buffer][K, V][TILE * ROW]
+  float(*gl)[TILE] = reinterpret_cast<float(*)[TILE]>(lds_raw + kGramLds);  // [buffer][token] gates (TG)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -55,6 +69,7 @@ __device__ __forceinline__ void gdn_gram_item(
   const int n1 = min(N, n0 + chunk);
   const uint16_t* kf = k + (size_t)bhf * N * DI;
   const uint16_t* vf = v + (size_t)bhf * N * DI;
+  const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
 
   floatx16 accG[4], accU[4];
 #pragma unroll
@@ -73,6 +88,7 @@ __device__ __forceinline__ void gdn_gram_item(
   constexpr int DEPTH = kGramDepth;
   struct Regs {
     u32x4 k[LPT], v[LPT];
+    float b;  // gate of token tid % 64 of the tile (TG)
   };
   Regs R[DEPTH];
   auto fetch = [&](Regs& X, int t0) {
@@ -85,6 +101,7 @@ __device__ __forceinline__ void gdn_gram_item(
       X.k[r] = ld16_stream(kf + off);
       X.v[r] = ld16_stream(vf + off);
     }
+    if (TG) X.b = gf[t0 + (tid & 63) < n1 ? t0 + (tid & 63) : n0];
   };
   auto stage = [&](const Regs& X, int buf, int t0) {
 #pragma unroll
@@ -101,6 +118,7 @@ __device__ __forceinline__ void gdn_gram_item(
       vd[0] = make_uint2(vv[0], vv[1]);
       vd[1] = make_uint2(vv[2], vv[3]);
     }
+    if (TG && tid < TILE) gl[buf][tid] = X.b;
   };
   auto contract = [&](int buf) {
     const uint16_t* kl = lds[buf][0];
@@ -111,6 +129,21 @@ __device__ __forceinline__ void gdn_gram_item(
 #pragma unroll
       for (int J = 0; J < 4; ++J) kfrag[J] = gather_tokens_32_swz<C>(kl, s * 16, J * 32, lane);
       const u32x4 vfrag = gather_tokens_32_swz<C>(vl, s * 16, wave * 32, lane);
+      if (TG) {  // gates of this lane's tokens s*16 + 8g + 0..7
+        const float4* gb = reinterpret_cast<const float4*>(&gl[buf][s * 16 + 8 * g]);
+        const float4 g0 = gb[0], g1 = gb[1];
+        u32x4 kh, kl2, vh, vl2;
+        scale_split_bf16x8(kfrag[wave], g0, g1, kh, kl2);
+        scale_split_bf16x8(vfrag, g0, g1, vh, vl2);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          accG[J] = mfma32x32x16(as_bf16x8(kh), as_bf16x8(kfrag[J]), accG[J]);
+          accG[J] = mfma32x32x16(as_bf16x8(kl2), as_bf16x8(kfrag[J]), accG[J]);
+          accU[J] = mfma32x32x16(as_bf16x8(vh), as_bf16x8(kfrag[J]), accU[J]);
+          accU[J] = mfma32x32x16(as_bf16x8(vl2), as_bf16x8(kfrag[J]), accU[J]);
+        }
+        continue;
+      }
 #pragma unroll
       for (int J = 0; J < 4; ++J) {
         accG[J] = mfma32x32x16(as_bf16x8(kfrag[wave]), as_bf16x8(kfrag[J]), accG[J]);
@@ -145,7 +178,7 @@ __device__ __forceinline__ void gdn_gram_item(
   // then beta*U in fp32 with each group of four rows interleaved, element
   // (m, n) at ((m / 4) * D + n) * 4 + m % 4, so that the four rows a scan lane
   // owns in one column are one 16-byte load
-  const float bf = beta[bhf];
+  const float bf = TG ? 1.0f : beta[bhf];
   const float gs = c2 * bf, us = c * bf;
   uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)wg * kRecBytes);
   uint16_t* Glo = Ghi + D * D;
@@ -181,9 +214,12 @@ __device__ __forceinline__ void gdn_gram_item(
 // their XCD's L2.
 constexpr int kGramRowsKRow = GD, kGramRowsVRow = 32;  // unpadded; K chunks swizzled by token
 constexpr int kGramRowsDepth = 4;  // tiles in flight per workgroup
-constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;
+constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;  // (+ kGateLds with TG)
 
-template <int DI = GD>
+// TG: per-token gates as in gdn_gram_item (the A operands, key and value
+// fragments, scaled and split into hi + lo before each MFMA pair; gates in
+// LDS after the tiles).
+template <int DI = GD, bool TG = false>
 __device__ __forceinline__ void gdn_gram_rows_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw) {
@@ -196,6 +232,7 @@ __device__ __forceinline__ void gdn_gram_rows_item(
                      reinterpret_cast<uint16_t*>(lds_raw) + TILE * KROW};
   uint16_t* vl[2] = {reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW,
                      reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW + TILE * VROW};
+  float(*gl)[TILE] = reinterpret_cast<float(*)[TILE]>(lds_raw + kGramRowsLds);  // [buffer][token] gates (TG)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -205,10 +242,12 @@ __device__ __forceinline__ void gdn_gram_rows_item(
   const uint16_t* kf = k + (size_t)bhf * N * DI;
   const uint16_t* vf = v + (size_t)bhf * N * DI;
   const int vchunk = 4 * w + (tid & 3);  // this thread's 16-byte chunk of the V rows
+  const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
 
   floatx16 accG = {}, accU = {};
   struct Regs {
     u32x4 k[KLPT], v;
+    float b;  // gate of token tid % 64 of the tile (TG)
   };
   constexpr int DEPTH = kGramRowsDepth;
   Regs R[DEPTH];
@@ -225,6 +264,7 @@ __device__ __forceinline__ void gdn_gram_rows_item(
     }
     const int n = t0 + (tid >> 2);
     R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * DI + (vchunk < CI ? vchunk : CI - 1) * 8);
+    if (TG) R.b = gf[t0 + (tid & 63) < N ? t0 + (tid & 63) : 0];
   };
   auto stage = [&](const Regs& R, int buf, int t0) {
 #pragma unroll
@@ -236,6 +276,7 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       kd[1] = make_uint2(kk[2], kk[3]);
     }
     const u32x4 vv = t0 + (tid >> 2) < N && vchunk < CI ? R.v : u32x4{0u, 0u, 0u, 0u};
+    if (TG && tid < TILE) gl[buf][tid] = R.b;
     uint2* vd = reinterpret_cast<uint2*>(vl[buf] + swz_offset<VROW / 8>(tid >> 2, tid & 3));
     vd[0] = make_uint2(vv[0], vv[1]);
     vd[1] = make_uint2(vv[2], vv[3]);
@@ -246,6 +287,18 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       const u32x4 kw = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * w, lane);
       const u32x4 kj = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * wave, lane);
       const u32x4 vw = gather_tokens_32_swz<VROW / 8>(vl[buf], s * 16, 0, lane);
+      if (TG) {  // gates of this lane's tokens s*16 + 8g + 0..7, hi + lo (see gdn_gram_item)
+        const float4* gb = reinterpret_cast<const float4*>(&gl[buf][s * 16 + 8 * g]);
+        const float4 g0 = gb[0], g1 = gb[1];
+        u32x4 kh, kl2, vh, vl2;
+        scale_split_bf16x8(kw, g0, g1, kh, kl2);
+        scale_split_bf16x8(vw, g0, g1, vh, vl2);
+        accG = mfma32x32x16(as_bf16x8(kh), as_bf16x8(kj), accG);
+        accG = mfma32x32x16(as_bf16x8(kl2), as_bf16x8(kj), accG);
+        accU = mfma32x32x16(as_bf16x8(vh), as_bf16x8(kj), accU);
+        accU = mfma32x32x16(as_bf16x8(vl2), as_bf16x8(kj), accU);
+        continue;
+      }
       accG = mfma32x32x16(as_bf16x8(kw), as_bf16x8(kj), accG);
       accU = mfma32x32x16(as_bf16x8(vw), as_bf16x8(kj), accU);
     }
@@ -280,7 +333,7 @@ __device__ __forceinline__ void gdn_gram_rows_item(
   }
 
   // block (w, wave) of the record: beta*G hi/lo planes and beta*U (layout as in gdn_gram_item)
-  const float bf = beta[bhf];
+  const float bf = TG ? 1.0f : beta[bhf];
   const float gs = c2 * bf, us = c * bf;
   uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)bhf * kRecBytes);
   uint16_t* Glo = Ghi + D * D;

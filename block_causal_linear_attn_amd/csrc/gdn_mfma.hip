@@ -25,12 +25,12 @@ namespace linscan {
 
 namespace {
 
-template <int DI>
+template <int DI, bool TG>
 __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk) {
-  __shared__ __align__(16) uint8_t lds[kGramLds];
-  gdn_gram_item<DI>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds);
+  __shared__ __align__(16) uint8_t lds[kGramLds + kGateLds];
+  gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds);
 }
 
 template <bool MULTI, int DI>
@@ -55,7 +55,10 @@ __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
 
 constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan item
 
-template <bool MULTI, int DI>
+constexpr int lds_max(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+
+// TG: `beta` holds per-token gates [B*H*F][N] (see gdn_gram_item).
+template <bool MULTI, int DI, bool TG>
 __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
     uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
   constexpr int kSL = scan_lds_bytes<kFusedRB>();
-  constexpr int LDS = kGramLds > kSL ? (kGramLds > kOutLds ? kGramLds : kOutLds) : (kSL > kOutLds ? kSL : kOutLds);
+  constexpr int LDS = lds_max(kGramLds + (TG ? kGateLds : 0), kSL, kOutLds);
   constexpr int NRB = kGdnFusedRowBlocks;
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     cidx = (int)(r % nco);
   }
   if (gram) {
-    gdn_gram_item<DI>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
+    gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
     publish(&gflags[(bh * F + f) * nc + cidx], epoch);
   } else {
     wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
 // whatever the number of heads.  For single-frame calls the scan has no
 // frame chain and the phases overlap across heads; longer calls run the
 // chain once all records are in.
-template <int DI>
+template <int DI, bool TG>
 __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
@@ -129,8 +132,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
   constexpr int RB = 32, NRB = GD / RB;
   constexpr int kSL = scan_lds_bytes<RB>();
-  constexpr int LDS = kGramRowsLds > kSL ? (kGramRowsLds > kOutLds ? kGramRowsLds : kOutLds)
-                                         : (kSL > kOutLds ? kSL : kOutLds);
+  constexpr int LDS = lds_max(kGramRowsLds + (TG ? kGateLds : 0), kSL, kOutLds);
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
   const long ngram = bhp * F * 4, nscan = bhp * NRB;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long bh = b % bhp, r = b / bhp;  // r = f * 4 + row block
     if (bh >= bh_n) return;
     const long item = (bh * F + r / 4) * 4 + r % 4;
-    gdn_gram_rows_item<DI>(k, v, beta, rec, c, c2, N, item, lds);
+    gdn_gram_rows_item<DI, TG>(k, v, beta, rec, c, c2, N, item, lds);
     publish(&gflags[item], epoch);
     return;
   }
@@ -174,20 +176,25 @@ hipError_t with_head_dim(int D, Body body) {
 hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
   const long grid = bhp * (long)a.F * 4 + bhp * (GD / 32) + bhp * (long)a.F * a.nco;
+  const float* gates = a.tg ? a.gate : a.beta;
   return with_head_dim(a.D, [&](auto di) {
-    hipLaunchKernelGGL((gdn_phased_mfma128<decltype(di)::value>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
-                       (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
-                       bhp, a.F, a.N, a.nco, a.chunko, gflags, sflags, epoch, err);
+    constexpr int DI = decltype(di)::value;
+    auto kern = a.tg ? gdn_phased_mfma128<DI, true> : gdn_phased_mfma128<DI, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
+                       (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
+                       sflags, epoch, err);
     return hipGetLastError();
   });
 }
 
-hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
+hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
   return with_head_dim(D, [&](auto di) {
-    hipLaunchKernelGGL((gdn_gram_mfma128<decltype(di)::value>), dim3((unsigned)(bhf * nc)), dim3(256), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, beta, (uint8_t*)rec, c, c2, N, nc, chunk);
+    constexpr int DI = decltype(di)::value;
+    auto kern = tg ? gdn_gram_mfma128<DI, true> : gdn_gram_mfma128<DI, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(bhf * nc)), dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
+                       gates, (uint8_t*)rec, c, c2, N, nc, chunk);
     return hipGetLastError();
   });
 }
@@ -219,21 +226,17 @@ hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* sta
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st) {
   const long grid = bhp * kGdnFusedRowBlocks + bhp * a.F * (a.nc + a.nco);
+  const float* gates = a.tg ? a.gate : a.beta;
   return with_head_dim(a.D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    const void* kern =
-        a.nc == 1 ? (const void*)gdn_fused_mfma128<false, DI> : (const void*)gdn_fused_mfma128<true, DI>;
-    const int lag = fused_lag(device_slots(kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1, a.F);
-    if (a.nc == 1)
-      hipLaunchKernelGGL((gdn_fused_mfma128<false, DI>), dim3((unsigned)grid), dim3(256), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
-                         (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
-                         bhp, a.F, a.N, a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
-    else
-      hipLaunchKernelGGL((gdn_fused_mfma128<true, DI>), dim3((unsigned)grid), dim3(256), 0, st,
-                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.alpha, a.beta,
-                         (uint16_t*)a.o, (uint8_t*)a.partial, (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh,
-                         bhp, a.F, a.N, a.nc, a.chunk, a.nco, a.chunko, lag, gflags, sflags, epoch, err);
+    auto kern = a.nc == 1 ? (a.tg ? gdn_fused_mfma128<false, DI, true> : gdn_fused_mfma128<false, DI, false>)
+                          : (a.tg ? gdn_fused_mfma128<true, DI, true> : gdn_fused_mfma128<true, DI, false>);
+    const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1,
+                              a.F);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
+                       (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,
+                       a.chunko, lag, gflags, sflags, epoch, err);
     return hipGetLastError();
   });
 }

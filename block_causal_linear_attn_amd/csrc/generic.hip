@@ -14,7 +14,8 @@ namespace {
 constexpr int GT = 32;  // tokens per LDS tile
 
 // dS = sum v phi(k)^T, dz = sum phi(k) over one token chunk (RELU), or
-// G = c2 sum k k^T, U = c sum v k^T (GDN).  Output row of `partial`.
+// G = c2 sum k k^T, U = c sum v k^T (GDN; with per-token gates `gate`
+// [B*H*F][N], each token's terms times its gate).  Output row of `partial`.
 // Entries of the D x D result per thread; larger results are split over
 // gridDim.y workgroups that share the token chunk.
 template <int D>
@@ -27,10 +28,11 @@ template <typename T, int D, bool RELU>
 __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, const T* __restrict__ v,
                                                    float* __restrict__ partial, float c, float c2,
                                                    const float* S0, const float* z0, float* init,
-                                                   int F, int N, int nc, int chunk) {
+                                                   const float* gate, int F, int N, int nc, int chunk) {
   constexpr int EPT = SummarySplit<D>::kEPT;
   __shared__ float ks[GT][D + 1];
   __shared__ float vs[GT][D + 1];
+  __shared__ float bs[GT];  // token gates (GDN)
   const int tid = threadIdx.x;
   const int e0 = blockIdx.y * 256 * EPT;  // first entry owned by this workgroup
   const long wg = blockIdx.x;
@@ -57,6 +59,10 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       ks[tok][d] = RELU ? relu_f32(kk) : kk;
       vs[tok][d] = vv;
     }
+    if (!RELU && tid < GT) {
+      const int n = t0 + tid;
+      bs[tid] = gate ? (n < n1 ? gate[(size_t)bhf * N + n] : 0.0f) : 1.0f;
+    }
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < EPT; ++x) {
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       if (e < D * D) {
         const int i = e / D, j = e % D;
         for (int tok = 0; tok < GT; ++tok) {
-          const float kj = ks[tok][j];
+          const float kj = RELU ? ks[tok][j] : bs[tok] * ks[tok][j];
           a1[x] = fmaf(vs[tok][i], kj, a1[x]);
           if (!RELU) a2[x] = fmaf(ks[tok][i], kj, a2[x]);
         }
@@ -160,10 +166,10 @@ hipError_t summary_launch(const GenArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.bhf * a.nc), SummarySplit<D>::kParts), block(256);
   if (a.relu)
     hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.F, a.N, a.nc, a.chunk);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk);
   else
     hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.F, a.N, a.nc, a.chunk);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk);
   return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@ struct ScanArgs {
   const void* v = nullptr;
   void* o = nullptr;
   const float* alpha = nullptr;
-  const float* beta = nullptr;
+  const float* beta = nullptr;   // GDN update gate per frame [B*H*F]
+  const float* gate = nullptr;   // GDN update gate per token [B*H*F][N] (tg; beta is then NULL)
+  bool tg = false;               // GDN gates per token
   const float* S0 = nullptr;   // initial state (NULL = zeros)
   const float* z0 = nullptr;   // initial ReLU normaliser (NULL = zeros)
   float* S_out = nullptr;

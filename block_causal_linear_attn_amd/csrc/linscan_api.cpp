@@ -419,10 +419,12 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   return ok();
 }
 
-ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
-                               const void* v, const float* alpha, const float* beta, void* o,
-                               const float* state_in, float* state_out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+// Both GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
+// token ([B*H*F][N]).
+static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, bool token_gate, void* o,
+                             const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   g_last_error.clear();
   Dims d;
   ls_status st = check_shape(s, &d);
@@ -431,18 +433,20 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   const int D = s->D;
   const size_t tok_bytes = d.elems * d.esize;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
-  const size_t gate_bytes = (size_t)d.bhf * sizeof(float);
+  const size_t gate_bytes = (size_t)d.bhf * (token_gate ? (size_t)s->N : 1) * sizeof(float);
+  const size_t alpha_bytes = (size_t)d.bhf * sizeof(float);
   if (d.bh == 0) return ok();
   if (tok_bytes > 0 && (!q || !k || !v || !o))
     return fail(LS_ERR_NULL_POINTER, "q, k, v and o are required when F*N > 0");
-  if (s->F > 0 && (!alpha || !beta)) return fail(LS_ERR_NULL_POINTER, "alpha and beta are required when F > 0");
+  if (s->F > 0 && (!alpha || (!beta && gate_bytes > 0)))
+    return fail(LS_ERR_NULL_POINTER, "alpha and beta are required when F > 0");
   if ((tok_bytes && (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o))) ||
       misaligned(state_in) || misaligned(state_out) || misaligned(workspace))
     return fail(LS_ERR_MISALIGNED, "token tensors, states and workspace must be 16-byte aligned");
   if (((uintptr_t)alpha & 3u) || ((uintptr_t)beta & 3u))
     return fail(LS_ERR_MISALIGNED, "alpha and beta must be 4-byte aligned");
   const void* ins[6] = {q, k, v, alpha, beta, state_in};
-  const size_t in_n[6] = {tok_bytes, tok_bytes, tok_bytes, gate_bytes, gate_bytes,
+  const size_t in_n[6] = {tok_bytes, tok_bytes, tok_bytes, alpha_bytes, gate_bytes,
                           state_in ? state_bytes : 0};
   for (int i = 0; i < 6; ++i) {
     if (overlap(o, tok_bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "o overlaps an input");
@@ -482,7 +486,9 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
   a.v = v;
   a.o = o;
   a.alpha = alpha;
-  a.beta = beta;
+  a.beta = token_gate ? nullptr : beta;
+  a.gate = token_gate ? beta : nullptr;
+  a.tg = token_gate;
   a.S0 = state_in;
   a.S_out = state_out;
   a.partial = (float*)(ws + p.partial_off);
@@ -520,6 +526,22 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
                         "gdn output")) != LS_OK)
       return st;
   return ok();
+}
+
+ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
+                               const void* v, const float* alpha, const float* beta, void* o,
+                               const float* state_in, float* state_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, o, state_in, state_out, workspace, workspace_bytes,
+                     stream);
+}
+
+ls_status ls_gdn_frame_forward_token_gate(const ls_shape* s, float key_scale, const void* q, const void* k,
+                                          const void* v, const float* alpha, const float* beta, void* o,
+                                          const float* state_in, float* state_out, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  return gdn_forward(s, key_scale, q, k, v, alpha, beta, true, o, state_in, state_out, workspace, workspace_bytes,
+                     stream);
 }
 
 ls_status ls_state_carry(int B, int H, int D, const float* state_src, const float* norm_src,

@@ -22,7 +22,7 @@ hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* 
 hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* partial,
                                    const float* init, float* S_out, float* z_out, float eps, long bhf,
                                    int F, int N, int nc, int bfr, int nco, int chunk, hipStream_t st);
-hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* beta, void* rec,
+hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st);
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
                                 void* states, float* S_out, long bh, int F, int nc, hipStream_t st);
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
 
   for (int f = 0; f < F; ++f) {
     const size_t bhf = (size_t)bh * F + f;
-    const float a = alpha[bhf], b = beta[bhf];
+    const float a = alpha[bhf], b = beta ? beta[bhf] : 1.0f;  // per-token gates are inside G and U
     const float* P = partial + bhf * nc * 2 * D * D;
     for (int e = tid; e < D * D; e += 256) {
       float gsum = P[e];
@@ -175,7 +175,8 @@ hipError_t launch_relu_output(const ScanArgs& a, hipStream_t st) {
 
 hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st) {
   if (a.mfma)
-    return launch_gdn_gram_mfma(a.D, a.k, a.v, a.beta, a.partial, a.c, a.c2, a.bhf, a.N, a.nc, a.chunk, st);
+    return launch_gdn_gram_mfma(a.D, a.k, a.v, a.tg ? a.gate : a.beta, a.tg, a.partial, a.c, a.c2, a.bhf, a.N, a.nc,
+                                a.chunk, st);
   return launch_summary_generic(a, st);
 }
 

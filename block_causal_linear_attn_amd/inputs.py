@@ -14,7 +14,8 @@ Recipe (one torch.Generator per tensor):
   round-to-nearest-even, or kept as fp32).  For the Gated-DeltaNet workloads
   with `l2_keys`, each key token is divided by its float32 L2 norm before the
   rounding.  alpha = sigmoid(N(alpha_mu, 0.5)), beta = sigmoid(N(0, 1)) per
-  (batch, head, frame), float32.
+  (batch, head, frame), float32; per-token update gates (stream 5) are
+  sigmoid(N(0, 1)) per (batch, head, frame, token), float32.
 
 Large tensors are drawn frame-chunk by frame-chunk from one generator so that
 peak temporary memory stays bounded; the chunking is fixed, so results depend
@@ -26,7 +27,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-Q, K, V, ALPHA, BETA = 0, 1, 2, 3, 4
+Q, K, V, ALPHA, BETA, TOKEN_GATE = 0, 1, 2, 3, 4, 5
 PREFIX = 10
 
 _DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -127,6 +128,12 @@ def gates(B, H, F, seed, alpha_mu, part=0, device="cpu", prefix=False):
     a = torch.sigmoid(alpha_mu + 0.5 * torch.randn((B, H, F), generator=ga, device=device))
     b = torch.sigmoid(torch.randn((B, H, F), generator=gb, device=device))
     return a.contiguous(), b.contiguous()
+
+
+def token_gates(B, H, F, N, seed, part=0, device="cpu"):
+    """Per-token update gates [B, H, F, N] float32, sigmoid(N(0, 1))."""
+    g = _gen(seed, TOKEN_GATE, part, device)
+    return torch.sigmoid(torch.randn((B, H, F, N), generator=g, device=device)).contiguous()
 
 
 def relu_inputs(B, H, F, N, D, dtype="bf16", seed=0, part=0, device="cpu"):

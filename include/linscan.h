@@ -155,6 +155,30 @@ ls_status ls_gdn_frame_forward(const ls_shape* shape, float key_scale,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Frame-wise Gated DeltaNet with a per-token update gate (SANA-WM summary,
+ * section 3 Method, item "Hybrid GDN/Softmax Attention": a decay and a
+ * per-token update gate control what the state keeps).  As
+ * ls_gdn_frame_forward, except that beta holds one gate per token and each
+ * token's terms of the frame's matrices carry its gate:
+ *     G = sum_n beta_n (c k_n)(c k_n)^T,   U = sum_n beta_n v_n (c k_n)^T
+ *     S <- alpha_f S (I - G) + U
+ *     o_n = S q_n   for every token n of frame f.
+ * With beta_n = beta_f for every token of frame f this is
+ * ls_gdn_frame_forward.  The bf16 kernels apply each gate to one operand of
+ * the token products, rounded to bf16 (the other operand stays exact).
+ *
+ *   alpha [B][H][F] fp32;  beta [B][H][F][N] fp32 (4-byte aligned)
+ *   everything else, including the workspace size
+ *   (ls_gdn_frame_workspace_size) and the error behaviour, as
+ *   ls_gdn_frame_forward.
+ */
+ls_status ls_gdn_frame_forward_token_gate(const ls_shape* shape, float key_scale,
+                                          const void* q, const void* k, const void* v,
+                                          const float* alpha, const float* beta, void* o,
+                                          const float* state_in, float* state_out,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block-autoregressive hand-off of the carried state: the state a finished
  * block leaves behind becomes the cache the next block starts from (SANA-Video
  * talk, block KV cache passage: the state of block i is cached and block i+1

@@ -95,6 +95,26 @@ def test_validation_errors_gdn(lib):
     assert _gdn(lib, shp, wsb=need - 1) == 6
 
 
+def _gdn_tg(lib, shp, scale=0.0, q=P[0], k=P[1], v=P[2], a=P[7], b=P[8], o=P[3], si=None, so=P[4],
+            ws=P[6], wsb=1 << 40):
+    return lib.lib.ls_gdn_frame_forward_token_gate(ctypes.byref(shp), scale, q, k, v, a, b, o, si, so, ws, wsb,
+                                                   None)
+
+
+def test_validation_errors_gdn_token_gate(lib):
+    assert _gdn_tg(lib, _shape(lib, D=100)) == 3
+    assert _gdn_tg(lib, _shape(lib), b=None) == 1
+    assert _gdn_tg(lib, _shape(lib), b=ctypes.c_void_p(A * 9 + 2)) == 5
+    # beta holds B*H*F*N gates (1536 bytes here): a state 1 KiB past its start overlaps
+    # it, while the per-frame entry point (24 bytes of beta) sees no overlap there
+    inside = ctypes.c_void_p(A * 9 + 1024)
+    assert _gdn_tg(lib, _shape(lib), so=inside) == 8
+    assert _gdn(lib, _shape(lib), so=inside, wsb=1) == 6
+    shp = _shape(lib, D=112)
+    need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    assert _gdn_tg(lib, shp, wsb=need - 1) == 6
+
+
 def test_in_place_state_is_not_an_aliasing_error(lib):
     """state_out == state_in is allowed; the call then fails only on the workspace check."""
     shp = _shape(lib)

@@ -132,6 +132,54 @@ def test_gdn_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, l2, with_state):
     check(tag + " S", S, rS, ts, dt)
 
 
+TG_CASES = [
+    # (B, H, F, N, D, dtype, with_state): per-token update gates
+    (1, 2, 4, 300, 128, "bf16", True),      # frame-interleaved launch, ragged token count
+    (2, 3, 5, 920, 112, "bf16", True),      # head dim 112, frame-interleaved launch
+    (1, 40, 3, 130, 128, "bf16", True),     # phased launch (40 heads)
+    (1, 2, 1, 200, 112, "bf16", True),      # phased launch, one frame
+    (3, 24, 1, 920, 128, "bf16", True),     # the chunk-step shape at B = 3
+    (1, 2, 3, 80, 64, "bf16", True),        # generic bf16 kernels
+    (1, 2, 3, 40, 32, "fp32", True),        # generic fp32 kernels
+    (1, 1, 2, 1, 128, "bf16", False),       # one token per frame
+]
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,with_state", TG_CASES)
+def test_gdn_token_gate_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, with_state):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=15, part=N, l2_keys=True)
+    bt = gen.token_gates(B, H, F, N, seed=15, part=N)
+    S0 = _rand_state(B, H, D, 7, scale=0.5) if with_state else None
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward_token_gate(xd["q"], xd["k"], xd["v"], xd["alpha"], bt.to(DEV),
+                                              None if S0 is None else S0.to(DEV))
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame_token_gate(x["q"], x["k"], x["v"], x["alpha"], bt, S0)
+    to, ts = TOL[dt]
+    tag = "gdn token-gate B%d H%d F%d N%d D%d %s" % (B, H, F, N, D, dt)
+    check(tag + " o", o, ro, to, dt)
+    check(tag + " S", S, rS, ts, dt)
+
+
+def test_gdn_token_gate_zero_gates_skip_tokens(ls, gen, oracle_mod):
+    """Zero gates on half of each frame's tokens: matches the oracle, and the
+    state equals the frame-gate path's over the other half (same key scale)."""
+    B, H, F, N, D = 1, 4, 3, 256, 128
+    x = gen.gdn_inputs(B, H, F, N, D, "bf16", seed=16, l2_keys=True)
+    bt = torch.zeros((B, H, F, N))
+    bt[..., 1::2] = x["beta"][..., None]
+    xd = _dev(x)
+    c = 1.0 / np.sqrt(D * N)
+    o, S = ls.ls_gdn_frame_forward_token_gate(xd["q"], xd["k"], xd["v"], xd["alpha"], bt.to(DEV), key_scale=c)
+    half = {n: xd[n][..., 1::2, :].contiguous() for n in ("q", "k", "v")}
+    o2, S2 = ls.ls_gdn_frame_forward(half["q"], half["k"], half["v"], xd["alpha"], xd["beta"], key_scale=c)
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame_token_gate(x["q"], x["k"], x["v"], x["alpha"], bt, key_scale=np.float32(c))
+    check("gdn token-gate zero-half o", o, ro, 2e-2)
+    check("gdn token-gate zero-half S", S, rS, 1e-2)
+    check("gdn token-gate zero-half S vs frame-gate half", S, S2.double().cpu().numpy(), 1e-2)
+
+
 def test_gdn_explicit_key_scale(ls, gen, oracle_mod):
     x = gen.gdn_inputs(1, 2, 3, 64, 128, "bf16", seed=14, l2_keys=True)
     xd = _dev(x)
@@ -293,7 +341,7 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
 
 
 # --------------------------------------------------------------------------- single-launch paths
-@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased"])
+@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased", "gdn_token_gate"])
 def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     """The one-launch paths hand data between work items through flags with
     bounded waits; the workspace's fault word must stay zero and results match."""
@@ -309,15 +357,22 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=32)
         shp = ls.ls_shape(1, 5, 9, 333, 128, 1)
         need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
-    else:  # 80 heads: the phased launch
+    elif op == "gdn_phased":  # 80 heads: the phased launch
         x = gen.gdn_inputs(2, 40, 2, 200, 128, "bf16", seed=33)
         shp = ls.ls_shape(2, 40, 2, 200, 128, 1)
+        need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+    else:  # per-token gates, frame-interleaved launch
+        x = gen.gdn_inputs(1, 5, 9, 333, 112, "bf16", seed=35)
+        x["beta_tok"] = gen.token_gates(1, 5, 9, 333, seed=35)
+        shp = ls.ls_shape(1, 5, 9, 333, 112, 1)
         need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     xd = _dev(x)
     for rep in range(3):  # reuse of a workspace across calls (fresh epochs)
         if op.startswith("relu"):
             o, S, z = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], block_frames=2, ws=ws)
+        elif op == "gdn_token_gate":
+            o, S = ls.ls_gdn_frame_forward_token_gate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta_tok"], ws=ws)
         else:
             o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], ws=ws)
         torch.cuda.synchronize()
@@ -326,6 +381,10 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], block_frames=2)
         check("single-launch relu o", o, ro, 2e-2)
         check("single-launch relu S", S, rS, 1e-2)
+    elif op == "gdn_token_gate":
+        ro, rS = oracle_mod.gdn_frame_token_gate(x["q"], x["k"], x["v"], x["alpha"], x["beta_tok"])
+        check("single-launch gdn token-gate o", o, ro, 2e-2)
+        check("single-launch gdn token-gate S", S, rS, 1e-2)
     else:
         ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
         check("single-launch gdn o", o, ro, 2e-2)
