@@ -85,6 +85,8 @@ def parse():
                          "the ReLU part, all for the GDN part)")
     ap.add_argument("--no-head-dim-112", action="store_true",
                     help="skip the side measurement of both workloads at head dim 112")
+    ap.add_argument("--no-token-gate", action="store_true",
+                    help="skip the side measurement of the GDN part with per-token update gates")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -220,6 +222,7 @@ def main():
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
     d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
+    tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -260,7 +263,7 @@ def main():
                                     round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112},
+        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -312,6 +315,33 @@ def time_head_dim_112(torch, ls, inputs, reps=3):
                      "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "workload": w.note}
     del calls, outs, g, g_out
     return res
+
+
+def time_token_gate(torch, ls, inputs, g, wg, reps=3):
+    """The GDN part with one update gate per token (same inputs, gates drawn
+    per token), timed over `reps` calls after one warm-up call."""
+    dev = torch.device("cuda:0")
+    bt = inputs.token_gates(wg.B, wg.H, wg.F, wg.N, seed=wg.seed, device=dev)
+    out = torch.empty_like(g["q"])
+    st = torch.empty((wg.B, wg.H, wg.D, wg.D), device=dev)
+
+    def call():
+        ls.ls_gdn_frame_forward_token_gate(g["q"], g["k"], g["v"], g["alpha"], bt, None, out=out, state_out=st)
+
+    call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    tokens = wg.B * wg.F * wg.N
+    nbytes = 4 * wg.B * wg.H * wg.F * wg.N * wg.D * 2 + wg.B * wg.H * wg.F * wg.N * 4  # + the gates
+    return {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "B1 H24 D128 F181 N920 bf16, one update gate per token"}
 
 
 def time_chunk_step(torch, ls, inputs):

@@ -114,6 +114,19 @@ def test_sana_wm_720p_60s_d112(ls, gen, oracle_mod):
     check("wm-60s D112 gdn S", _heads(S, hs), rS, 1e-2)
 
 
+def test_sana_wm_720p_60s_token_gate(ls, gen, oracle_mod):
+    """The 60 s GDN workload with one update gate per token (B1 H24 D128 F181 N920)."""
+    w = gen.WORKLOADS["sana_wm_720p_60s"]
+    x = gen.workload_call_inputs(w, 0, device=DEV)
+    bt = gen.token_gates(w.B, w.H, w.F, w.N, seed=w.seed, device=DEV)
+    o, S = ls.ls_gdn_frame_forward_token_gate(x["q"], x["k"], x["v"], x["alpha"], bt)
+    torch.cuda.synchronize()
+    hs = [7, 16]
+    ro, rS = oracle_mod.gdn_frame_token_gate(*(_heads(t, hs) for t in (x["q"], x["k"], x["v"], x["alpha"], bt)))
+    check("wm-60s gdn token-gate o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
+    check("wm-60s gdn token-gate S", _heads(S, hs), rS, 1e-2)
+
+
 def test_sana_wm_720p_60s(ls, gen, oracle_mod):
     w = gen.WORKLOADS["sana_wm_720p_60s"]
     x = gen.workload_call_inputs(w, 0, device=DEV)
