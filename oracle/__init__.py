@@ -53,6 +53,8 @@ def _load():
     lib.oracle_gdn_frame.restype = i
     lib.oracle_gdn_frame_token_gate.argtypes = [i, i, i, i, i, d, P, P, P, P, P, P, P, P, i]
     lib.oracle_gdn_frame_token_gate.restype = i
+    lib.oracle_gdn_frame_reversed.argtypes = [i, i, i, i, i, i, d, P, P, P, P, P, P, i]
+    lib.oracle_gdn_frame_reversed.restype = i
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -155,3 +157,24 @@ def gdn_frame_token_gate(q, k, v, alpha, beta, state=None, key_scale=None, with_
     if rc != 0:
         raise RuntimeError("oracle_gdn_frame_token_gate failed with code %d" % rc)
     return o, S
+
+
+def gdn_frame_reversed(q, k, v, alpha, beta, chunk_frames: int, key_scale=None, nthreads: int = 0):
+    """Reversed frame-wise Gated DeltaNet, reset at chunk boundaries, fp64.
+
+    Frames are cut into chunks of chunk_frames from frame 0; each chunk is
+    scanned from its last frame to its first, from a zero state.  Returns o.
+    """
+    k = _f32(k)
+    B, H, F, N, D = k.shape
+    v = _f32(v, k.shape)
+    q = _f32(q, k.shape)
+    a = _f32(alpha, (B, H, F))
+    b = _f32(beta, (B, H, F))
+    o = np.empty((B, H, F, N, D), np.float64)
+    c = -1.0 if key_scale is None else float(key_scale)
+    rc = _load().oracle_gdn_frame_reversed(B, H, F, N, D, int(chunk_frames), c, _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(a), _ptr(b), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_gdn_frame_reversed failed with code %d" % rc)
+    return o

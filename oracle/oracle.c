@@ -307,3 +307,84 @@ int oracle_gdn_frame_token_gate(int B, int H, int F, int N, int D, double key_sc
   }
   return status;
 }
+
+/*
+ * Reversed frame-wise Gated DeltaNet that resets at chunk boundaries.  The
+ * SANA-WM summary (paperlayer.ai), section 3 Method, item "Chunk-causal
+ * deployment": a reversed GDN scan, reset at each chunk boundary, gives every
+ * frame context from the later frames of its own chunk without leaking
+ * across chunks.  Frames are cut into chunks of `chunk` frames from frame 0
+ * (the last chunk may be shorter); within each chunk the state starts at
+ * zero at the chunk's LAST frame and the frames are taken in decreasing
+ * order, each with its own gates:
+ *   G, U of frame f as in oracle_gdn_frame;  S <- alpha_f S (I - beta_f G) + beta_f U
+ *   o_n = S q_n for the tokens of frame f.
+ * No initial or final state.  Other arguments as in oracle_gdn_frame.
+ */
+int oracle_gdn_frame_reversed(int B, int H, int F, int N, int D, int chunk, double key_scale,
+                              const float* q, const float* k, const float* v,
+                              const float* alpha, const float* beta, double* o, int nthreads) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1 || chunk < 1) return ORACLE_BAD_ARG;
+  if (!q || !k || !v || !alpha || !beta || !o) return ORACLE_BAD_ARG;
+  const double c = key_scale > 0.0 ? key_scale : 1.0 / sqrt((double)D * (double)N);
+  int status = ORACLE_OK;
+  long heads = (long)B * H;
+  size_t DD = (size_t)D * D;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (long bh = 0; bh < heads; ++bh) {
+    double* S = (double*)malloc(DD * sizeof(double));
+    double* G = (double*)malloc(DD * sizeof(double));
+    double* U = (double*)malloc(DD * sizeof(double));
+    double* T = (double*)malloc(DD * sizeof(double));
+    double* kt = (double*)malloc((size_t)D * sizeof(double));
+    if (!S || !G || !U || !T || !kt) {
+      status = ORACLE_NO_MEMORY;
+      free(S); free(G); free(U); free(T); free(kt);
+      continue;
+    }
+    for (int c0 = 0; c0 < F; c0 += chunk) {
+      const int c1 = c0 + chunk < F ? c0 + chunk : F;
+      memset(S, 0, DD * sizeof(double));  /* reset at the chunk boundary */
+      for (int f = c1 - 1; f >= c0; --f) {
+        const double a = (double)alpha[(size_t)bh * F + f];
+        const double b = (double)beta[(size_t)bh * F + f];
+        memset(G, 0, DD * sizeof(double));
+        memset(U, 0, DD * sizeof(double));
+        for (int n = 0; n < N; ++n) {
+          const float* kn = k + tok(bh, f, n, F, N, D);
+          const float* vn = v + tok(bh, f, n, F, N, D);
+          for (int j = 0; j < D; ++j) kt[j] = c * (double)kn[j];
+          for (int i = 0; i < D; ++i) {
+            for (int j = 0; j < D; ++j) {
+              G[(size_t)i * D + j] += kt[i] * kt[j];
+              U[(size_t)i * D + j] += (double)vn[i] * kt[j];
+            }
+          }
+        }
+        /* S <- alpha (S - beta S G) + beta U */
+        for (int i = 0; i < D; ++i) {
+          for (int j = 0; j < D; ++j) {
+            double acc = 0.0;
+            for (int l = 0; l < D; ++l) acc += S[(size_t)i * D + l] * G[(size_t)l * D + j];
+            T[(size_t)i * D + j] = S[(size_t)i * D + j] - b * acc;
+          }
+        }
+        for (size_t e = 0; e < DD; ++e) S[e] = a * T[e] + b * U[e];
+        for (int n = 0; n < N; ++n) {
+          const float* qn = q + tok(bh, f, n, F, N, D);
+          double* on = o + tok(bh, f, n, F, N, D);
+          for (int i = 0; i < D; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < D; ++j) acc += S[(size_t)i * D + j] * (double)qn[j];
+            on[i] = acc;
+          }
+        }
+      }
+    }
+    free(S); free(G); free(U); free(T); free(kt);
+  }
+  return status;
+}
