@@ -55,6 +55,8 @@ def _load():
     lib.ls_gdn_frame_forward.restype = I
     lib.ls_gdn_frame_forward_token_gate.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward_token_gate.restype = I
+    lib.ls_gdn_frame_forward_reversed.argtypes = [SP, I, F, P, P, P, P, P, P, P, Z, P]
+    lib.ls_gdn_frame_forward_reversed.restype = I
     lib.ls_state_carry.argtypes = [I, I, I, P, P, P, P, I, P]
     lib.ls_state_carry.restype = I
     lib.ls_status_string.argtypes = [I]
@@ -73,7 +75,8 @@ def _load():
 lib = _load()
 
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
-           "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate",
+           "ls_gdn_frame_forward_reversed", "ls_state_carry", "ls_status_string", "ls_last_error",
            "ls_version", "ls_profile_begin", "ls_profile_end")
 
 
@@ -220,6 +223,31 @@ def ls_gdn_frame_forward_token_gate(q, k, v, alpha, beta, state=None, key_scale=
                                                _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
                                                _stream(dev)))
     return o, so
+
+
+def ls_gdn_frame_forward_reversed(q, k, v, alpha, beta, chunk_frames: int, key_scale=None, out=None, ws=None):
+    """Reversed frame-wise Gated DeltaNet that resets every chunk_frames frames; returns o.
+
+    alpha, beta: [B, H, F] fp32.  Each chunk is scanned from its last frame to
+    its first from a zero state.
+    """
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    shp = _shape(q)
+    need = lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    w = ws if ws is not None else workspace(need, dev)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward_reversed(ctypes.byref(shp), int(chunk_frames), scale, _ptr(q), _ptr(k),
+                                             _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(w), w.numel(),
+                                             _stream(dev)))
+    return o
 
 
 def ls_state_carry(state_src, state_dst, norm_src=None, norm_dst=None, reset: bool = False):

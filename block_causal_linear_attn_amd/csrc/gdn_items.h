@@ -381,6 +381,10 @@ constexpr int kScanLds = scan_lds_bytes<kScanRB>();
 
 // Scan item of rows [r0, r0 + RB) of head `head`'s state over all F frames
 // (RB = 16 or 32: one or two 16-row sub-blocks per wave).
+// rchunk > 0: the reversed scan that resets at chunk boundaries.  Step f of
+// the loop then works on frame phys(f): the frames of each chunk of rchunk
+// frames (from frame 0) in decreasing order; the first step of a chunk uses
+// a decay of 0, which drops the previous chunk's state (S <- beta U).
 // FUSED: records come from gram items of the same launch (wait for gflags
 // before each frame, one flag per token chunk) and each frame's state is
 // announced on sflags[(head * F + f) * 8 + r0 / RB] for the output items.
@@ -388,7 +392,7 @@ template <bool MULTI, bool FUSED, int RB = kScanRB, int DI = GD>
 __device__ __forceinline__ void gdn_scan_item(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
     uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, int nc, uint8_t* lds_raw,
-    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err, int gpf = 0) {
+    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err, int gpf = 0, int rchunk = 0) {
   // gram flags per frame: one per record chunk, or gpf when the frame's record
   // is written in gpf disjoint parts
   const int nfl = gpf > 0 ? gpf : nc;
@@ -419,6 +423,12 @@ __device__ __forceinline__ void gdn_scan_item(
     float u[SB][2][4];
   };
   const size_t hf0 = (size_t)head * F;
+  auto phys = [&](int f) {
+    if (rchunk <= 0) return f;
+    const int c0 = f / rchunk * rchunk;
+    return c0 + min(rchunk, F - c0) - 1 - (f - c0);
+  };
+  // load_rec and store_state take physical frames
   auto load_rec = [&](int f, int cidx, Rec& R) {
     const uint8_t* base = rec + ((hf0 + f) * nc + cidx) * kRecBytes;
     const uint16_t* gh = reinterpret_cast<const uint16_t*>(base);
@@ -471,20 +481,22 @@ __device__ __forceinline__ void gdn_scan_item(
 
   Rec R0, R1;
   if (!FUSED && F > 0) {
-    load_rec(0, 0, R0);
-    load_rec(min(1, F - 1), 0, R1);
+    load_rec(phys(0), 0, R0);
+    load_rec(phys(min(1, F - 1)), 0, R1);
   }
 
   auto frame = [&](int f, Rec& R) {
     const int cur = f & 1;
+    const int pf = phys(f);
     if (FUSED) {
       // this frame's records are published by gram items; the previous
       // frame's state (stored by every thread) is announced once all are done
       __builtin_amdgcn_s_waitcnt(0);
-      wait_all(&gflags[(hf0 + f) * nfl], nfl, epoch, err);
+      wait_all(&gflags[(hf0 + pf) * nfl], nfl, epoch, err);
       if (f > 0 && tid == 0)
-        __hip_atomic_store(&sflags[(hf0 + f - 1) * 8 + r0 / RB], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      load_rec(f, 0, R);
+        __hip_atomic_store(&sflags[(hf0 + phys(f - 1)) * 8 + r0 / RB], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      load_rec(pf, 0, R);
     }
     const float a = As[f % kAlphaWin];
     // A operands: this workgroup's rows of S_{f-1}, split into bf16 hi + lo
@@ -525,7 +537,7 @@ __device__ __forceinline__ void gdn_scan_item(
     if (MULTI) {
       for (int cidx = 1; cidx < nc; ++cidx) {  // the frame's further token chunks
         Rec T;
-        load_rec(f, cidx, T);
+        load_rec(pf, cidx, T);
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
@@ -539,7 +551,7 @@ __device__ __forceinline__ void gdn_scan_item(
       }
     }
     // refill this ring slot two frames ahead (the last record again at the end)
-    if (!FUSED) load_rec(min(f + 2, F - 1), 0, R);
+    if (!FUSED) load_rec(phys(min(f + 2, F - 1)), 0, R);
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
@@ -552,12 +564,13 @@ __device__ __forceinline__ void gdn_scan_item(
           Ss[cur ^ 1][m][n] = s[sb][nb][r];
         }
     __syncthreads();
-    store_state(f, cur ^ 1);
+    store_state(pf, cur ^ 1);
   };
 
   for (int w0 = 0; w0 < F; w0 += kAlphaWin) {
     const int w1 = min(F, w0 + kAlphaWin);
-    for (int i = tid; i < w1 - w0; i += 256) As[i] = alpha[hf0 + w0 + i];
+    for (int i = tid; i < w1 - w0; i += 256)
+      As[i] = rchunk > 0 && (w0 + i) % rchunk == 0 ? 0.0f : alpha[hf0 + phys(w0 + i)];
     __syncthreads();
     int f = w0;
     for (; f + 2 <= w1; f += 2) {
@@ -567,7 +580,7 @@ __device__ __forceinline__ void gdn_scan_item(
     if (f < w1) frame(f, R0);  // window tail (kAlphaWin is even, so slot f % 2 == 0)
     __syncthreads();  // As is rewritten for the next window
   }
-  if (FUSED && F > 0) publish(&sflags[(hf0 + F - 1) * 8 + r0 / RB], epoch);
+  if (FUSED && F > 0) publish(&sflags[(hf0 + phys(F - 1)) * 8 + r0 / RB], epoch);
   if (S_out) {
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)

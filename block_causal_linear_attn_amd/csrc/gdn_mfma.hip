@@ -36,13 +36,13 @@ __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
 template <bool MULTI, int DI>
 __global__ __launch_bounds__(256) void gdn_scan_mfma128(
     const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
-    uint16_t* __restrict__ states, float* S_out, long bh, int F, int nc) {
+    uint16_t* __restrict__ states, float* S_out, long bh, int F, int nc, int rchunk) {
   __shared__ __align__(16) uint8_t lds[kScanLds];
   const long b = blockIdx.x;
   const long head = (b / 64) * 8 + (b % 8);
   if (head >= bh) return;  // whole workgroup leaves together
   gdn_scan_item<MULTI, false, kScanRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % 8) * kScanRB, F, nc,
-                              lds, nullptr, nullptr, 0, nullptr);
+                                           lds, nullptr, nullptr, 0, nullptr, 0, rchunk);
 }
 
 template <int DI>
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
-    uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
+    uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk) {
   constexpr int kSL = scan_lds_bytes<kFusedRB>();
   constexpr int LDS = lds_max(kGramLds + (TG ? kGateLds : 0), kSL, kOutLds);
   constexpr int NRB = kGdnFusedRowBlocks;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const long head = (b / (8 * NRB)) * 8 + (b % 8);
     if (head >= bh_n) return;
     gdn_scan_item<MULTI, true, kFusedRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
-                                         F, nc, lds, gflags, sflags, epoch, err);
+                                         F, nc, lds, gflags, sflags, epoch, err, 0, rchunk);
     return;
   }
   const long s = b - nscan;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nco, int chunko, uint64_t* __restrict__ gflags,
-    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err) {
+    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk) {
   constexpr int RB = 32, NRB = GD / RB;
   constexpr int kSL = scan_lds_bytes<RB>();
   constexpr int LDS = lds_max(kGramRowsLds + (TG ? kGateLds : 0), kSL, kOutLds);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long head = bs % bhp;
     if (head >= bh_n) return;
     gdn_scan_item<false, true, RB, DI>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
-                                   sflags, epoch, err, 4);
+                                       sflags, epoch, err, 4, rchunk);
     return;
   }
   const long bo = b - ngram - nscan;
@@ -183,7 +183,7 @@ hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags,
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
-                       sflags, epoch, err);
+                       sflags, epoch, err, a.rchunk);
     return hipGetLastError();
   });
 }
@@ -200,16 +200,16 @@ hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float
 }
 
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
-                                void* states, float* S_out, long bh, int F, int nc, hipStream_t st) {
+                                void* states, float* S_out, long bh, int F, int nc, int rchunk, hipStream_t st) {
   const long groups = (bh + 7) / 8;  // eight heads x eight row blocks per group of 64 workgroups
   return with_head_dim(D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
     if (nc == 1)
       hipLaunchKernelGGL((gdn_scan_mfma128<false, DI>), dim3((unsigned)(groups * 64)), dim3(256), 0, st,
-                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
+                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc, rchunk);
     else
       hipLaunchKernelGGL((gdn_scan_mfma128<true, DI>), dim3((unsigned)(groups * 64)), dim3(256), 0, st,
-                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc);
+                         (const uint8_t*)rec, alpha, S0, (uint16_t*)states, S_out, bh, F, nc, rchunk);
     return hipGetLastError();
   });
 }
@@ -231,12 +231,14 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
     constexpr int DI = decltype(di)::value;
     auto kern = a.nc == 1 ? (a.tg ? gdn_fused_mfma128<false, DI, true> : gdn_fused_mfma128<false, DI, false>)
                           : (a.tg ? gdn_fused_mfma128<true, DI, true> : gdn_fused_mfma128<true, DI, false>);
-    const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco), 1,
-                              a.F);
+    // an output item's state needs the records of every frame of its chunk
+    // (reversed scan): lag >= rchunk keeps those gram items at lower block ids
+    const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco),
+                              a.rchunk > 0 ? a.rchunk : 1, a.F);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,
-                       a.chunko, lag, gflags, sflags, epoch, err);
+                       a.chunko, lag, gflags, sflags, epoch, err, a.rchunk);
     return hipGetLastError();
   });
 }

@@ -31,6 +31,7 @@ struct ScanArgs {
   const float* beta = nullptr;   // GDN update gate per frame [B*H*F]
   const float* gate = nullptr;   // GDN update gate per token [B*H*F][N] (tg; beta is then NULL)
   bool tg = false;               // GDN gates per token
+  int rchunk = 0;                // GDN: > 0 for the reversed scan in chunks of rchunk frames
   const float* S0 = nullptr;   // initial state (NULL = zeros)
   const float* z0 = nullptr;   // initial ReLU normaliser (NULL = zeros)
   float* S_out = nullptr;

@@ -419,10 +419,11 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   return ok();
 }
 
-// Both GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
-// token ([B*H*F][N]).
+// The GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
+// token ([B*H*F][N]); rchunk > 0 runs the reversed scan in chunks of rchunk
+// frames (no state in or out).
 static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, const void* k, const void* v,
-                             const float* alpha, const float* beta, bool token_gate, void* o,
+                             const float* alpha, const float* beta, bool token_gate, int rchunk, void* o,
                              const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
   g_last_error.clear();
@@ -489,6 +490,7 @@ static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, 
   a.beta = token_gate ? nullptr : beta;
   a.gate = token_gate ? beta : nullptr;
   a.tg = token_gate;
+  a.rchunk = rchunk;
   a.S0 = state_in;
   a.S_out = state_out;
   a.partial = (float*)(ws + p.partial_off);
@@ -532,16 +534,25 @@ ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q
                                const void* v, const float* alpha, const float* beta, void* o,
                                const float* state_in, float* state_out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, o, state_in, state_out, workspace, workspace_bytes,
-                     stream);
+  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+                     workspace_bytes, stream);
 }
 
 ls_status ls_gdn_frame_forward_token_gate(const ls_shape* s, float key_scale, const void* q, const void* k,
                                           const void* v, const float* alpha, const float* beta, void* o,
                                           const float* state_in, float* state_out, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, key_scale, q, k, v, alpha, beta, true, o, state_in, state_out, workspace, workspace_bytes,
-                     stream);
+  return gdn_forward(s, key_scale, q, k, v, alpha, beta, true, 0, o, state_in, state_out, workspace,
+                     workspace_bytes, stream);
+}
+
+ls_status ls_gdn_frame_forward_reversed(const ls_shape* s, int chunk_frames, float key_scale, const void* q,
+                                        const void* k, const void* v, const float* alpha, const float* beta,
+                                        void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (chunk_frames < 1) return fail(LS_ERR_BAD_PARAM, "chunk_frames must be >= 1 (got %d)", chunk_frames);
+  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, chunk_frames, o, nullptr, nullptr, workspace,
+                     workspace_bytes, stream);
 }
 
 ls_status ls_state_carry(int B, int H, int D, const float* state_src, const float* norm_src,

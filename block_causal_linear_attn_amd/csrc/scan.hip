@@ -25,7 +25,7 @@ hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* p
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st);
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
-                                void* states, float* S_out, long bh, int F, int nc, hipStream_t st);
+                                void* states, float* S_out, long bh, int F, int nc, int rchunk, hipStream_t st);
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
                                   int N, int nco, int chunk, hipStream_t st);
 
@@ -34,12 +34,15 @@ namespace {
 // One workgroup per (batch*head, 16-row block).  State rows live in LDS; G_f
 // is summed over token chunks into LDS each frame; every thread owns EPT
 // (row, col) entries.  Each frame's state goes to `states` in fp32.
+// rchunk > 0: the reversed scan in chunks of rchunk frames (step l works on
+// frame phys(l), with decay 0 at the first step of each chunk, which drops the
+// previous chunk's state).
 template <int D>
 __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__ partial,
                                                        const float* __restrict__ alpha,
                                                        const float* __restrict__ beta,
                                                        const float* S0, void* __restrict__ states,
-                                                       float* S_out, int F, int nc) {
+                                                       float* S_out, int F, int nc, int rchunk) {
   constexpr int RB = 16;                       // rows per workgroup
   constexpr int EPT = (RB * D + 255) / 256;    // entries per thread
   constexpr int R = D / RB;                    // row blocks per head
@@ -61,9 +64,15 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
     }
   }
 
-  for (int f = 0; f < F; ++f) {
+  for (int l = 0; l < F; ++l) {
+    int f = l;
+    if (rchunk > 0) {
+      const int c0 = l / rchunk * rchunk;
+      f = c0 + min(rchunk, F - c0) - 1 - (l - c0);
+    }
     const size_t bhf = (size_t)bh * F + f;
-    const float a = alpha[bhf], b = beta ? beta[bhf] : 1.0f;  // per-token gates are inside G and U
+    const float a = rchunk > 0 && l % rchunk == 0 ? 0.0f : alpha[bhf];
+    const float b = beta ? beta[bhf] : 1.0f;  // per-token gates are inside G and U
     const float* P = partial + bhf * nc * 2 * D * D;
     for (int e = tid; e < D * D; e += 256) {
       float gsum = P[e];
@@ -113,9 +122,9 @@ __global__ __launch_bounds__(256) void gdn_scan_kernel(const float* __restrict__
 
 template <int D>
 hipError_t scan_launch(const float* partial, const float* alpha, const float* beta, const float* S0,
-                       void* states, float* S_out, long bh, int F, int nc, hipStream_t st) {
+                       void* states, float* S_out, long bh, int F, int nc, int rchunk, hipStream_t st) {
   dim3 grid((unsigned)(bh * (D / 16))), block(256);
-  hipLaunchKernelGGL(gdn_scan_kernel<D>, grid, block, 0, st, partial, alpha, beta, S0, states, S_out, F, nc);
+  hipLaunchKernelGGL(gdn_scan_kernel<D>, grid, block, 0, st, partial, alpha, beta, S0, states, S_out, F, nc, rchunk);
   return hipGetLastError();
 }
 
@@ -181,10 +190,11 @@ hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st) {
-  if (a.mfma) return launch_gdn_scan_mfma(a.D, a.partial, a.alpha, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
+  if (a.mfma)
+    return launch_gdn_scan_mfma(a.D, a.partial, a.alpha, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, a.rchunk, st);
   switch (a.D) {
 #define CASE(d) \
-  case d: return scan_launch<d>(a.partial, a.alpha, a.beta, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, st);
+  case d: return scan_launch<d>(a.partial, a.alpha, a.beta, a.S0, a.states, a.S_out, a.bh, a.F, a.nc, a.rchunk, st);
     CASE(16) CASE(32) CASE(48) CASE(64) CASE(80) CASE(96) CASE(112) CASE(128)
 #undef CASE
     default: return hipErrorInvalidValue;

@@ -179,6 +179,24 @@ ls_status ls_gdn_frame_forward_token_gate(const ls_shape* shape, float key_scale
                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Reversed frame-wise Gated DeltaNet that resets at chunk boundaries (SANA-WM
+ * summary, section 3 Method, item "Chunk-causal deployment": a reversed GDN
+ * scan, reset at each chunk boundary, gives each frame context from the later
+ * frames of its chunk without leaking across chunks).  Frames are cut into
+ * chunks of chunk_frames from frame 0 (the last one may be shorter); each
+ * chunk is scanned from its last frame to its first, from a zero state, with
+ * each frame's own gates and the update of ls_gdn_frame_forward:
+ *     S <- alpha_f S (I - beta_f G_f) + beta_f U_f,   o_n = S q_n (tokens of f).
+ * There is no initial or final state.  chunk_frames < 1 is LS_ERR_BAD_PARAM;
+ * every other argument, the workspace size (ls_gdn_frame_workspace_size) and
+ * the error behaviour are those of ls_gdn_frame_forward.
+ */
+ls_status ls_gdn_frame_forward_reversed(const ls_shape* shape, int chunk_frames, float key_scale,
+                                        const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta, void* o,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block-autoregressive hand-off of the carried state: the state a finished
  * block leaves behind becomes the cache the next block starts from (SANA-Video
  * talk, block KV cache passage: the state of block i is cached and block i+1

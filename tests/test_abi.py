@@ -115,6 +115,19 @@ def test_validation_errors_gdn_token_gate(lib):
     assert _gdn_tg(lib, shp, wsb=need - 1) == 6
 
 
+def test_validation_errors_gdn_reversed(lib):
+    r = lambda shp, C, **kw: lib.lib.ls_gdn_frame_forward_reversed(
+        ctypes.byref(shp), C, 0.0, kw.get("q", P[0]), P[1], P[2], P[7], P[8], kw.get("o", P[3]), P[6],
+        kw.get("wsb", 1 << 40), None)
+    assert r(_shape(lib), 0) == 7
+    assert r(_shape(lib, D=100), 2) == 3
+    assert r(_shape(lib), 2, q=None) == 1
+    assert r(_shape(lib), 2, o=P[1]) == 8
+    shp = _shape(lib, D=128)
+    need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    assert r(shp, 2, wsb=need - 1) == 6
+
+
 def test_in_place_state_is_not_an_aliasing_error(lib):
     """state_out == state_in is allowed; the call then fails only on the workspace check."""
     shp = _shape(lib)

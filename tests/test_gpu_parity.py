@@ -180,6 +180,28 @@ def test_gdn_token_gate_zero_gates_skip_tokens(ls, gen, oracle_mod):
     check("gdn token-gate zero-half S vs frame-gate half", S, S2.double().cpu().numpy(), 1e-2)
 
 
+RV_CASES = [
+    # (B, H, F, N, D, dtype, chunk_frames): reversed scan, reset at chunk boundaries
+    (1, 2, 7, 300, 128, "bf16", 3),     # frame-interleaved launch, ragged last chunk
+    (2, 3, 6, 920, 112, "bf16", 6),     # head dim 112, one chunk of all frames
+    (1, 8, 20, 256, 128, "bf16", 16),   # chunks longer than the launch's default lag
+    (1, 40, 5, 130, 128, "bf16", 2),    # phased launch (40 heads)
+    (1, 2, 9, 200, 128, "bf16", 1),     # one-frame chunks: no history
+    (1, 2, 5, 64, 64, "bf16", 2),       # generic bf16 kernels
+    (1, 2, 5, 40, 32, "fp32", 4),       # generic fp32 kernels
+]
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,C", RV_CASES)
+def test_gdn_reversed_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, C):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=17, part=N, l2_keys=True)
+    xd = _dev(x)
+    o = ls.ls_gdn_frame_forward_reversed(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], C)
+    torch.cuda.synchronize()
+    ro = oracle_mod.gdn_frame_reversed(x["q"], x["k"], x["v"], x["alpha"], x["beta"], C)
+    check("gdn reversed B%d H%d F%d N%d D%d %s C%d o" % (B, H, F, N, D, dt, C), o, ro, TOL[dt][0], dt)
+
+
 def test_gdn_explicit_key_scale(ls, gen, oracle_mod):
     x = gen.gdn_inputs(1, 2, 3, 64, 128, "bf16", seed=14, l2_keys=True)
     xd = _dev(x)
@@ -341,7 +363,7 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
 
 
 # --------------------------------------------------------------------------- single-launch paths
-@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased", "gdn_token_gate"])
+@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased", "gdn_token_gate", "gdn_reversed"])
 def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     """The one-launch paths hand data between work items through flags with
     bounded waits; the workspace's fault word must stay zero and results match."""
@@ -361,6 +383,10 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         x = gen.gdn_inputs(2, 40, 2, 200, 128, "bf16", seed=33)
         shp = ls.ls_shape(2, 40, 2, 200, 128, 1)
         need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+    elif op == "gdn_reversed":  # reversed scan in chunks of 4, frame-interleaved launch
+        x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=36)
+        shp = ls.ls_shape(1, 5, 9, 333, 128, 1)
+        need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
     else:  # per-token gates, frame-interleaved launch
         x = gen.gdn_inputs(1, 5, 9, 333, 112, "bf16", seed=35)
         x["beta_tok"] = gen.token_gates(1, 5, 9, 333, seed=35)
@@ -373,6 +399,8 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
             o, S, z = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], block_frames=2, ws=ws)
         elif op == "gdn_token_gate":
             o, S = ls.ls_gdn_frame_forward_token_gate(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta_tok"], ws=ws)
+        elif op == "gdn_reversed":
+            o = ls.ls_gdn_frame_forward_reversed(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], 4, ws=ws)
         else:
             o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], ws=ws)
         torch.cuda.synchronize()
@@ -381,6 +409,9 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
         ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], block_frames=2)
         check("single-launch relu o", o, ro, 2e-2)
         check("single-launch relu S", S, rS, 1e-2)
+    elif op == "gdn_reversed":
+        ro = oracle_mod.gdn_frame_reversed(x["q"], x["k"], x["v"], x["alpha"], x["beta"], 4)
+        check("single-launch gdn reversed o", o, ro, 2e-2)
     elif op == "gdn_token_gate":
         ro, rS = oracle_mod.gdn_frame_token_gate(x["q"], x["k"], x["v"], x["alpha"], x["beta_tok"])
         check("single-launch gdn token-gate o", o, ro, 2e-2)
