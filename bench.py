@@ -87,6 +87,8 @@ def parse():
                     help="skip the side measurement of both workloads at head dim 112")
     ap.add_argument("--no-token-gate", action="store_true",
                     help="skip the side measurement of the GDN part with per-token update gates")
+    ap.add_argument("--no-reversed", action="store_true",
+                    help="skip the side measurement of the reversed GDN scan (chunks of 8 frames)")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -223,6 +225,7 @@ def main():
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
     d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
     tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
+    rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -263,7 +266,8 @@ def main():
                                     round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate},
+        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
+                 "sana_wm_720p_60s_reversed_c8": rev},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -342,6 +346,30 @@ def time_token_gate(torch, ls, inputs, g, wg, reps=3):
     return {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
             "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "B1 H24 D128 F181 N920 bf16, one update gate per token"}
+
+
+def time_reversed(torch, ls, g, wg, chunk=8, reps=3):
+    """The GDN part through the reversed scan that resets every `chunk` frames,
+    timed over `reps` calls after one warm-up call."""
+    out = torch.empty_like(g["q"])
+
+    def call():
+        ls.ls_gdn_frame_forward_reversed(g["q"], g["k"], g["v"], g["alpha"], g["beta"], chunk, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    tokens = wg.B * wg.F * wg.N
+    nbytes = 4 * wg.B * wg.H * wg.F * wg.N * wg.D * 2
+    return {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "B1 H24 D128 F181 N920 bf16, reversed scan reset every %d frames" % chunk}
 
 
 def time_chunk_step(torch, ls, inputs):

@@ -127,6 +127,17 @@ def test_sana_wm_720p_60s_token_gate(ls, gen, oracle_mod):
     check("wm-60s gdn token-gate S", _heads(S, hs), rS, 1e-2)
 
 
+def test_sana_wm_720p_60s_reversed(ls, gen, oracle_mod):
+    """The 60 s GDN workload through the reversed scan in chunks of 8 frames."""
+    w = gen.WORKLOADS["sana_wm_720p_60s"]
+    x = gen.workload_call_inputs(w, 0, device=DEV)
+    o = ls.ls_gdn_frame_forward_reversed(x["q"], x["k"], x["v"], x["alpha"], x["beta"], 8)
+    torch.cuda.synchronize()
+    hs = [2, 23]
+    ro = oracle_mod.gdn_frame_reversed(*(_heads(x[n], hs) for n in ("q", "k", "v", "alpha", "beta")), 8)
+    check("wm-60s gdn reversed c8 o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
+
+
 def test_sana_wm_720p_60s(ls, gen, oracle_mod):
     w = gen.WORKLOADS["sana_wm_720p_60s"]
     x = gen.workload_call_inputs(w, 0, device=DEV)
