@@ -55,6 +55,8 @@ def _load():
     lib.oracle_gdn_frame_token_gate.restype = i
     lib.oracle_gdn_frame_reversed.argtypes = [i, i, i, i, i, i, d, P, P, P, P, P, P, i]
     lib.oracle_gdn_frame_reversed.restype = i
+    lib.oracle_temporal_conv3.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P]
+    lib.oracle_temporal_conv3.restype = i
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -178,3 +180,25 @@ def gdn_frame_reversed(q, k, v, alpha, beta, chunk_frames: int, key_scale=None, 
     if rc != 0:
         raise RuntimeError("oracle_gdn_frame_reversed failed with code %d" % rc)
     return o
+
+
+def temporal_conv3(x, weight, bias=None, carry=None, block_frames: int = 1, with_carry: bool = True):
+    """Block-causal temporal convolution of kernel 3 along frames, fp64.
+
+    x: [B, H, F, N, D]; weight: [H, D, 3] (taps on frames f-1, f, f+1);
+    bias: [H, D] or None; carry: [B, H, N, D] (frame -1) or None (zeros).
+    Frame f's next-frame tap sees zero when f ends its block of block_frames.
+    Returns (y, carry_out) with carry_out = x[:, :, F-1].
+    """
+    x = _f32(x)
+    B, H, F, N, D = x.shape
+    w = _f32(weight, (H, D, 3))
+    b = _f32(bias, (H, D))
+    c = _f32(carry, (B, H, N, D))
+    y = np.empty((B, H, F, N, D), np.float64)
+    co = np.empty((B, H, N, D), np.float64) if with_carry else None
+    rc = _load().oracle_temporal_conv3(B, H, F, N, D, int(block_frames), _ptr(x), _ptr(w), _ptr(b), _ptr(c),
+                                       _ptr(y), _ptr(co))
+    if rc != 0:
+        raise RuntimeError("oracle_temporal_conv3 failed with code %d" % rc)
+    return y, co

@@ -388,3 +388,53 @@ int oracle_gdn_frame_reversed(int B, int H, int F, int N, int D, int chunk, doub
   }
   return status;
 }
+
+/*
+ * Block-causal temporal convolution of kernel 3 along frames (the Causal
+ * Mix-FFN).  The SANA-Video practical guide (lpnh.cn), section on core
+ * mechanisms, gives the FFN a causal temporal convolution of kernel size 3;
+ * the SANA-Video talk, passage on causal FFN with temporal convolution,
+ * separates blocks by a zero frame in training (a block cannot see the next
+ * one) and hands the last frame of one block to the next (a block sees the
+ * previous block's last frame).  Per channel (h, d) and token n, with blocks
+ * of block_frames frames from frame 0:
+ *   y_f = w[0] x_{f-1} + w[1] x_f + w[2] x_{f+1} + bias
+ * where x_{f+1} is 0 when frame f ends its block (or the call), and x_{-1}
+ * is the carried frame (zero when carry is NULL).
+ * x: [B][H][F][N][D] float32; w: [H][D][3]; bias: [H][D] or NULL;
+ * carry: [B][H][N][D] or NULL.  y: [B][H][F][N][D] float64;
+ * carry_out: [B][H][N][D] float64 = x_{F-1}, or NULL.
+ */
+int oracle_temporal_conv3(int B, int H, int F, int N, int D, int block_frames, const float* x,
+                          const float* w, const float* bias, const float* carry, double* y,
+                          double* carry_out) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1 || block_frames < 1) return ORACLE_BAD_ARG;
+  if (!x || !w || !y) return ORACLE_BAD_ARG;
+  for (long bh = 0; bh < (long)B * H; ++bh) {
+    const int h = (int)(bh % H);
+    for (int f = 0; f < F; ++f) {
+      const int ends_block = (f + 1) % block_frames == 0 || f + 1 == F;
+      for (int n = 0; n < N; ++n) {
+        for (int d = 0; d < D; ++d) {
+          const size_t cell = ((size_t)bh * N + n) * D + d;
+          double prev = 0.0, next = 0.0;
+          if (f > 0)
+            prev = (double)x[tok(bh, f - 1, n, F, N, D) + d];
+          else if (carry)
+            prev = (double)carry[cell];
+          if (!ends_block) next = (double)x[tok(bh, f + 1, n, F, N, D) + d];
+          const float* wt = w + ((size_t)h * D + d) * 3;
+          double acc = (double)wt[0] * prev + (double)wt[1] * (double)x[tok(bh, f, n, F, N, D) + d] +
+                       (double)wt[2] * next;
+          if (bias) acc += (double)bias[(size_t)h * D + d];
+          y[tok(bh, f, n, F, N, D) + d] = acc;
+        }
+      }
+    }
+    if (carry_out)
+      for (int n = 0; n < N; ++n)
+        for (int d = 0; d < D; ++d)
+          carry_out[((size_t)bh * N + n) * D + d] = (double)x[tok(bh, F - 1, n, F, N, D) + d];
+  }
+  return ORACLE_OK;
+}
