@@ -57,6 +57,8 @@ def _load():
     lib.ls_gdn_frame_forward_token_gate.restype = I
     lib.ls_gdn_frame_forward_reversed.argtypes = [SP, I, F, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward_reversed.restype = I
+    lib.ls_temporal_conv3.argtypes = [SP, I, P, P, P, P, P, P, P]
+    lib.ls_temporal_conv3.restype = I
     lib.ls_state_carry.argtypes = [I, I, I, P, P, P, P, I, P]
     lib.ls_state_carry.restype = I
     lib.ls_status_string.argtypes = [I]
@@ -76,7 +78,7 @@ lib = _load()
 
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
            "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate",
-           "ls_gdn_frame_forward_reversed", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_gdn_frame_forward_reversed", "ls_temporal_conv3", "ls_state_carry", "ls_status_string", "ls_last_error",
            "ls_version", "ls_profile_begin", "ls_profile_end")
 
 
@@ -248,6 +250,36 @@ def ls_gdn_frame_forward_reversed(q, k, v, alpha, beta, chunk_frames: int, key_s
                                              _ptr(v), _ptr(alpha), _ptr(beta), _ptr(o), _ptr(w), w.numel(),
                                              _stream(dev)))
     return o
+
+
+def ls_temporal_conv3(x, weight, bias=None, carry=None, block_frames: int = 1, out=None, carry_out=None):
+    """Block-causal temporal convolution of kernel 3 along frames; returns (y, carry_out).
+
+    x: [B, H, F, N, D] fp32 or bf16; weight: [H, D, 3] fp32 (taps on frames
+    f-1, f, f+1); bias: [H, D] fp32 or None; carry: [B, H, N, D] (x's dtype),
+    the previous block's last frame, or None for zeros.  carry_out receives
+    x's last frame (allocated unless given; may be `carry`).
+    """
+    if not isinstance(x, torch.Tensor) or x.dim() != 5 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 5-d GPU tensor [B, H, F, N, D]")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    B, H, F, N, D = x.shape
+    dev = x.device
+    _f32("weight", weight, (H, D, 3), dev)
+    _f32("bias", bias, (H, D), dev)
+    for name, t in (("carry", carry), ("carry_out", carry_out)):
+        if t is not None and (t.dtype != x.dtype or tuple(t.shape) != (B, H, N, D) or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous %s tensor [B, H, N, D] on %s" % (name, x.dtype, dev))
+    y = out if out is not None else torch.empty_like(x)
+    if y.shape != x.shape or y.dtype != x.dtype or y.device != dev or not y.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    co = carry_out if carry_out is not None else torch.empty((B, H, N, D), dtype=x.dtype, device=dev)
+    shp = _shape(x)
+    _check(lib.ls_temporal_conv3(ctypes.byref(shp), int(block_frames), _ptr(x), _ptr(weight), _ptr(bias),
+                                 _ptr(carry), _ptr(y), _ptr(co), _stream(dev)))
+    return y, co
 
 
 def ls_state_carry(state_src, state_dst, norm_src=None, norm_dst=None, reset: bool = False):

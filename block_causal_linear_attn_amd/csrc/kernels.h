@@ -113,6 +113,12 @@ hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags,
 hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);
 hipError_t launch_output_generic(const ScanArgs& a, hipStream_t st);
 
+// Block-causal temporal convolution of kernel 3 along frames (x, y, carries
+// in `dtype`; F >= 1; D a multiple of 16 bytes of elements): see conv.hip.
+hipError_t launch_temporal_conv3(int dtype, const void* x, const float* w, const float* bias, const void* carry_in,
+                                 void* y, void* carry_out, long BH, int H, int F, int N, int D, int bfr,
+                                 hipStream_t st);
+
 // Copy n0 floats src0 -> dst0 and n1 floats src1 -> dst1 (or zero both
 // destinations when `reset`) in one launch.
 hipError_t launch_carry(const float* src0, float* dst0, size_t n0, const float* src1, float* dst1,

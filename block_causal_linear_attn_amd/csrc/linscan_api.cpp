@@ -555,6 +555,52 @@ ls_status ls_gdn_frame_forward_reversed(const ls_shape* s, int chunk_frames, flo
                      workspace_bytes, stream);
 }
 
+ls_status ls_temporal_conv3(const ls_shape* s, int block_frames, const void* x, const float* weight,
+                            const float* bias, const void* carry_in, void* y, void* carry_out, void* stream) {
+  g_last_error.clear();
+  if (!s) return fail(LS_ERR_NULL_POINTER, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->F < 0 || s->N < 0)
+    return fail(LS_ERR_BAD_SHAPE, "negative dimension (B=%d H=%d F=%d N=%d)", s->B, s->H, s->F, s->N);
+  if (s->dtype != LS_DTYPE_FP32 && s->dtype != LS_DTYPE_BF16)
+    return fail(LS_ERR_BAD_DTYPE, "dtype %d is neither LS_DTYPE_FP32 nor LS_DTYPE_BF16", s->dtype);
+  const size_t esize = s->dtype == LS_DTYPE_BF16 ? 2 : 4;
+  if (s->D < 1 || s->D > 65536 || (s->D * esize) % 16 != 0)
+    return fail(LS_ERR_BAD_SHAPE, "channels D=%d must be in [1, 65536] and a multiple of %zu", s->D, 16 / esize);
+  if ((double)s->B * s->H * s->F * s->N * s->D > 4.0e18 || (double)s->B * s->H * s->N * s->D / (16 / esize) > 2.0e11)
+    return fail(LS_ERR_BAD_SHAPE, "shape too large");
+  if (block_frames < 1) return fail(LS_ERR_BAD_PARAM, "block_frames must be >= 1 (got %d)", block_frames);
+  const long BH = (long)s->B * s->H;
+  const size_t frame_bytes = (size_t)BH * s->N * s->D * esize;  // one frame of every (b, h): carry size
+  const size_t tok_bytes = frame_bytes * s->F;
+  const size_t w_bytes = (size_t)s->H * s->D * 3 * sizeof(float), b_bytes = (size_t)s->H * s->D * sizeof(float);
+  if (frame_bytes == 0) return ok();
+  if (tok_bytes > 0 && (!x || !y || !weight)) return fail(LS_ERR_NULL_POINTER, "x, y and weight are required when F > 0");
+  if (misaligned(x) || misaligned(y) || misaligned(weight) || misaligned(bias) || misaligned(carry_in) ||
+      misaligned(carry_out))
+    return fail(LS_ERR_MISALIGNED, "tensors must be 16-byte aligned");
+  const void* ins[4] = {x, weight, bias, carry_in};
+  const size_t in_n[4] = {tok_bytes, weight ? w_bytes : 0, bias ? b_bytes : 0, carry_in ? frame_bytes : 0};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(y, tok_bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "y overlaps an input");
+    if (carry_out && !(i == 3 && carry_out == carry_in) && overlap(carry_out, frame_bytes, ins[i], in_n[i]))
+      return fail(LS_ERR_ALIASING, "carry_out overlaps an input other than carry_in");
+  }
+  if (overlap(y, tok_bytes, carry_out, carry_out ? frame_bytes : 0)) return fail(LS_ERR_ALIASING, "y overlaps carry_out");
+  hipStream_t hs = (hipStream_t)stream;
+  if (s->F == 0) {  // no frames: the carried frame passes through
+    if (carry_out && carry_out != carry_in)
+      return hip_check(linscan::launch_carry((const float*)carry_in, (float*)carry_out, frame_bytes / 4, nullptr,
+                                             nullptr, 0, carry_in == nullptr, hs),
+                       "carry copy");
+    return ok();
+  }
+  const int dt = s->dtype == LS_DTYPE_BF16 ? linscan::DT_BF16 : linscan::DT_F32;
+  return hip_check(timed("temporal_conv3", hs, [&] {
+                     return linscan::launch_temporal_conv3(dt, x, weight, bias, carry_in, y, carry_out, BH, s->H,
+                                                           s->F, s->N, s->D, block_frames, hs);
+                   }), "temporal conv");
+}
+
 ls_status ls_state_carry(int B, int H, int D, const float* state_src, const float* norm_src,
                          float* state_dst, float* norm_dst, int reset, void* stream) {
   g_last_error.clear();

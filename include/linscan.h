@@ -197,6 +197,36 @@ ls_status ls_gdn_frame_forward_reversed(const ls_shape* shape, int chunk_frames,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-causal temporal convolution of kernel 3 along frames: the temporal
+ * mixing of SANA-Video's Causal Mix-FFN (practical guide, section on core
+ * mechanisms: a causal temporal convolution of kernel size 3 in the FFN;
+ * talk transcript, passage on causal FFN with temporal convolution: blocks
+ * are separated by a zero frame, so a block never sees the next one, and the
+ * last frame of a block is handed to the next block, which sees it).
+ *
+ * For every channel (h, d) and token n, with blocks of block_frames frames
+ * from frame 0 of the call,
+ *     y_f = w[h][d][0] x_{f-1} + w[h][d][1] x_f + w[h][d][2] x_{f+1} + bias[h][d]
+ * where x_{f+1} is zero when frame f ends its block or the call, and x_{-1}
+ * is carry_in (zeros when NULL).  Accumulation is fp32; bf16 outputs are
+ * rounded to nearest even.
+ *
+ *   shape       B, H, F, N and D = channels per (b, h): any multiple of 8
+ *               (bf16) or 4 (fp32) up to 65536 (not limited to head dims)
+ *   x, y        [B][H][F][N][D] of shape->dtype; y may not overlap an input
+ *   weight      [H][D][3] fp32 taps on frames f-1, f, f+1
+ *   bias        [H][D] fp32, or NULL
+ *   carry_in    [B][H][N][D] of shape->dtype, or NULL
+ *   carry_out   [B][H][N][D] of shape->dtype, or NULL: receives x_{F-1} (the
+ *               carry of the next call); may equal carry_in.  With F = 0 it
+ *               receives carry_in (or zeros).
+ * All pointers 16-byte aligned; no workspace.  block_frames < 1 is
+ * LS_ERR_BAD_PARAM; other errors as for the scans.
+ */
+ls_status ls_temporal_conv3(const ls_shape* shape, int block_frames, const void* x, const float* weight,
+                            const float* bias, const void* carry_in, void* y, void* carry_out, void* stream);
+
+/*
  * Block-autoregressive hand-off of the carried state: the state a finished
  * block leaves behind becomes the cache the next block starts from (SANA-Video
  * talk, block KV cache passage: the state of block i is cached and block i+1

@@ -128,6 +128,20 @@ def test_validation_errors_gdn_reversed(lib):
     assert r(shp, 2, wsb=need - 1) == 6
 
 
+def test_validation_errors_temporal_conv(lib):
+    def cv(shp, bf=1, x=P[0], w=P[1], b=None, ci=None, y=P[2], co=None):
+        return lib.lib.ls_temporal_conv3(ctypes.byref(shp), bf, x, w, b, ci, y, co, None)
+    assert cv(_shape(lib, D=12)) == 2                  # bf16 channels not a multiple of 8
+    assert cv(_shape(lib, D=6, dtype=0)) == 2          # fp32 channels not a multiple of 4
+    assert cv(_shape(lib, dtype=5)) == 4
+    assert cv(_shape(lib), bf=0) == 7
+    assert cv(_shape(lib), w=None) == 1
+    assert cv(_shape(lib), x=ctypes.c_void_p(A + 8)) == 5
+    assert cv(_shape(lib), y=P[0]) == 8                # y over x
+    assert cv(_shape(lib), co=P[0]) == 8               # carry_out over x
+    assert cv(_shape(lib, B=0)) == 0                   # nothing to do
+
+
 def test_in_place_state_is_not_an_aliasing_error(lib):
     """state_out == state_in is allowed; the call then fails only on the workspace check."""
     shp = _shape(lib)

@@ -461,3 +461,56 @@ def test_concurrent_streams_match_sequential(ls, gen):
         assert int(ws[:4].view(torch.int32).item()) == 0, i
         for a, b in zip(r, o):
             assert torch.equal(a, b), i
+
+
+# --------------------------------------------------------------------------- temporal conv
+CONV_CASES = [
+    # (B, H, F, N, D, dtype, block_frames, bias, carry)
+    (1, 1, 10, 500, 2240, "bf16", 10, True, True),    # FFN-width channels, one 10-frame block
+    (2, 3, 7, 33, 64, "bf16", 3, True, True),         # several blocks, ragged last block
+    (1, 2, 5, 17, 40, "fp32", 1, False, True),        # fp32, one-frame blocks
+    (1, 1, 1, 100, 128, "bf16", 1, True, False),      # a single frame, no carry
+    (1, 70, 9, 50, 32, "bf16", 4, True, True),        # per-head channels of the attention layout
+    (1, 1, 20, 64, 8, "bf16", 20, True, True),        # more frames than one register group, D = 8
+    (1, 1, 17, 40, 16, "fp32", 5, True, True),
+]
+
+
+def _conv_params(H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return 0.5 * torch.randn((H, D, 3), generator=g), 0.1 * torch.randn((H, D), generator=g)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,bf,with_bias,with_carry", CONV_CASES)
+def test_temporal_conv_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, bf, with_bias, with_carry):
+    x = gen.token_tensor(B, H, F, N, D, dt, seed=18, stream=0, part=N)
+    carry = gen.token_tensor(B, H, 1, N, D, dt, seed=18, stream=1, part=N)[:, :, 0].contiguous() if with_carry else None
+    w, b = _conv_params(H, D, 19)
+    b = b if with_bias else None
+    y, co = ls.ls_temporal_conv3(x.to(DEV), w.to(DEV), None if b is None else b.to(DEV),
+                                 None if carry is None else carry.to(DEV), block_frames=bf)
+    torch.cuda.synchronize()
+    ry, rco = oracle_mod.temporal_conv3(x, w, b, carry, block_frames=bf)
+    tag = "conv B%d H%d F%d N%d D%d %s bf%d" % (B, H, F, N, D, dt, bf)
+    check(tag + " y", y, ry, 1e-2 if dt == "bf16" else 1e-5, dt)
+    assert torch.equal(co.cpu().float(), torch.from_numpy(rco).float())
+
+
+def test_temporal_conv_blocks_chain_through_the_carry(ls, gen):
+    """Calls of one block each, carrying in place, equal one call over all blocks (bitwise)."""
+    B, H, F, N, D, bf = 1, 4, 12, 300, 96, 3
+    x = gen.token_tensor(B, H, F, N, D, "bf16", seed=20, stream=0).to(DEV)
+    w, b = (t.to(DEV) for t in _conv_params(H, D, 21))
+    carry0 = gen.token_tensor(B, H, 1, N, D, "bf16", seed=20, stream=1)[:, :, 0].contiguous().to(DEV)
+    y1, co1 = ls.ls_temporal_conv3(x, w, b, carry0, block_frames=bf)
+    carry = carry0.clone()
+    parts = []
+    for f0 in range(0, F, bf):
+        yp, _ = ls.ls_temporal_conv3(x[:, :, f0:f0 + bf].contiguous(), w, b, carry, block_frames=bf,
+                                     carry_out=carry)
+        parts.append(yp)
+    empty = torch.empty((B, H, 0, N, D), dtype=x.dtype, device=DEV)
+    _, passed = ls.ls_temporal_conv3(empty, w, b, carry, block_frames=bf)  # F = 0: the carry passes through
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts, dim=2), y1)
+    assert torch.equal(carry, co1) and torch.equal(passed, carry)
