@@ -89,6 +89,8 @@ def parse():
                     help="skip the side measurement of the GDN part with per-token update gates")
     ap.add_argument("--no-reversed", action="store_true",
                     help="skip the side measurement of the reversed GDN scan (chunks of 8 frames)")
+    ap.add_argument("--no-temporal-conv", action="store_true",
+                    help="skip the side measurement of the block-causal temporal convolution")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -226,6 +228,7 @@ def main():
     d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
     tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
+    conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -267,7 +270,7 @@ def main():
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
-                 "sana_wm_720p_60s_reversed_c8": rev},
+                 "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -370,6 +373,42 @@ def time_reversed(torch, ls, g, wg, chunk=8, reps=3):
     return {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
             "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "B1 H24 D128 F181 N920 bf16, reversed scan reset every %d frames" % chunk}
+
+
+def time_temporal_conv(torch, ls, reps=5):
+    """The Causal Mix-FFN's temporal convolution over one 10-frame block of
+    720p tokens at the hidden width (B1 F10 N3600, 2240 channels, bf16), with
+    a carried frame; two input sets alternate.  Mean kernel time over `reps` calls."""
+    dev = torch.device("cuda:0")
+    F, N, C = 10, 3600, 2240
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    xs = [torch.randn((1, 1, F, N, C), generator=g, device=dev).to(torch.bfloat16) for _ in range(2)]
+    w = 0.5 * torch.randn((1, C, 3), generator=g, device=dev)
+    b = 0.1 * torch.randn((1, C), generator=g, device=dev)
+    carry = torch.zeros((1, 1, N, C), dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty_like(x) for x in xs]
+    co = torch.empty_like(carry)
+
+    def call(i):
+        ls.ls_temporal_conv3(xs[i % 2], w, b, carry, block_frames=F, out=ys[i % 2], carry_out=co)
+
+    call(0)
+    call(1)
+    torch.cuda.synchronize()
+    # a call is ~0.1 ms, close to the binding's host time per call: the library's
+    # per-launch events time the kernel itself
+    ls.ls_profile_begin()
+    for i in range(reps):
+        call(i)
+    torch.cuda.synchronize()
+    launches, total_ms = ls.ls_profile_end()["temporal_conv3"]
+    us = 1e3 * total_ms / launches
+    nbytes = 2 * F * N * C * 2 + 2 * N * C * 2  # x read, y written, carry in and out
+    return {"us_mean": round(us, 2), "alg_bytes": nbytes,
+            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "workload": "B1 F10 N3600 C2240 bf16, one block of 10 frames with a carried frame"}
 
 
 def time_chunk_step(torch, ls, inputs):
