@@ -23,6 +23,11 @@ LS_DTYPE_BF16 = 1
 _DT = {torch.float32: LS_DTYPE_FP32, torch.bfloat16: LS_DTYPE_BF16}
 
 
+class ls_strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_longlong), ("head", ctypes.c_longlong), ("frame", ctypes.c_longlong),
+                ("token", ctypes.c_longlong)]
+
+
 class LinscanError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__("liblinscan status %d: %s" % (status, message))
@@ -53,6 +58,11 @@ def _load():
     lib.ls_gdn_frame_workspace_size.restype = Z
     lib.ls_gdn_frame_forward.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward.restype = I
+    ST = ctypes.POINTER(ls_strides)
+    lib.ls_relu_block_forward_strided.argtypes = [SP, ST, I, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_relu_block_forward_strided.restype = I
+    lib.ls_gdn_frame_forward_strided.argtypes = [SP, ST, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_gdn_frame_forward_strided.restype = I
     lib.ls_gdn_frame_forward_token_gate.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward_token_gate.restype = I
     lib.ls_gdn_frame_forward_reversed.argtypes = [SP, I, F, P, P, P, P, P, P, P, Z, P]
@@ -78,7 +88,8 @@ lib = _load()
 
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
            "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate",
-           "ls_gdn_frame_forward_reversed", "ls_temporal_conv3", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_gdn_frame_forward_reversed", "ls_temporal_conv3", "ls_relu_block_forward_strided",
+           "ls_gdn_frame_forward_strided", "ls_state_carry", "ls_status_string", "ls_last_error",
            "ls_version", "ls_profile_begin", "ls_profile_end")
 
 
@@ -108,6 +119,24 @@ def _tokens(name, t, like=None):
     if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
         raise ValueError("%s must match q in shape, dtype and device" % name)
     return t
+
+
+def _strided_tokens(name, t, like=None):
+    """A 5-D [B, H, F, N, D] view with D contiguous (any other strides), matching `like`'s strides."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 5:
+        raise ValueError("%s must be a 5-D [B, H, F, N, D] tensor (a view of any layout)" % name)
+    if t.device.type != "cuda" or t.dtype not in _DT:
+        raise ValueError("%s must be a float32 or bfloat16 GPU tensor" % name)
+    if t.shape[4] > 1 and t.stride(4) != 1:
+        raise ValueError("%s must have its last dimension contiguous" % name)
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device
+                             or t.stride() != like.stride()):
+        raise ValueError("%s must match q in shape, dtype, device and strides" % name)
+    return t
+
+
+def _layout(t) -> ls_strides:
+    return ls_strides(*t.stride()[:4])
 
 
 def _f32(name, t, shape, device):
@@ -196,6 +225,64 @@ def ls_gdn_frame_forward(q, k, v, alpha, beta, state=None, key_scale=None, out=N
     _check(lib.ls_gdn_frame_forward(ctypes.byref(shp), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                     _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
                                     _stream(dev)))
+    return o, so
+
+
+def ls_relu_block_forward_strided(q, k, v, state=None, norm=None, block_frames: int = 1, eps: float = 1e-6,
+                                  out=None, state_out=None, norm_out=None, ws=None):
+    """ls_relu_block_forward on [B, H, F, N, D] views of another layout.
+
+    q, k, v (and out) share one set of strides, with D contiguous; for
+    tensors stored [B, F, N, H, D] pass x.permute(0, 3, 1, 2, 4).  A new
+    output gets q's strides.
+    """
+    _strided_tokens("q", q)
+    _strided_tokens("k", k, q)
+    _strided_tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("state", state, (B, H, D, D), dev)
+    _f32("norm", norm, (B, H, D), dev)
+    o = out if out is not None else torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    _strided_tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    no = norm_out if norm_out is not None else torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    _f32("norm_out", no, (B, H, D), dev)
+    shp = _shape(q)
+    st = _layout(q)
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    w = ws if ws is not None else workspace(need, dev)
+    _check(lib.ls_relu_block_forward_strided(ctypes.byref(shp), ctypes.byref(st), int(block_frames), float(eps),
+                                             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so),
+                                             _ptr(no), _ptr(w), w.numel(), _stream(dev)))
+    return o, so, no
+
+
+def ls_gdn_frame_forward_strided(q, k, v, alpha, beta, state=None, key_scale=None, out=None, state_out=None,
+                                 ws=None):
+    """ls_gdn_frame_forward on [B, H, F, N, D] views of another layout (see
+    ls_relu_block_forward_strided)."""
+    _strided_tokens("q", q)
+    _strided_tokens("k", k, q)
+    _strided_tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F), dev)
+    _f32("state", state, (B, H, D, D), dev)
+    o = out if out is not None else torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    _strided_tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    shp = _shape(q)
+    st = _layout(q)
+    need = lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    w = ws if ws is not None else workspace(need, dev)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward_strided(ctypes.byref(shp), ctypes.byref(st), scale, _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(alpha), _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w),
+                                            w.numel(), _stream(dev)))
     return o, so
 
 

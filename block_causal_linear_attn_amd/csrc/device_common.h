@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.h"
+
 namespace linscan {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -50,7 +50,8 @@ constexpr int kGateLds = 2 * 64 * 4;
 template <int DI = GD, bool TG = false>
 __device__ __forceinline__ void gdn_gram_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw) {
+    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw,
+    TokLayout L) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -67,8 +68,8 @@ __device__ __forceinline__ void gdn_gram_item(
   const long bhf = wg / nc;
   const int n0 = (int)(wg % nc) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const uint16_t* kf = k + (size_t)bhf * N * DI;
-  const uint16_t* vf = v + (size_t)bhf * N * DI;
+  const uint16_t* kf = k + L.base(bhf);
+  const uint16_t* vf = v + L.base(bhf);
   const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
 
   floatx16 accG[4], accU[4];
@@ -97,7 +98,7 @@ __device__ __forceinline__ void gdn_gram_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      const size_t off = (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8;
+      const size_t off = (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8;
       X.k[r] = ld16_stream(kf + off);
       X.v[r] = ld16_stream(vf + off);
     }
@@ -222,7 +223,7 @@ constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;  // (
 template <int DI = GD, bool TG = false>
 __device__ __forceinline__ void gdn_gram_rows_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw) {
+    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw, TokLayout L) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -239,8 +240,8 @@ __device__ __forceinline__ void gdn_gram_rows_item(
   const int g = lane >> 5, col = lane & 31;
   const long bhf = item >> 2;
   const int w = (int)(item & 3);
-  const uint16_t* kf = k + (size_t)bhf * N * DI;
-  const uint16_t* vf = v + (size_t)bhf * N * DI;
+  const uint16_t* kf = k + L.base(bhf);
+  const uint16_t* vf = v + L.base(bhf);
   const int vchunk = 4 * w + (tid & 3);  // this thread's 16-byte chunk of the V rows
   const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
 
@@ -260,10 +261,10 @@ __device__ __forceinline__ void gdn_gram_rows_item(
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
       const int n = t0 + (ci >> 4);
-      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * DI + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
+      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * L.sn + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
     }
     const int n = t0 + (tid >> 2);
-    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * DI + (vchunk < CI ? vchunk : CI - 1) * 8);
+    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * L.sn + (vchunk < CI ? vchunk : CI - 1) * 8);
     if (TG) R.b = gf[t0 + (tid & 63) < N ? t0 + (tid & 63) : 0];
   };
   auto stage = [&](const Regs& R, int buf, int t0) {
@@ -602,7 +603,7 @@ constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;
 template <int DI = GD>
 __device__ __forceinline__ void gdn_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
-    int N, int nco, int chunk, long wg, uint8_t* lds_raw) {
+    int N, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -630,8 +631,8 @@ __device__ __forceinline__ void gdn_output_item(
     alo[s] = ld16(lo + off);
   }
 
-  const uint16_t* qf = q + (size_t)bhf * N * DI;
-  uint16_t* of = o + (size_t)bhf * N * DI;
+  const uint16_t* qf = q + L.base(bhf);
+  uint16_t* of = o + L.base(bhf);
   // query tiles come in through two register sets (tile t in set t % 2
   // until staged), so two tiles are in flight while one is contracted
   struct Regs {
@@ -645,7 +646,7 @@ __device__ __forceinline__ void gdn_output_item(
       const int n = t0 + tok;
       // rows past the chunk re-read its first token: their outputs are never stored
       // (dims past DI re-read a real chunk: S_f is zero in those columns)
-      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8);
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
     }
   };
   auto stage = [&](const Regs& X, int buf) {
@@ -680,7 +681,7 @@ __device__ __forceinline__ void gdn_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
-      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * DI + cb * 8, w);
+      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * L.sn + cb * 8, w);
     }
   };
   // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3

@@ -28,9 +28,9 @@ namespace {
 template <int DI, bool TG>
 __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk) {
+    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, TokLayout L) {
   __shared__ __align__(16) uint8_t lds[kGramLds + kGateLds];
-  gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds);
+  gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds, L);
 }
 
 template <bool MULTI, int DI>
@@ -48,9 +48,9 @@ __global__ __launch_bounds__(256) void gdn_scan_mfma128(
 template <int DI>
 __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
-    int N, int nco, int chunk) {
+    int N, int nco, int chunk, TokLayout L) {
   __shared__ __align__(16) uint8_t lds[kOutLds];
-  gdn_output_item<DI>(q, o, states, N, nco, chunk, blockIdx.x, lds);
+  gdn_output_item<DI>(q, o, states, N, nco, chunk, blockIdx.x, lds, L);
 }
 
 constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan item
@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
-    uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk) {
+    uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk,
+    TokLayout L) {
   constexpr int kSL = scan_lds_bytes<kFusedRB>();
   constexpr int LDS = lds_max(kGramLds + (TG ? kGateLds : 0), kSL, kOutLds);
   constexpr int NRB = kGdnFusedRowBlocks;
@@ -73,14 +74,14 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
   const long nscan = (bhp / 8) * 8 * NRB;
   if (b < nscan) {
     // eight heads x NRB row blocks per group; a head's row blocks keep its XCD
-    const long head = (b / (8 * NRB)) * 8 + (b % 8);
+    const long head = L.head_of_slot((b / (8 * NRB)) * 8 + (b % 8));
     if (head >= bh_n) return;
     gdn_scan_item<MULTI, true, kFusedRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
                                          F, nc, lds, gflags, sflags, epoch, err, 0, rchunk);
     return;
   }
   const long s = b - nscan;
-  const long bh = s % bhp;
+  const long bh = L.head_of_slot(s % bhp);
   const long u = s / bhp;  // unit: one item per head
   if (bh >= bh_n) return;
   // units of step j: the gram chunks of frame j (j < F), then the output
@@ -106,11 +107,11 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     cidx = (int)(r % nco);
   }
   if (gram) {
-    gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds);
+    gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds, L);
     publish(&gflags[(bh * F + f) * nc + cidx], epoch);
   } else {
     wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-    gdn_output_item<DI>(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds);
+    gdn_output_item<DI>(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds, L);
   }
 }
 
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nco, int chunko, uint64_t* __restrict__ gflags,
-    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk) {
+    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk, TokLayout L) {
   constexpr int RB = 32, NRB = GD / RB;
   constexpr int kSL = scan_lds_bytes<RB>();
   constexpr int LDS = lds_max(kGramRowsLds + (TG ? kGateLds : 0), kSL, kOutLds);
@@ -137,27 +138,27 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
   const long b = blockIdx.x;
   const long ngram = bhp * F * 4, nscan = bhp * NRB;
   if (b < ngram) {
-    const long bh = b % bhp, r = b / bhp;  // r = f * 4 + row block
+    const long bh = L.head_of_slot(b % bhp), r = b / bhp;  // r = f * 4 + row block
     if (bh >= bh_n) return;
     const long item = (bh * F + r / 4) * 4 + r % 4;
-    gdn_gram_rows_item<DI, TG>(k, v, beta, rec, c, c2, N, item, lds);
+    gdn_gram_rows_item<DI, TG>(k, v, beta, rec, c, c2, N, item, lds, L);
     publish(&gflags[item], epoch);
     return;
   }
   if (b < ngram + nscan) {
     const long bs = b - ngram;
-    const long head = bs % bhp;
+    const long head = L.head_of_slot(bs % bhp);
     if (head >= bh_n) return;
     gdn_scan_item<false, true, RB, DI>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
                                        sflags, epoch, err, 4, rchunk);
     return;
   }
   const long bo = b - ngram - nscan;
-  const long bh = bo % bhp, r = bo / bhp;  // r = f * nco + chunk
+  const long bh = L.head_of_slot(bo % bhp), r = bo / bhp;  // r = f * nco + chunk
   if (bh >= bh_n) return;
   const int f = (int)(r / nco);
   wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-  gdn_output_item<DI>(q, o, states, N, nco, chunko, bh * F * nco + r, lds);
+  gdn_output_item<DI>(q, o, states, N, nco, chunko, bh * F * nco + r, lds, L);
 }
 
 }  // namespace
@@ -183,18 +184,19 @@ hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags,
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
-                       sflags, epoch, err, a.rchunk);
+                       sflags, epoch, err, a.rchunk, a.L);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
-                                float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st) {
+                                float c, float c2, long bhf, int N, int nc, int chunk, const TokLayout& L,
+                                hipStream_t st) {
   return with_head_dim(D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
     auto kern = tg ? gdn_gram_mfma128<DI, true> : gdn_gram_mfma128<DI, false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)(bhf * nc)), dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
-                       gates, (uint8_t*)rec, c, c2, N, nc, chunk);
+                       gates, (uint8_t*)rec, c, c2, N, nc, chunk, L);
     return hipGetLastError();
   });
 }
@@ -215,10 +217,10 @@ hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, cons
 }
 
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
-                                  int N, int nco, int chunk, hipStream_t st) {
+                                  int N, int nco, int chunk, const TokLayout& L, hipStream_t st) {
   return with_head_dim(D, [&](auto di) {
     hipLaunchKernelGGL((gdn_output_mfma128<decltype(di)::value>), dim3((unsigned)(bhf * nco)), dim3(256), 0, st,
-                       (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk);
+                       (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk, L);
     return hipGetLastError();
   });
 }
@@ -238,7 +240,7 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,
-                       a.chunko, lag, gflags, sflags, epoch, err, a.rchunk);
+                       a.chunko, lag, gflags, sflags, epoch, err, a.rchunk, a.L);
     return hipGetLastError();
   });
 }

@@ -28,7 +28,8 @@ template <typename T, int D, bool RELU>
 __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, const T* __restrict__ v,
                                                    float* __restrict__ partial, float c, float c2,
                                                    const float* S0, const float* z0, float* init,
-                                                   const float* gate, int F, int N, int nc, int chunk) {
+                                                   const float* gate, int F, int N, int nc, int chunk,
+                                                   TokLayout L) {
   constexpr int EPT = SummarySplit<D>::kEPT;
   __shared__ float ks[GT][D + 1];
   __shared__ float vs[GT][D + 1];
@@ -39,8 +40,8 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
   const long bhf = wg / nc;
   const int n0 = (int)(wg % nc) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const T* kf = k + (size_t)bhf * N * D;
-  const T* vf = v + (size_t)bhf * N * D;
+  const T* kf = k + L.base(bhf);
+  const T* vf = v + L.base(bhf);
 
   float a1[EPT], a2[EPT];
 #pragma unroll
@@ -53,8 +54,8 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       const int n = t0 + tok;
       float kk = 0.0f, vv = 0.0f;
       if (n < n1) {
-        kk = Elem<T>::load(kf, (size_t)n * D + d);
-        vv = Elem<T>::load(vf, (size_t)n * D + d);
+        kk = Elem<T>::load(kf, (size_t)n * L.sn + d);
+        vv = Elem<T>::load(vf, (size_t)n * L.sn + d);
       }
       ks[tok][d] = RELU ? relu_f32(kk) : kk;
       vs[tok][d] = vv;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
                                                   const float* __restrict__ states,
                                                   const float* __restrict__ init, float* S_out,
                                                   float* z_out, float eps, int F, int N, int nc,
-                                                  int bfr, int nco, int chunk) {
+                                                  int bfr, int nco, int chunk, TokLayout L) {
   constexpr int SLOTS = 256 / D;
   __shared__ float Ss[D][D + 1];
   __shared__ float zs[D];
@@ -138,13 +139,13 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
     for (int e = tid; e < D * D; e += 256) Ss[e / D][e % D] = Sf[e];
   }
   const int slot = tid / D, i = tid % D;
-  const T* qf = q + (size_t)bhf * N * D;
-  T* of = o + (size_t)bhf * N * D;
+  const T* qf = q + L.base(bhf);
+  T* of = o + L.base(bhf);
   for (int t0 = n0; t0 < n1; t0 += SLOTS) {
     __syncthreads();
     if (slot < SLOTS) {
       const int n = t0 + slot;
-      float x = (n < n1) ? Elem<T>::load(qf, (size_t)n * D + i) : 0.0f;
+      float x = (n < n1) ? Elem<T>::load(qf, (size_t)n * L.sn + i) : 0.0f;
       qs[slot][i] = RELU ? relu_f32(x) : x;
     }
     __syncthreads();
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
         if (RELU) den = fmaf(zs[j], qj, den);
       }
       const float out = RELU ? num / (den + eps) : num;
-      Elem<T>::store(of, (size_t)(t0 + slot) * D + i, out);
+      Elem<T>::store(of, (size_t)(t0 + slot) * L.sn + i, out);
     }
   }
 }
@@ -166,10 +167,10 @@ hipError_t summary_launch(const GenArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.bhf * a.nc), SummarySplit<D>::kParts), block(256);
   if (a.relu)
     hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L);
   else
     hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L);
   return hipGetLastError();
 }
 
@@ -178,10 +179,11 @@ hipError_t output_launch(const GenArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.bhf * a.nco)), block(256);
   if (a.relu)
     hipLaunchKernelGGL((gen_output<T, D, true>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
-                       a.partial, a.init, a.S_out, a.z_out, a.eps, a.F, a.N, a.nc, a.bfr, a.nco, a.chunko);
+                       a.partial, a.init, a.S_out, a.z_out, a.eps, a.F, a.N, a.nc, a.bfr, a.nco, a.chunko, a.L);
   else
     hipLaunchKernelGGL((gen_output<T, D, false>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
-                       (const float*)a.states, nullptr, nullptr, nullptr, 0.0f, a.F, a.N, 1, 1, a.nco, a.chunko);
+                       (const float*)a.states, nullptr, nullptr, nullptr, 0.0f, a.F, a.N, 1, 1, a.nco, a.chunko,
+                       a.L);
   return hipGetLastError();
 }
 

@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "layout.h"
+
 namespace linscan {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };
@@ -46,6 +48,7 @@ struct ScanArgs {
   int nc = 1, chunk = 1;       // token chunks of the summary/gram pass
   int nco = 1, chunko = 1;     // token chunks of the output pass
   int bfr = 1;                 // ReLU frames per causal block
+  TokLayout L;                 // element strides of q, k, v, o
 };
 using GenArgs = ScanArgs;
 

@@ -1,0 +1,46 @@
+// layout.h -- element strides of the token tensors q, k, v, o.
+//
+// A token tensor is indexed [b][h][f][n][d] with d contiguous; the library's
+// default is the packed [B][H][F][N][D] layout, and any layout whose four
+// outer strides are given, such as [B][F][N][H][D] (frames and tokens outer,
+// heads inner), is read and written in place.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace linscan {
+
+struct TokLayout {
+  long long sb = 0, sh = 0, sf = 0, sn = 0;  // element strides of batch, head, frame, token
+  int H = 1, F = 1;
+  // Heads whose rows share 128-byte lines (layouts with heads interleaved in a
+  // token row and rows shorter than a line) run in groups of hg on one XCD, so
+  // a line is fetched into one L2 rather than into hg of them.
+  int hg = 1;
+  // element offset of token 0 of frame f of head (b, h), with bhf = (b*H + h)*F + f
+  __host__ __device__ __forceinline__ size_t base(long bhf) const {
+    const long f = bhf % F, bh = bhf / F;
+    return (size_t)((bh / H) * sb + (bh % H) * sh + f * sf);
+  }
+  // Head (b*H + h) served by work-item slot `slot` of a launch whose block ids
+  // put slot % 8 on XCD slot % 8: with hg > 1, slots 8m + x for m = hg*j ..
+  // hg*j + hg - 1 (one XCD) serve hg consecutive heads.  A bijection on
+  // [0, bhp) when bhp is a multiple of 8*hg.
+  __host__ __device__ __forceinline__ long head_of_slot(long slot) const {
+    const long m = slot / 8, x = slot % 8;
+    return hg * (8 * (m / hg) + x) + m % hg;
+  }
+  static TokLayout packed(int H, int F, int N, int D) {
+    TokLayout L;
+    L.sn = D;
+    L.sf = (long long)N * D;
+    L.sh = (long long)F * N * D;
+    L.sb = (long long)H * F * N * D;
+    L.H = H > 0 ? H : 1;
+    L.F = F > 0 ? F : 1;
+    return L;
+  }
+};
+
+}  // namespace linscan

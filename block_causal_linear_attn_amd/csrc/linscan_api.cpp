@@ -93,6 +93,65 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// The layout of the token tensors: packed [B][H][F][N][D] when `st` is NULL,
+// else the caller's element strides (D contiguous).  Strides must keep every
+// token row 16-byte aligned and map distinct (b, h, f, n) to disjoint rows:
+// sorted by stride, the dims with more than one index must nest (each stride
+// at least the previous stride times the previous extent, the smallest at
+// least D).  *span = bytes from the base to the end of the last row.
+ls_status token_layout(const ls_shape* s, const Dims& d, const ls_strides* st, linscan::TokLayout* L,
+                       size_t* span) {
+  *L = linscan::TokLayout::packed(s->H, s->F, s->N, s->D);
+  *span = d.elems * d.esize;
+  if (!st || d.elems == 0) return LS_OK;
+  const long long str[4] = {st->batch, st->head, st->frame, st->token};
+  const long long ext[4] = {s->B, s->H, s->F, s->N};
+  int idx[4] = {0, 1, 2, 3};
+  for (int i = 0; i < 4; ++i) {
+    if (str[i] < 0 || str[i] > (1LL << 40))
+      return fail(LS_ERR_BAD_PARAM, "stride %lld out of range [0, 2^40]", str[i]);
+    if ((str[i] * (long long)d.esize) % 16 != 0)
+      return fail(LS_ERR_MISALIGNED, "stride %lld elements is not a multiple of 16 bytes", str[i]);
+  }
+  for (int i = 1; i < 4; ++i)  // insertion sort of the dims by stride
+    for (int j = i; j > 0 && str[idx[j]] < str[idx[j - 1]]; --j) {
+      const int t = idx[j];
+      idx[j] = idx[j - 1];
+      idx[j - 1] = t;
+    }
+  long long need = s->D;  // the next stride that keeps rows disjoint
+  double last = 0.0;      // element offset of the last row
+  for (int i = 0; i < 4; ++i) {
+    const int k = idx[i];
+    if (ext[k] <= 1) continue;
+    if (str[k] < need)
+      return fail(LS_ERR_BAD_PARAM, "strides overlap rows: stride %lld < %lld", str[k], need);
+    need = str[k] * ext[k];
+    last += (double)str[k] * (double)(ext[k] - 1);
+  }
+  if ((last + s->D) * d.esize > 4.0e18) return fail(LS_ERR_BAD_SHAPE, "strided span too large");
+  L->sb = st->batch;
+  L->sh = st->head;
+  L->sf = st->frame;
+  L->sn = st->token;
+  // heads adjacent in a token row with rows that do not fill whole 128-byte
+  // lines share lines with their neighbours: group them onto one XCD, when
+  // there are enough groups (4 per XCD) to keep the XCDs evenly loaded
+  const long long row = (long long)s->D * d.esize;
+  if (s->H > 1 && st->head == s->D && row % 128 != 0) {
+    long long a = row, b = 128;
+    while (b) {
+      const long long t = a % b;
+      a = b;
+      b = t;
+    }
+    const int hg = (int)(128 / a);
+    if (d.bh / hg >= 32) L->hg = hg;
+  }
+  *span = (size_t)((last + s->D) * d.esize);
+  return LS_OK;
+}
+
 // Token chunking: enough workgroups to fill 256 CUs several times over, with
 // chunks of at least `min_chunk` tokens (a multiple of `quantum`).
 void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, int* nc, int* chunk) {
@@ -311,10 +370,11 @@ size_t ls_gdn_frame_workspace_size(const ls_shape* s) {
   return gdn_plan(s, d).bytes;
 }
 
-ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, const void* q,
-                                const void* k, const void* v, void* o, const float* state_in,
-                                const float* norm_in, float* state_out, float* norm_out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Both ReLU entry points: packed token tensors (strides NULL) or strided ones.
+static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int block_frames, float eps,
+                              const void* q, const void* k, const void* v, void* o, const float* state_in,
+                              const float* norm_in, float* state_out, float* norm_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   Dims d;
   ls_status st = check_shape(s, &d);
@@ -322,7 +382,9 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   if (block_frames < 1) return fail(LS_ERR_BAD_PARAM, "block_frames=%d < 1", block_frames);
   if (!(eps > 0.0f) || !isfinite(eps)) return fail(LS_ERR_BAD_PARAM, "eps=%g must be finite and > 0", (double)eps);
   const int D = s->D;
-  const size_t tok_bytes = d.elems * d.esize;
+  linscan::TokLayout layout;
+  size_t tok_bytes = 0;  // bytes each token tensor spans
+  if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t norm_bytes = (size_t)d.bh * D * sizeof(float);
   if (d.bh == 0) return ok();
@@ -398,8 +460,9 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
   a.nco = p.nco;
   a.chunko = p.chunko;
   a.bfr = block_frames;
+  a.L = layout;
   if (p.fused) {
-    const long bhp = (d.bh + 7) / 8 * 8;
+    const long bhp = (d.bh + 8 * layout.hg - 1) / (8 * layout.hg) * (8 * layout.hg);
     uint64_t* flags = (uint64_t*)(ws + p.flags_off);
     uint32_t* err = (uint32_t*)ws;
     const uint64_t epoch = next_epoch();
@@ -422,17 +485,19 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
 // The GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
 // token ([B*H*F][N]); rchunk > 0 runs the reversed scan in chunks of rchunk
 // frames (no state in or out).
-static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, const void* k, const void* v,
-                             const float* alpha, const float* beta, bool token_gate, int rchunk, void* o,
-                             const float* state_in, float* state_out, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, float key_scale, const void* q,
+                             const void* k, const void* v, const float* alpha, const float* beta, bool token_gate,
+                             int rchunk, void* o, const float* state_in, float* state_out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   Dims d;
   ls_status st = check_shape(s, &d);
   if (st != LS_OK) return st;
   if (!isfinite(key_scale)) return fail(LS_ERR_BAD_PARAM, "key_scale is not finite");
   const int D = s->D;
-  const size_t tok_bytes = d.elems * d.esize;
+  linscan::TokLayout layout;
+  size_t tok_bytes = 0;  // bytes each token tensor spans
+  if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t gate_bytes = (size_t)d.bhf * (token_gate ? (size_t)s->N : 1) * sizeof(float);
   const size_t alpha_bytes = (size_t)d.bhf * sizeof(float);
@@ -491,6 +556,7 @@ static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, 
   a.gate = token_gate ? beta : nullptr;
   a.tg = token_gate;
   a.rchunk = rchunk;
+  a.L = layout;
   a.S0 = state_in;
   a.S_out = state_out;
   a.partial = (float*)(ws + p.partial_off);
@@ -506,7 +572,7 @@ static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, 
   a.nco = p.nco;
   a.chunko = p.chunko;
   if (p.fused || p.phased) {
-    const long bhp = (d.bh + 7) / 8 * 8;
+    const long bhp = (d.bh + 8 * layout.hg - 1) / (8 * layout.hg) * (8 * layout.hg);
     uint64_t* gflags = (uint64_t*)(ws + p.gflags_off);
     uint64_t* sflags = (uint64_t*)(ws + p.sflags_off);
     uint32_t* err = (uint32_t*)ws;
@@ -530,11 +596,35 @@ static ls_status gdn_forward(const ls_shape* s, float key_scale, const void* q, 
   return ok();
 }
 
+ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, const void* q,
+                                const void* k, const void* v, void* o, const float* state_in,
+                                const float* norm_in, float* state_out, float* norm_out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return relu_forward(s, nullptr, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out, workspace,
+                      workspace_bytes, stream);
+}
+
+ls_status ls_relu_block_forward_strided(const ls_shape* s, const ls_strides* strides, int block_frames, float eps,
+                                        const void* q, const void* k, const void* v, void* o,
+                                        const float* state_in, const float* norm_in, float* state_out,
+                                        float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return relu_forward(s, strides, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out, workspace,
+                      workspace_bytes, stream);
+}
+
+ls_status ls_gdn_frame_forward_strided(const ls_shape* s, const ls_strides* strides, float key_scale, const void* q,
+                                       const void* k, const void* v, const float* alpha, const float* beta, void* o,
+                                       const float* state_in, float* state_out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return gdn_forward(s, strides, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+                     workspace_bytes, stream);
+}
+
 ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
                                const void* v, const float* alpha, const float* beta, void* o,
                                const float* state_in, float* state_out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
                      workspace_bytes, stream);
 }
 
@@ -542,7 +632,7 @@ ls_status ls_gdn_frame_forward_token_gate(const ls_shape* s, float key_scale, co
                                           const void* v, const float* alpha, const float* beta, void* o,
                                           const float* state_in, float* state_out, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, key_scale, q, k, v, alpha, beta, true, 0, o, state_in, state_out, workspace,
+  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, true, 0, o, state_in, state_out, workspace,
                      workspace_bytes, stream);
 }
 
@@ -551,8 +641,8 @@ ls_status ls_gdn_frame_forward_reversed(const ls_shape* s, int chunk_frames, flo
                                         void* o, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (chunk_frames < 1) return fail(LS_ERR_BAD_PARAM, "chunk_frames must be >= 1 (got %d)", chunk_frames);
-  return gdn_forward(s, key_scale, q, k, v, alpha, beta, false, chunk_frames, o, nullptr, nullptr, workspace,
-                     workspace_bytes, stream);
+  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, false, chunk_frames, o, nullptr, nullptr,
+                     workspace, workspace_bytes, stream);
 }
 
 ls_status ls_temporal_conv3(const ls_shape* s, int block_frames, const void* x, const float* weight,

@@ -36,7 +36,7 @@ template <int D>
 __device__ __forceinline__ void relu_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
     const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk,
-    long wg, uint8_t* lds_raw) {
+    long wg, uint8_t* lds_raw, TokLayout L) {
   constexpr int DB = D / 32;            // 32-wide dimension blocks
   constexpr int TILE = 64;              // tokens per wave per step
   constexpr int ROW = D;                // unpadded rows, chunks swizzled by token
@@ -51,8 +51,8 @@ __device__ __forceinline__ void relu_summary_item(
   const long bhf = wg / nc;
   const int n0 = (int)(wg % nc) * chunk;
   const int n1 = min(N, n0 + chunk);
-  const uint16_t* kf = k + (size_t)bhf * N * D;
-  const uint16_t* vf = v + (size_t)bhf * N * D;
+  const uint16_t* kf = k + L.base(bhf);
+  const uint16_t* vf = v + L.base(bhf);
   uint16_t* kl = lds[wave][0];
   uint16_t* vl = lds[wave][1];
 
@@ -76,7 +76,7 @@ __device__ __forceinline__ void relu_summary_item(
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 64 + lane;
       const int n = t0 + ci / CPR, cb = ci % CPR;
-      const size_t off = (size_t)(n < n1 ? n : n0) * D + cb * 8;
+      const size_t off = (size_t)(n < n1 ? n : n0) * L.sn + cb * 8;
       kr[r] = ld16(kf + off);
       vr[r] = ld16(vf + off);
     }
@@ -163,7 +163,7 @@ template <int D>
 __device__ __forceinline__ void relu_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
     const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
-    int bfr, int nco, int chunk, long wg, uint8_t* lds_raw) {
+    int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
   constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
   constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
   constexpr int U = 4;        // 32-token groups per wave per step
@@ -215,15 +215,15 @@ __device__ __forceinline__ void relu_output_item(
 #pragma unroll
     for (int e = 0; e < 8; ++e) zr[s][e] = zs[s * 16 + g * 8 + e];
 
-  const uint16_t* qf = q + (size_t)bhf * N * D;
-  uint16_t* of = o + (size_t)bhf * N * D;
+  const uint16_t* qf = q + L.base(bhf);
+  uint16_t* of = o + L.base(bhf);
   // U groups of 32 tokens per wave; the next step's query fragments are in
   // flight while the current ones are contracted
   auto load = [&](u32x4 (&b)[U][KS], int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 32 + col;
-      const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * D + g * 8;
+      const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * L.sn + g * 8;
 #pragma unroll
       for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
     }
@@ -275,7 +275,7 @@ __device__ __forceinline__ void relu_output_item(
         const int tl = i * TPI + lane / LPR, cb = lane % LPR;
         const u32x4 w = *reinterpret_cast<const u32x4*>(ost + tl * OP + cb * 8);
         const int tt = t0 + u * 32 + tl;
-        if (full || tt < n1) st16(of + (size_t)tt * D + cb * 8, w);
+        if (full || tt < n1) st16(of + (size_t)tt * L.sn + cb * 8, w);
       }
       __builtin_amdgcn_wave_barrier();
     }

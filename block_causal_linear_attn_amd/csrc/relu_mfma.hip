@@ -1,5 +1,5 @@
-// relu_mfma.hip -- kernels and launchers of the bf16 MFMA ReLU linear-attention
-// scan (head dims 32 and 64), built from the work items in relu_items.h.
+// relu_mfma.hip -- the single-launch bf16 MFMA ReLU linear-attention scan
+// (head dims 32 and 64), built from the work items in relu_items.h.
 //
 // relu_fused_mfma runs one call in a single launch: summary items of each
 // frame interleaved with output items of earlier frames.  An output item waits (bounded spin)
@@ -7,9 +7,7 @@
 // head are published; since every item it waits on has a lower block id and
 // block ids dispatch in order, those items are running or done, so the wait
 // ends.  Every item of a head gets block ids equal to the head modulo 8, so
-// they share one XCD and exchange partials through its L2.  The separate
-// summary and output kernels remain for shapes where a single launch does not
-// apply.
+// they share one XCD and exchange partials through its L2.
 #include "relu_items.h"
 #include "kernels.h"
 #include "sync.h"
@@ -17,23 +15,6 @@
 namespace linscan {
 
 namespace {
-
-template <int D>
-__global__ __launch_bounds__(256, 2) void relu_summary_mfma(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
-    const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk) {
-  __shared__ __align__(16) uint8_t lds[relu_summary_lds_bytes<D>()];
-  relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, nc, chunk, blockIdx.x, lds);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void relu_output_mfma(
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
-    const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
-    int bfr, int nco, int chunk) {
-  __shared__ __align__(16) uint8_t lds[relu_output_lds_bytes<D>()];
-  relu_output_item<D>(q, o, partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk, blockIdx.x, lds);
-}
 
 // Block ids run over steps j = 0, 1, ...: step j holds the summary items of
 // frame j (one per head, whole frame) and then the output items of frame
@@ -47,12 +28,12 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
     const float* z0, float* S_out, float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr,
-    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err) {
+    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L) {
   constexpr int LDS = relu_summary_lds_bytes<D>() > relu_output_lds_bytes<D>() ? relu_summary_lds_bytes<D>()
                                                                                 : relu_output_lds_bytes<D>();
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
-  const long bh = b % bhp;
+  const long bh = L.head_of_slot(b % bhp);
   const long u = b / bhp;  // unit: one item per head
   if (bh >= bh_n) return;
   const long head_units = lag, mid_units = (long)(F - lag) * (1 + nco);
@@ -73,48 +54,18 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     c = (int)(r % nco);
   }
   if (summary) {
-    relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds);
+    relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L);
     publish(&flags[bh * F + f], epoch);
     return;
   }
   const int fend = min(F, (f / bfr + 1) * bfr);
   wait_all(&flags[bh * F], fend, epoch, err);
   relu_output_item<D>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
-                      (bh * F + f) * nco + c, lds);
+                      (bh * F + f) * nco + c, lds, L);
 }
 
 }  // namespace
 bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D == 64 || relu_wide_mfma(D, dtype)); }
-
-hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
-                                    const float* S0, const float* z0, float* init, long bhf, int F,
-                                    int N, int nc, int chunk, hipStream_t st) {
-  dim3 grid((unsigned)(bhf * nc)), block(256);
-  if (D == 32)
-    hipLaunchKernelGGL(relu_summary_mfma<32>, grid, block, 0, st, (const uint16_t*)k,
-                       (const uint16_t*)v, partial, S0, z0, init, F, N, nc, chunk);
-  else if (D == 64)
-    hipLaunchKernelGGL(relu_summary_mfma<64>, grid, block, 0, st, (const uint16_t*)k,
-                       (const uint16_t*)v, partial, S0, z0, init, F, N, nc, chunk);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* partial,
-                                   const float* init, float* S_out, float* z_out, float eps, long bhf,
-                                   int F, int N, int nc, int bfr, int nco, int chunk, hipStream_t st) {
-  dim3 grid((unsigned)(bhf * nco)), block(256);
-  if (D == 32)
-    hipLaunchKernelGGL(relu_output_mfma<32>, grid, block, 0, st, (const uint16_t*)q, (uint16_t*)o,
-                       partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk);
-  else if (D == 64)
-    hipLaunchKernelGGL(relu_output_mfma<64>, grid, block, 0, st, (const uint16_t*)q, (uint16_t*)o,
-                       partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunk);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
 
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
@@ -125,12 +76,12 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
     hipLaunchKernelGGL(relu_fused_mfma<32>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
                        a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
-                       epoch, err);
+                       epoch, err, a.L);
   else if (a.D == 64)
     hipLaunchKernelGGL(relu_fused_mfma<64>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
                        a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
-                       epoch, err);
+                       epoch, err, a.L);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -69,7 +69,7 @@ template <int DI>
 __device__ __forceinline__ void relu_wide_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ cum,
     const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f,
-    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw) {
+    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -82,8 +82,8 @@ __device__ __forceinline__ void relu_wide_summary_item(
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, col = lane & 31;
   const long bhf = bh * F + f;
-  const uint16_t* kf = k + (size_t)bhf * N * DI;
-  const uint16_t* vf = v + (size_t)bhf * N * DI;
+  const uint16_t* kf = k + L.base(bhf);
+  const uint16_t* vf = v + L.base(bhf);
 
   // z: with DI < 128, value dim DI (zero padding) is set to 1 for every live
   // token, so row DI of dS is dz at no cost; at DI = 128 an MFMA with an
@@ -111,7 +111,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      const size_t off = (size_t)(n < N ? n : 0) * DI + (cb < CI ? cb : CI - 1) * 8;
+      const size_t off = (size_t)(n < N ? n : 0) * L.sn + (cb < CI ? cb : CI - 1) * 8;
       X.k[r] = ld16_stream(kf + off);
       X.v[r] = ld16_stream(vf + off);
     }
@@ -228,7 +228,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
 template <int DI>
 __device__ __forceinline__ void relu_wide_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ cum, float eps,
-    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw) {
+    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -272,8 +272,8 @@ __device__ __forceinline__ void relu_wide_output_item(
     zr[4] = z1.x, zr[5] = z1.y, zr[6] = z1.z, zr[7] = z1.w;
   }
 
-  const uint16_t* qf = q + (size_t)bhf * N * DI;
-  uint16_t* of = o + (size_t)bhf * N * DI;
+  const uint16_t* qf = q + L.base(bhf);
+  uint16_t* of = o + L.base(bhf);
   struct Regs {
     u32x4 q[LPT];
   };
@@ -285,7 +285,7 @@ __device__ __forceinline__ void relu_wide_output_item(
       const int n = t0 + tok;
       // rows past the chunk re-read its first token: their outputs are never
       // stored; dims past DI re-read a real chunk and are zeroed when staged
-      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * DI + (cb < CI ? cb : CI - 1) * 8);
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
     }
   };
   // phi(q) into LDS buffer buf, and each token's denominator into den[buf]
@@ -326,7 +326,7 @@ __device__ __forceinline__ void relu_wide_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const u32x4 w = *reinterpret_cast<const u32x4*>(&ost[it & 1][tok * ROW + cb * 8]);
-      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * DI + cb * 8, w);
+      if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * L.sn + cb * 8, w);
     }
   };
   // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3

@@ -16,18 +16,13 @@
 
 namespace linscan {
 
-hipError_t launch_relu_summary_mfma(int D, const void* k, const void* v, float* partial,
-                                    const float* S0, const float* z0, float* init, long bhf, int F,
-                                    int N, int nc, int chunk, hipStream_t st);
-hipError_t launch_relu_output_mfma(int D, const void* q, void* o, const float* partial,
-                                   const float* init, float* S_out, float* z_out, float eps, long bhf,
-                                   int F, int N, int nc, int bfr, int nco, int chunk, hipStream_t st);
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
-                                float c, float c2, long bhf, int N, int nc, int chunk, hipStream_t st);
+                                float c, float c2, long bhf, int N, int nc, int chunk, const TokLayout& L,
+                                hipStream_t st);
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
                                 void* states, float* S_out, long bh, int F, int nc, int rchunk, hipStream_t st);
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
-                                  int N, int nco, int chunk, hipStream_t st);
+                                  int N, int nco, int chunk, const TokLayout& L, hipStream_t st);
 
 namespace {
 
@@ -168,24 +163,21 @@ int fused_lag(long slots, long items_per_step, int min_lag, int F) {
   return lag < 1 ? 1 : (int)lag;
 }
 
+// bf16 MFMA head dims always run the single-launch kernels
 hipError_t launch_relu_summary(const ScanArgs& a, hipStream_t st) {
-  if (a.mfma)
-    return launch_relu_summary_mfma(a.D, a.k, a.v, a.partial, a.S0, a.z0, a.init, a.bhf, a.F, a.N,
-                                    a.nc, a.chunk, st);
+  if (a.mfma) return hipErrorInvalidValue;
   return launch_summary_generic(a, st);
 }
 
 hipError_t launch_relu_output(const ScanArgs& a, hipStream_t st) {
-  if (a.mfma)
-    return launch_relu_output_mfma(a.D, a.q, a.o, a.partial, a.init, a.S_out, a.z_out, a.eps, a.bhf,
-                                   a.F, a.N, a.nc, a.bfr, a.nco, a.chunko, st);
+  if (a.mfma) return hipErrorInvalidValue;
   return launch_output_generic(a, st);
 }
 
 hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st) {
   if (a.mfma)
     return launch_gdn_gram_mfma(a.D, a.k, a.v, a.tg ? a.gate : a.beta, a.tg, a.partial, a.c, a.c2, a.bhf, a.N, a.nc,
-                                a.chunk, st);
+                                a.chunk, a.L, st);
   return launch_summary_generic(a, st);
 }
 
@@ -202,7 +194,7 @@ hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st) {
-  if (a.mfma) return launch_gdn_output_mfma(a.D, a.q, a.o, a.states, a.bhf, a.N, a.nco, a.chunko, st);
+  if (a.mfma) return launch_gdn_output_mfma(a.D, a.q, a.o, a.states, a.bhf, a.N, a.nco, a.chunko, a.L, st);
   return launch_output_generic(a, st);
 }
 

@@ -24,7 +24,8 @@
  * ---------------------------------------
  *  - Token tensors q, k, v, o are contiguous [B][H][F][N][D], D fastest,
  *    either fp32 or bf16 (ls_shape.dtype); o has the dtype of the inputs and
- *    bf16 outputs are rounded to nearest even from fp32.
+ *    bf16 outputs are rounded to nearest even from fp32.  The *_strided
+ *    entry points take other layouts (ls_strides below).
  *  - The state S is fp32 [B][H][D][D] with S[i][j], i a value dimension and
  *    j a key dimension, so that a query reads o = S q.  The ReLU normaliser
  *    z is fp32 [B][H][D].  Gates alpha, beta are fp32 [B][H][F].
@@ -39,8 +40,9 @@
  *    the status names the reason (ls_last_error() gives details).  A device
  *    fault surfaces at the caller's next synchronisation.
  *  - The first 4 bytes of a workspace are its fault word.  Calls that run
- *    as a single launch (bf16 at head dims 32/64 for the ReLU scan, bf16 at
- *    head dim 128 for the GDN scan whenever it has tokens) hand data between
+ *    as a single launch (bf16 at head dims 32, 64, 112 and 128 for the ReLU
+ *    scan, bf16 at head dims 112 and 128 for the GDN scan whenever it has
+ *    tokens) hand data between
  *    their work items through flags with bounded waits; if a wait ever gave
  *    up, the call's results are invalid and the fault word becomes nonzero.
  *    The library never clears it; callers that check it zero it beforehand.
@@ -95,6 +97,21 @@ typedef struct {
 } ls_shape;
 
 /*
+ * Element strides of the token tensors q, k, v and o (all four share them;
+ * D stays contiguous), for the *_strided entry points: element (b, h, f, n, d)
+ * sits at b*batch + h*head + f*frame + n*token + d.  For example [B][F][N][H][D]
+ * (tokens of all heads interleaved) has token = H*D, head = D, frame = N*H*D,
+ * batch = F*N*H*D.  Each stride times the element size must be a multiple of
+ * 16 bytes (LS_ERR_MISALIGNED), and distinct (b, h, f, n) must map to
+ * disjoint rows: sorted by stride, the dimensions with more than one index
+ * must nest, each stride at least the previous stride times the previous
+ * extent and the smallest at least D (LS_ERR_BAD_PARAM otherwise).
+ */
+typedef struct {
+  long long batch, head, frame, token;
+} ls_strides;
+
+/*
  * Workspace bytes ls_relu_block_forward needs for `shape` and `block_frames`
  * (0 if the shape is invalid).  The size depends on the shape only.
  */
@@ -127,6 +144,18 @@ ls_status ls_relu_block_forward(const ls_shape* shape, int block_frames, float e
                                 float* state_out, float* norm_out,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ls_relu_block_forward with token tensors in the layout `strides` (NULL:
+ * packed [B][H][F][N][D]).  Workspace size and everything else as there.
+ * Layouts that interleave heads inside a token row ([B][F][N][H][D]) share
+ * 128-byte lines between heads at D = 32, which the kernels read from
+ * different work items.
+ */
+ls_status ls_relu_block_forward_strided(const ls_shape* shape, const ls_strides* strides, int block_frames,
+                                        float eps, const void* q, const void* k, const void* v, void* o,
+                                        const float* state_in, const float* norm_in, float* state_out,
+                                        float* norm_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes ls_gdn_frame_forward needs for `shape` (0 if invalid). */
 size_t ls_gdn_frame_workspace_size(const ls_shape* shape);
 
@@ -153,6 +182,16 @@ ls_status ls_gdn_frame_forward(const ls_shape* shape, float key_scale,
                                const float* alpha, const float* beta, void* o,
                                const float* state_in, float* state_out,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ls_gdn_frame_forward with token tensors in the layout `strides` (NULL:
+ * packed [B][H][F][N][D]).  Workspace size and everything else as there.
+ */
+ls_status ls_gdn_frame_forward_strided(const ls_shape* shape, const ls_strides* strides, float key_scale,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta, void* o,
+                                       const float* state_in, float* state_out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Frame-wise Gated DeltaNet with a per-token update gate (SANA-WM summary,

@@ -142,6 +142,23 @@ def test_validation_errors_temporal_conv(lib):
     assert cv(_shape(lib, B=0)) == 0                   # nothing to do
 
 
+def test_validation_errors_strided(lib):
+    shp = _shape(lib, B=1, H=4, F=3, N=10, D=32)
+    def rs(st, wsb=1):
+        return lib.lib.ls_relu_block_forward_strided(ctypes.byref(shp), ctypes.byref(st), 1, 1e-6, P[0], P[1], P[2],
+                                                     P[3], None, None, P[4], P[5], P[6], wsb, None)
+    def gs(st, wsb=1):
+        return lib.lib.ls_gdn_frame_forward_strided(ctypes.byref(shp), ctypes.byref(st), 0.0, P[0], P[1], P[2],
+                                                    P[7], P[8], P[3], None, P[4], P[6], wsb, None)
+    S = lib.ls_strides
+    bshd = S(3 * 10 * 4 * 32, 32, 10 * 4 * 32, 4 * 32)          # [B][F][N][H][D]
+    assert rs(bshd) == 6 and gs(bshd) == 6                        # valid: fails only on the workspace
+    assert rs(S(3 * 10 * 4 * 32, 32, 10 * 4 * 32, 3 * 32)) == 7   # token stride too small for 4 heads
+    assert gs(S(3 * 10 * 4 * 32, 16, 10 * 4 * 32, 4 * 32)) == 7   # head rows of 32 at stride 16 overlap
+    assert rs(S(3 * 10 * 4 * 32, 36, 10 * 4 * 36, 4 * 36)) == 5   # 72-byte strides: rows not 16-byte aligned
+    assert rs(S(-1, 32, 10 * 4 * 32, 4 * 32)) == 7
+
+
 def test_in_place_state_is_not_an_aliasing_error(lib):
     """state_out == state_in is allowed; the call then fails only on the workspace check."""
     shp = _shape(lib)

@@ -514,3 +514,43 @@ def test_temporal_conv_blocks_chain_through_the_carry(ls, gen):
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(parts, dim=2), y1)
     assert torch.equal(carry, co1) and torch.equal(passed, carry)
+
+
+# --------------------------------------------------------------------------- strided token layouts
+def _bshd(x):
+    """A [B, H, F, N, D] view of a copy of x stored [B, F, N, H, D] (heads interleaved in each token)."""
+    return x.permute(0, 2, 3, 1, 4).contiguous().permute(0, 3, 1, 2, 4)
+
+
+@pytest.mark.parametrize("H,F,N,D,dt", [(5, 4, 333, 32, "bf16"), (3, 3, 200, 112, "bf16"), (2, 3, 300, 128, "bf16"),
+                                        (2, 3, 50, 16, "bf16"), (2, 3, 40, 48, "fp32")])
+def test_relu_strided_layout(ls, gen, oracle_mod, H, F, N, D, dt):
+    """[B, F, N, H, D] storage matches the oracle and, bit for bit, the packed call."""
+    x = gen.relu_inputs(1, H, F, N, D, dt, seed=41, part=N)
+    xd = _dev(x)
+    o1, S1, z1 = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], block_frames=2)
+    q, k, v = (_bshd(xd[n]) for n in ("q", "k", "v"))
+    o2, S2, z2 = ls.ls_relu_block_forward_strided(q, k, v, block_frames=2)
+    torch.cuda.synchronize()
+    assert o2.stride() == q.stride()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], block_frames=2)
+    tag = "relu strided H%d F%d N%d D%d %s" % (H, F, N, D, dt)
+    check(tag + " o", o2, ro, TOL[dt][0], dt)
+    check(tag + " S", S2, rS, TOL[dt][1], dt)
+    assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1) and torch.equal(z2, z1)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt", [(1, 3, 4, 300, 128, "bf16"), (1, 40, 2, 130, 128, "bf16"),
+                                          (2, 2, 3, 97, 112, "bf16"), (1, 2, 3, 80, 64, "bf16")])
+def test_gdn_strided_layout(ls, gen, oracle_mod, B, H, F, N, D, dt):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=42, part=N, l2_keys=True)
+    xd = _dev(x)
+    o1, S1 = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"])
+    q, k, v = (_bshd(xd[n]) for n in ("q", "k", "v"))
+    o2, S2 = ls.ls_gdn_frame_forward_strided(q, k, v, xd["alpha"], xd["beta"])
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    tag = "gdn strided B%d H%d F%d N%d D%d %s" % (B, H, F, N, D, dt)
+    check(tag + " o", o2, ro, TOL[dt][0], dt)
+    check(tag + " S", S2, rS, TOL[dt][1], dt)
+    assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1)
