@@ -91,6 +91,8 @@ def parse():
                     help="skip the side measurement of the reversed GDN scan (chunks of 8 frames)")
     ap.add_argument("--no-temporal-conv", action="store_true",
                     help="skip the side measurement of the block-causal temporal convolution")
+    ap.add_argument("--no-strided", action="store_true",
+                    help="skip the side measurement of the strided [B][F][N][H][D] layout")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -229,6 +231,7 @@ def main():
     tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
     conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
+    strided = None if args.no_strided else time_strided(torch, ls, calls[0], g)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -270,7 +273,8 @@ def main():
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
-                 "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv},
+                 "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv,
+                 "bshd_layout": strided},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -409,6 +413,41 @@ def time_temporal_conv(torch, ls, reps=5):
             "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "B1 F10 N3600 C2240 bf16, one block of 10 frames with a carried frame"}
+
+
+def time_strided(torch, ls, relu_call, g, reps=4):
+    """One 10-frame ReLU call of the rollout and the GDN call with q, k, v, o
+    stored [B][F][N][H][D] (heads interleaved in every token row), against
+    the same calls on the packed layout; mean kernel time from the library's
+    per-launch events."""
+    def bshd(x):
+        return x.permute(0, 2, 3, 1, 4).contiguous().permute(0, 3, 1, 2, 4)
+
+    def kernel_us(fn, name):
+        fn()
+        torch.cuda.synchronize()
+        ls.ls_profile_begin()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        n, ms = ls.ls_profile_end()[name]
+        return round(1e3 * ms / n, 2)
+
+    res = {}
+    r = relu_call
+    rs = {n: bshd(r[n]) for n in ("q", "k", "v")}
+    res["relu_h70_d32_10_frames_us"] = {
+        "packed": kernel_us(lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused"),
+        "bshd": kernel_us(lambda: ls.ls_relu_block_forward_strided(rs["q"], rs["k"], rs["v"]), "relu_fused")}
+    del rs
+    gs = {n: bshd(g[n]) for n in ("q", "k", "v")}
+    res["gdn_h24_d128_181_frames_us"] = {
+        "packed": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"]),
+                            "gdn_fused"),
+        "bshd": kernel_us(lambda: ls.ls_gdn_frame_forward_strided(gs["q"], gs["k"], gs["v"], g["alpha"], g["beta"]),
+                          "gdn_fused")}
+    del gs
+    return res
 
 
 def time_chunk_step(torch, ls, inputs):
