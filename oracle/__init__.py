@@ -202,3 +202,35 @@ def temporal_conv3(x, weight, bias=None, carry=None, block_frames: int = 1, with
     if rc != 0:
         raise RuntimeError("oracle_temporal_conv3 failed with code %d" % rc)
     return y, co
+
+
+def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = False, round_to=None):
+    """The per-token prologue fused into the scans' load stage, fp64.
+
+    The SANA-WM digest (paragraph on context parallelism and the fused kernel)
+    fuses RMSNorm, ReLU and the key scaling into the GDN scan; SANA-Video's
+    linear attention normalises q and k (qk_norm) before its ReLU feature map.
+    Per token row x (the D channels of one head):
+      RMSNorm:  x <- x / sqrt(mean(x^2) + eps) * weight[h]   (when weight is given)
+      ReLU:     x <- max(x, 0)                               (when relu)
+      L2:       x <- x / |x|  (0 stays 0)                     (when l2)
+    x: [B, H, F, N, D]; weight: [H, D] or None.  round_to = "bf16" rounds the
+    result to bfloat16 (nearest even), the precision in which the scan
+    consumes it for bf16 tokens.  Returns float64 (or the rounded values as
+    float64).
+    """
+    x = np.asarray(_f32(x), dtype=np.float64)
+    y = x
+    if weight is not None:
+        w = np.asarray(_f32(weight), dtype=np.float64)
+        ms = np.mean(y * y, axis=-1, keepdims=True)
+        y = y / np.sqrt(ms + eps) * w[None, :, None, None, :]
+    if relu:
+        y = np.where(np.signbit(y), 0.0, y)
+    if l2:
+        nrm = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
+        y = np.where(nrm > 0, y / np.where(nrm > 0, nrm, 1.0), 0.0)
+    if round_to == "bf16":
+        import torch
+        y = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    return y
