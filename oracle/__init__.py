@@ -231,6 +231,27 @@ def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = F
         nrm = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
         y = np.where(nrm > 0, y / np.where(nrm > 0, nrm, 1.0), 0.0)
     if round_to == "bf16":
-        import torch
-        y = torch.from_numpy(y).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+        y = round_bf16(y)
     return y
+
+
+def round_bf16(y):
+    """Round float64 values to the nearest bfloat16 value, ties to the even one.
+
+    One rounding from the exact float64 value: of the two bfloat16 neighbours
+    (the value cut to its top 8 significant bits, and that plus one bfloat16
+    step away from zero) take the nearer, and on a tie the one whose last kept
+    bit is 0.  (Going through float32 first would round twice: a value just
+    past a halfway point can land on it and then go to the even side.)
+    Finite values in the normal float32 range.  Returns float64.
+    """
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float64))
+    bits = y.view(np.uint64)
+    drop = np.uint64((1 << 45) - 1)                  # fraction bits below bfloat16's 7
+    lo_bits = bits & ~drop
+    lo = lo_bits.view(np.float64)                     # toward zero
+    hi = (lo_bits + np.uint64(1 << 45)).view(np.float64)  # one step away from zero
+    d_lo = np.abs(y - lo)                             # both differences are exact
+    d_hi = np.abs(hi - y)
+    odd = ((lo_bits >> np.uint64(45)) & np.uint64(1)) == 1
+    return np.where((d_hi < d_lo) | ((d_hi == d_lo) & odd), hi, lo)

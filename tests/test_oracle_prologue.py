@@ -3,7 +3,9 @@
 Checked against: rows of mean square 1 (unit weight, eps -> 0); invariance
 under positive scaling of a token; the weight acting per channel; ReLU leaving
 no negative entry; unit L2 norms, and an all-zero row staying zero; and the
-bf16 rounding agreeing with torch's own conversion of the fp32 values.
+bf16 rounding agreeing with torch's own conversion of values exact in fp32,
+going to the nearer neighbour next to halfway points (one rounding, not
+two), and staying within half a bf16 step.
 """
 import numpy as np
 import torch
@@ -50,11 +52,43 @@ def test_relu_and_l2(oracle_mod):
     np.testing.assert_allclose(y, np.divide(r, n, out=np.zeros_like(r), where=n > 0), rtol=1e-14)
 
 
-def test_bf16_rounding_matches_torch(oracle_mod):
+def test_bf16_rounding_of_fp32_values_matches_torch(oracle_mod):
+    """On values that are exact in fp32, one rounding from fp64 is torch's
+    fp32 -> bf16 conversion (round to nearest even)."""
+    x = _rand((4096,), 8) * np.float32(3.0) ** np.random.default_rng(10).integers(-8, 9, 4096).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle_mod.round_bf16(x.astype(np.float64)), want)
+
+
+def test_bf16_rounding_near_halfway_points(oracle_mod):
+    """Near 1 the bf16 step is 2^-7: halfway points go to the even neighbour,
+    and a value past one by less than fp32 resolves (2^-30) goes to the
+    nearer neighbour (rounding through fp32 would land on the halfway point
+    first and pick the even one)."""
+    e = 2.0 ** -7
+    cases = [
+        (1 + e / 2, 1.0),                     # tie, 1.0 is even
+        (1 + 3 * e / 2, 1 + 2 * e),           # tie, 1 + 2^-6 is even
+        (1 + e / 2 + 2.0 ** -30, 1 + e),      # just past the tie
+        (1 + e / 2 - 2.0 ** -30, 1.0),        # just before it
+        (1 + 3 * e / 2 - 2.0 ** -30, 1 + e),
+        (0.0, 0.0),
+    ]
+    y = np.array([c[0] for c in cases] + [-c[0] for c in cases])
+    want = np.array([c[1] for c in cases] + [-c[1] for c in cases])
+    np.testing.assert_array_equal(oracle_mod.round_bf16(y), want)
+    via_fp32 = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert via_fp32[2] == 1.0  # the double rounding this avoids
+
+
+def test_bf16_rounding_is_within_half_a_step(oracle_mod):
     x = _rand((1, 1, 2, 7, 32), 8)
     w = _rand((1, 32), 9)
     y = oracle_mod.prologue(x, w)
     yb = oracle_mod.prologue(x, w, round_to="bf16")
-    want = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    np.testing.assert_array_equal(yb, want)
-    assert np.max(np.abs(yb - y) / np.maximum(np.abs(y), 1e-30)) <= 2.0 ** -8
+    np.testing.assert_array_equal(yb, oracle_mod.round_bf16(y))
+    # bf16 values (fp32 with 16 zero low bits) within half a step of y
+    assert (yb.astype(np.float32).view(np.uint32) & 0xFFFF == 0).all()
+    assert np.array_equal(yb.astype(np.float32).astype(np.float64), yb)
+    step = 2.0 ** (np.floor(np.log2(np.abs(y))) - 7)
+    assert (np.abs(yb - y) <= step / 2).all()
