@@ -93,6 +93,8 @@ def parse():
                     help="skip the side measurement of the block-causal temporal convolution")
     ap.add_argument("--no-strided", action="store_true",
                     help="skip the side measurement of the strided [B][F][N][H][D] layout")
+    ap.add_argument("--no-prologue", action="store_true",
+                    help="skip the side measurement of the fused per-token prologue")
     ap.add_argument("--no-chunk-step", action="store_true",
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
@@ -232,6 +234,7 @@ def main():
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
     conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
     strided = None if args.no_strided else time_strided(torch, ls, calls[0], g)
+    pro = None if args.no_prologue else time_prologue(torch, ls, calls[0], g)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -274,7 +277,7 @@ def main():
         },
         "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
                  "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv,
-                 "bshd_layout": strided},
+                 "bshd_layout": strided, "fused_prologue": pro},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
@@ -447,6 +450,72 @@ def time_strided(torch, ls, relu_call, g, reps=4):
         "bshd": kernel_us(lambda: ls.ls_gdn_frame_forward_strided(gs["q"], gs["k"], gs["v"], g["alpha"], g["beta"]),
                           "gdn_fused")}
     del gs
+    return res
+
+
+def time_prologue(torch, ls, relu_call, g, reps=4):
+    """The per-token prologue fused into the load stage: one 10-frame ReLU call
+    of the rollout with RMSNorm (weights) on q and k, and the GDN call with
+    RMSNorm on q and k, ReLU and L2 keys, against the same calls without a
+    prologue (mean kernel time from the library's per-launch events), and the
+    GDN call after the same prologue as separate torch ops (wall time of both,
+    CUDA events), which reads and writes q and k once more."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+
+    def kernel_us(fn, name):
+        fn()
+        torch.cuda.synchronize()
+        ls.ls_profile_begin()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        n, ms = ls.ls_profile_end()[name]
+        return round(1e3 * ms / n, 2)
+
+    res = {}
+    r = relu_call
+    H, D = r["q"].shape[1], r["q"].shape[-1]
+    wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
+    res["relu_h70_d32_10_frames_rmsnorm_qk_us"] = {
+        "plain": kernel_us(lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused"),
+        "fused_prologue": kernel_us(lambda: ls.ls_relu_block_forward_prologue(r["q"], r["k"], r["v"], wq, wk,
+                                                                               norm_eps=1e-6), "relu_fused")}
+    H, D = g["q"].shape[1], g["q"].shape[-1]
+    wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
+    out = torch.empty_like(g["q"])
+
+    def fused():
+        ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk, norm_eps=1e-6,
+                                         relu=True, l2_keys=True, out=out)
+
+    def torch_prologue(x, w, l2):
+        y = x.float()
+        y = y * torch.rsqrt(y.pow(2).mean(-1, keepdim=True) + 1e-6) * w[None, :, None, None, :]
+        y = torch.relu(y)
+        if l2:
+            y = y / y.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+        return y.to(torch.bfloat16)
+
+    def unfused():
+        q2, k2 = torch_prologue(g["q"], wq, False), torch_prologue(g["k"], wk, True)
+        ls.ls_gdn_frame_forward(q2, k2, g["v"], g["alpha"], g["beta"], out=out)
+
+    unfused()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        unfused()
+        b.record()
+    torch.cuda.synchronize()
+    ms_unfused = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    res["gdn_h24_d128_181_frames_rmsnorm_relu_l2_us"] = {
+        "plain": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out),
+                           "gdn_fused"),
+        "fused_prologue": kernel_us(fused, "gdn_fused"),
+        "torch_prologue_then_plain_wall": round(1e3 * ms_unfused, 2)}
     return res
 
 

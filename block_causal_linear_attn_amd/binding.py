@@ -28,6 +28,11 @@ class ls_strides(ctypes.Structure):
                 ("token", ctypes.c_longlong)]
 
 
+class ls_prologue(ctypes.Structure):
+    _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("relu", ctypes.c_int), ("l2_keys", ctypes.c_int)]
+
+
 class LinscanError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__("liblinscan status %d: %s" % (status, message))
@@ -59,6 +64,11 @@ def _load():
     lib.ls_gdn_frame_forward.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward.restype = I
     ST = ctypes.POINTER(ls_strides)
+    PR = ctypes.POINTER(ls_prologue)
+    lib.ls_relu_block_forward_prologue.argtypes = [SP, PR, I, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_relu_block_forward_prologue.restype = I
+    lib.ls_gdn_frame_forward_prologue.argtypes = [SP, PR, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.ls_gdn_frame_forward_prologue.restype = I
     lib.ls_relu_block_forward_strided.argtypes = [SP, ST, I, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_relu_block_forward_strided.restype = I
     lib.ls_gdn_frame_forward_strided.argtypes = [SP, ST, F, P, P, P, P, P, P, P, P, P, Z, P]
@@ -89,7 +99,8 @@ lib = _load()
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
            "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate",
            "ls_gdn_frame_forward_reversed", "ls_temporal_conv3", "ls_relu_block_forward_strided",
-           "ls_gdn_frame_forward_strided", "ls_state_carry", "ls_status_string", "ls_last_error",
+           "ls_gdn_frame_forward_strided", "ls_relu_block_forward_prologue", "ls_gdn_frame_forward_prologue",
+           "ls_state_carry", "ls_status_string", "ls_last_error",
            "ls_version", "ls_profile_begin", "ls_profile_end")
 
 
@@ -283,6 +294,68 @@ def ls_gdn_frame_forward_strided(q, k, v, alpha, beta, state=None, key_scale=Non
     _check(lib.ls_gdn_frame_forward_strided(ctypes.byref(shp), ctypes.byref(st), scale, _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(alpha), _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w),
                                             w.numel(), _stream(dev)))
+    return o, so
+
+
+def _prologue(q, q_weight, k_weight, eps, relu, l2_keys):
+    B, H, F, N, D = q.shape
+    _f32("q_weight", q_weight, (H, D), q.device)
+    _f32("k_weight", k_weight, (H, D), q.device)
+    return ls_prologue(None if q_weight is None else q_weight.data_ptr(),
+                       None if k_weight is None else k_weight.data_ptr(), float(eps), int(relu), int(l2_keys))
+
+
+def ls_relu_block_forward_prologue(q, k, v, q_weight=None, k_weight=None, norm_eps: float = 1e-6, state=None,
+                                   norm=None, block_frames: int = 1, eps: float = 1e-6, out=None, state_out=None,
+                                   norm_out=None, ws=None):
+    """ls_relu_block_forward with RMSNorm of q and/or k (weights [H, D] fp32) fused into the load."""
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    pr = _prologue(q, q_weight, k_weight, norm_eps, 0, 0)
+    _f32("state", state, (B, H, D, D), dev)
+    _f32("norm", norm, (B, H, D), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    no = norm_out if norm_out is not None else torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    _f32("norm_out", no, (B, H, D), dev)
+    shp = _shape(q)
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    w = ws if ws is not None else workspace(need, dev)
+    _check(lib.ls_relu_block_forward_prologue(ctypes.byref(shp), ctypes.byref(pr), int(block_frames), float(eps),
+                                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so),
+                                              _ptr(no), _ptr(w), w.numel(), _stream(dev)))
+    return o, so, no
+
+
+def ls_gdn_frame_forward_prologue(q, k, v, alpha, beta, q_weight=None, k_weight=None, norm_eps: float = 1e-6,
+                                  relu: bool = False, l2_keys: bool = False, state=None, key_scale=None, out=None,
+                                  state_out=None, ws=None):
+    """ls_gdn_frame_forward with the per-token prologue (RMSNorm, ReLU, L2 of keys) fused into the load."""
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    pr = _prologue(q, q_weight, k_weight, norm_eps, relu, l2_keys)
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F), dev)
+    _f32("state", state, (B, H, D, D), dev)
+    o = out if out is not None else torch.empty_like(q)
+    _tokens("out", o, q)
+    so = state_out if state_out is not None else torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    _f32("state_out", so, (B, H, D, D), dev)
+    shp = _shape(q)
+    need = lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
+    w = ws if ws is not None else workspace(need, dev)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward_prologue(ctypes.byref(shp), ctypes.byref(pr), scale, _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(alpha), _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w),
+                                             w.numel(), _stream(dev)))
     return o, so
 
 

@@ -68,6 +68,110 @@ __device__ __forceinline__ uint2 split_bf16x2(float x0, float x1) {
   return make_uint2(hi, pack_bf16x2(x0 - bf16lo_to_f32(hi), x1 - bf16hi_to_f32(hi)));
 }
 
+// Sum over groups of G consecutive lanes (G = 4, 8 or 16, within a DPP row),
+// every lane of a group getting the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 lanes");
+  auto add = [](float v, int s) { return v + __int_as_float(s); };
+  x = add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lanes ^1
+  x = add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lanes ^2
+  if (G >= 8) x = add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
+  if (G >= 16) x = add(x, __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
+  return x;
+}
+
+// fp64 -> bf16, round to nearest even in one step: the 45 dropped bits of
+// the double's fraction decide, so no second rounding (as through fp32) can
+// move a value that lies just off a halfway point onto it.  For finite values
+// in the normal fp32 range.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  u += ((1ull << 44) - 1) + ((u >> 45) & 1ull);
+  u &= ~((1ull << 45) - 1);
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;  // exact: 8 significant bits
+}
+__device__ __forceinline__ uint32_t pack_bf16x2_f64(double lo, double hi) {
+  return f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
+}
+
+// A 64-bit value from another lane of the DPP row, as two 32-bit moves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const long long u = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(u & 0xffffffffll), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(uint32_t)lo);
+}
+// group_sum in fp64.
+template <int G>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  static_assert(G == 4 || G == 8 || G == 16, "groups of 4, 8 or 16 lanes");
+  x += dpp_f64<0xB1>(x);
+  x += dpp_f64<0x4E>(x);
+  if (G >= 8) x += dpp_f64<0x141>(x);
+  if (G >= 16) x += dpp_f64<0x140>(x);
+  return x;
+}
+
+// The prologue (see Prologue) on 8 channels of one token, held by one lane as
+// packed bf16; `red` completes a per-token fp64 sum over the lanes that hold
+// the token's other channels (every lane calls it: DPP or cross-lane
+// exchange).  wt: the RMSNorm weights of these 8 channels (zero past the head
+// dim), inv_d = 1 / D.  Returns the result rounded to bf16.
+//
+// The arithmetic is fp64 and the result is rounded once, from fp64: rounding
+// to bf16 picks one of two neighbours, and an fp32 chain (a few rounding
+// errors of 2^-24) picks the other neighbour than the exact value for about
+// one channel in 10^4 to 10^5.  One such 2^-8 step in a key moves every later
+// state, and outputs that cancel (a query nearly orthogonal to the state's
+// rows) turn it into a large relative error.  In fp64 the chance is ~2^-40.
+template <typename Red>
+__device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], bool norm, const Prologue& P,
+                                                 bool is_k, double inv_d, Red red) {
+  double x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16lo_to_f32(w[e]);
+    x[2 * e + 1] = bf16hi_to_f32(w[e]);
+  }
+  if (norm) {
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
+    const double inv = 1.0 / sqrt(fma(red(ss), inv_d, (double)P.eps));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * (double)wt[e] * inv;  // x * w exact in fp64
+  }
+  if (P.relu) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = signbit(x[e]) ? 0.0 : x[e];
+  }
+  if (is_k && P.l2) {
+    double ss = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
+    ss = red(ss);
+    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= inv;
+  }
+  return u32x4{pack_bf16x2_f64(x[0], x[1]), pack_bf16x2_f64(x[2], x[3]), pack_bf16x2_f64(x[4], x[5]),
+               pack_bf16x2_f64(x[6], x[7])};
+}
+
+// The 8 RMSNorm weights of channels c0 .. c0 + 7 of head h (zero at and past
+// channel DI, or all zero without weights), loaded without a branch on the
+// lane: past DI the address is clamped and the values are zeroed.
+__device__ __forceinline__ void load_weights8(const float* w, long h, int DI, int c0, float (&wt)[8]) {
+  const float* p = w ? w + (size_t)h * DI + (c0 < DI ? c0 : 0) : nullptr;
+  const float4 a = p ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 b = p ? *reinterpret_cast<const float4*>(p + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool in = c0 < DI;
+  wt[0] = in ? a.x : 0.f, wt[1] = in ? a.y : 0.f, wt[2] = in ? a.z : 0.f, wt[3] = in ? a.w : 0.f;
+  wt[4] = in ? b.x : 0.f, wt[5] = in ? b.y : 0.f, wt[6] = in ? b.z : 0.f, wt[7] = in ? b.w : 0.f;
+}
+
 // The 8 bf16 values of an MFMA operand fragment (element e in half e % 2 of
 // word e / 2) times 8 fp32 factors, as bf16 hi + lo terms (16 significant
 // bits), so that MFMAs on hi and on lo together take products with the
@@ -215,10 +319,21 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
   static __device__ __forceinline__ void store(float* p, size_t i, float x) { p[i] = x; }
+  // an fp64 result in this precision (one rounding)
+  static __device__ __forceinline__ float round(double x) { return (float)x; }
 };
 template <> struct Elem<uint16_t> {  // bf16 bits
   static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
   static __device__ __forceinline__ void store(uint16_t* p, size_t i, float x) { p[i] = f32_to_bf16(x); }
+  static __device__ __forceinline__ float round(double x) { return __uint_as_float(f64_to_bf16(x) << 16); }
 };
+
+// One channel of the prologue in fp64: x w s1 (RMSNorm factor s1, weight w;
+// s1 = w = 1 without it), then ReLU, then the L2 factor s2 (1 without it).
+__device__ __forceinline__ double prologue_chan(float x, float w, double s1, int relu, double s2) {
+  double y = (double)x * (double)w * s1;
+  if (relu) y = signbit(y) ? 0.0 : y;
+  return y * s2;
+}
 
 }  // namespace linscan

@@ -31,6 +31,22 @@ constexpr int kGramLds = 2 * 2 * 64 * GD * 2;
 constexpr int kGramDepth = 2;  // tiles in flight per gram item
 // per-token gates of the two staged tiles, after the tiles (gated items only)
 constexpr int kGateLds = 2 * 64 * 4;
+// the prologue's key weights of the item's head, after the gates
+constexpr int kPrologueLds = GD * 4;
+
+// The prologue's weights of head h (zero past DI) into LDS, then a barrier;
+// a no-op without weights.
+__device__ __forceinline__ void stage_weights(const float* w, long h, int DI, float* wl) {
+  if (!w) return;
+  if (threadIdx.x < GD) wl[threadIdx.x] = (int)threadIdx.x < DI ? w[(size_t)h * DI + threadIdx.x] : 0.0f;
+  __syncthreads();
+}
+// The 8 weights of channels 8 cb .. 8 cb + 7 from LDS (two 16-byte reads).
+__device__ __forceinline__ void weights8_lds(const float* wl, int cb, float (&wt)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb);
+  const float4 b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
+  wt[0] = a.x, wt[1] = a.y, wt[2] = a.z, wt[3] = a.w, wt[4] = b.x, wt[5] = b.y, wt[6] = b.z, wt[7] = b.w;
+}
 
 // Work item `wg` = (frame of one head) * nc + token chunk: the chunk's record
 // (beta*G hi/lo planes, beta*U) -> rec + wg * kRecBytes.  DI is the head dim
@@ -47,11 +63,15 @@ constexpr int kGateLds = 2 * 64 * 4;
 // leaves errors of 2^-9 of single products, which outputs that cancel, such
 // as a query nearly orthogonal to the keys, turn into large relative errors.)
 // The record then carries no further gate factor.
-template <int DI = GD, bool TG = false>
+//
+// PRO: keys pass through the per-token prologue P when it is on (see
+// prologue_bf16x8); a separate instantiation, so that calls without it keep
+// the registers its fp64 arithmetic takes.
+template <int DI = GD, bool TG = false, bool PRO = false>
 __device__ __forceinline__ void gdn_gram_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, long wg, uint8_t* lds_raw,
-    TokLayout L) {
+    TokLayout L, Prologue P) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -71,6 +91,10 @@ __device__ __forceinline__ void gdn_gram_item(
   const uint16_t* kf = k + L.base(bhf);
   const uint16_t* vf = v + L.base(bhf);
   const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
+  // the prologue's key weights of the head, in LDS after the gates
+  float* wl = reinterpret_cast<float*>(lds_raw + kGramLds + kGateLds);
+  if (PRO) stage_weights(P.wk, (bhf / L.F) % L.H, DI, wl);
+  auto row16 = [](double x) { return group_sum_f64<16>(x); };
 
   floatx16 accG[4], accU[4];
 #pragma unroll
@@ -110,8 +134,14 @@ __device__ __forceinline__ void gdn_gram_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const bool live = t0 + tok < n1 && cb < CI;
-      const u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
+      // the 16 lanes of a DPP row hold the 16 chunks of token `tok`
+      if (PRO && P.on_k()) {
+        float wk8[8];
+        weights8_lds(wl, cb, wk8);
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16);
+      }
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -220,10 +250,11 @@ constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;  // (
 // TG: per-token gates as in gdn_gram_item (the A operands, key and value
 // fragments, scaled and split into hi + lo before each MFMA pair; gates in
 // LDS after the tiles).
-template <int DI = GD, bool TG = false>
+template <int DI = GD, bool TG = false, bool PRO = false>
 __device__ __forceinline__ void gdn_gram_rows_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw, TokLayout L) {
+    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw, TokLayout L,
+    Prologue P) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -244,6 +275,9 @@ __device__ __forceinline__ void gdn_gram_rows_item(
   const uint16_t* vf = v + L.base(bhf);
   const int vchunk = 4 * w + (tid & 3);  // this thread's 16-byte chunk of the V rows
   const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
+  float* wl = reinterpret_cast<float*>(lds_raw + kGramRowsLds + kGateLds);  // the prologue's key weights
+  if (PRO) stage_weights(P.wk, (bhf / L.F) % L.H, DI, wl);
+  auto row16 = [](double x) { return group_sum_f64<16>(x); };
 
   floatx16 accG = {}, accU = {};
   struct Regs {
@@ -271,7 +305,12 @@ __device__ __forceinline__ void gdn_gram_rows_item(
 #pragma unroll
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
-      const u32x4 kk = t0 + (ci >> 4) < N && (ci & 15) < CI ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 kk = t0 + (ci >> 4) < N && (ci & 15) < CI ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
+      if (PRO && P.on_k()) {
+        float wk8[8];
+        weights8_lds(wl, ci & 15, wk8);
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16);
+      }
       uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
       kd[0] = make_uint2(kk[0], kk[1]);
       kd[1] = make_uint2(kk[2], kk[3]);
@@ -600,10 +639,10 @@ constexpr int kOutPitch = GD + 8;
 constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;
 
 // Work item `wg` = (frame of one head) * nco + token chunk: o = S_f q.
-template <int DI = GD>
+template <int DI = GD, bool PRO = false>
 __device__ __forceinline__ void gdn_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
-    int N, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
+    int N, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -649,12 +688,20 @@ __device__ __forceinline__ void gdn_output_item(
       X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
     }
   };
+  float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
+  if (PRO) load_weights8(P.wq, (bhf / L.F) % L.H, DI, (tid & 15) * 8, wq8);
+  auto row16 = [](double x) { return group_sum_f64<16>(x); };
   auto stage = [&](const Regs& X, int buf) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = X.q[r];
+      u32x4 qq = X.q[r];
+      if (PRO && P.on_q()) {  // chunks past DI re-read a real chunk: zero them out of the token's sums
+        qq = cb < CI ? qq : u32x4{0u, 0u, 0u, 0u};
+        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16);
+      }
+      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qq;
     }
   };
 

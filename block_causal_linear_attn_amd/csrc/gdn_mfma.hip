@@ -25,12 +25,12 @@ namespace linscan {
 
 namespace {
 
-template <int DI, bool TG>
+template <int DI, bool TG, bool PRO>
 __global__ __launch_bounds__(256, 2) void gdn_gram_mfma128(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, TokLayout L) {
-  __shared__ __align__(16) uint8_t lds[kGramLds + kGateLds];
-  gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds, L);
+    uint8_t* __restrict__ rec, float c, float c2, int N, int nc, int chunk, TokLayout L, Prologue P) {
+  __shared__ __align__(16) uint8_t lds[kGramLds + kGateLds + kPrologueLds];
+  gdn_gram_item<DI, TG, PRO>(k, v, beta, rec, c, c2, N, nc, chunk, blockIdx.x, lds, L, P);
 }
 
 template <bool MULTI, int DI>
@@ -45,12 +45,12 @@ __global__ __launch_bounds__(256) void gdn_scan_mfma128(
                                            lds, nullptr, nullptr, 0, nullptr, 0, rchunk);
 }
 
-template <int DI>
+template <int DI, bool PRO>
 __global__ __launch_bounds__(256, 2) void gdn_output_mfma128(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
-    int N, int nco, int chunk, TokLayout L) {
+    int N, int nco, int chunk, TokLayout L, Prologue P) {
   __shared__ __align__(16) uint8_t lds[kOutLds];
-  gdn_output_item<DI>(q, o, states, N, nco, chunk, blockIdx.x, lds, L);
+  gdn_output_item<DI, PRO>(q, o, states, N, nco, chunk, blockIdx.x, lds, L, P);
 }
 
 constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan item
@@ -58,16 +58,17 @@ constexpr int kFusedRB = GD / kGdnFusedRowBlocks;  // rows of S per fused scan i
 constexpr int lds_max(int a, int b, int c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
 
 // TG: `beta` holds per-token gates [B*H*F][N] (see gdn_gram_item).
-template <bool MULTI, int DI, bool TG>
+// PRO: the per-token prologue may be on (see gdn_gram_item).
+template <bool MULTI, int DI, bool TG, bool PRO>
 __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
     uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk,
-    TokLayout L) {
+    TokLayout L, Prologue P) {
   constexpr int kSL = scan_lds_bytes<kFusedRB>();
-  constexpr int LDS = lds_max(kGramLds + (TG ? kGateLds : 0), kSL, kOutLds);
+  constexpr int LDS = lds_max(kGramLds + kGateLds + kPrologueLds, kSL, kOutLds);
   constexpr int NRB = kGdnFusedRowBlocks;
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
@@ -107,11 +108,11 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     cidx = (int)(r % nco);
   }
   if (gram) {
-    gdn_gram_item<DI, TG>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds, L);
+    gdn_gram_item<DI, TG, PRO>(k, v, beta, rec, c, c2, N, nc, chunk, (bh * F + f) * nc + cidx, lds, L, P);
     publish(&gflags[(bh * F + f) * nc + cidx], epoch);
   } else {
     wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-    gdn_output_item<DI>(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds, L);
+    gdn_output_item<DI, PRO>(q, o, states, N, nco, chunko, (bh * F + f) * nco + cidx, lds, L, P);
   }
 }
 
@@ -124,16 +125,16 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
 // whatever the number of heads.  For single-frame calls the scan has no
 // frame chain and the phases overlap across heads; longer calls run the
 // chain once all records are in.
-template <int DI, bool TG>
+template <int DI, bool TG, bool PRO>
 __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nco, int chunko, uint64_t* __restrict__ gflags,
-    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk, TokLayout L) {
+    uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk, TokLayout L, Prologue P) {
   constexpr int RB = 32, NRB = GD / RB;
   constexpr int kSL = scan_lds_bytes<RB>();
-  constexpr int LDS = lds_max(kGramRowsLds + (TG ? kGateLds : 0), kSL, kOutLds);
+  constexpr int LDS = lds_max(kGramRowsLds + kGateLds + kPrologueLds, kSL, kOutLds);
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
   const long ngram = bhp * F * 4, nscan = bhp * NRB;
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long bh = L.head_of_slot(b % bhp), r = b / bhp;  // r = f * 4 + row block
     if (bh >= bh_n) return;
     const long item = (bh * F + r / 4) * 4 + r % 4;
-    gdn_gram_rows_item<DI, TG>(k, v, beta, rec, c, c2, N, item, lds, L);
+    gdn_gram_rows_item<DI, TG, PRO>(k, v, beta, rec, c, c2, N, item, lds, L, P);
     publish(&gflags[item], epoch);
     return;
   }
@@ -158,10 +159,13 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
   if (bh >= bh_n) return;
   const int f = (int)(r / nco);
   wait_all(&sflags[(bh * F + f) * 8], NRB, epoch, err);
-  gdn_output_item<DI>(q, o, states, N, nco, chunko, bh * F * nco + r, lds, L);
+  gdn_output_item<DI, PRO>(q, o, states, N, nco, chunko, bh * F * nco + r, lds, L, P);
 }
 
 }  // namespace
+// The prologue does some work (the kernels take it as a template switch).
+static bool pro_on(const Prologue& P) { return P.on_k() || P.on_q(); }
+
 // Head dims with an MFMA path: 128, and 112 (the items run on 128 dims with
 // the last 16 zero).
 bool gdn_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == GD || D == 112); }
@@ -180,23 +184,27 @@ hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags,
   const float* gates = a.tg ? a.gate : a.beta;
   return with_head_dim(a.D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    auto kern = a.tg ? gdn_phased_mfma128<DI, true> : gdn_phased_mfma128<DI, false>;
+    if (a.tg && pro_on(a.P)) return hipErrorInvalidValue;  // not instantiated: no entry point combines them
+    auto kern = a.tg ? gdn_phased_mfma128<DI, true, false>
+                     : (pro_on(a.P) ? gdn_phased_mfma128<DI, false, true> : gdn_phased_mfma128<DI, false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
-                       sflags, epoch, err, a.rchunk, a.L);
+                       sflags, epoch, err, a.rchunk, a.L, a.P);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, const TokLayout& L,
-                                hipStream_t st) {
+                                const Prologue& P, hipStream_t st) {
   return with_head_dim(D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    auto kern = tg ? gdn_gram_mfma128<DI, true> : gdn_gram_mfma128<DI, false>;
+    if (tg && pro_on(P)) return hipErrorInvalidValue;
+    auto kern = tg ? gdn_gram_mfma128<DI, true, false>
+                   : (pro_on(P) ? gdn_gram_mfma128<DI, false, true> : gdn_gram_mfma128<DI, false, false>);
     hipLaunchKernelGGL(kern, dim3((unsigned)(bhf * nc)), dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v,
-                       gates, (uint8_t*)rec, c, c2, N, nc, chunk, L);
+                       gates, (uint8_t*)rec, c, c2, N, nc, chunk, L, P);
     return hipGetLastError();
   });
 }
@@ -217,10 +225,12 @@ hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, cons
 }
 
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
-                                  int N, int nco, int chunk, const TokLayout& L, hipStream_t st) {
+                                  int N, int nco, int chunk, const TokLayout& L, const Prologue& P, hipStream_t st) {
   return with_head_dim(D, [&](auto di) {
-    hipLaunchKernelGGL((gdn_output_mfma128<decltype(di)::value>), dim3((unsigned)(bhf * nco)), dim3(256), 0, st,
-                       (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk, L);
+    constexpr int DI = decltype(di)::value;
+    auto kern = pro_on(P) ? gdn_output_mfma128<DI, true> : gdn_output_mfma128<DI, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(bhf * nco)), dim3(256), 0, st,
+                       (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk, L, P);
     return hipGetLastError();
   });
 }
@@ -231,8 +241,13 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
   const float* gates = a.tg ? a.gate : a.beta;
   return with_head_dim(a.D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    auto kern = a.nc == 1 ? (a.tg ? gdn_fused_mfma128<false, DI, true> : gdn_fused_mfma128<false, DI, false>)
-                          : (a.tg ? gdn_fused_mfma128<true, DI, true> : gdn_fused_mfma128<true, DI, false>);
+    if (a.tg && pro_on(a.P)) return hipErrorInvalidValue;
+    const bool pro = pro_on(a.P);
+    auto kern = a.nc == 1
+                    ? (a.tg ? gdn_fused_mfma128<false, DI, true, false>
+                            : (pro ? gdn_fused_mfma128<false, DI, false, true> : gdn_fused_mfma128<false, DI, false, false>))
+                    : (a.tg ? gdn_fused_mfma128<true, DI, true, false>
+                            : (pro ? gdn_fused_mfma128<true, DI, false, true> : gdn_fused_mfma128<true, DI, false, false>));
     // an output item's state needs the records of every frame of its chunk
     // (reversed scan): lag >= rchunk keeps those gram items at lower block ids
     const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco),
@@ -240,7 +255,7 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,
-                       a.chunko, lag, gflags, sflags, epoch, err, a.rchunk, a.L);
+                       a.chunko, lag, gflags, sflags, epoch, err, a.rchunk, a.L, a.P);
     return hipGetLastError();
   });
 }

@@ -29,11 +29,12 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
                                                    float* __restrict__ partial, float c, float c2,
                                                    const float* S0, const float* z0, float* init,
                                                    const float* gate, int F, int N, int nc, int chunk,
-                                                   TokLayout L) {
+                                                   TokLayout L, Prologue P) {
   constexpr int EPT = SummarySplit<D>::kEPT;
   __shared__ float ks[GT][D + 1];
   __shared__ float vs[GT][D + 1];
   __shared__ float bs[GT];  // token gates (GDN)
+  __shared__ double sc[GT], sc2[GT];  // per-token prologue factors (RMSNorm, L2)
   const int tid = threadIdx.x;
   const int e0 = blockIdx.y * 256 * EPT;  // first entry owned by this workgroup
   const long wg = blockIdx.x;
@@ -57,8 +58,36 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
         kk = Elem<T>::load(kf, (size_t)n * L.sn + d);
         vv = Elem<T>::load(vf, (size_t)n * L.sn + d);
       }
-      ks[tok][d] = RELU ? relu_f32(kk) : kk;
+      ks[tok][d] = RELU && !P.on_k() ? relu_f32(kk) : kk;
       vs[tok][d] = vv;
+    }
+    if (P.on_k()) {  // the prologue on the staged keys (fp64, one rounding), then the feature map
+      const float* wk = P.wk ? P.wk + (size_t)((bhf / L.F) % L.H) * D : nullptr;
+      __syncthreads();
+      if (tid < GT) {  // the token's RMSNorm and L2 factors
+        double s1 = 1.0, s2 = 1.0;
+        if (wk) {
+          double ss = 0.0;
+          for (int d = 0; d < D; ++d) ss = fma((double)ks[tid][d], (double)ks[tid][d], ss);
+          s1 = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+        }
+        if (P.l2) {
+          double ss = 0.0;
+          for (int d = 0; d < D; ++d) {
+            const double y = prologue_chan(ks[tid][d], wk ? wk[d] : 1.0f, s1, P.relu, 1.0);
+            ss = fma(y, y, ss);
+          }
+          s2 = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+        }
+        sc[tid] = s1;
+        sc2[tid] = s2;
+      }
+      __syncthreads();
+      for (int e = tid; e < GT * D; e += 256) {
+        const int tok = e / D, d = e % D;
+        const float x = Elem<T>::round(prologue_chan(ks[tok][d], wk ? wk[d] : 1.0f, sc[tok], P.relu, sc2[tok]));
+        ks[tok][d] = RELU ? relu_f32(x) : x;
+      }
     }
     if (!RELU && tid < GT) {
       const int n = t0 + tid;
@@ -114,7 +143,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
                                                   const float* __restrict__ states,
                                                   const float* __restrict__ init, float* S_out,
                                                   float* z_out, float eps, int F, int N, int nc,
-                                                  int bfr, int nco, int chunk, TokLayout L) {
+                                                  int bfr, int nco, int chunk, TokLayout L, Prologue P) {
   constexpr int SLOTS = 256 / D;
   __shared__ float Ss[D][D + 1];
   __shared__ float zs[D];
@@ -146,9 +175,27 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
     if (slot < SLOTS) {
       const int n = t0 + slot;
       float x = (n < n1) ? Elem<T>::load(qf, (size_t)n * L.sn + i) : 0.0f;
-      qs[slot][i] = RELU ? relu_f32(x) : x;
+      qs[slot][i] = RELU && !P.on_q() ? relu_f32(x) : x;
     }
     __syncthreads();
+    if (P.on_q()) {  // the prologue on the staged queries (every thread sums its token), then the feature map
+      float y = 0.0f;
+      if (slot < SLOTS) {
+        double s1 = 1.0;
+        float wv = 1.0f;
+        if (P.wq) {
+          double ss = 0.0;
+          for (int j = 0; j < D; ++j) ss = fma((double)qs[slot][j], (double)qs[slot][j], ss);
+          s1 = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+          wv = P.wq[(size_t)((bhf / L.F) % L.H) * D + i];
+        }
+        y = Elem<T>::round(prologue_chan(qs[slot][i], wv, s1, P.relu, 1.0));
+        if (RELU) y = relu_f32(y);
+      }
+      __syncthreads();
+      if (slot < SLOTS) qs[slot][i] = y;
+      __syncthreads();
+    }
     if (slot < SLOTS && t0 + slot < n1) {
       float num = 0.0f, den = 0.0f;
       for (int j = 0; j < D; ++j) {
@@ -167,10 +214,10 @@ hipError_t summary_launch(const GenArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.bhf * a.nc), SummarySplit<D>::kParts), block(256);
   if (a.relu)
     hipLaunchKernelGGL((gen_summary<T, D, true>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L, a.P);
   else
     hipLaunchKernelGGL((gen_summary<T, D, false>), grid, block, 0, st, (const T*)a.k, (const T*)a.v,
-                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L);
+                       a.partial, a.c, a.c2, a.S0, a.z0, a.init, a.gate, a.F, a.N, a.nc, a.chunk, a.L, a.P);
   return hipGetLastError();
 }
 
@@ -179,11 +226,12 @@ hipError_t output_launch(const GenArgs& a, hipStream_t st) {
   dim3 grid((unsigned)(a.bhf * a.nco)), block(256);
   if (a.relu)
     hipLaunchKernelGGL((gen_output<T, D, true>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
-                       a.partial, a.init, a.S_out, a.z_out, a.eps, a.F, a.N, a.nc, a.bfr, a.nco, a.chunko, a.L);
+                       a.partial, a.init, a.S_out, a.z_out, a.eps, a.F, a.N, a.nc, a.bfr, a.nco, a.chunko, a.L,
+                       a.P);
   else
     hipLaunchKernelGGL((gen_output<T, D, false>), grid, block, 0, st, (const T*)a.q, (T*)a.o,
                        (const float*)a.states, nullptr, nullptr, nullptr, 0.0f, a.F, a.N, 1, 1, a.nco, a.chunko,
-                       a.L);
+                       a.L, a.P);
   return hipGetLastError();
 }
 

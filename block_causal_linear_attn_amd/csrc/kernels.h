@@ -49,6 +49,7 @@ struct ScanArgs {
   int nco = 1, chunko = 1;     // token chunks of the output pass
   int bfr = 1;                 // ReLU frames per causal block
   TokLayout L;                 // element strides of q, k, v, o
+  Prologue P;                  // per-token prologue of q and k
 };
 using GenArgs = ScanArgs;
 

@@ -31,7 +31,7 @@ struct TokLayout {
     const long m = slot / 8, x = slot % 8;
     return hg * (8 * (m / hg) + x) + m % hg;
   }
-  static TokLayout packed(int H, int F, int N, int D) {
+  __host__ __device__ static TokLayout packed(int H, int F, int N, int D) {
     TokLayout L;
     L.sn = D;
     L.sf = (long long)N * D;
@@ -41,6 +41,20 @@ struct TokLayout {
     L.F = F > 0 ? F : 1;
     return L;
   }
+};
+
+// The per-token prologue applied to q and k as they are loaded, before the
+// scan's own feature map and key scale: RMSNorm over the D channels of a
+// head with per-(head, channel) weights, then (GDN) ReLU, then (GDN, keys)
+// division by the L2 norm.  Results enter the contractions rounded to bf16.
+struct Prologue {
+  const float* wq = nullptr;  // [H][D] RMSNorm weights of q, or nullptr: no norm on q
+  const float* wk = nullptr;  // [H][D] RMSNorm weights of k, or nullptr: no norm on k
+  float eps = 1e-6f;
+  int relu = 0;               // ReLU on q and k after the norm
+  int l2 = 0;                 // keys divided by their L2 norm, last
+  __host__ __device__ bool on_q() const { return wq != nullptr || relu; }
+  __host__ __device__ bool on_k() const { return wk != nullptr || relu || l2; }
 };
 
 }  // namespace linscan

@@ -152,6 +152,28 @@ ls_status token_layout(const ls_shape* s, const Dims& d, const ls_strides* st, l
   return LS_OK;
 }
 
+// The per-token prologue of a call (nullptr: none); `gdn` allows the GDN-only
+// parts (ReLU, L2 of keys).  Weights are [H][D] fp32, 16-byte aligned.
+ls_status prologue_of(const ls_prologue* pr, const ls_shape* s, bool gdn, linscan::Prologue* P, size_t* w_bytes) {
+  *P = linscan::Prologue();
+  *w_bytes = (size_t)s->H * s->D * sizeof(float);
+  if (!pr) return LS_OK;
+  if (pr->relu != 0 && pr->relu != 1) return fail(LS_ERR_BAD_PARAM, "prologue relu must be 0 or 1");
+  if (pr->l2_keys != 0 && pr->l2_keys != 1) return fail(LS_ERR_BAD_PARAM, "prologue l2_keys must be 0 or 1");
+  if (!gdn && (pr->relu || pr->l2_keys))
+    return fail(LS_ERR_BAD_PARAM, "the ReLU scan applies its own feature map: prologue relu and l2_keys must be 0");
+  if ((pr->q_weight || pr->k_weight) && (!(pr->eps > 0.0f) || !isfinite(pr->eps)))
+    return fail(LS_ERR_BAD_PARAM, "prologue eps=%g must be finite and > 0", (double)pr->eps);
+  if (misaligned(pr->q_weight) || misaligned(pr->k_weight))
+    return fail(LS_ERR_MISALIGNED, "prologue weights must be 16-byte aligned");
+  P->wq = pr->q_weight;
+  P->wk = pr->k_weight;
+  P->eps = pr->eps;
+  P->relu = pr->relu;
+  P->l2 = pr->l2_keys;
+  return LS_OK;
+}
+
 // Token chunking: enough workgroups to fill 256 CUs several times over, with
 // chunks of at least `min_chunk` tokens (a multiple of `quantum`).
 void plan_chunks(long frames, int N, int target_wg, int min_chunk, int quantum, int* nc, int* chunk) {
@@ -371,8 +393,9 @@ size_t ls_gdn_frame_workspace_size(const ls_shape* s) {
 }
 
 // Both ReLU entry points: packed token tensors (strides NULL) or strided ones.
-static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int block_frames, float eps,
-                              const void* q, const void* k, const void* v, void* o, const float* state_in,
+static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, const ls_prologue* pro,
+                              int block_frames, float eps, const void* q, const void* k, const void* v, void* o,
+                              const float* state_in,
                               const float* norm_in, float* state_out, float* norm_out, void* workspace,
                               size_t workspace_bytes, void* stream) {
   g_last_error.clear();
@@ -385,6 +408,9 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int 
   linscan::TokLayout layout;
   size_t tok_bytes = 0;  // bytes each token tensor spans
   if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
+  linscan::Prologue prolog;
+  size_t pw_bytes = 0;
+  if ((st = prologue_of(pro, s, false, &prolog, &pw_bytes)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t norm_bytes = (size_t)d.bh * D * sizeof(float);
   if (d.bh == 0) return ok();
@@ -409,6 +435,11 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int 
       overlap(o, tok_bytes, norm_out, norm_out ? norm_bytes : 0) ||
       overlap(state_out, state_out ? state_bytes : 0, norm_out, norm_out ? norm_bytes : 0))
     return fail(LS_ERR_ALIASING, "outputs overlap each other");
+  for (const float* w : {prolog.wq, prolog.wk})
+    if (overlap(o, tok_bytes, w, w ? pw_bytes : 0) || overlap(state_out, state_out ? state_bytes : 0, w, w ? pw_bytes : 0) ||
+        overlap(norm_out, norm_out ? norm_bytes : 0, w, w ? pw_bytes : 0) ||
+        overlap(workspace, workspace ? workspace_bytes : 0, w, w ? pw_bytes : 0))
+      return fail(LS_ERR_ALIASING, "an output or the workspace overlaps the prologue weights");
 
   hipStream_t hs = (hipStream_t)stream;
   if (s->F == 0 || s->N == 0) {
@@ -461,6 +492,7 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int 
   a.chunko = p.chunko;
   a.bfr = block_frames;
   a.L = layout;
+  a.P = prolog;
   if (p.fused) {
     const long bhp = (d.bh + 8 * layout.hg - 1) / (8 * layout.hg) * (8 * layout.hg);
     uint64_t* flags = (uint64_t*)(ws + p.flags_off);
@@ -485,7 +517,8 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, int 
 // The GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
 // token ([B*H*F][N]); rchunk > 0 runs the reversed scan in chunks of rchunk
 // frames (no state in or out).
-static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, float key_scale, const void* q,
+static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const ls_prologue* pro, float key_scale,
+                             const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta, bool token_gate,
                              int rchunk, void* o, const float* state_in, float* state_out, void* workspace,
                              size_t workspace_bytes, void* stream) {
@@ -498,6 +531,9 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, float
   linscan::TokLayout layout;
   size_t tok_bytes = 0;  // bytes each token tensor spans
   if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
+  linscan::Prologue prolog;
+  size_t pw_bytes = 0;
+  if ((st = prologue_of(pro, s, true, &prolog, &pw_bytes)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t gate_bytes = (size_t)d.bhf * (token_gate ? (size_t)s->N : 1) * sizeof(float);
   const size_t alpha_bytes = (size_t)d.bhf * sizeof(float);
@@ -521,6 +557,10 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, float
   }
   if (overlap(o, tok_bytes, state_out, state_out ? state_bytes : 0))
     return fail(LS_ERR_ALIASING, "outputs overlap each other");
+  for (const float* w : {prolog.wq, prolog.wk})
+    if (overlap(o, tok_bytes, w, w ? pw_bytes : 0) || overlap(state_out, state_out ? state_bytes : 0, w, w ? pw_bytes : 0) ||
+        overlap(workspace, workspace ? workspace_bytes : 0, w, w ? pw_bytes : 0))
+      return fail(LS_ERR_ALIASING, "an output or the workspace overlaps the prologue weights");
 
   hipStream_t hs = (hipStream_t)stream;
   if (s->F == 0) {
@@ -557,6 +597,7 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, float
   a.tg = token_gate;
   a.rchunk = rchunk;
   a.L = layout;
+  a.P = prolog;
   a.S0 = state_in;
   a.S_out = state_out;
   a.partial = (float*)(ws + p.partial_off);
@@ -600,31 +641,47 @@ ls_status ls_relu_block_forward(const ls_shape* s, int block_frames, float eps, 
                                 const void* k, const void* v, void* o, const float* state_in,
                                 const float* norm_in, float* state_out, float* norm_out,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-  return relu_forward(s, nullptr, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out, workspace,
-                      workspace_bytes, stream);
+  return relu_forward(s, nullptr, nullptr, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out,
+                      workspace, workspace_bytes, stream);
 }
 
 ls_status ls_relu_block_forward_strided(const ls_shape* s, const ls_strides* strides, int block_frames, float eps,
                                         const void* q, const void* k, const void* v, void* o,
                                         const float* state_in, const float* norm_in, float* state_out,
                                         float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
-  return relu_forward(s, strides, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out, workspace,
-                      workspace_bytes, stream);
+  return relu_forward(s, strides, nullptr, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out,
+                      workspace, workspace_bytes, stream);
 }
 
 ls_status ls_gdn_frame_forward_strided(const ls_shape* s, const ls_strides* strides, float key_scale, const void* q,
                                        const void* k, const void* v, const float* alpha, const float* beta, void* o,
                                        const float* state_in, float* state_out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, strides, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+  return gdn_forward(s, strides, nullptr, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
                      workspace_bytes, stream);
+}
+
+ls_status ls_relu_block_forward_prologue(const ls_shape* s, const ls_prologue* prologue, int block_frames, float eps,
+                                         const void* q, const void* k, const void* v, void* o,
+                                         const float* state_in, const float* norm_in, float* state_out,
+                                         float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return relu_forward(s, nullptr, prologue, block_frames, eps, q, k, v, o, state_in, norm_in, state_out, norm_out,
+                      workspace, workspace_bytes, stream);
+}
+
+ls_status ls_gdn_frame_forward_prologue(const ls_shape* s, const ls_prologue* prologue, float key_scale, const void* q,
+                                        const void* k, const void* v, const float* alpha, const float* beta, void* o,
+                                        const float* state_in, float* state_out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  return gdn_forward(s, nullptr, prologue, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out,
+                     workspace, workspace_bytes, stream);
 }
 
 ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
                                const void* v, const float* alpha, const float* beta, void* o,
                                const float* state_in, float* state_out, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+  return gdn_forward(s, nullptr, nullptr, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
                      workspace_bytes, stream);
 }
 
@@ -632,7 +689,7 @@ ls_status ls_gdn_frame_forward_token_gate(const ls_shape* s, float key_scale, co
                                           const void* v, const float* alpha, const float* beta, void* o,
                                           const float* state_in, float* state_out, void* workspace,
                                           size_t workspace_bytes, void* stream) {
-  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, true, 0, o, state_in, state_out, workspace,
+  return gdn_forward(s, nullptr, nullptr, key_scale, q, k, v, alpha, beta, true, 0, o, state_in, state_out, workspace,
                      workspace_bytes, stream);
 }
 
@@ -641,7 +698,7 @@ ls_status ls_gdn_frame_forward_reversed(const ls_shape* s, int chunk_frames, flo
                                         void* o, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (chunk_frames < 1) return fail(LS_ERR_BAD_PARAM, "chunk_frames must be >= 1 (got %d)", chunk_frames);
-  return gdn_forward(s, nullptr, key_scale, q, k, v, alpha, beta, false, chunk_frames, o, nullptr, nullptr,
+  return gdn_forward(s, nullptr, nullptr, key_scale, q, k, v, alpha, beta, false, chunk_frames, o, nullptr, nullptr,
                      workspace, workspace_bytes, stream);
 }
 

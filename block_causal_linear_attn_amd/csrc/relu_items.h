@@ -32,11 +32,13 @@ constexpr int relu_summary_lds_bytes() {
 // Work item `wg` = (frame of one head) * nc + token chunk: dS, dz partials of
 // the chunk -> partial[wg]; item (frame 0, chunk 0) of each head also copies
 // (S0, z0) into init[head].
-template <int D>
+// PRO: the per-token prologue may be on (a separate instantiation keeps the
+// registers of the plain item).
+template <int D, bool PRO = false>
 __device__ __forceinline__ void relu_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
     const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk,
-    long wg, uint8_t* lds_raw, TokLayout L) {
+    long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int DB = D / 32;            // 32-wide dimension blocks
   constexpr int TILE = 64;              // tokens per wave per step
   constexpr int ROW = D;                // unpadded rows, chunks swizzled by token
@@ -55,6 +57,12 @@ __device__ __forceinline__ void relu_summary_item(
   const uint16_t* vf = v + L.base(bhf);
   uint16_t* kl = lds[wave][0];
   uint16_t* vl = lds[wave][1];
+  // the prologue's key weights of the head (RMSNorm), in LDS after the tiles
+  float* wl = reinterpret_cast<float*>(lds_raw + relu_summary_lds_bytes<D>());
+  if (PRO && P.wk) {
+    if (threadIdx.x < D) wl[threadIdx.x] = P.wk[(size_t)((bhf / L.F) % L.H) * D + threadIdx.x];
+    __syncthreads();
+  }
 
   floatx16 acc[DB][DB];
   floatx16 accz[DB];
@@ -91,6 +99,12 @@ __device__ __forceinline__ void relu_summary_item(
       const bool live = t0 + tok < n1;
       u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
+      if (PRO && P.wk) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
+        float wk8[8];
+        const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
+        wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
+        kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / D, [](double x) { return group_sum_f64<CPR>(x); });
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
       uint2* kd = reinterpret_cast<uint2*>(kl + swz_offset<CPR>(tok, cb));
@@ -159,14 +173,16 @@ constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4 + 4 * 32 * 
 // Work item `wg` = (frame of one head) * nco + token chunk: the frame's state
 // from init + partials, then o = S phi(q) / (z . phi(q) + eps) for the chunk;
 // the last frame's chunk-0 item writes the final state.
-template <int D>
+template <int D, bool PRO = false>
 __device__ __forceinline__ void relu_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
     const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
-    int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
+    int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
   constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
-  constexpr int U = 4;        // 32-token groups per wave per step
+  // 32-token groups per wave per step (two with the D = 64 prologue: its
+  // fp64 RMSNorm does not fit beside four groups of fragments in registers)
+  constexpr int U = PRO && D >= 64 ? 2 : 4;
   constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
   constexpr int PITCH = D + 4;
   float* Ss = reinterpret_cast<float*>(lds_raw);  // [D][PITCH]
@@ -186,6 +202,9 @@ __device__ __forceinline__ void relu_output_item(
 
   // the state this frame reads: initial state plus every frame of its block and before
   relu_frame_state<D>(partial, init, bh, f, F, nc, bfr, Ss, PITCH, zs);
+  // the prologue's query weights of the head (RMSNorm), in LDS after the rest
+  float* wql = reinterpret_cast<float*>(lds_raw + relu_output_lds_bytes<D>());
+  if (PRO && P.wq && threadIdx.x < D) wql[threadIdx.x] = P.wq[(size_t)(bh % L.H) * D + threadIdx.x];
   __syncthreads();
   if (f == F - 1 && wg % nco == 0) {  // the last frame's state is the call's final state
     for (int e = threadIdx.x; e < D * D; e += 256) {
@@ -235,6 +254,29 @@ __device__ __forceinline__ void relu_output_item(
   auto compute = [&](u32x4 (&b)[U][KS], int t0, const bool full) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (PRO && P.wq) {  // RMSNorm of token col's query: this lane holds its dims 16 s + 8 g + 0..7
+        // in fp64, rounded once to bf16 (as prologue_bf16x8)
+        double ss = 0.0;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const double x0 = bf16lo_to_f32(b[u][s][e]), x1 = bf16hi_to_f32(b[u][s][e]);
+            ss = fma(x0, x0, fma(x1, x1, ss));
+          }
+        ss += __shfl_xor(ss, 32);  // the partner lane holds the token's other dims
+        const double inv = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const float4 a = *reinterpret_cast<const float4*>(wql + 16 * s + 8 * g);
+          const float4 c = *reinterpret_cast<const float4*>(wql + 16 * s + 8 * g + 4);
+          const float wv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            b[u][s][e] = pack_bf16x2_f64((double)bf16lo_to_f32(b[u][s][e]) * (double)wv[2 * e] * inv,
+                                         (double)bf16hi_to_f32(b[u][s][e]) * (double)wv[2 * e + 1] * inv);
+        }
+      }
       float den = 0.0f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {

@@ -12,6 +12,8 @@
 #include "kernels.h"
 #include "sync.h"
 
+#include <type_traits>
+
 namespace linscan {
 
 namespace {
@@ -23,14 +25,17 @@ namespace {
 // keeps every summary an output item waits for at a lower block id.  Within
 // a step items are head-minor with B*H padded to BHp (a multiple of 8);
 // padding items leave at once.
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
     const float* z0, float* S_out, float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr,
-    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L) {
-  constexpr int LDS = relu_summary_lds_bytes<D>() > relu_output_lds_bytes<D>() ? relu_summary_lds_bytes<D>()
-                                                                                : relu_output_lds_bytes<D>();
+    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L,
+    Prologue P) {
+  // (each item keeps the prologue's D weights after its own LDS)
+  constexpr int LDS = (relu_summary_lds_bytes<D>() > relu_output_lds_bytes<D>() ? relu_summary_lds_bytes<D>()
+                                                                                 : relu_output_lds_bytes<D>()) +
+                      D * 4;
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
   const long bh = L.head_of_slot(b % bhp);
@@ -54,14 +59,14 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     c = (int)(r % nco);
   }
   if (summary) {
-    relu_summary_item<D>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L);
+    relu_summary_item<D, PRO>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L, P);
     publish(&flags[bh * F + f], epoch);
     return;
   }
   const int fend = min(F, (f / bfr + 1) * bfr);
   wait_all(&flags[bh * F], fend, epoch, err);
-  relu_output_item<D>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
-                      (bh * F + f) * nco + c, lds, L);
+  relu_output_item<D, PRO>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
+                      (bh * F + f) * nco + c, lds, L, P);
 }
 
 }  // namespace
@@ -70,21 +75,21 @@ bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D 
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
   const long grid = (long)a.F * bhp * (1 + a.nco);
-  const void* kern = a.D == 32 ? (const void*)relu_fused_mfma<32> : (const void*)relu_fused_mfma<64>;
-  const int lag = fused_lag(device_slots(kern), bhp * (1 + a.nco), a.bfr, a.F);
-  if (a.D == 32)
-    hipLaunchKernelGGL(relu_fused_mfma<32>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
-                       a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
-                       epoch, err, a.L);
-  else if (a.D == 64)
-    hipLaunchKernelGGL(relu_fused_mfma<64>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0,
-                       a.z0, a.S_out, a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags,
-                       epoch, err, a.L);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const bool pro = a.P.wq != nullptr || a.P.wk != nullptr;
+  auto pick = [&](auto d) {
+    constexpr int D = decltype(d)::value;
+    return pro ? relu_fused_mfma<D, true> : relu_fused_mfma<D, false>;
+  };
+  auto run = [&](auto kern) {
+    const int lag = fused_lag(device_slots((const void*)kern), bhp * (1 + a.nco), a.bfr, a.F);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0, a.z0, a.S_out, a.z_out, a.eps,
+                       a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err, a.L, a.P);
+    return hipGetLastError();
+  };
+  if (a.D == 32) return run(pick(std::integral_constant<int, 32>{}));
+  if (a.D == 64) return run(pick(std::integral_constant<int, 64>{}));
+  return hipErrorInvalidValue;
 }
 
 }  // namespace linscan

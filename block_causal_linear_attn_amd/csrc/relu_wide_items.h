@@ -37,28 +37,10 @@ namespace linscan {
 constexpr int kReluWide = 128;                                   // padded head dim
 constexpr int kReluWideRec = kReluWide * kReluWide + kReluWide;  // floats per cumulative record
 constexpr int kReluWideDepth = 2;                                // tiles in flight per summary item
-constexpr int kReluWideSumLds = 2 * 2 * 64 * kReluWide * 2;      // K, V tiles, double buffered
+constexpr int kReluWideSumLds = 2 * 2 * 64 * kReluWide * 2;      // K, V tiles, double buffered (+ weights)
 constexpr int kReluWideOutPitch = kReluWide + 8;
 // query tiles and output staging tiles (double buffered, bf16) + per-token denominators
 constexpr int kReluWideOutLds = 4 * 64 * kReluWideOutPitch * 2 + 2 * 64 * 4;
-
-// Sum over the 16 lanes of a DPP row (every lane of the row gets the sum).
-__device__ __forceinline__ float row16_sum(float x) {
-  auto step = [](float v, int ctrl) {
-    int s;
-    switch (ctrl) {  // the DPP control must be a constant
-      case 0: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false); break;   // lanes ^1
-      case 1: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false); break;   // lanes ^2
-      case 2: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); break;  // half-row mirror
-      default: s = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); break; // row mirror
-    }
-    return v + __int_as_float(s);
-  };
-  x = step(x, 0);  // pairs
-  x = step(x, 1);  // quads
-  x = step(x, 2);  // lane i + lane 7 - i within 8: both quads of the half-row
-  return step(x, 3);  // lane i + lane 15 - i: both half-rows
-}
 
 // Summary item of frame f of head bh: cum[bh][f] = cum[bh][f - 1] + (dS, dz),
 // with cum[bh][-1] the initial state (S0, z0; zero where NULL).  The last
@@ -69,7 +51,7 @@ template <int DI>
 __device__ __forceinline__ void relu_wide_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ cum,
     const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f,
-    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L) {
+    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -84,6 +66,12 @@ __device__ __forceinline__ void relu_wide_summary_item(
   const long bhf = bh * F + f;
   const uint16_t* kf = k + L.base(bhf);
   const uint16_t* vf = v + L.base(bhf);
+  // the prologue's key weights of the head (RMSNorm), in LDS after the tiles
+  float* wl = reinterpret_cast<float*>(lds_raw + kReluWideSumLds);
+  if (P.wk) {
+    if (tid < D) wl[tid] = tid < DI ? P.wk[(size_t)(bh % L.H) * DI + tid] : 0.0f;
+    __syncthreads();
+  }
 
   // z: with DI < 128, value dim DI (zero padding) is set to 1 for every live
   // token, so row DI of dS is dz at no cost; at DI = 128 an MFMA with an
@@ -123,6 +111,12 @@ __device__ __forceinline__ void relu_wide_summary_item(
       const int tok = ci >> 4, cb = ci & 15;
       const bool live = t0 + tok < N && cb < CI;
       u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      if (P.wk) {  // the 16 lanes of a DPP row hold the 16 chunks of token `tok`
+        float wk8[8];
+        const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
+        wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
+        kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
+      }
       u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
       if (ZROW) vv[0] = t0 + tok < N && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
 #pragma unroll
@@ -228,7 +222,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
 template <int DI>
 __device__ __forceinline__ void relu_wide_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ cum, float eps,
-    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L) {
+    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -288,6 +282,8 @@ __device__ __forceinline__ void relu_wide_output_item(
       X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
     }
   };
+  float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
+  load_weights8(P.wq, bh % L.H, DI, (tid & 15) * 8, wq8);
   // phi(q) into LDS buffer buf, and each token's denominator into den[buf]
   auto stage = [&](const Regs& X, int buf) {
 #pragma unroll
@@ -295,6 +291,7 @@ __device__ __forceinline__ void relu_wide_output_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       u32x4 w = cb < CI ? X.q[r] : u32x4{0u, 0u, 0u, 0u};
+      if (P.wq) w = prologue_bf16x8(w, wq8, true, P, false, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
       float d = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -303,7 +300,7 @@ __device__ __forceinline__ void relu_wide_output_item(
         d = fmaf(zr[2 * e + 1], bf16hi_to_f32(w[e]), d);
       }
       *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = w;
-      d = row16_sum(d);  // the 16 lanes of a DPP row hold the 16 chunks of this token
+      d = group_sum<16>(d);  // the 16 lanes of a DPP row hold the 16 chunks of this token
       if (cb == 0) den[buf][tok] = d;
     }
   };

@@ -25,14 +25,15 @@ namespace linscan {
 
 namespace {
 
-constexpr int kReluWideLds = kReluWideSumLds > kReluWideOutLds ? kReluWideSumLds : kReluWideOutLds;
+constexpr int kReluWideLds = kReluWideSumLds + kReluWide * 4 > kReluWideOutLds ? kReluWideSumLds + kReluWide * 4
+                                                                                : kReluWideOutLds;
 
 template <int DI>
 __global__ __launch_bounds__(256, 2) void relu_wide_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ cum, const float* S0, const float* z0, float* S_out,
     float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr, int nco, int chunko, int lag,
-    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L) {
+    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L, Prologue P) {
   __shared__ __align__(16) uint8_t lds[kReluWideLds];
   const long b = blockIdx.x;
   const long bh = L.head_of_slot(b % bhp);
@@ -56,12 +57,12 @@ __global__ __launch_bounds__(256, 2) void relu_wide_fused_mfma(
     c = (int)(r % nco);
   }
   if (summary) {
-    relu_wide_summary_item<DI>(k, v, cum, S0, z0, S_out, z_out, F, N, bh, f, flags, epoch, err, lds, L);
+    relu_wide_summary_item<DI>(k, v, cum, S0, z0, S_out, z_out, F, N, bh, f, flags, epoch, err, lds, L, P);
     return;
   }
   const int fend = min(F, (f / bfr + 1) * bfr);
   wait_all(&flags[bh * F + fend - 1], 1, epoch, err);
-  relu_wide_output_item<DI>(q, o, cum, eps, F, N, bfr, nco, chunko, (bh * F + f) * nco + c, lds, L);
+  relu_wide_output_item<DI>(q, o, cum, eps, F, N, bfr, nco, chunko, (bh * F + f) * nco + c, lds, L, P);
 }
 
 template <typename Body>
@@ -83,7 +84,8 @@ hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* fl
     const int lag = a.F;
     hipLaunchKernelGGL(relu_wide_fused_mfma<DI>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.S0, a.z0, a.S_out,
-                       a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err, a.L);
+                       a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err, a.L,
+                       a.P);
     return hipGetLastError();
   });
 }

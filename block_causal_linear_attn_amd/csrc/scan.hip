@@ -18,11 +18,11 @@ namespace linscan {
 
 hipError_t launch_gdn_gram_mfma(int D, const void* k, const void* v, const float* gates, bool tg, void* rec,
                                 float c, float c2, long bhf, int N, int nc, int chunk, const TokLayout& L,
-                                hipStream_t st);
+                                const Prologue& P, hipStream_t st);
 hipError_t launch_gdn_scan_mfma(int D, const void* rec, const float* alpha, const float* S0,
                                 void* states, float* S_out, long bh, int F, int nc, int rchunk, hipStream_t st);
 hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* states, long bhf,
-                                  int N, int nco, int chunk, const TokLayout& L, hipStream_t st);
+                                  int N, int nco, int chunk, const TokLayout& L, const Prologue& P, hipStream_t st);
 
 namespace {
 
@@ -177,7 +177,7 @@ hipError_t launch_relu_output(const ScanArgs& a, hipStream_t st) {
 hipError_t launch_gdn_gram(const ScanArgs& a, hipStream_t st) {
   if (a.mfma)
     return launch_gdn_gram_mfma(a.D, a.k, a.v, a.tg ? a.gate : a.beta, a.tg, a.partial, a.c, a.c2, a.bhf, a.N, a.nc,
-                                a.chunk, a.L, st);
+                                a.chunk, a.L, a.P, st);
   return launch_summary_generic(a, st);
 }
 
@@ -194,7 +194,7 @@ hipError_t launch_gdn_scan(const ScanArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st) {
-  if (a.mfma) return launch_gdn_output_mfma(a.D, a.q, a.o, a.states, a.bhf, a.N, a.nco, a.chunko, a.L, st);
+  if (a.mfma) return launch_gdn_output_mfma(a.D, a.q, a.o, a.states, a.bhf, a.N, a.nco, a.chunko, a.L, a.P, st);
   return launch_output_generic(a, st);
 }
 

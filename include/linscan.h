@@ -112,6 +112,27 @@ typedef struct {
 } ls_strides;
 
 /*
+ * Per-token prologue of the *_prologue entry points, applied to q and k as
+ * the scan loads them (SANA-WM digest, paragraph on context parallelism and
+ * the fused kernel: RMSNorm, ReLU and the key scaling fused into the GDN
+ * scan; SANA-Video's linear attention normalises q and k before its ReLU
+ * feature map).  For each token row x (the D channels of one head):
+ *   RMSNorm  x <- x / sqrt(mean(x^2) + eps) * weight[h][:]   (weight not NULL)
+ *   ReLU     x <- max(x, 0)                                   (GDN, relu = 1)
+ *   L2       x <- x / |x|, 0 staying 0                        (GDN keys, l2_keys = 1)
+ * in that order, before the scan's own feature map (ReLU scan) or key scale
+ * (GDN).  Sums are fp32; for bf16 tokens the result enters the contractions
+ * rounded to bf16, as a separate pass writing bf16 would give.
+ */
+typedef struct {
+  const float* q_weight;  /* [H][D] fp32 RMSNorm weights of q, or NULL: q not normalised */
+  const float* k_weight;  /* [H][D] fp32 RMSNorm weights of k, or NULL */
+  float eps;              /* RMSNorm epsilon, finite and > 0 when a weight is given */
+  int relu;               /* GDN only: 1 = ReLU on q and k after their norms */
+  int l2_keys;            /* GDN only: 1 = keys divided by their L2 norm, last */
+} ls_prologue;
+
+/*
  * Workspace bytes ls_relu_block_forward needs for `shape` and `block_frames`
  * (0 if the shape is invalid).  The size depends on the shape only.
  */
@@ -156,6 +177,18 @@ ls_status ls_relu_block_forward_strided(const ls_shape* shape, const ls_strides*
                                         const float* state_in, const float* norm_in, float* state_out,
                                         float* norm_out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ls_relu_block_forward with the per-token prologue `prologue` (NULL: none;
+ * relu and l2_keys must be 0: the scan applies its own ReLU feature map).
+ * Weights 16-byte aligned (LS_ERR_MISALIGNED) and not overlapping any output
+ * or the workspace (LS_ERR_ALIASING); a bad eps or flag is LS_ERR_BAD_PARAM.
+ * Workspace size and everything else as ls_relu_block_forward.
+ */
+ls_status ls_relu_block_forward_prologue(const ls_shape* shape, const ls_prologue* prologue, int block_frames,
+                                         float eps, const void* q, const void* k, const void* v, void* o,
+                                         const float* state_in, const float* norm_in, float* state_out,
+                                         float* norm_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes ls_gdn_frame_forward needs for `shape` (0 if invalid). */
 size_t ls_gdn_frame_workspace_size(const ls_shape* shape);
 
@@ -192,6 +225,17 @@ ls_status ls_gdn_frame_forward_strided(const ls_shape* shape, const ls_strides* 
                                        const float* alpha, const float* beta, void* o,
                                        const float* state_in, float* state_out,
                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ls_gdn_frame_forward with the per-token prologue `prologue` (NULL: none),
+ * which runs before the key scale.  Argument checks of the weights as for
+ * ls_relu_block_forward_prologue; everything else as ls_gdn_frame_forward.
+ */
+ls_status ls_gdn_frame_forward_prologue(const ls_shape* shape, const ls_prologue* prologue, float key_scale,
+                                        const void* q, const void* k, const void* v,
+                                        const float* alpha, const float* beta, void* o,
+                                        const float* state_in, float* state_out,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Frame-wise Gated DeltaNet with a per-token update gate (SANA-WM summary,

@@ -159,6 +159,25 @@ def test_validation_errors_strided(lib):
     assert rs(S(-1, 32, 10 * 4 * 32, 4 * 32)) == 7
 
 
+def test_validation_errors_prologue(lib):
+    shp = _shape(lib, B=1, H=2, F=3, N=10, D=32)
+    Pr = lib.ls_prologue
+    def rp(pr):
+        return lib.lib.ls_relu_block_forward_prologue(ctypes.byref(shp), ctypes.byref(pr), 1, 1e-6, P[0], P[1], P[2],
+                                                      P[3], None, None, P[4], P[5], P[6], 1, None)
+    def gp(pr):
+        return lib.lib.ls_gdn_frame_forward_prologue(ctypes.byref(shp), ctypes.byref(pr), 0.0, P[0], P[1], P[2],
+                                                     P[7], P[8], P[3], None, P[4], P[6], 1, None)
+    w = P[10].value
+    assert rp(Pr(w, w, 1e-6, 0, 0)) == 6 and gp(Pr(w, w, 1e-6, 1, 1)) == 6   # valid: workspace too small
+    assert rp(Pr(w, None, 1e-6, 1, 0)) == 7                                  # no ReLU flag on the ReLU scan
+    assert rp(Pr(None, None, 1e-6, 0, 1)) == 7
+    assert gp(Pr(w, None, 0.0, 0, 0)) == 7                                   # eps must be > 0 with weights
+    assert gp(Pr(None, None, 0.0, 2, 0)) == 7
+    assert gp(Pr(w + 4, None, 1e-6, 0, 0)) == 5                              # misaligned weights
+    assert gp(Pr(P[3].value, None, 1e-6, 0, 0)) == 8                         # weights inside o
+
+
 def test_in_place_state_is_not_an_aliasing_error(lib):
     """state_out == state_in is allowed; the call then fails only on the workspace check."""
     shp = _shape(lib)

@@ -554,3 +554,98 @@ def test_gdn_strided_layout(ls, gen, oracle_mod, B, H, F, N, D, dt):
     check(tag + " o", o2, ro, TOL[dt][0], dt)
     check(tag + " S", S2, rS, TOL[dt][1], dt)
     assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1)
+
+
+# --------------------------------------------------------------------------- fused per-token prologue
+def _weights(H, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return 1.0 + 0.5 * torch.randn((H, D), generator=g), 1.0 + 0.5 * torch.randn((H, D), generator=g)
+
+
+@pytest.mark.parametrize("H,F,N,D,dt,qw,kw", [(3, 4, 333, 32, "bf16", True, True), (2, 3, 200, 64, "bf16", True, True),
+                                              (3, 3, 200, 112, "bf16", True, False), (2, 3, 150, 128, "bf16", False, True),
+                                              (2, 3, 50, 16, "bf16", True, True), (2, 3, 40, 48, "fp32", True, True)])
+def test_relu_prologue_parity(ls, gen, oracle_mod, H, F, N, D, dt, qw, kw):
+    x = gen.relu_inputs(1, H, F, N, D, dt, seed=51, part=N)
+    wq, wk = _weights(H, D, 52)
+    wq, wk = (wq if qw else None), (wk if kw else None)
+    xd = _dev(x)
+    o, S, z = ls.ls_relu_block_forward_prologue(xd["q"], xd["k"], xd["v"], None if wq is None else wq.to(DEV),
+                                                None if wk is None else wk.to(DEV), norm_eps=1e-5)
+    torch.cuda.synchronize()
+    rnd = "bf16" if dt == "bf16" else None
+    qp = oracle_mod.prologue(x["q"], wq, eps=1e-5, round_to=rnd) if qw else x["q"]
+    kp = oracle_mod.prologue(x["k"], wk, eps=1e-5, round_to=rnd) if kw else x["k"]
+    ro, rS, rz = oracle_mod.relu_block(qp, kp, x["v"])
+    tag = "relu prologue H%d F%d N%d D%d %s q%d k%d" % (H, F, N, D, dt, qw, kw)
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+    check(tag + " z", z, rz, TOL[dt][1], dt)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,qw,kw,relu,l2", [
+    (1, 3, 4, 300, 128, "bf16", True, True, True, True),      # frame-interleaved launch, the whole prologue
+    (1, 40, 2, 130, 128, "bf16", True, True, True, False),    # phased launch
+    (2, 2, 3, 97, 112, "bf16", False, True, False, True),     # head dim 112: RMSNorm + L2 of keys
+    (1, 2, 3, 200, 128, "bf16", False, False, True, False),   # ReLU alone
+    (1, 2, 3, 80, 64, "bf16", True, True, True, True),        # generic bf16 kernels
+    (1, 2, 3, 40, 32, "fp32", True, True, True, True),        # generic fp32 kernels
+])
+def test_gdn_prologue_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, qw, kw, relu, l2):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=53, part=N, l2_keys=False)
+    wq, wk = _weights(H, D, 54)
+    wq, wk = (wq if qw else None), (wk if kw else None)
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward_prologue(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
+                                            None if wq is None else wq.to(DEV), None if wk is None else wk.to(DEV),
+                                            norm_eps=1e-5, relu=relu, l2_keys=l2)
+    torch.cuda.synchronize()
+    rnd = "bf16" if dt == "bf16" else None
+    qp = oracle_mod.prologue(x["q"], wq, eps=1e-5, relu=relu, round_to=rnd) if (qw or relu) else x["q"]
+    kp = oracle_mod.prologue(x["k"], wk, eps=1e-5, relu=relu, l2=l2, round_to=rnd) if (kw or relu or l2) else x["k"]
+    ro, rS = oracle_mod.gdn_frame(qp, kp, x["v"], x["alpha"], x["beta"])
+    tag = "gdn prologue B%d H%d F%d N%d D%d %s q%d k%d r%d l%d" % (B, H, F, N, D, dt, qw, kw, relu, l2)
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+
+
+def _as_tokens(a, dt):
+    """Oracle values (already exact in the token precision) as a device token tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.float32)
+    return (t.to(torch.bfloat16) if dt == "bf16" else t).to(DEV)
+
+
+@pytest.mark.parametrize("H,F,N,D,dt", [(3, 4, 333, 32, "bf16"), (2, 3, 200, 64, "bf16"), (3, 3, 200, 112, "bf16"),
+                                        (2, 3, 150, 128, "bf16"), (2, 3, 50, 16, "bf16"), (2, 3, 40, 48, "fp32")])
+def test_relu_prologue_matches_plain_scan_bitwise(ls, gen, oracle_mod, H, F, N, D, dt):
+    """The fused prologue rounds its fp64 result once to the token precision,
+    as the oracle does: the scan of the fused call is then the plain scan of
+    the oracle's prologue output, bit for bit."""
+    x = gen.relu_inputs(1, H, F, N, D, dt, seed=55, part=N)
+    wq, wk = _weights(H, D, 56)
+    xd = _dev(x)
+    o, S, z = ls.ls_relu_block_forward_prologue(xd["q"], xd["k"], xd["v"], wq.to(DEV), wk.to(DEV), norm_eps=1e-5)
+    rnd = "bf16" if dt == "bf16" else None
+    qp = oracle_mod.prologue(x["q"], wq, eps=1e-5, round_to=rnd)
+    kp = oracle_mod.prologue(x["k"], wk, eps=1e-5, round_to=rnd)
+    o2, S2, z2 = ls.ls_relu_block_forward(_as_tokens(qp, dt), _as_tokens(kp, dt), xd["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2) and torch.equal(z, z2)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,relu,l2", [
+    (1, 3, 4, 300, 128, "bf16", True, True), (1, 40, 2, 130, 128, "bf16", False, True),
+    (1, 3, 4, 300, 128, "bf16", False, False), (2, 2, 3, 97, 112, "bf16", True, False),
+    (1, 2, 3, 80, 64, "bf16", True, True), (1, 2, 3, 40, 32, "fp32", False, True)])
+def test_gdn_prologue_matches_plain_scan_bitwise(ls, gen, oracle_mod, B, H, F, N, D, dt, relu, l2):
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=57, part=N, l2_keys=False)
+    wq, wk = _weights(H, D, 58)
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward_prologue(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], wq.to(DEV),
+                                            wk.to(DEV), norm_eps=1e-5, relu=relu, l2_keys=l2)
+    rnd = "bf16" if dt == "bf16" else None
+    qp = oracle_mod.prologue(x["q"], wq, eps=1e-5, relu=relu, round_to=rnd)
+    kp = oracle_mod.prologue(x["k"], wk, eps=1e-5, relu=relu, l2=l2, round_to=rnd)
+    o2, S2 = ls.ls_gdn_frame_forward(_as_tokens(qp, dt), _as_tokens(kp, dt), xd["v"], xd["alpha"], xd["beta"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2)
