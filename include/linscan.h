@@ -121,8 +121,9 @@ typedef struct {
  *   ReLU     x <- max(x, 0)                                   (GDN, relu = 1)
  *   L2       x <- x / |x|, 0 staying 0                        (GDN keys, l2_keys = 1)
  * in that order, before the scan's own feature map (ReLU scan) or key scale
- * (GDN).  Sums are fp32; for bf16 tokens the result enters the contractions
- * rounded to bf16, as a separate pass writing bf16 would give.
+ * (GDN).  The arithmetic is fp64 and the result enters the contractions
+ * rounded once to the token precision (bf16: nearest, ties to even), as a
+ * separate exact pass writing the token dtype would give.
  */
 typedef struct {
   const float* q_weight;  /* [H][D] fp32 RMSNorm weights of q, or NULL: q not normalised */
