@@ -136,6 +136,34 @@ def token_gates(B, H, F, N, seed, part=0, device="cpu"):
     return torch.sigmoid(torch.randn((B, H, F, N), generator=g, device=device)).contiguous()
 
 
+def rope_tables(T, N, W, D, frame_pairs, base=10000.0, device="cpu"):
+    """(cos, sin) tables of a 3D rotary embedding at synthetic positions.
+
+    Positions: frame t in [0, T); token n of a frame at row n // W, column
+    n % W of the latent grid.  The first `frame_pairs` channel pairs turn with
+    the frame index, the remaining pairs split between row (first half) and
+    column; pair j of an axis group of m pairs has frequency base^(-j/m).
+    Returns (frame_cs [T, frame_pairs, 2], token_cs [N, D/2 - frame_pairs, 2])
+    float32, angles formed in float64 and rounded once.
+    """
+    half = D // 2
+    sp = half - frame_pairs
+    rows = sp // 2
+
+    def table(pos, m):
+        j = torch.arange(m, dtype=torch.float64)
+        ang = pos[:, None].double() * base ** (-j / max(m, 1))[None, :]
+        return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1)
+
+    frame_cs = table(torch.arange(T), frame_pairs) if frame_pairs > 0 else None
+    token_cs = None
+    if sp > 0:
+        n = torch.arange(N)
+        token_cs = torch.cat([table(n // W, rows), table(n % W, sp - rows)], dim=1)
+    cast = lambda t: None if t is None else t.to(torch.float32).contiguous().to(device)
+    return cast(frame_cs), cast(token_cs)
+
+
 def relu_inputs(B, H, F, N, D, dtype="bf16", seed=0, part=0, device="cpu"):
     """q, k, v for the ReLU linear-attention scan."""
     return {

@@ -204,7 +204,7 @@ def temporal_conv3(x, weight, bias=None, carry=None, block_frames: int = 1, with
     return y, co
 
 
-def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = False, round_to=None):
+def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = False, round_to=None, rope=None):
     """The per-token prologue fused into the scans' load stage, fp64.
 
     The SANA-WM digest (paragraph on context parallelism and the fused kernel)
@@ -214,6 +214,7 @@ def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = F
       RMSNorm:  x <- x / sqrt(mean(x^2) + eps) * weight[h]   (when weight is given)
       ReLU:     x <- max(x, 0)                               (when relu)
       L2:       x <- x / |x|  (0 stays 0)                     (when l2)
+      RoPE:     rope_rotate(x, *rope)                         (when rope is given)
     x: [B, H, F, N, D]; weight: [H, D] or None.  round_to = "bf16" rounds the
     result to bfloat16 (nearest even), the precision in which the scan
     consumes it for bf16 tokens.  Returns float64 (or the rounded values as
@@ -230,9 +231,45 @@ def prologue(x, weight=None, eps: float = 1e-6, relu: bool = False, l2: bool = F
     if l2:
         nrm = np.sqrt(np.sum(y * y, axis=-1, keepdims=True))
         y = np.where(nrm > 0, y / np.where(nrm > 0, nrm, 1.0), 0.0)
+    if rope is not None:
+        y = rope_rotate(y, *rope)
     if round_to == "bf16":
         y = round_bf16(y)
     return y
+
+
+def rope_rotate(x, frame_cs, token_cs, frame_pairs: int, frame_offset: int = 0):
+    """Rotary position embedding of the token rows, fp64.
+
+    The SANA-WM digest (paragraph on context parallelism and the fused kernel)
+    lists the positional encoding among the steps fused into the GDN scan, and
+    SANA-Video's talk uses a 3D RoPE in its linear attention.  Each channel
+    pair (x[2i], x[2i+1]) of the token of frame f (of the call) and index n
+    turns by an angle whose (cos, sin) the caller tabulates:
+        (x0, x1) <- (x0 cos - x1 sin, x0 sin + x1 cos)
+    with (cos, sin) = frame_cs[frame_offset + f, i] for i < frame_pairs (the
+    frame axis) and token_cs[n, i - frame_pairs] for the other pairs (the
+    spatial axes).  x: [B, H, F, N, D]; frame_cs: [T, frame_pairs, 2];
+    token_cs: [N, D/2 - frame_pairs, 2] (either None when it has no pairs).
+    """
+    y = np.asarray(_f32(x), dtype=np.float64) if not (isinstance(x, np.ndarray) and x.dtype == np.float64) else x
+    B, H, F, N, D = y.shape
+    half = D // 2
+    cos = np.empty((F, N, half))
+    sin = np.empty((F, N, half))
+    if frame_pairs > 0:
+        fc = np.asarray(_f32(frame_cs), dtype=np.float64)[frame_offset:frame_offset + F]
+        cos[:, :, :frame_pairs] = fc[:, None, :, 0]
+        sin[:, :, :frame_pairs] = fc[:, None, :, 1]
+    if frame_pairs < half:
+        tc = np.asarray(_f32(token_cs), dtype=np.float64)
+        cos[:, :, frame_pairs:] = tc[None, :, :, 0]
+        sin[:, :, frame_pairs:] = tc[None, :, :, 1]
+    x0, x1 = y[..., 0::2], y[..., 1::2]
+    out = np.empty_like(y)
+    out[..., 0::2] = x0 * cos - x1 * sin
+    out[..., 1::2] = x0 * sin + x1 * cos
+    return out
 
 
 def round_bf16(y):
