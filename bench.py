@@ -234,7 +234,7 @@ def main():
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
     conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
     strided = None if args.no_strided else time_strided(torch, ls, calls[0], g)
-    pro = None if args.no_prologue else time_prologue(torch, ls, calls[0], g)
+    pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     cpu = None
@@ -453,13 +453,14 @@ def time_strided(torch, ls, relu_call, g, reps=4):
     return res
 
 
-def time_prologue(torch, ls, relu_call, g, reps=4):
+def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
     """The per-token prologue fused into the load stage: one 10-frame ReLU call
     of the rollout with RMSNorm (weights) on q and k, and the GDN call with
-    RMSNorm on q and k, ReLU and L2 keys, against the same calls without a
-    prologue (mean kernel time from the library's per-launch events), and the
-    GDN call after the same prologue as separate torch ops (wall time of both,
-    CUDA events), which reads and writes q and k once more."""
+    RMSNorm on q and k, ReLU and L2 keys (and once more with a 3D rotary
+    embedding), against the same calls without a prologue (mean kernel time
+    from the library's per-launch events), and the GDN call after the same
+    prologue as separate torch ops (wall time of both, CUDA events), which
+    reads and writes q and k once more."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
@@ -511,11 +512,21 @@ def time_prologue(torch, ls, relu_call, g, reps=4):
         b.record()
     torch.cuda.synchronize()
     ms_unfused = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    # 3D rotary embedding at synthetic positions: 16 pairs by frame, 48 by the
+    # 23 x 40 latent grid's rows and columns
+    fcs, tcs = inputs.rope_tables(g["q"].shape[2], g["q"].shape[3], 40, D, 16, device=dev)
+
+    def fused_rope():
+        ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk, norm_eps=1e-6,
+                                         relu=True, l2_keys=True, out=out, rope=(fcs, tcs, 16, 0))
+
     res["gdn_h24_d128_181_frames_rmsnorm_relu_l2_us"] = {
         "plain": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out),
                            "gdn_fused"),
         "fused_prologue": kernel_us(fused, "gdn_fused"),
+        "fused_prologue_with_3d_rope": kernel_us(fused_rope, "gdn_fused"),
         "torch_prologue_then_plain_wall": round(1e3 * ms_unfused, 2)}
+    del fcs, tcs
     return res
 
 

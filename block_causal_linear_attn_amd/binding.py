@@ -30,7 +30,9 @@ class ls_strides(ctypes.Structure):
 
 class ls_prologue(ctypes.Structure):
     _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p), ("eps", ctypes.c_float),
-                ("relu", ctypes.c_int), ("l2_keys", ctypes.c_int)]
+                ("relu", ctypes.c_int), ("l2_keys", ctypes.c_int), ("rope_frame", ctypes.c_void_p),
+                ("rope_token", ctypes.c_void_p), ("rope_frame_pairs", ctypes.c_int),
+                ("rope_frame_offset", ctypes.c_int), ("rope_frames", ctypes.c_longlong)]
 
 
 class LinscanError(RuntimeError):
@@ -297,12 +299,26 @@ def ls_gdn_frame_forward_strided(q, k, v, alpha, beta, state=None, key_scale=Non
     return o, so
 
 
-def _prologue(q, q_weight, k_weight, eps, relu, l2_keys):
+def _prologue(q, q_weight, k_weight, eps, relu, l2_keys, rope=None):
+    """rope: None, or (frame_cs, token_cs, frame_pairs, frame_offset) with frame_cs [T, frame_pairs, 2] and
+    token_cs [N, D/2 - frame_pairs, 2] fp32 (cos, sin) tables on the device (either None when unused)."""
     B, H, F, N, D = q.shape
     _f32("q_weight", q_weight, (H, D), q.device)
     _f32("k_weight", k_weight, (H, D), q.device)
-    return ls_prologue(None if q_weight is None else q_weight.data_ptr(),
-                       None if k_weight is None else k_weight.data_ptr(), float(eps), int(relu), int(l2_keys))
+    pr = ls_prologue(None if q_weight is None else q_weight.data_ptr(),
+                     None if k_weight is None else k_weight.data_ptr(), float(eps), int(relu), int(l2_keys))
+    if rope is not None:
+        frame_cs, token_cs, pf, off = rope
+        if frame_cs is not None:
+            if frame_cs.dim() != 3:
+                raise ValueError("rope frame table must be [T, frame_pairs, 2]")
+            _f32("rope frame table", frame_cs, (frame_cs.shape[0], pf, 2), q.device)
+            pr.rope_frame, pr.rope_frames = frame_cs.data_ptr(), frame_cs.shape[0]
+        _f32("rope token table", token_cs, (N, D // 2 - pf, 2), q.device)
+        if token_cs is not None:
+            pr.rope_token = token_cs.data_ptr()
+        pr.rope_frame_pairs, pr.rope_frame_offset = int(pf), int(off)
+    return pr
 
 
 def ls_relu_block_forward_prologue(q, k, v, q_weight=None, k_weight=None, norm_eps: float = 1e-6, state=None,
@@ -334,14 +350,15 @@ def ls_relu_block_forward_prologue(q, k, v, q_weight=None, k_weight=None, norm_e
 
 def ls_gdn_frame_forward_prologue(q, k, v, alpha, beta, q_weight=None, k_weight=None, norm_eps: float = 1e-6,
                                   relu: bool = False, l2_keys: bool = False, state=None, key_scale=None, out=None,
-                                  state_out=None, ws=None):
-    """ls_gdn_frame_forward with the per-token prologue (RMSNorm, ReLU, L2 of keys) fused into the load."""
+                                  state_out=None, ws=None, rope=None):
+    """ls_gdn_frame_forward with the per-token prologue (RMSNorm, ReLU, L2 of keys, rotary embedding) fused
+    into the load; rope as for _prologue."""
     _tokens("q", q)
     _tokens("k", k, q)
     _tokens("v", v, q)
     B, H, F, N, D = q.shape
     dev = q.device
-    pr = _prologue(q, q_weight, k_weight, norm_eps, relu, l2_keys)
+    pr = _prologue(q, q_weight, k_weight, norm_eps, relu, l2_keys, rope)
     _f32("alpha", alpha, (B, H, F), dev)
     _f32("beta", beta, (B, H, F), dev)
     _f32("state", state, (B, H, D, D), dev)

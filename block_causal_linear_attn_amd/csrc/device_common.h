@@ -126,9 +126,12 @@ __device__ __forceinline__ double group_sum_f64(double x) {
 // one channel in 10^4 to 10^5.  One such 2^-8 step in a key moves every later
 // state, and outputs that cancel (a query nearly orthogonal to the state's
 // rows) turn it into a large relative error.  In fp64 the chance is ~2^-40.
+//
+// cs: the (cos, sin) of the rotary embedding of these 4 channel pairs
+// (Prologue::rope8), or nullptr: no rotation.
 template <typename Red>
 __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], bool norm, const Prologue& P,
-                                                 bool is_k, double inv_d, Red red) {
+                                                 bool is_k, double inv_d, Red red, const float* cs = nullptr) {
   double x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -155,6 +158,16 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
     const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= inv;
+  }
+  if (cs) {
+    const float4 a = *reinterpret_cast<const float4*>(cs), b = *reinterpret_cast<const float4*>(cs + 4);
+    const float c[4] = {a.x, a.z, b.x, b.z}, s[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double x0 = x[2 * j], x1 = x[2 * j + 1];
+      x[2 * j] = x0 * (double)c[j] - x1 * (double)s[j];
+      x[2 * j + 1] = x0 * (double)s[j] + x1 * (double)c[j];
+    }
   }
   return u32x4{pack_bf16x2_f64(x[0], x[1]), pack_bf16x2_f64(x[2], x[3]), pack_bf16x2_f64(x[4], x[5]),
                pack_bf16x2_f64(x[6], x[7])};

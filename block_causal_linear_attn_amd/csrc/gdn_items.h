@@ -140,7 +140,9 @@ __device__ __forceinline__ void gdn_gram_item(
       if (PRO && P.on_k()) {
         float wk8[8];
         weights8_lds(wl, cb, wk8);
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16);
+        // rotary table row of this token (rows past the chunk: a real token's)
+        const float* cs = P.rope() ? P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI) : nullptr;
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, cs);
       }
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
@@ -309,7 +311,9 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       if (PRO && P.on_k()) {
         float wk8[8];
         weights8_lds(wl, ci & 15, wk8);
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16);
+        const int n = t0 + (ci >> 4);
+        const float* cs = P.rope() ? P.rope8(bhf % L.F, n < N ? n : 0, (ci & 15) < CI ? (ci & 15) : 0, DI) : nullptr;
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, cs);
       }
       uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -691,7 +695,8 @@ __device__ __forceinline__ void gdn_output_item(
   float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
   if (PRO) load_weights8(P.wq, (bhf / L.F) % L.H, DI, (tid & 15) * 8, wq8);
   auto row16 = [](double x) { return group_sum_f64<16>(x); };
-  auto stage = [&](const Regs& X, int buf) {
+  // t0: the first token of the staged tile (its rows past the chunk hold token n0)
+  auto stage = [&](const Regs& X, int buf, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
@@ -699,7 +704,8 @@ __device__ __forceinline__ void gdn_output_item(
       u32x4 qq = X.q[r];
       if (PRO && P.on_q()) {  // chunks past DI re-read a real chunk: zero them out of the token's sums
         qq = cb < CI ? qq : u32x4{0u, 0u, 0u, 0u};
-        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16);
+        const float* cs = P.rope() ? P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI) : nullptr;
+        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16, cs);
       }
       *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qq;
     }
@@ -716,7 +722,7 @@ __device__ __forceinline__ void gdn_output_item(
   Regs R0, R1;
   fetch(R0, n0);
   fetch(R1, min(n0 + TILE, tlast));
-  stage(R0, 0);
+  stage(R0, 0, n0);
   fetch(R0, min(n0 + 2 * TILE, tlast));
   __syncthreads();
   // a tile's outputs leave as whole 256-byte rows (16 lanes per token, 16
@@ -754,7 +760,7 @@ __device__ __forceinline__ void gdn_output_item(
         *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
       }
     }
-    stage(nxt, buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
+    stage(nxt, buf ^ 1, min(n0 + (it + 1) * TILE, tlast));  // the next tile (past the end: a copy of the last, never read)
     fetch(nxt, min(n0 + (it + 3) * TILE, tlast));
     __syncthreads();
     drain(it, full);

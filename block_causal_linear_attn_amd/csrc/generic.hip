@@ -83,10 +83,20 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
         sc2[tid] = s2;
       }
       __syncthreads();
-      for (int e = tid; e < GT * D; e += 256) {
-        const int tok = e / D, d = e % D;
-        const float x = Elem<T>::round(prologue_chan(ks[tok][d], wk ? wk[d] : 1.0f, sc[tok], P.relu, sc2[tok]));
-        ks[tok][d] = RELU ? relu_f32(x) : x;
+      // one channel pair per thread: the rotary embedding mixes the two
+      for (int e = tid; e < GT * D / 2; e += 256) {
+        const int tok = e / (D / 2), d = 2 * (e % (D / 2));
+        double y0 = prologue_chan(ks[tok][d], wk ? wk[d] : 1.0f, sc[tok], P.relu, sc2[tok]);
+        double y1 = prologue_chan(ks[tok][d + 1], wk ? wk[d + 1] : 1.0f, sc[tok], P.relu, sc2[tok]);
+        if (P.rope()) {
+          const float* cs = P.rope1(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, d / 2, D);
+          const double c = cs[0], s = cs[1], x0 = y0;
+          y0 = x0 * c - y1 * s;
+          y1 = x0 * s + y1 * c;
+        }
+        const float x0 = Elem<T>::round(y0), x1 = Elem<T>::round(y1);
+        ks[tok][d] = RELU ? relu_f32(x0) : x0;
+        ks[tok][d + 1] = RELU ? relu_f32(x1) : x1;
       }
     }
     if (!RELU && tid < GT) {
@@ -189,7 +199,15 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
           s1 = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
           wv = P.wq[(size_t)((bhf / L.F) % L.H) * D + i];
         }
-        y = Elem<T>::round(prologue_chan(qs[slot][i], wv, s1, P.relu, 1.0));
+        double yd = prologue_chan(qs[slot][i], wv, s1, P.relu, 1.0);
+        if (P.rope()) {  // the pair partner's value, then the rotation of the pair
+          const float wp = P.wq ? P.wq[(size_t)((bhf / L.F) % L.H) * D + (i ^ 1)] : 1.0f;
+          const double yp = prologue_chan(qs[slot][i ^ 1], wp, s1, P.relu, 1.0);
+          const float* cs = P.rope1(bhf % L.F, t0 + slot < n1 ? t0 + slot : n0, i / 2, D);
+          const double c = cs[0], sn = cs[1];
+          yd = (i & 1) ? yp * sn + yd * c : yd * c - yp * sn;
+        }
+        y = Elem<T>::round(yd);
         if (RELU) y = relu_f32(y);
       }
       __syncthreads();

@@ -46,15 +46,33 @@ struct TokLayout {
 // The per-token prologue applied to q and k as they are loaded, before the
 // scan's own feature map and key scale: RMSNorm over the D channels of a
 // head with per-(head, channel) weights, then (GDN) ReLU, then (GDN, keys)
-// division by the L2 norm.  Results enter the contractions rounded to bf16.
+// division by the L2 norm, then (GDN) the rotary position embedding.
+// Results enter the contractions rounded to bf16.
 struct Prologue {
   const float* wq = nullptr;  // [H][D] RMSNorm weights of q, or nullptr: no norm on q
   const float* wk = nullptr;  // [H][D] RMSNorm weights of k, or nullptr: no norm on k
   float eps = 1e-6f;
   int relu = 0;               // ReLU on q and k after the norm
-  int l2 = 0;                 // keys divided by their L2 norm, last
-  __host__ __device__ bool on_q() const { return wq != nullptr || relu; }
-  __host__ __device__ bool on_k() const { return wk != nullptr || relu || l2; }
+  int l2 = 0;                 // keys divided by their L2 norm
+  // Rotary embedding: channel pair (2i, 2i+1) of a token of frame f (of the
+  // call) and index n turns by the angle whose (cos, sin) is row roff + f,
+  // pair i of rf ([T][rpf][2]) for i < rpf, else row n, pair i - rpf of rt
+  // ([N][D/2 - rpf][2]).  rpf is a multiple of 4, so the 8 channels of one
+  // 16-byte chunk take one table.
+  const float* rf = nullptr;
+  const float* rt = nullptr;
+  int rpf = 0;
+  int roff = 0;
+  __host__ __device__ bool rope() const { return rf != nullptr || rt != nullptr; }
+  __host__ __device__ bool on_q() const { return wq != nullptr || relu || rope(); }
+  __host__ __device__ bool on_k() const { return wk != nullptr || relu || l2 || rope(); }
+  // (cos, sin) of channel chunk c (pairs 4c .. 4c + 3, 8 floats, 16-byte
+  // aligned) of token n of frame f, for head dim D
+  __host__ __device__ const float* rope8(long f, long n, int c, int D) const { return rope1(f, n, 4 * c, D); }
+  // (cos, sin) of channel pair p of token n of frame f
+  __host__ __device__ const float* rope1(long f, long n, int p, int D) const {
+    return p < rpf ? rf + ((size_t)(roff + f) * rpf + p) * 2 : rt + ((size_t)n * (D / 2 - rpf) + (p - rpf)) * 2;
+  }
 };
 
 }  // namespace linscan

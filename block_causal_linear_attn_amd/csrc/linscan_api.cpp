@@ -154,9 +154,16 @@ ls_status token_layout(const ls_shape* s, const Dims& d, const ls_strides* st, l
 
 // The per-token prologue of a call (nullptr: none); `gdn` allows the GDN-only
 // parts (ReLU, L2 of keys).  Weights are [H][D] fp32, 16-byte aligned.
-ls_status prologue_of(const ls_prologue* pr, const ls_shape* s, bool gdn, linscan::Prologue* P, size_t* w_bytes) {
+// The prologue's read-only buffers (weights, rotary tables), for the
+// overlap checks against outputs.
+struct ProBufs {
+  const void* p[4] = {nullptr, nullptr, nullptr, nullptr};
+  size_t n[4] = {0, 0, 0, 0};
+};
+
+ls_status prologue_of(const ls_prologue* pr, const ls_shape* s, bool gdn, linscan::Prologue* P, ProBufs* bufs) {
   *P = linscan::Prologue();
-  *w_bytes = (size_t)s->H * s->D * sizeof(float);
+  *bufs = ProBufs();
   if (!pr) return LS_OK;
   if (pr->relu != 0 && pr->relu != 1) return fail(LS_ERR_BAD_PARAM, "prologue relu must be 0 or 1");
   if (pr->l2_keys != 0 && pr->l2_keys != 1) return fail(LS_ERR_BAD_PARAM, "prologue l2_keys must be 0 or 1");
@@ -166,6 +173,33 @@ ls_status prologue_of(const ls_prologue* pr, const ls_shape* s, bool gdn, linsca
     return fail(LS_ERR_BAD_PARAM, "prologue eps=%g must be finite and > 0", (double)pr->eps);
   if (misaligned(pr->q_weight) || misaligned(pr->k_weight))
     return fail(LS_ERR_MISALIGNED, "prologue weights must be 16-byte aligned");
+  const size_t w_bytes = (size_t)s->H * s->D * sizeof(float);
+  bufs->p[0] = pr->q_weight, bufs->n[0] = pr->q_weight ? w_bytes : 0;
+  bufs->p[1] = pr->k_weight, bufs->n[1] = pr->k_weight ? w_bytes : 0;
+  if (pr->rope_frame || pr->rope_token) {
+    if (!gdn) return fail(LS_ERR_BAD_PARAM, "the rotary embedding is available in the GDN prologue only");
+    const int half = s->D / 2, pf = pr->rope_frame_pairs;
+    if (pf < 0 || pf > half || pf % 4 != 0)
+      return fail(LS_ERR_BAD_PARAM, "rope_frame_pairs=%d must be a multiple of 4 in [0, D/2=%d]", pf, half);
+    if (pf > 0 && !pr->rope_frame) return fail(LS_ERR_NULL_POINTER, "rope_frame is NULL but rope_frame_pairs=%d", pf);
+    if (pf < half && !pr->rope_token)
+      return fail(LS_ERR_NULL_POINTER, "rope_token is NULL but %d pairs turn by token", half - pf);
+    if (pr->rope_frame_offset < 0 || (pf > 0 && (long long)pr->rope_frame_offset + s->F > pr->rope_frames))
+      return fail(LS_ERR_BAD_PARAM, "rope_frame_offset=%d + F=%d exceeds rope_frames=%lld", pr->rope_frame_offset,
+                  s->F, pr->rope_frames);
+    if (misaligned(pr->rope_frame) || misaligned(pr->rope_token))
+      return fail(LS_ERR_MISALIGNED, "rotary tables must be 16-byte aligned");
+    if (pf > 0) {
+      P->rf = pr->rope_frame;
+      bufs->p[2] = pr->rope_frame, bufs->n[2] = (size_t)pr->rope_frames * pf * 2 * sizeof(float);
+    }
+    if (pf < half) {
+      P->rt = pr->rope_token;
+      bufs->p[3] = pr->rope_token, bufs->n[3] = (size_t)s->N * (half - pf) * 2 * sizeof(float);
+    }
+    P->rpf = pf;
+    P->roff = pr->rope_frame_offset;
+  }
   P->wq = pr->q_weight;
   P->wk = pr->k_weight;
   P->eps = pr->eps;
@@ -409,8 +443,8 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
   size_t tok_bytes = 0;  // bytes each token tensor spans
   if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
   linscan::Prologue prolog;
-  size_t pw_bytes = 0;
-  if ((st = prologue_of(pro, s, false, &prolog, &pw_bytes)) != LS_OK) return st;
+  ProBufs pbufs;
+  if ((st = prologue_of(pro, s, false, &prolog, &pbufs)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t norm_bytes = (size_t)d.bh * D * sizeof(float);
   if (d.bh == 0) return ok();
@@ -435,10 +469,11 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
       overlap(o, tok_bytes, norm_out, norm_out ? norm_bytes : 0) ||
       overlap(state_out, state_out ? state_bytes : 0, norm_out, norm_out ? norm_bytes : 0))
     return fail(LS_ERR_ALIASING, "outputs overlap each other");
-  for (const float* w : {prolog.wq, prolog.wk})
-    if (overlap(o, tok_bytes, w, w ? pw_bytes : 0) || overlap(state_out, state_out ? state_bytes : 0, w, w ? pw_bytes : 0) ||
-        overlap(norm_out, norm_out ? norm_bytes : 0, w, w ? pw_bytes : 0) ||
-        overlap(workspace, workspace ? workspace_bytes : 0, w, w ? pw_bytes : 0))
+  for (int i = 0; i < 4; ++i)
+    if (overlap(o, tok_bytes, pbufs.p[i], pbufs.n[i]) ||
+        overlap(state_out, state_out ? state_bytes : 0, pbufs.p[i], pbufs.n[i]) ||
+        overlap(norm_out, norm_out ? norm_bytes : 0, pbufs.p[i], pbufs.n[i]) ||
+        overlap(workspace, workspace ? workspace_bytes : 0, pbufs.p[i], pbufs.n[i]))
       return fail(LS_ERR_ALIASING, "an output or the workspace overlaps the prologue weights");
 
   hipStream_t hs = (hipStream_t)stream;
@@ -532,8 +567,8 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const
   size_t tok_bytes = 0;  // bytes each token tensor spans
   if ((st = token_layout(s, d, strides, &layout, &tok_bytes)) != LS_OK) return st;
   linscan::Prologue prolog;
-  size_t pw_bytes = 0;
-  if ((st = prologue_of(pro, s, true, &prolog, &pw_bytes)) != LS_OK) return st;
+  ProBufs pbufs;
+  if ((st = prologue_of(pro, s, true, &prolog, &pbufs)) != LS_OK) return st;
   const size_t state_bytes = (size_t)d.bh * D * D * sizeof(float);
   const size_t gate_bytes = (size_t)d.bhf * (token_gate ? (size_t)s->N : 1) * sizeof(float);
   const size_t alpha_bytes = (size_t)d.bhf * sizeof(float);
@@ -557,10 +592,11 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const
   }
   if (overlap(o, tok_bytes, state_out, state_out ? state_bytes : 0))
     return fail(LS_ERR_ALIASING, "outputs overlap each other");
-  for (const float* w : {prolog.wq, prolog.wk})
-    if (overlap(o, tok_bytes, w, w ? pw_bytes : 0) || overlap(state_out, state_out ? state_bytes : 0, w, w ? pw_bytes : 0) ||
-        overlap(workspace, workspace ? workspace_bytes : 0, w, w ? pw_bytes : 0))
-      return fail(LS_ERR_ALIASING, "an output or the workspace overlaps the prologue weights");
+  for (int i = 0; i < 4; ++i)
+    if (overlap(o, tok_bytes, pbufs.p[i], pbufs.n[i]) ||
+        overlap(state_out, state_out ? state_bytes : 0, pbufs.p[i], pbufs.n[i]) ||
+        overlap(workspace, workspace ? workspace_bytes : 0, pbufs.p[i], pbufs.n[i]))
+      return fail(LS_ERR_ALIASING, "an output or the workspace overlaps the prologue weights or rotary tables");
 
   hipStream_t hs = (hipStream_t)stream;
   if (s->F == 0) {

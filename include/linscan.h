@@ -120,6 +120,15 @@ typedef struct {
  *   RMSNorm  x <- x / sqrt(mean(x^2) + eps) * weight[h][:]   (weight not NULL)
  *   ReLU     x <- max(x, 0)                                   (GDN, relu = 1)
  *   L2       x <- x / |x|, 0 staying 0                        (GDN keys, l2_keys = 1)
+ *   RoPE     (GDN, rope_frame or rope_token not NULL) channel pair (2i, 2i+1)
+ *            of q and k turns by its token's angle:
+ *              (x0, x1) <- (x0 cos - x1 sin, x0 sin + x1 cos)
+ *            with (cos, sin) = rope_frame[rope_frame_offset + f][i] for the
+ *            first rope_frame_pairs pairs (by frame f of the call) and
+ *            rope_token[n][i - rope_frame_pairs] for the rest (by token n)
+ *            (SANA-WM digest, same paragraph: the fused kernel also prepares
+ *            the positional encoding; SANA-Video's guide, core mechanisms:
+ *            3D RoPE in the linear attention)
  * in that order, before the scan's own feature map (ReLU scan) or key scale
  * (GDN).  The arithmetic is fp64 and the result enters the contractions
  * rounded once to the token precision (bf16: nearest, ties to even), as a
@@ -130,7 +139,18 @@ typedef struct {
   const float* k_weight;  /* [H][D] fp32 RMSNorm weights of k, or NULL */
   float eps;              /* RMSNorm epsilon, finite and > 0 when a weight is given */
   int relu;               /* GDN only: 1 = ReLU on q and k after their norms */
-  int l2_keys;            /* GDN only: 1 = keys divided by their L2 norm, last */
+  int l2_keys;            /* GDN only: 1 = keys divided by their L2 norm */
+  /* GDN only, the rotary embedding (both NULL: none).  Tables are fp32, 16-byte
+   * aligned, read only: rope_frame [rope_frames][rope_frame_pairs][2] (needed
+   * when rope_frame_pairs > 0) and rope_token [N][D/2 - rope_frame_pairs][2]
+   * (needed when rope_frame_pairs < D/2).  rope_frame_pairs is a multiple of 4
+   * in [0, D/2]; rope_frame_offset >= 0 and rope_frame_offset + F <=
+   * rope_frames (LS_ERR_BAD_PARAM / LS_ERR_NULL_POINTER / LS_ERR_MISALIGNED). */
+  const float* rope_frame;
+  const float* rope_token;
+  int rope_frame_pairs;
+  int rope_frame_offset;
+  long long rope_frames;
 } ls_prologue;
 
 /*

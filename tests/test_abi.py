@@ -176,6 +176,21 @@ def test_validation_errors_prologue(lib):
     assert gp(Pr(None, None, 0.0, 2, 0)) == 7
     assert gp(Pr(w + 4, None, 1e-6, 0, 0)) == 5                              # misaligned weights
     assert gp(Pr(P[3].value, None, 1e-6, 0, 0)) == 8                         # weights inside o
+    # the rotary embedding: D/2 = 16 pairs, F = 3, N = 10
+    rf, rt = P[11].value, P[12].value
+    def rope(f=rf, t=rt, pf=8, off=0, T=3):
+        return Pr(None, None, 1e-6, 0, 0, f, t, pf, off, T)
+    assert gp(rope()) == 6 and gp(rope(f=None, pf=0)) == 6 and gp(rope(t=None, pf=16)) == 6
+    assert gp(rope(off=2, T=5)) == 6
+    assert rp(rope()) == 7                                                   # GDN prologue only
+    assert gp(rope(pf=6)) == 7                                               # not a multiple of 4
+    assert gp(rope(pf=20)) == 7                                              # more than D/2 pairs
+    assert gp(rope(f=None)) == 1                                             # frame pairs need the frame table
+    assert gp(rope(t=None)) == 1                                             # token pairs need the token table
+    assert gp(rope(off=1, T=3)) == 7                                         # rows 1..3 of a 3-row table
+    assert gp(rope(off=-1)) == 7
+    assert gp(rope(t=rt + 8)) == 5                                           # misaligned table
+    assert gp(rope(t=P[3].value)) == 8                                       # table inside o
 
 
 def test_in_place_state_is_not_an_aliasing_error(lib):

@@ -649,3 +649,36 @@ def test_gdn_prologue_matches_plain_scan_bitwise(ls, gen, oracle_mod, B, H, F, N
     o2, S2 = ls.ls_gdn_frame_forward(_as_tokens(qp, dt), _as_tokens(kp, dt), xd["v"], xd["alpha"], xd["beta"])
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,dt,qw,kw,relu,l2,P,off", [
+    (1, 3, 4, 300, 128, "bf16", True, True, True, True, 16, 0),      # frame-interleaved launch, whole prologue
+    (1, 40, 2, 130, 128, "bf16", False, False, False, False, 0, 0),  # phased launch, token table only
+    (1, 2, 3, 200, 128, "bf16", False, True, False, True, 64, 5),    # frame table only, rows from 5
+    (2, 2, 3, 97, 112, "bf16", True, True, False, True, 8, 2),       # head dim 112
+    (1, 2, 3, 80, 64, "bf16", True, True, True, True, 8, 1),         # generic bf16 kernels
+    (1, 2, 3, 40, 32, "fp32", True, True, True, True, 4, 0),         # generic fp32 kernels
+])
+def test_gdn_rope_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, qw, kw, relu, l2, P, off):
+    """The rotary embedding at the end of the prologue: against the oracle, and
+    bit for bit against the plain scan of the oracle's prologue output."""
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=59, part=N, l2_keys=False)
+    wq, wk = _weights(H, D, 60)
+    wq, wk = (wq if qw else None), (wk if kw else None)
+    fcs, tcs = gen.rope_tables(off + F + 1, N, 20, D, P)
+    xd = _dev(x)
+    dev_rope = (None if fcs is None else fcs.to(DEV), None if tcs is None else tcs.to(DEV), P, off)
+    o, S = ls.ls_gdn_frame_forward_prologue(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"],
+                                            None if wq is None else wq.to(DEV), None if wk is None else wk.to(DEV),
+                                            norm_eps=1e-5, relu=relu, l2_keys=l2, rope=dev_rope)
+    rnd = "bf16" if dt == "bf16" else None
+    rope = (fcs, tcs, P, off)
+    qp = oracle_mod.prologue(x["q"], wq, eps=1e-5, relu=relu, round_to=rnd, rope=rope)
+    kp = oracle_mod.prologue(x["k"], wk, eps=1e-5, relu=relu, l2=l2, round_to=rnd, rope=rope)
+    o2, S2 = ls.ls_gdn_frame_forward(_as_tokens(qp, dt), _as_tokens(kp, dt), xd["v"], xd["alpha"], xd["beta"])
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(qp, kp, x["v"], x["alpha"], x["beta"])
+    tag = "gdn rope B%d H%d F%d N%d D%d %s q%d k%d r%d l%d P%d off%d" % (B, H, F, N, D, dt, qw, kw, relu, l2, P, off)
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+    assert torch.equal(o, o2) and torch.equal(S, S2)
