@@ -95,6 +95,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2_f64(double lo, double hi) {
   return f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
 }
 
+// 1 / sqrt(v) for normal v > 0, to within a few fp64 ulps: the hardware
+// estimate (about 2^-29 relative error) and two Newton steps, which square the
+// error each time.  Cheaper than a correctly rounded square root and
+// division, and far inside what could change a later rounding to bf16.
+__device__ __forceinline__ double rsqrt_f64(double v) {
+  double y = __builtin_amdgcn_rsq(v);
+  const double h = 0.5 * v;
+  y = y * fma(-h * y, y, 1.5);
+  y = y * fma(-h * y, y, 1.5);
+  return y;
+}
+
 // A 64-bit value from another lane of the DPP row, as two 32-bit moves.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
@@ -142,7 +154,7 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
-    const double inv = 1.0 / sqrt(fma(red(ss), inv_d, (double)P.eps));
+    const double inv = rsqrt_f64(fma(red(ss), inv_d, (double)P.eps));
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = x[e] * (double)wt[e] * inv;  // x * w exact in fp64
   }
@@ -155,7 +167,7 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);
     ss = red(ss);
-    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+    const double inv = ss > 0.0 ? rsqrt_f64(ss) : 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= inv;
   }

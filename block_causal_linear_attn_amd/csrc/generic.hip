@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
         if (wk) {
           double ss = 0.0;
           for (int d = 0; d < D; ++d) ss = fma((double)ks[tid][d], (double)ks[tid][d], ss);
-          s1 = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+          s1 = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
         }
         if (P.l2) {
           double ss = 0.0;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
             const double y = prologue_chan(ks[tid][d], wk ? wk[d] : 1.0f, s1, P.relu, 1.0);
             ss = fma(y, y, ss);
           }
-          s2 = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+          s2 = ss > 0.0 ? rsqrt_f64(ss) : 0.0;
         }
         sc[tid] = s1;
         sc2[tid] = s2;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
         if (P.wq) {
           double ss = 0.0;
           for (int j = 0; j < D; ++j) ss = fma((double)qs[slot][j], (double)qs[slot][j], ss);
-          s1 = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+          s1 = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
           wv = P.wq[(size_t)((bhf / L.F) % L.H) * D + i];
         }
         double yd = prologue_chan(qs[slot][i], wv, s1, P.relu, 1.0);

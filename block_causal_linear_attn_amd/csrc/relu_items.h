@@ -265,7 +265,7 @@ __device__ __forceinline__ void relu_output_item(
             ss = fma(x0, x0, fma(x1, x1, ss));
           }
         ss += __shfl_xor(ss, 32);  // the partner lane holds the token's other dims
-        const double inv = 1.0 / sqrt(fma(ss, 1.0 / D, (double)P.eps));
+        const double inv = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           const float4 a = *reinterpret_cast<const float4*>(wql + 16 * s + 8 * g);
