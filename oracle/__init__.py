@@ -57,6 +57,8 @@ def _load():
     lib.oracle_gdn_frame_reversed.restype = i
     lib.oracle_temporal_conv3.argtypes = [i, i, i, i, i, i, P, P, P, P, P, P]
     lib.oracle_temporal_conv3.restype = i
+    lib.oracle_linear_block_split.argtypes = [i, i, i, i, i, i, d, P, P, P, P, P, P, P, P, P, P, i]
+    lib.oracle_linear_block_split.restype = i
     lib.oracle_max_threads.restype = i
     _lib = lib
     return lib
@@ -111,6 +113,46 @@ def relu_block(q, k, v, state=None, norm=None, block_frames: int = 1, eps: float
     if rc != 0:
         raise RuntimeError("oracle_relu_block failed with code %d" % rc)
     return o, S, z
+
+
+def linear_block_split(qn, kn, qd, kd, v, state=None, norm=None, block_frames: int = 1, eps: float = 1e-6,
+                       nthreads: int = 0):
+    """Block-causal linear attention with numerator features (qn, kn) and
+    denominator features (qd, kd), fp64 (oracle.c, oracle_linear_block_split).
+
+    Features: [B, H, F, N, D] (float64 kept exact); v as for relu_block.
+    Returns (o, S, z) as float64.
+    """
+    kn = _f64(kn, np.shape(kn))
+    B, H, F, N, D = kn.shape
+    qn, qd, kd = (_f64(a, (B, H, F, N, D)) for a in (qn, qd, kd))
+    v = _f32(v, (B, H, F, N, D))
+    S0 = _f64(state, (B, H, D, D))
+    z0 = _f64(norm, (B, H, D))
+    o = np.empty((B, H, F, N, D), np.float64)
+    S = np.empty((B, H, D, D), np.float64)
+    z = np.empty((B, H, D), np.float64)
+    rc = _load().oracle_linear_block_split(B, H, F, N, D, int(block_frames), float(eps), _ptr(qn), _ptr(kn),
+                                           _ptr(qd), _ptr(kd), _ptr(v), _ptr(S0), _ptr(z0), _ptr(o), _ptr(S),
+                                           _ptr(z), int(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_linear_block_split failed with code %d" % rc)
+    return o, S, z
+
+
+def relu_rope_features(x, weight=None, eps: float = 1e-6, rope=None, round_to=None):
+    """Numerator and denominator features of the ReLU scan with the prologue.
+
+    The denominator takes phi(x') = ReLU of the prologue's RMSNorm result x'
+    (fp64, unrounded); the numerator takes the rotated phi(x'), rounded to the
+    token precision (round_to) as the contractions consume it.  Without rope
+    both are phi(x') (the numerator rounded).  Returns (numerator, denominator).
+    """
+    d = prologue(x, weight, eps=eps, relu=True)
+    n = rope_rotate(d, *rope) if rope is not None else d
+    if round_to == "bf16":
+        n = round_bf16(n)
+    return n, d
 
 
 def gdn_frame(q, k, v, alpha, beta, state=None, key_scale=None, with_output: bool = True,

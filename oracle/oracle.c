@@ -142,6 +142,76 @@ int oracle_relu_block(int B, int H, int F, int N, int D, int block_frames, doubl
 }
 
 /*
+ * Block-causal linear attention with separate numerator and denominator
+ * features, for the ReLU scan with a rotary position embedding: the SANA-Video
+ * practical guide (section on core mechanisms) names the attention
+ * LiteLAReLURope, a ReLU linear attention with RoPE, and the talk (passage on
+ * the 3D RoPE) adds the rotary embedding to the linear attention.  Rotated
+ * features can be negative, so they serve the numerator only and the
+ * normaliser keeps the unrotated ReLU features (the pages give no formula;
+ * this keeps the denominator positive):
+ *   S += v kn^T and z += kd for every token of a block, then
+ *   o = S qn / (z . qd + eps) for every token of the block.
+ * qn, kn, qd, kd: [B][H][F][N][D] float64 features (the caller applies the
+ * feature map and the rotation); v float32; S0, z0, o, S_out, z_out as in
+ * oracle_relu_block.
+ */
+int oracle_linear_block_split(int B, int H, int F, int N, int D, int block_frames, double eps,
+                              const double* qn, const double* kn, const double* qd, const double* kd,
+                              const float* v, const double* S0, const double* z0, double* o, double* S_out,
+                              double* z_out, int nthreads) {
+  if (B < 1 || H < 1 || F < 1 || N < 1 || D < 1 || block_frames < 1) return ORACLE_BAD_ARG;
+  if (!kn || !kd || !v || (o && (!qn || !qd))) return ORACLE_BAD_ARG;
+  int status = ORACLE_OK;
+  long heads = (long)B * H;
+#ifdef _OPENMP
+  if (nthreads < 1) nthreads = omp_get_max_threads();
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+#endif
+  for (long bh = 0; bh < heads; ++bh) {
+    double* S = (double*)calloc((size_t)D * D, sizeof(double));
+    double* z = (double*)calloc((size_t)D, sizeof(double));
+    if (!S || !z) {
+      status = ORACLE_NO_MEMORY;
+      free(S); free(z);
+      continue;
+    }
+    if (S0) memcpy(S, S0 + (size_t)bh * D * D, (size_t)D * D * sizeof(double));
+    if (z0) memcpy(z, z0 + (size_t)bh * D, (size_t)D * sizeof(double));
+    for (int f0 = 0; f0 < F; f0 += block_frames) {
+      int f1 = f0 + block_frames < F ? f0 + block_frames : F;
+      for (int f = f0; f < f1; ++f) {
+        for (int n = 0; n < N; ++n) {
+          const size_t t = tok(bh, f, n, F, N, D);
+          for (int i = 0; i < D; ++i)
+            for (int j = 0; j < D; ++j) S[(size_t)i * D + j] += (double)v[t + i] * kn[t + j];
+          for (int j = 0; j < D; ++j) z[j] += kd[t + j];
+        }
+      }
+      if (o) {
+        for (int f = f0; f < f1; ++f) {
+          for (int n = 0; n < N; ++n) {
+            const size_t t = tok(bh, f, n, F, N, D);
+            double den = 0.0;
+            for (int j = 0; j < D; ++j) den += z[j] * qd[t + j];
+            den += eps;
+            for (int i = 0; i < D; ++i) {
+              double num = 0.0;
+              for (int j = 0; j < D; ++j) num += S[(size_t)i * D + j] * qn[t + j];
+              o[t + i] = num / den;
+            }
+          }
+        }
+      }
+    }
+    if (S_out) memcpy(S_out + (size_t)bh * D * D, S, (size_t)D * D * sizeof(double));
+    if (z_out) memcpy(z_out + (size_t)bh * D, z, (size_t)D * sizeof(double));
+    free(S); free(z);
+  }
+  return status;
+}
+
+/*
  * Frame-wise Gated DeltaNet.
  * c = key_scale if key_scale > 0, else 1/sqrt(D*N).  For each frame f in order:
  *   G = sum_n (c k_n)(c k_n)^T,  U = sum_n v_n (c k_n)^T   (frame f's tokens)
