@@ -456,7 +456,7 @@ def time_strided(torch, ls, relu_call, g, reps=4):
 def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
     """The per-token prologue fused into the load stage: one 10-frame ReLU call
     of the rollout with RMSNorm (weights) on q and k, and the GDN call with
-    RMSNorm on q and k, ReLU and L2 keys (and once more with a 3D rotary
+    RMSNorm on q and k, ReLU and L2 keys (each once more with a 3D rotary
     embedding), against the same calls without a prologue (mean kernel time
     from the library's per-launch events), and the GDN call after the same
     prologue as separate torch ops (wall time of both, CUDA events), which
@@ -479,10 +479,15 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
     r = relu_call
     H, D = r["q"].shape[1], r["q"].shape[-1]
     wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
+    # 3D rotary embedding: 4 pairs by frame, 12 by the 45 x 80 latent grid
+    fr, tr = inputs.rope_tables(r["q"].shape[2], r["q"].shape[3], 80, D, 4, device=dev)
     res["relu_h70_d32_10_frames_rmsnorm_qk_us"] = {
         "plain": kernel_us(lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused"),
         "fused_prologue": kernel_us(lambda: ls.ls_relu_block_forward_prologue(r["q"], r["k"], r["v"], wq, wk,
-                                                                               norm_eps=1e-6), "relu_fused")}
+                                                                               norm_eps=1e-6), "relu_fused"),
+        "fused_prologue_with_3d_rope": kernel_us(lambda: ls.ls_relu_block_forward_prologue(
+            r["q"], r["k"], r["v"], wq, wk, norm_eps=1e-6, rope=(fr, tr, 4, 0)), "relu_fused")}
+    del fr, tr
     H, D = g["q"].shape[1], g["q"].shape[-1]
     wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
     out = torch.empty_like(g["q"])

@@ -323,14 +323,15 @@ def _prologue(q, q_weight, k_weight, eps, relu, l2_keys, rope=None):
 
 def ls_relu_block_forward_prologue(q, k, v, q_weight=None, k_weight=None, norm_eps: float = 1e-6, state=None,
                                    norm=None, block_frames: int = 1, eps: float = 1e-6, out=None, state_out=None,
-                                   norm_out=None, ws=None):
-    """ls_relu_block_forward with RMSNorm of q and/or k (weights [H, D] fp32) fused into the load."""
+                                   norm_out=None, ws=None, rope=None):
+    """ls_relu_block_forward with RMSNorm of q and/or k (weights [H, D] fp32) and the rotary embedding (rope as
+    for _prologue; numerator only) fused into the load."""
     _tokens("q", q)
     _tokens("k", k, q)
     _tokens("v", v, q)
     B, H, F, N, D = q.shape
     dev = q.device
-    pr = _prologue(q, q_weight, k_weight, norm_eps, 0, 0)
+    pr = _prologue(q, q_weight, k_weight, norm_eps, 0, 0, rope)
     _f32("state", state, (B, H, D, D), dev)
     _f32("norm", norm, (B, H, D), dev)
     o = out if out is not None else torch.empty_like(q)

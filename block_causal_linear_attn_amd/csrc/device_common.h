@@ -126,6 +126,19 @@ __device__ __forceinline__ double group_sum_f64(double x) {
   return x;
 }
 
+// The rotary embedding of 4 channel pairs held as fp64 (cs as for
+// prologue_bf16x8).
+__device__ __forceinline__ void rope_rotate8(double (&x)[8], const float* cs) {
+  const float4 a = *reinterpret_cast<const float4*>(cs), b = *reinterpret_cast<const float4*>(cs + 4);
+  const float c[4] = {a.x, a.z, b.x, b.z}, s[4] = {a.y, a.w, b.y, b.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double x0 = x[2 * j], x1 = x[2 * j + 1];
+    x[2 * j] = x0 * (double)c[j] - x1 * (double)s[j];
+    x[2 * j + 1] = x0 * (double)s[j] + x1 * (double)c[j];
+  }
+}
+
 // The prologue (see Prologue) on 8 channels of one token, held by one lane as
 // packed bf16; `red` completes a per-token fp64 sum over the lanes that hold
 // the token's other channels (every lane calls it: DPP or cross-lane
@@ -140,10 +153,12 @@ __device__ __forceinline__ double group_sum_f64(double x) {
 // rows) turn it into a large relative error.  In fp64 the chance is ~2^-40.
 //
 // cs: the (cos, sin) of the rotary embedding of these 4 channel pairs
-// (Prologue::rope8), or nullptr: no rotation.
+// (Prologue::rope8), or nullptr: no rotation.  pre: if not nullptr, receives
+// the 8 values before the rotation, as fp32.
 template <typename Red>
 __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], bool norm, const Prologue& P,
-                                                 bool is_k, double inv_d, Red red, const float* cs = nullptr) {
+                                                 bool is_k, double inv_d, Red red, const float* cs = nullptr,
+                                                 float* pre = nullptr) {
   double x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -171,16 +186,11 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] *= inv;
   }
-  if (cs) {
-    const float4 a = *reinterpret_cast<const float4*>(cs), b = *reinterpret_cast<const float4*>(cs + 4);
-    const float c[4] = {a.x, a.z, b.x, b.z}, s[4] = {a.y, a.w, b.y, b.w};
+  if (pre) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double x0 = x[2 * j], x1 = x[2 * j + 1];
-      x[2 * j] = x0 * (double)c[j] - x1 * (double)s[j];
-      x[2 * j + 1] = x0 * (double)s[j] + x1 * (double)c[j];
-    }
+    for (int e = 0; e < 8; ++e) pre[e] = (float)x[e];
   }
+  if (cs) rope_rotate8(x, cs);
   return u32x4{pack_bf16x2_f64(x[0], x[1]), pack_bf16x2_f64(x[2], x[3]), pack_bf16x2_f64(x[4], x[5]),
                pack_bf16x2_f64(x[6], x[7])};
 }

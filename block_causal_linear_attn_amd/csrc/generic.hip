@@ -35,6 +35,8 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
   __shared__ float vs[GT][D + 1];
   __shared__ float bs[GT];  // token gates (GDN)
   __shared__ double sc[GT], sc2[GT];  // per-token prologue factors (RMSNorm, L2)
+  // RELU with the rotary embedding: the unrotated features, for the normaliser
+  __shared__ float kd[RELU ? GT : 1][RELU ? D + 1 : 1];
   const int tid = threadIdx.x;
   const int e0 = blockIdx.y * 256 * EPT;  // first entry owned by this workgroup
   const long wg = blockIdx.x;
@@ -86,8 +88,14 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       // one channel pair per thread: the rotary embedding mixes the two
       for (int e = tid; e < GT * D / 2; e += 256) {
         const int tok = e / (D / 2), d = 2 * (e % (D / 2));
-        double y0 = prologue_chan(ks[tok][d], wk ? wk[d] : 1.0f, sc[tok], P.relu, sc2[tok]);
-        double y1 = prologue_chan(ks[tok][d + 1], wk ? wk[d + 1] : 1.0f, sc[tok], P.relu, sc2[tok]);
+        // RELU with the rotary embedding: the feature map comes before the rotation
+        const int fm = P.relu || (RELU && P.rope());
+        double y0 = prologue_chan(ks[tok][d], wk ? wk[d] : 1.0f, sc[tok], fm, sc2[tok]);
+        double y1 = prologue_chan(ks[tok][d + 1], wk ? wk[d + 1] : 1.0f, sc[tok], fm, sc2[tok]);
+        if (RELU && P.rope()) {
+          kd[tok][d] = (float)y0;
+          kd[tok][d + 1] = (float)y1;
+        }
         if (P.rope()) {
           const float* cs = P.rope1(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, d / 2, D);
           const double c = cs[0], s = cs[1], x0 = y0;
@@ -95,8 +103,8 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
           y1 = x0 * s + y1 * c;
         }
         const float x0 = Elem<T>::round(y0), x1 = Elem<T>::round(y1);
-        ks[tok][d] = RELU ? relu_f32(x0) : x0;
-        ks[tok][d + 1] = RELU ? relu_f32(x1) : x1;
+        ks[tok][d] = RELU && !P.rope() ? relu_f32(x0) : x0;
+        ks[tok][d + 1] = RELU && !P.rope() ? relu_f32(x1) : x1;
       }
     }
     if (!RELU && tid < GT) {
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(256) void gen_summary(const T* __restrict__ k, cons
       }
     }
     if (RELU && blockIdx.y == 0 && tid < D)
-      for (int tok = 0; tok < GT; ++tok) az += ks[tok][tid];
+      for (int tok = 0; tok < GT; ++tok) az += P.rope() ? kd[tok][tid] : ks[tok][tid];
     __syncthreads();
   }
 
@@ -158,6 +166,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
   __shared__ float Ss[D][D + 1];
   __shared__ float zs[D];
   __shared__ float qs[SLOTS][D];
+  __shared__ float qd[RELU ? SLOTS : 1][RELU ? D : 1];  // RELU with the rotary embedding: unrotated features
   const int tid = threadIdx.x;
   const long wg = blockIdx.x;
   const long bhf = wg / nco;
@@ -199,16 +208,18 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
           s1 = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
           wv = P.wq[(size_t)((bhf / L.F) % L.H) * D + i];
         }
-        double yd = prologue_chan(qs[slot][i], wv, s1, P.relu, 1.0);
+        const int fm = P.relu || (RELU && P.rope());  // RELU: the feature map comes before the rotation
+        double yd = prologue_chan(qs[slot][i], wv, s1, fm, 1.0);
+        if (RELU && P.rope()) qd[slot][i] = (float)yd;
         if (P.rope()) {  // the pair partner's value, then the rotation of the pair
           const float wp = P.wq ? P.wq[(size_t)((bhf / L.F) % L.H) * D + (i ^ 1)] : 1.0f;
-          const double yp = prologue_chan(qs[slot][i ^ 1], wp, s1, P.relu, 1.0);
+          const double yp = prologue_chan(qs[slot][i ^ 1], wp, s1, fm, 1.0);
           const float* cs = P.rope1(bhf % L.F, t0 + slot < n1 ? t0 + slot : n0, i / 2, D);
           const double c = cs[0], sn = cs[1];
           yd = (i & 1) ? yp * sn + yd * c : yd * c - yp * sn;
         }
         y = Elem<T>::round(yd);
-        if (RELU) y = relu_f32(y);
+        if (RELU && !P.rope()) y = relu_f32(y);
       }
       __syncthreads();
       if (slot < SLOTS) qs[slot][i] = y;
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(256) void gen_output(const T* __restrict__ q, T* __
       for (int j = 0; j < D; ++j) {
         const float qj = qs[slot][j];
         num = fmaf(Ss[i][j], qj, num);
-        if (RELU) den = fmaf(zs[j], qj, den);
+        if (RELU) den = fmaf(zs[j], P.rope() ? qd[slot][j] : qj, den);
       }
       const float out = RELU ? num / (den + eps) : num;
       Elem<T>::store(of, (size_t)(t0 + slot) * L.sn + i, out);

@@ -177,7 +177,6 @@ ls_status prologue_of(const ls_prologue* pr, const ls_shape* s, bool gdn, linsca
   bufs->p[0] = pr->q_weight, bufs->n[0] = pr->q_weight ? w_bytes : 0;
   bufs->p[1] = pr->k_weight, bufs->n[1] = pr->k_weight ? w_bytes : 0;
   if (pr->rope_frame || pr->rope_token) {
-    if (!gdn) return fail(LS_ERR_BAD_PARAM, "the rotary embedding is available in the GDN prologue only");
     const int half = s->D / 2, pf = pr->rope_frame_pairs;
     if (pf < 0 || pf > half || pf % 4 != 0)
       return fail(LS_ERR_BAD_PARAM, "rope_frame_pairs=%d must be a multiple of 4 in [0, D/2=%d]", pf, half);

@@ -73,6 +73,9 @@ __device__ __forceinline__ void relu_summary_item(
     for (int j = 0; j < DB; ++j) acc[i][j] = floatx16{};
   }
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  // with the rotary embedding: this lane's sums of the unrotated features of
+  // its channels 8 (lane % CPR) .. + 7 (the staged tiles hold rotated ones)
+  float zk[8] = {};
 
   // the next tile's rows are loaded into registers while the current tile is
   // contracted.  Every load is issued (rows past the chunk re-read its first
@@ -99,14 +102,32 @@ __device__ __forceinline__ void relu_summary_item(
       const bool live = t0 + tok < n1;
       u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
-      if (PRO && P.wk) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
-        float wk8[8];
-        const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
-        wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
-        kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / D, [](double x) { return group_sum_f64<CPR>(x); });
-      }
+      if (PRO && P.rope()) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
+        // RMSNorm, the feature map, then the rotation (numerator only): the
+        // normaliser sums the unrotated features
+        float wk8[8] = {};
+        if (P.wk) {
+          const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
+          wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
+        }
+        Prologue Pf = P;
+        Pf.relu = 1;
+        float pre[8];
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, Pf, true, 1.0 / D,
+                             [](double x) { return group_sum_f64<CPR>(x); },
+                             P.rope8(bhf % F, live ? t0 + tok : n0, cb, D), pre);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
+        for (int e = 0; e < 8; ++e) zk[e] += pre[e];
+      } else {
+        if (PRO && P.wk) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
+          float wk8[8];
+          const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
+          wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
+          kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / D, [](double x) { return group_sum_f64<CPR>(x); });
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
+      }
       uint2* kd = reinterpret_cast<uint2*>(kl + swz_offset<CPR>(tok, cb));
       uint2* vd = reinterpret_cast<uint2*>(vl + swz_offset<CPR>(tok, cb));
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -129,7 +150,7 @@ __device__ __forceinline__ void relu_summary_item(
       for (int j = 0; j < DB; ++j) {
 #pragma unroll
         for (int i = 0; i < DB; ++i) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
-        accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
+        if (!(PRO && P.rope())) accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -151,7 +172,17 @@ __device__ __forceinline__ void relu_summary_item(
       }
     }
   }
-  if (g == 0) {
+  if (PRO && P.rope()) {
+    // lanes lane % CPR + CPR m hold the same channels: sum over m
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zk[e] += __shfl_xor(zk[e], o);
+    if (lane < CPR) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mine[D * D + lane * 8 + e] = zk[e];
+    }
+  } else if (g == 0) {
 #pragma unroll
     for (int j = 0; j < DB; ++j) mine[D * D + j * 32 + col] = accz[j][0];
   }
@@ -254,7 +285,7 @@ __device__ __forceinline__ void relu_output_item(
   auto compute = [&](u32x4 (&b)[U][KS], int t0, const bool full) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (PRO && P.wq) {  // RMSNorm of token col's query: this lane holds its dims 16 s + 8 g + 0..7
+      if (PRO && P.wq && !P.rope()) {  // RMSNorm of token col's query: this lane holds its dims 16 s + 8 g + 0..7
         // in fp64, rounded once to bf16 (as prologue_bf16x8)
         double ss = 0.0;
 #pragma unroll
@@ -278,13 +309,56 @@ __device__ __forceinline__ void relu_output_item(
         }
       }
       float den = 0.0f;
+      if (PRO && P.rope()) {
+        // fp64: RMSNorm (weights), the feature map, the normaliser's dot
+        // product on the unrotated features, then the rotation; one rounding
+        double inv = 1.0;
+        if (P.wq) {
+          double ss = 0.0;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+          for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          b[u][s][e] = relu_bf16x2(b[u][s][e]);
-          den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
-          den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
+            for (int e = 0; e < 4; ++e) {
+              const double x0 = bf16lo_to_f32(b[u][s][e]), x1 = bf16hi_to_f32(b[u][s][e]);
+              ss = fma(x0, x0, fma(x1, x1, ss));
+            }
+          ss += __shfl_xor(ss, 32);
+          inv = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
+        }
+        const int tq = t0 + u * 32 + col;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          double x[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = bf16lo_to_f32(b[u][s][e]);
+            x[2 * e + 1] = bf16hi_to_f32(b[u][s][e]);
+          }
+          if (P.wq) {
+            const float4 a = *reinterpret_cast<const float4*>(wql + 16 * s + 8 * g);
+            const float4 c = *reinterpret_cast<const float4*>(wql + 16 * s + 8 * g + 4);
+            const float wv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * (double)wv[e] * inv;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x[e] = signbit(x[e]) ? 0.0 : x[e];
+            den = fmaf(zr[s][e], (float)x[e], den);
+          }
+          rope_rotate8(x, P.rope8(f, tq < n1 ? tq : n0, 2 * s + g, D));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[u][s][e] = pack_bf16x2_f64(x[2 * e], x[2 * e + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            b[u][s][e] = relu_bf16x2(b[u][s][e]);
+            den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
+            den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
+          }
         }
       }
       den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims

@@ -75,7 +75,7 @@ bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D 
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
   const long grid = (long)a.F * bhp * (1 + a.nco);
-  const bool pro = a.P.wq != nullptr || a.P.wk != nullptr;
+  const bool pro = a.P.wq != nullptr || a.P.wk != nullptr || a.P.rope();
   auto pick = [&](auto d) {
     constexpr int D = decltype(d)::value;
     return pro ? relu_fused_mfma<D, true> : relu_fused_mfma<D, false>;

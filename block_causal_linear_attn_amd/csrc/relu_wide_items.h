@@ -77,6 +77,11 @@ __device__ __forceinline__ void relu_wide_summary_item(
   // token, so row DI of dS is dz at no cost; at DI = 128 an MFMA with an
   // all-ones A operand forms it (register 0 of accz holds z[32 wave + col])
   constexpr bool ZROW = DI < D;
+  // With the rotary embedding the staged keys are rotated, so neither way
+  // gives dz: each thread sums the unrotated features of its channel chunk
+  // (tid % 16) instead (ZV), and the padding row stays zero.
+  const bool ZV = P.rope();
+  float zk[8] = {};
   floatx16 acc[4], accz = {};
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = floatx16{};
@@ -111,16 +116,27 @@ __device__ __forceinline__ void relu_wide_summary_item(
       const int tok = ci >> 4, cb = ci & 15;
       const bool live = t0 + tok < N && cb < CI;
       u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      float wk8[8] = {};
       if (P.wk) {  // the 16 lanes of a DPP row hold the 16 chunks of token `tok`
-        float wk8[8];
         const float4 a = *reinterpret_cast<const float4*>(wl + 8 * cb), b = *reinterpret_cast<const float4*>(wl + 8 * cb + 4);
         wk8[0] = a.x, wk8[1] = a.y, wk8[2] = a.z, wk8[3] = a.w, wk8[4] = b.x, wk8[5] = b.y, wk8[6] = b.z, wk8[7] = b.w;
-        kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
+      }
+      if (ZV) {  // RMSNorm, the feature map, the unrotated sum, then the rotation
+        Prologue Pf = P;
+        Pf.relu = 1;
+        float pre[8];
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, Pf, true, 1.0 / DI,
+                             [](double x) { return group_sum_f64<16>(x); },
+                             P.rope8(f, t0 + tok < N ? t0 + tok : 0, cb < CI ? cb : 0, DI), pre);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zk[e] += pre[e];
+      } else {
+        if (P.wk) kk = prologue_bf16x8(kk, wk8, true, P, true, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
       }
       u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
-      if (ZROW) vv[0] = t0 + tok < N && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
+      if (ZROW && !ZV) vv[0] = t0 + tok < N && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -140,7 +156,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
       const u32x4 vfrag = gather_tokens_32_swz<C>(vl, s * 16, wave * 32, lane);
 #pragma unroll
       for (int J = 0; J < 4; ++J) acc[J] = mfma32x32x16(as_bf16x8(vfrag), as_bf16x8(kfrag[J]), acc[J]);
-      if (!ZROW) accz = mfma32x32x16(as_bf16x8(ones), as_bf16x8(kfrag[wave]), accz);
+      if (!ZROW && !ZV) accz = mfma32x32x16(as_bf16x8(ones), as_bf16x8(kfrag[wave]), accz);
     }
   };
 
@@ -166,6 +182,25 @@ __device__ __forceinline__ void relu_wide_summary_item(
     }
   }
 
+  // ZV: the frame's dz[c] in LDS (the tiles are no longer read): lanes
+  // l, l + 16, l + 32, l + 48 of a wave hold chunk l % 16, then the four
+  // waves' sums are added in a fixed order
+  float* zred = reinterpret_cast<float*>(lds_raw);  // [4][128]
+  float dz = 0.0f;                                 // thread tid < 128: dz[tid]
+  if (ZV) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      zk[e] += __shfl_xor(zk[e], 16);
+      zk[e] += __shfl_xor(zk[e], 32);
+    }
+    if (ntiles > 0 && lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zred[wave * D + lane * 8 + e] = zk[e];
+    }
+    __syncthreads();
+    if (ntiles > 0 && tid < D) dz = ((zred[tid] + zred[D + tid]) + zred[2 * D + tid]) + zred[3 * D + tid];
+  }
+
   // Add the previous cumulative state.  Lane (col, g), register r of acc[J]
   // holds S[32 wave + 8 (r / 4) + 4 g + r % 4][32 J + col]; z[n] sits in row
   // DI, column n (ZROW; the record keeps that row, and a copy of it as its z
@@ -179,6 +214,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[J][r] += prv[row_of(r) * D + J * 32 + col];
     if (!ZROW) accz[0] += prv[D * D + wave * 32 + col];
+    if (ZV && tid < D) dz += prv[D * D + tid];
   } else {
 #pragma unroll
     for (int J = 0; J < 4; ++J)
@@ -186,9 +222,10 @@ __device__ __forceinline__ void relu_wide_summary_item(
       for (int r = 0; r < 16; ++r) {
         const int m = row_of(r), n = J * 32 + col;
         if (S0 && m < DI && n < DI) acc[J][r] += S0[(size_t)bh * DI * DI + m * DI + n];
-        if (ZROW && z0 && m == DI && n < DI) acc[J][r] += z0[(size_t)bh * DI + n];
+        if (ZROW && !ZV && z0 && m == DI && n < DI) acc[J][r] += z0[(size_t)bh * DI + n];
       }
     if (!ZROW && z0) accz[0] += z0[(size_t)bh * DI + wave * 32 + col];
+    if (ZV && z0 && tid < DI) dz += z0[(size_t)bh * DI + tid];
   }
   float* cur = cum + (size_t)bhf * kReluWideRec;
 #pragma unroll
@@ -196,9 +233,10 @@ __device__ __forceinline__ void relu_wide_summary_item(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       cur[row_of(r) * D + J * 32 + col] = acc[J][r];
-      if (ZROW && row_of(r) == DI) cur[D * D + J * 32 + col] = acc[J][r];
+      if (ZROW && !ZV && row_of(r) == DI) cur[D * D + J * 32 + col] = acc[J][r];
     }
-  if (!ZROW && g == 0) cur[D * D + wave * 32 + col] = accz[0];
+  if (!ZROW && !ZV && g == 0) cur[D * D + wave * 32 + col] = accz[0];
+  if (ZV && tid < D) cur[D * D + tid] = dz;
   if (f == F - 1) {
     // every element of S_out / z_out is written by the lane that read the
     // same element of S0 / z0 (frame 0 of this head is this item when F = 1)
@@ -208,9 +246,10 @@ __device__ __forceinline__ void relu_wide_summary_item(
       for (int r = 0; r < 16; ++r) {
         const int m = row_of(r), n = J * 32 + col;
         if (S_out && m < DI && n < DI) S_out[(size_t)bh * DI * DI + m * DI + n] = acc[J][r];
-        if (ZROW && z_out && m == DI && n < DI) z_out[(size_t)bh * DI + n] = acc[J][r];
+        if (ZROW && !ZV && z_out && m == DI && n < DI) z_out[(size_t)bh * DI + n] = acc[J][r];
       }
-    if (!ZROW && z_out && g == 0) z_out[(size_t)bh * DI + wave * 32 + col] = accz[0];
+    if (!ZROW && !ZV && z_out && g == 0) z_out[(size_t)bh * DI + wave * 32 + col] = accz[0];
+    if (ZV && z_out && tid < DI) z_out[(size_t)bh * DI + tid] = dz;
   }
   publish(&flags[bhf], epoch);
 }
@@ -284,20 +323,32 @@ __device__ __forceinline__ void relu_wide_output_item(
   };
   float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
   load_weights8(P.wq, bh % L.H, DI, (tid & 15) * 8, wq8);
-  // phi(q) into LDS buffer buf, and each token's denominator into den[buf]
-  auto stage = [&](const Regs& X, int buf) {
+  // phi(q) into LDS buffer buf, and each token's denominator into den[buf];
+  // t0: the tile's first token (its rows past the chunk hold token n0)
+  auto stage = [&](const Regs& X, int buf, int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       u32x4 w = cb < CI ? X.q[r] : u32x4{0u, 0u, 0u, 0u};
-      if (P.wq) w = prologue_bf16x8(w, wq8, true, P, false, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
       float d = 0.0f;
+      if (P.rope()) {  // the denominator takes the unrotated features, the numerator the rotated ones
+        Prologue Pf = P;
+        Pf.relu = 1;
+        float pre[8];
+        w = prologue_bf16x8(w, wq8, P.wq != nullptr, Pf, false, 1.0 / DI,
+                            [](double x) { return group_sum_f64<16>(x); },
+                            P.rope8(f, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI), pre);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[e] = relu_bf16x2(w[e]);
-        d = fmaf(zr[2 * e], bf16lo_to_f32(w[e]), d);
-        d = fmaf(zr[2 * e + 1], bf16hi_to_f32(w[e]), d);
+        for (int e = 0; e < 8; ++e) d = fmaf(zr[e], pre[e], d);
+      } else {
+        if (P.wq) w = prologue_bf16x8(w, wq8, true, P, false, 1.0 / DI, [](double x) { return group_sum_f64<16>(x); });
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = relu_bf16x2(w[e]);
+          d = fmaf(zr[2 * e], bf16lo_to_f32(w[e]), d);
+          d = fmaf(zr[2 * e + 1], bf16hi_to_f32(w[e]), d);
+        }
       }
       *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = w;
       d = group_sum<16>(d);  // the 16 lanes of a DPP row hold the 16 chunks of this token
@@ -311,7 +362,7 @@ __device__ __forceinline__ void relu_wide_output_item(
   Regs R0, R1;
   fetch(R0, n0);
   fetch(R1, min(n0 + TILE, tlast));
-  stage(R0, 0);
+  stage(R0, 0, n0);
   fetch(R0, min(n0 + 2 * TILE, tlast));
   __syncthreads();
   // a tile's outputs leave as whole rows (16-byte chunks, consecutive lanes on
@@ -350,7 +401,7 @@ __device__ __forceinline__ void relu_wide_output_item(
         *reinterpret_cast<uint2*>(srow + 8 * q4) = w;
       }
     }
-    stage(nxt, buf ^ 1);  // the next tile (past the end: a copy of the last, never read)
+    stage(nxt, buf ^ 1, min(n0 + (it + 1) * TILE, tlast));  // the next tile (past the end: a copy of the last, never read)
     fetch(nxt, min(n0 + (it + 3) * TILE, tlast));
     __syncthreads();
     drain(it, full);

@@ -120,7 +120,7 @@ typedef struct {
  *   RMSNorm  x <- x / sqrt(mean(x^2) + eps) * weight[h][:]   (weight not NULL)
  *   ReLU     x <- max(x, 0)                                   (GDN, relu = 1)
  *   L2       x <- x / |x|, 0 staying 0                        (GDN keys, l2_keys = 1)
- *   RoPE     (GDN, rope_frame or rope_token not NULL) channel pair (2i, 2i+1)
+ *   RoPE     (rope_frame or rope_token not NULL) channel pair (2i, 2i+1)
  *            of q and k turns by its token's angle:
  *              (x0, x1) <- (x0 cos - x1 sin, x0 sin + x1 cos)
  *            with (cos, sin) = rope_frame[rope_frame_offset + f][i] for the
@@ -129,10 +129,15 @@ typedef struct {
  *            (SANA-WM digest, same paragraph: the fused kernel also prepares
  *            the positional encoding; SANA-Video's guide, core mechanisms:
  *            3D RoPE in the linear attention)
- * in that order, before the scan's own feature map (ReLU scan) or key scale
- * (GDN).  The arithmetic is fp64 and the result enters the contractions
- * rounded once to the token precision (bf16: nearest, ties to even), as a
- * separate exact pass writing the token dtype would give.
+ * in that order, before the key scale (GDN).  The ReLU scan applies its
+ * feature map phi after RMSNorm; with the rotary embedding it rotates phi(q)
+ * and phi(k) for the numerator only and keeps the unrotated features in the
+ * normaliser, which stays positive:
+ *     S += v (R phi(k))^T,  z += phi(k),  o = S (R phi(q)) / (z . phi(q) + eps).
+ * The arithmetic is fp64; what enters the contractions is rounded once to the
+ * token precision (bf16: nearest, ties to even), as a separate exact pass
+ * writing the token dtype would give, and the normaliser sums the unrotated
+ * features in fp32.
  */
 typedef struct {
   const float* q_weight;  /* [H][D] fp32 RMSNorm weights of q, or NULL: q not normalised */
@@ -140,7 +145,7 @@ typedef struct {
   float eps;              /* RMSNorm epsilon, finite and > 0 when a weight is given */
   int relu;               /* GDN only: 1 = ReLU on q and k after their norms */
   int l2_keys;            /* GDN only: 1 = keys divided by their L2 norm */
-  /* GDN only, the rotary embedding (both NULL: none).  Tables are fp32, 16-byte
+  /* The rotary embedding (both NULL: none).  Tables are fp32, 16-byte
    * aligned, read only: rope_frame [rope_frames][rope_frame_pairs][2] (needed
    * when rope_frame_pairs > 0) and rope_token [N][D/2 - rope_frame_pairs][2]
    * (needed when rope_frame_pairs < D/2).  rope_frame_pairs is a multiple of 4
@@ -200,7 +205,8 @@ ls_status ls_relu_block_forward_strided(const ls_shape* shape, const ls_strides*
 
 /*
  * ls_relu_block_forward with the per-token prologue `prologue` (NULL: none;
- * relu and l2_keys must be 0: the scan applies its own ReLU feature map).
+ * relu and l2_keys must be 0: the scan applies its own ReLU feature map;
+ * RMSNorm and the rotary embedding as described at ls_prologue).
  * Weights 16-byte aligned (LS_ERR_MISALIGNED) and not overlapping any output
  * or the workspace (LS_ERR_ALIASING); a bad eps or flag is LS_ERR_BAD_PARAM.
  * Workspace size and everything else as ls_relu_block_forward.

@@ -182,7 +182,7 @@ def test_validation_errors_prologue(lib):
         return Pr(None, None, 1e-6, 0, 0, f, t, pf, off, T)
     assert gp(rope()) == 6 and gp(rope(f=None, pf=0)) == 6 and gp(rope(t=None, pf=16)) == 6
     assert gp(rope(off=2, T=5)) == 6
-    assert rp(rope()) == 7                                                   # GDN prologue only
+    assert rp(rope()) == 6                                                   # the ReLU scan takes it too
     assert gp(rope(pf=6)) == 7                                               # not a multiple of 4
     assert gp(rope(pf=20)) == 7                                              # more than D/2 pairs
     assert gp(rope(f=None)) == 1                                             # frame pairs need the frame table

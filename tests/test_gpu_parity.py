@@ -682,3 +682,35 @@ def test_gdn_rope_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, qw, kw, relu, l
     check(tag + " o", o, ro, TOL[dt][0], dt)
     check(tag + " S", S, rS, TOL[dt][1], dt)
     assert torch.equal(o, o2) and torch.equal(S, S2)
+
+
+@pytest.mark.parametrize("H,F,N,D,dt,qw,kw,P,off,bf", [
+    (3, 4, 333, 32, "bf16", True, True, 4, 0, 1),      # narrow items, RMSNorm and RoPE
+    (2, 3, 200, 64, "bf16", False, False, 0, 0, 2),    # narrow items, token table only, 2-frame blocks
+    (3, 3, 200, 112, "bf16", True, True, 8, 2, 1),     # wide items, head dim 112
+    (2, 3, 150, 128, "bf16", False, True, 64, 1, 1),   # wide items, frame table only
+    (2, 3, 50, 16, "bf16", True, True, 4, 0, 1),       # generic bf16 kernels
+    (2, 3, 40, 48, "fp32", True, True, 8, 0, 2),       # generic fp32 kernels
+])
+def test_relu_rope_parity(ls, gen, oracle_mod, H, F, N, D, dt, qw, kw, P, off, bf):
+    """The ReLU scan with the rotary embedding: rotated features in the
+    numerator, unrotated ones in the normaliser, against the oracle."""
+    x = gen.relu_inputs(1, H, F, N, D, dt, seed=61, part=N)
+    wq, wk = _weights(H, D, 62)
+    wq, wk = (wq if qw else None), (wk if kw else None)
+    fcs, tcs = gen.rope_tables(off + F + 1, N, 20, D, P)
+    xd = _dev(x)
+    dev_rope = (None if fcs is None else fcs.to(DEV), None if tcs is None else tcs.to(DEV), P, off)
+    o, S, z = ls.ls_relu_block_forward_prologue(xd["q"], xd["k"], xd["v"], None if wq is None else wq.to(DEV),
+                                                None if wk is None else wk.to(DEV), norm_eps=1e-5,
+                                                block_frames=bf, rope=dev_rope)
+    torch.cuda.synchronize()
+    rnd = "bf16" if dt == "bf16" else None
+    rope = (fcs, tcs, P, off)
+    qn, qd = oracle_mod.relu_rope_features(x["q"], wq, eps=1e-5, rope=rope, round_to=rnd)
+    kn, kd = oracle_mod.relu_rope_features(x["k"], wk, eps=1e-5, rope=rope, round_to=rnd)
+    ro, rS, rz = oracle_mod.linear_block_split(qn, kn, qd, kd, x["v"], block_frames=bf)
+    tag = "relu rope H%d F%d N%d D%d %s q%d k%d P%d off%d bf%d" % (H, F, N, D, dt, qw, kw, P, off, bf)
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+    check(tag + " z", z, rz, TOL[dt][1], dt)
