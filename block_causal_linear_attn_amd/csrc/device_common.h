@@ -126,10 +126,17 @@ __device__ __forceinline__ double group_sum_f64(double x) {
   return x;
 }
 
-// The rotary embedding of 4 channel pairs held as fp64 (cs as for
-// prologue_bf16x8).
-__device__ __forceinline__ void rope_rotate8(double (&x)[8], const float* cs) {
-  const float4 a = *reinterpret_cast<const float4*>(cs), b = *reinterpret_cast<const float4*>(cs + 4);
+// The (cos, sin) of the rotary embedding of 4 channel pairs (one lane's 8
+// channels): a = pairs 0 and 1, b = pairs 2 and 3.
+struct Rot8 {
+  float4 a, b;
+};
+__device__ __forceinline__ Rot8 rot8_load(const float* cs) {
+  return Rot8{*reinterpret_cast<const float4*>(cs), *reinterpret_cast<const float4*>(cs + 4)};
+}
+// The rotary embedding of 4 channel pairs held as fp64.
+__device__ __forceinline__ void rope_rotate8(double (&x)[8], const Rot8& r) {
+  const float4 a = r.a, b = r.b;
   const float c[4] = {a.x, a.z, b.x, b.z}, s[4] = {a.y, a.w, b.y, b.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -152,13 +159,13 @@ __device__ __forceinline__ void rope_rotate8(double (&x)[8], const float* cs) {
 // state, and outputs that cancel (a query nearly orthogonal to the state's
 // rows) turn it into a large relative error.  In fp64 the chance is ~2^-40.
 //
-// cs: the (cos, sin) of the rotary embedding of these 4 channel pairs
-// (Prologue::rope8), or nullptr: no rotation.  pre: if not nullptr, receives
-// the 8 values before the rotation, as fp32.
+// rope: rotate the 4 channel pairs by rot (their rows of the tables,
+// Prologue::rope8).  pre: if not nullptr, receives the 8 values before the
+// rotation, as fp32.
 template <typename Red>
 __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], bool norm, const Prologue& P,
-                                                 bool is_k, double inv_d, Red red, const float* cs = nullptr,
-                                                 float* pre = nullptr) {
+                                                 bool is_k, double inv_d, Red red, bool rope = false,
+                                                 const Rot8& rot = Rot8{}, float* pre = nullptr) {
   double x[8];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -190,7 +197,7 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
 #pragma unroll
     for (int e = 0; e < 8; ++e) pre[e] = (float)x[e];
   }
-  if (cs) rope_rotate8(x, cs);
+  if (rope) rope_rotate8(x, rot);
   return u32x4{pack_bf16x2_f64(x[0], x[1]), pack_bf16x2_f64(x[2], x[3]), pack_bf16x2_f64(x[4], x[5]),
                pack_bf16x2_f64(x[6], x[7])};
 }

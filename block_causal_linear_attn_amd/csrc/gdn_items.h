@@ -141,8 +141,9 @@ __device__ __forceinline__ void gdn_gram_item(
         float wk8[8];
         weights8_lds(wl, cb, wk8);
         // rotary table row of this token (rows past the chunk: a real token's)
-        const float* cs = P.rope() ? P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI) : nullptr;
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, cs);
+        const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI))
+                                  : Rot8{};
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
       }
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
@@ -312,8 +313,9 @@ __device__ __forceinline__ void gdn_gram_rows_item(
         float wk8[8];
         weights8_lds(wl, ci & 15, wk8);
         const int n = t0 + (ci >> 4);
-        const float* cs = P.rope() ? P.rope8(bhf % L.F, n < N ? n : 0, (ci & 15) < CI ? (ci & 15) : 0, DI) : nullptr;
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, cs);
+        const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, n < N ? n : 0, (ci & 15) < CI ? (ci & 15) : 0, DI))
+                                  : Rot8{};
+        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
       }
       uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -704,8 +706,9 @@ __device__ __forceinline__ void gdn_output_item(
       u32x4 qq = X.q[r];
       if (PRO && P.on_q()) {  // chunks past DI re-read a real chunk: zero them out of the token's sums
         qq = cb < CI ? qq : u32x4{0u, 0u, 0u, 0u};
-        const float* cs = P.rope() ? P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI) : nullptr;
-        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16, cs);
+        const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI))
+                                  : Rot8{};
+        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16, P.rope(), rot);
       }
       *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qq;
     }

@@ -32,9 +32,9 @@ constexpr int relu_summary_lds_bytes() {
 // Work item `wg` = (frame of one head) * nc + token chunk: dS, dz partials of
 // the chunk -> partial[wg]; item (frame 0, chunk 0) of each head also copies
 // (S0, z0) into init[head].
-// PRO: the per-token prologue may be on (a separate instantiation keeps the
-// registers of the plain item).
-template <int D, bool PRO = false>
+// PRO: 0 without the per-token prologue, 1 with it, 2 with it and the rotary
+// embedding (separate instantiations keep the registers of the simpler items).
+template <int D, int PRO = 0>
 __device__ __forceinline__ void relu_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
     const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk,
@@ -81,7 +81,11 @@ __device__ __forceinline__ void relu_summary_item(
   // contracted.  Every load is issued (rows past the chunk re-read its first
   // token) and such rows are zeroed when staged: loads under a lane condition
   // would make the compiler wait for every load in flight before staging.
+  // (PRO == 2 at D = 32: the rotary table rows of the tile's chunks come with
+  // them; at D = 64 they do not fit in registers and are read when staged)
+  constexpr bool RPRE = PRO == 2 && LPT <= 4;
   u32x4 kr[LPT], vr[LPT];
+  Rot8 rr[RPRE ? LPT : 1];
   auto fetch = [&](int t0) {
 #pragma unroll
     for (int r = 0; r < LPT; ++r) {
@@ -90,6 +94,7 @@ __device__ __forceinline__ void relu_summary_item(
       const size_t off = (size_t)(n < n1 ? n : n0) * L.sn + cb * 8;
       kr[r] = ld16(kf + off);
       vr[r] = ld16(vf + off);
+      if (RPRE) rr[RPRE ? r : 0] = rot8_load(P.rope8(bhf % F, n < n1 ? n : n0, cb, D));
     }
   };
   int t0 = n0 + wave * TILE;
@@ -102,7 +107,7 @@ __device__ __forceinline__ void relu_summary_item(
       const bool live = t0 + tok < n1;
       u32x4 kk = live ? kr[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? vr[r] : u32x4{0u, 0u, 0u, 0u};
-      if (PRO && P.rope()) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
+      if (PRO == 2) {  // CPR consecutive lanes hold the CPR chunks of token `tok`
         // RMSNorm, the feature map, then the rotation (numerator only): the
         // normaliser sums the unrotated features
         float wk8[8] = {};
@@ -115,7 +120,8 @@ __device__ __forceinline__ void relu_summary_item(
         float pre[8];
         kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, Pf, true, 1.0 / D,
                              [](double x) { return group_sum_f64<CPR>(x); },
-                             P.rope8(bhf % F, live ? t0 + tok : n0, cb, D), pre);
+                             true, RPRE ? rr[RPRE ? r : 0] : rot8_load(P.rope8(bhf % F, live ? t0 + tok : n0, cb, D)),
+                             pre);
 #pragma unroll
         for (int e = 0; e < 8; ++e) zk[e] += pre[e];
       } else {
@@ -150,7 +156,7 @@ __device__ __forceinline__ void relu_summary_item(
       for (int j = 0; j < DB; ++j) {
 #pragma unroll
         for (int i = 0; i < DB; ++i) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
-        if (!(PRO && P.rope())) accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
+        if (PRO != 2) accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -172,7 +178,7 @@ __device__ __forceinline__ void relu_summary_item(
       }
     }
   }
-  if (PRO && P.rope()) {
+  if (PRO == 2) {
     // lanes lane % CPR + CPR m hold the same channels: sum over m
 #pragma unroll
     for (int o = CPR; o < 64; o <<= 1)
@@ -204,7 +210,7 @@ constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4 + 4 * 32 * 
 // Work item `wg` = (frame of one head) * nco + token chunk: the frame's state
 // from init + partials, then o = S phi(q) / (z . phi(q) + eps) for the chunk;
 // the last frame's chunk-0 item writes the final state.
-template <int D, bool PRO = false>
+template <int D, int PRO = 0>
 __device__ __forceinline__ void relu_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
     const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
@@ -213,7 +219,7 @@ __device__ __forceinline__ void relu_output_item(
   constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
   // 32-token groups per wave per step (two with the D = 64 prologue: its
   // fp64 RMSNorm does not fit beside four groups of fragments in registers)
-  constexpr int U = PRO && D >= 64 ? 2 : 4;
+  constexpr int U = PRO != 0 && D >= 64 ? 2 : 4;
   constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
   constexpr int PITCH = D + 4;
   float* Ss = reinterpret_cast<float*>(lds_raw);  // [D][PITCH]
@@ -269,23 +275,41 @@ __device__ __forceinline__ void relu_output_item(
   uint16_t* of = o + L.base(bhf);
   // U groups of 32 tokens per wave; the next step's query fragments are in
   // flight while the current ones are contracted
-  auto load = [&](u32x4 (&b)[U][KS], int t0) {
+  struct Step {
+    u32x4 b[U][KS];
+  };
+  auto load = [&](Step& X, int t0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 32 + col;
       const uint16_t* qrow = qf + (size_t)(t < n1 ? t : n0) * L.sn + g * 8;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) b[u][s] = ld16(qrow + s * 16);
+      for (int s = 0; s < KS; ++s) {
+        X.b[u][s] = ld16(qrow + s * 16);
+      }
     }
   };
   // FULL: every token of the group step is inside the chunk, so the stores
   // need no lane condition (a store under a condition would make the
   // compiler wait for every memory operation in flight before the next
   // group's loads are used)
-  auto compute = [&](u32x4 (&b)[U][KS], int t0, const bool full) {
+  // PRO == 2: the rotary table rows of group u + 1 are read while group u is
+  // computed (rows of the chunks 2 s + g this lane holds); at D = 64 they do
+  // not fit in registers and are read where used
+  constexpr bool OPRE = PRO == 2 && KS <= 2;
+  constexpr int RK = OPRE ? KS : 1;
+  auto rot_rows = [&](Rot8 (&r)[RK], int t) {
+#pragma unroll
+    for (int s = 0; s < RK; ++s) r[s] = rot8_load(P.rope8(f, t < n1 ? t : n0, 2 * s + g, D));
+  };
+  auto compute = [&](Step& X, int t0, const bool full) {
+    auto& b = X.b;
+    Rot8 rcur[RK], rnext[RK];
+    if (OPRE) rot_rows(rcur, t0 + col);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (PRO && P.wq && !P.rope()) {  // RMSNorm of token col's query: this lane holds its dims 16 s + 8 g + 0..7
+      if (OPRE && u + 1 < U) rot_rows(rnext, t0 + (u + 1) * 32 + col);
+      if (PRO == 1 && P.wq) {  // RMSNorm of token col's query: this lane holds its dims 16 s + 8 g + 0..7
         // in fp64, rounded once to bf16 (as prologue_bf16x8)
         double ss = 0.0;
 #pragma unroll
@@ -309,7 +333,7 @@ __device__ __forceinline__ void relu_output_item(
         }
       }
       float den = 0.0f;
-      if (PRO && P.rope()) {
+      if (PRO == 2) {
         // fp64: RMSNorm (weights), the feature map, the normaliser's dot
         // product on the unrotated features, then the rotation; one rounding
         double inv = 1.0;
@@ -325,7 +349,6 @@ __device__ __forceinline__ void relu_output_item(
           ss += __shfl_xor(ss, 32);
           inv = rsqrt_f64(fma(ss, 1.0 / D, (double)P.eps));
         }
-        const int tq = t0 + u * 32 + col;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           double x[8];
@@ -346,7 +369,8 @@ __device__ __forceinline__ void relu_output_item(
             x[e] = signbit(x[e]) ? 0.0 : x[e];
             den = fmaf(zr[s][e], (float)x[e], den);
           }
-          rope_rotate8(x, P.rope8(f, tq < n1 ? tq : n0, 2 * s + g, D));
+          const int tq = t0 + u * 32 + col;
+          rope_rotate8(x, OPRE ? rcur[OPRE ? s : 0] : rot8_load(P.rope8(f, tq < n1 ? tq : n0, 2 * s + g, D)));
 #pragma unroll
           for (int e = 0; e < 4; ++e) b[u][s][e] = pack_bf16x2_f64(x[2 * e], x[2 * e + 1]);
         }
@@ -394,6 +418,10 @@ __device__ __forceinline__ void relu_output_item(
         if (full || tt < n1) st16(of + (size_t)tt * L.sn + cb * 8, w);
       }
       __builtin_amdgcn_wave_barrier();
+      if (OPRE) {
+#pragma unroll
+        for (int s = 0; s < RK; ++s) rcur[s] = rnext[s];
+      }
     }
   };
   // This wave's steps of U * 32 tokens start at n0 + wave * U * 32 and every
@@ -403,7 +431,7 @@ __device__ __forceinline__ void relu_output_item(
   if (n0 >= n1) return;
   const int first = n0 + wave * U * 32;
   const int nfull = first + U * 32 <= n1 ? (n1 - first - U * 32) / STEP + 1 : 0;
-  u32x4 b0[U][KS], b1[U][KS];
+  Step b0, b1;
   int t0 = first;
   load(b0, t0);
   int k = 0;

@@ -25,7 +25,7 @@ namespace {
 // keeps every summary an output item waits for at a lower block id.  Within
 // a step items are head-minor with B*H padded to BHp (a multiple of 8);
 // padding items leave at once.
-template <int D, bool PRO>
+template <int D, int PRO>
 __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
@@ -75,10 +75,11 @@ bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D 
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
   const long grid = (long)a.F * bhp * (1 + a.nco);
-  const bool pro = a.P.wq != nullptr || a.P.wk != nullptr || a.P.rope();
+  // the prologue's instantiation: 0 none, 1 RMSNorm, 2 with the rotary embedding
+  const int pro = a.P.rope() ? 2 : (a.P.wq != nullptr || a.P.wk != nullptr) ? 1 : 0;
   auto pick = [&](auto d) {
     constexpr int D = decltype(d)::value;
-    return pro ? relu_fused_mfma<D, true> : relu_fused_mfma<D, false>;
+    return pro == 2 ? relu_fused_mfma<D, 2> : pro == 1 ? relu_fused_mfma<D, 1> : relu_fused_mfma<D, 0>;
   };
   auto run = [&](auto kern) {
     const int lag = fused_lag(device_slots((const void*)kern), bhp * (1 + a.nco), a.bfr, a.F);

@@ -127,7 +127,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
         float pre[8];
         kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, Pf, true, 1.0 / DI,
                              [](double x) { return group_sum_f64<16>(x); },
-                             P.rope8(f, t0 + tok < N ? t0 + tok : 0, cb < CI ? cb : 0, DI), pre);
+                             true, rot8_load(P.rope8(f, t0 + tok < N ? t0 + tok : 0, cb < CI ? cb : 0, DI)), pre);
 #pragma unroll
         for (int e = 0; e < 8; ++e) zk[e] += pre[e];
       } else {
@@ -338,7 +338,7 @@ __device__ __forceinline__ void relu_wide_output_item(
         float pre[8];
         w = prologue_bf16x8(w, wq8, P.wq != nullptr, Pf, false, 1.0 / DI,
                             [](double x) { return group_sum_f64<16>(x); },
-                            P.rope8(f, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI), pre);
+                            true, rot8_load(P.rope8(f, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI)), pre);
 #pragma unroll
         for (int e = 0; e < 8; ++e) d = fmaf(zr[e], pre[e], d);
       } else {
