@@ -508,6 +508,19 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
         q2, k2 = torch_prologue(g["q"], wq, False), torch_prologue(g["k"], wk, True)
         ls.ls_gdn_frame_forward(q2, k2, g["v"], g["alpha"], g["beta"], out=out)
 
+    # 3D rotary embedding at synthetic positions: 16 pairs by frame, 48 by the
+    # 23 x 40 latent grid's rows and columns
+    fcs, tcs = inputs.rope_tables(g["q"].shape[2], g["q"].shape[3], 40, D, 16, device=dev)
+
+    def fused_rope():
+        ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk, norm_eps=1e-6,
+                                         relu=True, l2_keys=True, out=out, rope=(fcs, tcs, 16, 0))
+
+    gdn = {"plain": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out),
+                              "gdn_fused"),
+           "fused_prologue": kernel_us(fused, "gdn_fused"),
+           "fused_prologue_with_3d_rope": kernel_us(fused_rope, "gdn_fused")}
+    # the torch variant last: its fp32 temporaries come and go after the library's timings
     unfused()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -517,20 +530,8 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
         b.record()
     torch.cuda.synchronize()
     ms_unfused = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
-    # 3D rotary embedding at synthetic positions: 16 pairs by frame, 48 by the
-    # 23 x 40 latent grid's rows and columns
-    fcs, tcs = inputs.rope_tables(g["q"].shape[2], g["q"].shape[3], 40, D, 16, device=dev)
-
-    def fused_rope():
-        ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk, norm_eps=1e-6,
-                                         relu=True, l2_keys=True, out=out, rope=(fcs, tcs, 16, 0))
-
-    res["gdn_h24_d128_181_frames_rmsnorm_relu_l2_us"] = {
-        "plain": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out),
-                           "gdn_fused"),
-        "fused_prologue": kernel_us(fused, "gdn_fused"),
-        "fused_prologue_with_3d_rope": kernel_us(fused_rope, "gdn_fused"),
-        "torch_prologue_then_plain_wall": round(1e3 * ms_unfused, 2)}
+    gdn["torch_prologue_then_plain_wall"] = round(1e3 * ms_unfused, 2)
+    res["gdn_h24_d128_181_frames_rmsnorm_relu_l2_us"] = gdn
     del fcs, tcs
     return res
 

@@ -123,8 +123,10 @@ __device__ __forceinline__ void gdn_gram_item(
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
       const size_t off = (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8;
-      X.k[r] = ld16_stream(kf + off);
-      X.v[r] = ld16_stream(vf + off);
+      // plain loads: the GDN call at 720p 60 s ran 1170 -> 1139 us against
+      // non-temporal ones (the output stores stay non-temporal)
+      X.k[r] = ld16(kf + off);
+      X.v[r] = ld16(vf + off);
     }
     if (TG) X.b = gf[t0 + (tid & 63) < n1 ? t0 + (tid & 63) : n0];
   };
@@ -298,10 +300,10 @@ __device__ __forceinline__ void gdn_gram_rows_item(
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
       const int n = t0 + (ci >> 4);
-      R.k[r] = ld16_stream(kf + (size_t)(n < N ? n : 0) * L.sn + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
+      R.k[r] = ld16(kf + (size_t)(n < N ? n : 0) * L.sn + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
     }
     const int n = t0 + (tid >> 2);
-    R.v = ld16_stream(vf + (size_t)(n < N ? n : 0) * L.sn + (vchunk < CI ? vchunk : CI - 1) * 8);
+    R.v = ld16(vf + (size_t)(n < N ? n : 0) * L.sn + (vchunk < CI ? vchunk : CI - 1) * 8);
     if (TG) R.b = gf[t0 + (tid & 63) < N ? t0 + (tid & 63) : 0];
   };
   auto stage = [&](const Regs& R, int buf, int t0) {
@@ -691,7 +693,7 @@ __device__ __forceinline__ void gdn_output_item(
       const int n = t0 + tok;
       // rows past the chunk re-read its first token: their outputs are never stored
       // (dims past DI re-read a real chunk: S_f is zero in those columns)
-      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
+      X.q[r] = ld16(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
     }
   };
   float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
