@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "scan tokens/sec (1 GPU) at 720p minute-scale; % of MFMA/HBM roofline"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_720p_minute.md")
 # sources each fused kernel is built from: counters taken on other sources are stale
@@ -208,6 +209,14 @@ def main():
         "gdn_gram": half_wm,                     # k, v in
         "gdn_output": half_wm,                   # q in, o out
     }
+    # algorithmic MFMA work per launch (for information): ReLU 4 H D^2 flop per
+    # token (v phi(k)^T and S phi(q)), GDN 6 H D^2 per token (G, U and S q) plus
+    # 2 H D^3 per frame (the state times beta G)
+    flops = {
+        "relu_fused": 4 * wv.B * wv.H * wv.F * wv.N * wv.D ** 2 / n_calls,
+        "gdn_fused": 6 * wg.B * wg.H * wg.F * wg.N * wg.D ** 2 + 2 * wg.B * wg.H * wg.F * wg.D ** 3,
+    }
+    copy_gbs = device_copy_gbs(torch)
     kernels = {}
     for name, (launches, total_ms) in kstats.items():
         avg_us = 1e3 * total_ms / max(1, launches)
@@ -218,6 +227,9 @@ def main():
             k["alg_bytes_per_launch"] = int(alg[name])
             k["achieved_GBs"] = round(gbs, 1)
             k["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+            k["copy_frac"] = round(gbs / copy_gbs, 4)
+        if name in flops:
+            k["mfma_frac"] = round(flops[name] / (avg_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
         kernels[name] = k
     roofline = None
     if kernels:
@@ -226,7 +238,9 @@ def main():
         roofline = {"bound": "hbm", "kernel": dom, "achieved": kernels[dom]["achieved_GBs"],
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kernels[dom]["hbm_frac"],
                     "traffic": None if traffic is None else int(traffic),
-                    "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note}
+                    "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note,
+                    "copy_GBs": round(copy_gbs, 1), "frac_of_copy": kernels[dom]["copy_frac"],
+                    "mfma_frac": kernels[dom].get("mfma_frac")}
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
     d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
@@ -281,6 +295,25 @@ def main():
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def device_copy_gbs(torch, nbytes=1 << 30, reps=5):
+    """Bandwidth of a plain device-to-device copy (bytes read + written per
+    second, median of `reps` copies of 1 GiB), the practical ceiling the
+    roofline's second line divides by."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del src, dst
+    return 2 * nbytes / (ms / 1e3) / 1e9
 
 
 def time_head_dim_112(torch, ls, inputs, reps=3):
