@@ -630,13 +630,29 @@ def cpu_baseline(args, inputs, wv, wg, tokens):
     oracle.gdn_frame(xg["q"], xg["k"], xg["v"], xg["alpha"], xg["beta"], nthreads=threads)
     tg = time.perf_counter() - t0
     step_s = tv * wv.H / hv + tg * wg.H / hg
-    print("oracle: %d+%d heads in %.2f+%.2f s on %d threads" % (hv, hg, tv, tg, threads),
-          file=sys.stderr, flush=True)
+    # the same on one thread, one head of each part (about 3 s)
+    x1 = inputs.relu_inputs(1, 1, wv.F, wv.N, wv.D, "bf16", seed=wv.seed, part=998)
+    x1 = {k: t.float().numpy() for k, t in x1.items()}
+    t0 = time.perf_counter()
+    oracle.relu_block(x1["q"], x1["k"], x1["v"], nthreads=1)
+    tv1 = time.perf_counter() - t0
+    x1 = inputs.gdn_inputs(1, 1, wg.F, wg.N, wg.D, "bf16", seed=wg.seed, part=998, l2_keys=True)
+    x1 = {k: t.float().numpy() for k, t in x1.items()}
+    t0 = time.perf_counter()
+    oracle.gdn_frame(x1["q"], x1["k"], x1["v"], x1["alpha"], x1["beta"], nthreads=1)
+    tg1 = time.perf_counter() - t0
+    del x1
+    step_1 = tv1 * wv.H + tg1 * wg.H
+    print("oracle: %d+%d heads in %.2f+%.2f s on %d threads; one head each on one thread %.2f+%.2f s"
+          % (hv, hg, tv, tg, threads, tv1, tg1), file=sys.stderr, flush=True)
     return {"value": round(tokens / step_s, 1), "unit": "tokens/s", "cores": min(threads, max(hv, hg)),
             "kind": "oracle",
             "sample": "%d of %d heads of the ReLU rollout (all 241 frames) and %d of %d heads of the GDN "
                       "scan (all 181 frames), same shapes and distributions, timed %.1f s + %.1f s and "
-                      "scaled by the head ratio" % (hv, wv.H, hg, wg.H, tv, tg)}
+                      "scaled by the head ratio" % (hv, wv.H, hg, wg.H, tv, tg),
+            "value_1thread": round(tokens / step_1, 1),
+            "sample_1thread": "one head of each part on one thread, %.2f s + %.2f s, scaled by the head "
+                              "counts" % (tv1, tg1)}
 
 
 if __name__ == "__main__":
