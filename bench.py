@@ -94,6 +94,8 @@ def parse():
                     help="skip the side measurement of the block-causal temporal convolution")
     ap.add_argument("--no-strided", action="store_true",
                     help="skip the side measurement of the strided [B][F][N][H][D] layout")
+    ap.add_argument("--no-480p", action="store_true",
+                    help="skip the side measurement of the 480p 5 s ReLU call")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip the side measurement of the fused per-token prologue")
     ap.add_argument("--no-chunk-step", action="store_true",
@@ -243,6 +245,7 @@ def main():
                     "mfma_frac": kernels[dom].get("mfma_frac")}
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
+    v480 = None if args.no_480p else time_480p(torch, ls, inputs)
     d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
     tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
@@ -289,12 +292,38 @@ def main():
                                     round(ms_step[int(0.9 * (len(ms_step) - 1))], 4)],
             "step_hbm_frac": round((bytes_video + bytes_wm) / (med(ms_step) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "side": {"sana_wm_chunk_step": chunk_step, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
+        "side": {"sana_wm_chunk_step": chunk_step, "sana_video_480p_5s": v480, "head_dim_112": d112, "sana_wm_720p_60s_token_gate": tgate,
                  "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv,
                  "bshd_layout": strided, "fused_prologue": pro},
         "kernels": kernels,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_480p(torch, ls, inputs, reps=5):
+    """The SANA-Video 480p 5 s ReLU call (B1 H70 D32 F21 N1560, one call of
+    21 frames, frame-causal), two input sets alternating; median of `reps`
+    calls after one warm-up call each."""
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS["sana_video_480p_5s"]
+    xs = [inputs.relu_inputs(w.B, w.H, w.F, w.N, w.D, "bf16", seed=w.seed, part=p, device=dev) for p in (0, 1)]
+    outs = [torch.empty_like(x["q"]) for x in xs]
+    for i in range(2):
+        ls.ls_relu_block_forward(xs[i]["q"], xs[i]["k"], xs[i]["v"], out=outs[i])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for j, (a, b) in enumerate(ev):
+        x = xs[j % 2]
+        a.record()
+        ls.ls_relu_block_forward(x["q"], x["k"], x["v"], out=outs[j % 2])
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    tokens = w.B * w.F * w.N
+    nbytes = 4 * w.B * w.H * w.F * w.N * w.D * 2
+    del xs, outs
+    return {"ms_median": round(ms, 4), "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "workload": w.note}
 
 
 def device_copy_gbs(torch, nbytes=1 << 30, reps=5):
