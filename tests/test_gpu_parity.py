@@ -714,3 +714,60 @@ def test_relu_rope_parity(ls, gen, oracle_mod, H, F, N, D, dt, qw, kw, P, off, b
     check(tag + " o", o, ro, TOL[dt][0], dt)
     check(tag + " S", S, rS, TOL[dt][1], dt)
     check(tag + " z", z, rz, TOL[dt][1], dt)
+
+
+# --------------------------------------------------------------------------- degenerate cases
+@pytest.mark.parametrize("B,H,F,N,D,dt", [(1, 2, 10, 300, 128, "bf16"), (1, 40, 5, 130, 128, "bf16"),
+                                          (1, 2, 10, 200, 112, "bf16"), (1, 2, 10, 40, 64, "bf16"),
+                                          (1, 2, 10, 20, 32, "fp32")])
+def test_gdn_degenerate_gates(ls, gen, oracle_mod, B, H, F, N, D, dt):
+    """Frames with alpha = 0 (the state resets to beta U), beta = 0 (pure
+    decay), alpha = 1 and beta = 0 (the state passes unchanged) and alpha =
+    beta = 1, mixed in one call from a nonzero initial state."""
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=63, part=N, l2_keys=True)
+    a, b = x["alpha"].clone(), x["beta"].clone()
+    for f in range(F):
+        if f % 5 == 1:
+            a[:, :, f] = 0.0
+        elif f % 5 == 2:
+            b[:, :, f] = 0.0
+        elif f % 5 == 3:
+            a[:, :, f], b[:, :, f] = 1.0, 0.0
+        elif f % 5 == 4:
+            a[:, :, f], b[:, :, f] = 1.0, 1.0
+    x["alpha"], x["beta"] = a.contiguous(), b.contiguous()
+    S0 = _rand_state(B, H, D, 64, scale=0.5)
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"], S0.to(DEV))
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"], S0)
+    tag = "gdn degenerate gates B%d H%d F%d N%d D%d %s" % (B, H, F, N, D, dt)
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+
+
+def test_gdn_more_frames_than_the_decay_window(ls, gen, oracle_mod):
+    """2098 frames in one call: the scan items hold the decays of 2048 frames at
+    a time, so the call crosses a window boundary (frame-interleaved launch)."""
+    B, H, F, N, D, dt = 1, 2, 2098, 4, 128, "bf16"
+    x = gen.gdn_inputs(B, H, F, N, D, dt, seed=65, part=N, l2_keys=True)
+    xd = _dev(x)
+    o, S = ls.ls_gdn_frame_forward(xd["q"], xd["k"], xd["v"], xd["alpha"], xd["beta"])
+    torch.cuda.synchronize()
+    ro, rS = oracle_mod.gdn_frame(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
+    tag = "gdn long call F%d" % F
+    check(tag + " o", o, ro, TOL[dt][0], dt)
+    check(tag + " S", S, rS, TOL[dt][1], dt)
+
+
+@pytest.mark.parametrize("H,F,N,D,dt", [(3, 4, 333, 32, "bf16"), (2, 3, 200, 64, "bf16"), (2, 3, 150, 112, "bf16"),
+                                        (2, 3, 150, 128, "bf16"), (2, 3, 40, 48, "fp32")])
+def test_relu_zero_features_give_zero_outputs(ls, gen, H, F, N, D, dt):
+    """Queries with every entry negative have phi(q) = 0: the numerator is an
+    empty sum and the output is exactly zero (denominator eps)."""
+    x = gen.relu_inputs(1, H, F, N, D, dt, seed=67, part=N)
+    q = -x["q"].abs()
+    xd = _dev(x)
+    o, S, z = ls.ls_relu_block_forward(q.to(DEV), xd["k"], xd["v"])
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
