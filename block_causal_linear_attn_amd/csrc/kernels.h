@@ -85,7 +85,9 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
                                   uint32_t* err, hipStream_t st);
 //  ReLU, wide heads: `partial` holds the cumulative state of every frame,
 //  [B*H*F][128*128 + 128] floats (S row-major, then z; 128 dims wide, zero
-//  past D); flags[B*H*F] mark them complete.  `init` is unused.
+//  past D), then [B*H*F][nc - 1] records of the summary parts past the first
+//  (nc parts per frame); flags[B*H*F] mark the cumulative states complete,
+//  flags[B*H*F ..][nc - 1] the parts.  `init` is unused.
 hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                        uint32_t* err, hipStream_t st);
 //  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states,

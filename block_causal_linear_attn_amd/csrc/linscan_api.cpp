@@ -244,16 +244,25 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   if (p.fused) {
     p.nc = 1;
     p.chunk = s->N > 0 ? s->N : 1;
+    // wide heads: a frame's summary is split over up to 8 parts (runs of at
+    // least 6 tiles of 64 tokens) while all parts of all frames still fit in
+    // the device's 512 resident slots of this kernel (2 per CU), so that few
+    // heads or frames still fill the chip; part 0 adds the others' sums
+    if (p.wide) {
+      const long tiles = (s->N + 63) / 64;
+      while (p.nc < 8 && (p.nc + 1) * d.bhf <= 512 && tiles >= 6 * (p.nc + 1)) ++p.nc;
+    }
   } else {
     plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
   }
   plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
-  // wide heads keep one cumulative record per frame, 128 dims wide, and no init copy
+  // wide heads keep one cumulative record per frame, 128 dims wide, then one
+  // record per summary part past the first, and no init copy
   const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;
   p.partial_off = kHeaderBytes;
   p.init_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * out * sizeof(float), 256);
   p.flags_off = align_up(p.init_off + (p.wide ? 0 : (size_t)d.bh * out * sizeof(float)), 256);
-  p.bytes = align_up(p.flags_off + (p.fused ? (size_t)d.bhf * sizeof(uint64_t) : 0), 256);
+  p.bytes = align_up(p.flags_off + (p.fused ? (size_t)d.bhf * p.nc * sizeof(uint64_t) : 0), 256);
   return p;
 }
 

@@ -7,17 +7,19 @@
 // tensors are taken as 128 dims wide, the dims past the head dim being zero
 // (they add nothing to any sum), and wave w owns rows [32w, 32w + 32).
 //
-// Summary item, one per (head, frame): dS = V^T phi(K) over all of the
-// frame's tokens.  The workgroup stages 64-token K and V tiles in LDS (ring of
+// Summary items, np per (head, frame) (np = 1 when there are enough frames
+// and heads to fill the chip): dS = V^T phi(K) over one run of the frame's
+// tokens.  The workgroup stages 64-token K and V tiles in LDS (ring of
 // register sets in flight, rows unpadded with their 16-byte chunks swizzled
 // by token; phi applied to K when staged) and each lane gathers 8 tokens of
 // one dimension per MFMA operand with two LDS transpose reads.  dz = 1^T phi(K)
 // comes from a padding row (head dim 112: value dim 112 is set to 1, so row
 // 112 of dS is dz) or, at head dim 128, from one more MFMA with an all-ones
-// A operand.  The item then adds the cumulative state of the previous frame
-// (the initial state for frame 0) and writes the cumulative state of its own
-// frame: the frames of a head form a chain of short hand-offs (about 2 us
-// each), and no later reader has to sum partials.  (A decoupled look-back
+// A operand.  Part 0 of a frame then adds the other parts' sums and the
+// cumulative state of the previous frame (the initial state for frame 0) and
+// writes the cumulative state of its own frame: the frames of a head form a
+// chain of short hand-offs (about 2 us each), and no later reader has to sum
+// partials.  (A decoupled look-back
 // over earlier frames' own sums was measured slower: every item then reads
 // several 66 KB records from L2 at once.)
 //
@@ -42,16 +44,23 @@ constexpr int kReluWideOutPitch = kReluWide + 8;
 // query tiles and output staging tiles (double buffered, bf16) + per-token denominators
 constexpr int kReluWideOutLds = 4 * 64 * kReluWideOutPitch * 2 + 2 * 64 * 4;
 
-// Summary item of frame f of head bh: cum[bh][f] = cum[bh][f - 1] + (dS, dz),
-// with cum[bh][-1] the initial state (S0, z0; zero where NULL).  The last
-// frame's item also writes the final state to (S_out, z_out), which may alias
-// (S0, z0).  flags[bh * F + f] is published when cum[bh][f] is complete;
-// the item waits for flags[bh * F + f - 1] before reading the previous one.
+// Summary item `part` (of np) of frame f of head bh.  The frame's tiles of 64
+// tokens are split into np runs of consecutive tiles, one per part.  Part
+// p > 0 writes the sums over its run to parts[(bh * F + f) * (np - 1) + p - 1]
+// (a record in accumulator order) and publishes the flag of the same index in
+// pflags.  Part 0 sums its own run, adds the other parts' records (once all
+// their flags are set) in the order p = 1, 2, ..., then forms
+// cum[bh][f] = cum[bh][f - 1] + (dS, dz), with cum[bh][-1] the initial state
+// (S0, z0; zero where NULL).  The last frame's part 0 also writes the final
+// state to (S_out, z_out), which may alias (S0, z0).  flags[bh * F + f] is
+// published when cum[bh][f] is complete; part 0 waits for
+// flags[bh * F + f - 1] before reading the previous one.
 template <int DI>
 __device__ __forceinline__ void relu_wide_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ cum,
-    const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f,
-    uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L, Prologue P) {
+    const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f, int np,
+    int part, float* __restrict__ parts, uint64_t* __restrict__ pflags, uint64_t* __restrict__ flags,
+    uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -87,9 +96,13 @@ __device__ __forceinline__ void relu_wide_summary_item(
   for (int j = 0; j < 4; ++j) acc[j] = floatx16{};
   const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
 
+  // this part's tokens [nb, ne): a run of tpp whole tiles (the last part's may be shorter or empty)
+  const int tpp = ((N + TILE - 1) / TILE + np - 1) / np;
+  const int nb = min(N, part * tpp * TILE), ne = min(N, nb + tpp * TILE);
+
   // Tile t sits in register set t % DEPTH from its fetch until it is staged.
   // The loop runs a whole number of ring passes with no branch: tiles past
-  // the frame are staged as zeros and add nothing, fetches past the frame
+  // the run are staged as zeros and add nothing, fetches past the run
   // re-read its last tile, and dims past DI re-read a real chunk and are
   // zeroed when staged.  (A load or stage under a condition would make the
   // compiler wait for every load in flight at each stage.)
@@ -104,7 +117,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const int n = t0 + tok;
-      const size_t off = (size_t)(n < N ? n : 0) * L.sn + (cb < CI ? cb : CI - 1) * 8;
+      const size_t off = (size_t)(n < ne ? n : nb) * L.sn + (cb < CI ? cb : CI - 1) * 8;
       X.k[r] = ld16_stream(kf + off);
       X.v[r] = ld16_stream(vf + off);
     }
@@ -114,7 +127,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      const bool live = t0 + tok < N && cb < CI;
+      const bool live = t0 + tok < ne && cb < CI;
       u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
       float wk8[8] = {};
       if (P.wk) {  // the 16 lanes of a DPP row hold the 16 chunks of token `tok`
@@ -127,7 +140,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
         float pre[8];
         kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, Pf, true, 1.0 / DI,
                              [](double x) { return group_sum_f64<16>(x); },
-                             true, rot8_load(P.rope8(f, t0 + tok < N ? t0 + tok : 0, cb < CI ? cb : 0, DI)), pre);
+                             true, rot8_load(P.rope8(f, t0 + tok < ne ? t0 + tok : nb, cb < CI ? cb : 0, DI)), pre);
 #pragma unroll
         for (int e = 0; e < 8; ++e) zk[e] += pre[e];
       } else {
@@ -136,7 +149,7 @@ __device__ __forceinline__ void relu_wide_summary_item(
         for (int e = 0; e < 4; ++e) kk[e] = relu_bf16x2(kk[e]);
       }
       u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
-      if (ZROW && !ZV) vv[0] = t0 + tok < N && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
+      if (ZROW && !ZV) vv[0] = t0 + tok < ne && cb == CI ? 0x3f80u : vv[0];  // v[token][DI] = 1
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -160,14 +173,14 @@ __device__ __forceinline__ void relu_wide_summary_item(
     }
   };
 
-  const int ntiles = (N + TILE - 1) / TILE;
+  const int ntiles = (ne - nb + TILE - 1) / TILE;
   if (ntiles > 0) {
-    const int tlast = (ntiles - 1) * TILE;
+    const int tlast = nb + (ntiles - 1) * TILE;
     const int nsteps = (ntiles + DEPTH - 1) / DEPTH * DEPTH;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) fetch(R[d], min(d * TILE, tlast));
-    stage(R[0], 0, 0);
-    fetch(R[0], min(DEPTH * TILE, tlast));
+    for (int d = 0; d < DEPTH; ++d) fetch(R[d], min(nb + d * TILE, tlast));
+    stage(R[0], 0, nb);
+    fetch(R[0], min(nb + DEPTH * TILE, tlast));
     __syncthreads();
     for (int it0 = 0; it0 < nsteps; it0 += DEPTH) {
 #pragma unroll
@@ -175,8 +188,8 @@ __device__ __forceinline__ void relu_wide_summary_item(
         const int it = it0 + u;
         contract(it & 1);
         Regs& nxt = R[(u + 1) % DEPTH];  // holds tile it + 1
-        stage(nxt, (it + 1) & 1, (it + 1) * TILE);
-        fetch(nxt, min((it + 1 + DEPTH) * TILE, tlast));
+        stage(nxt, (it + 1) & 1, nb + (it + 1) * TILE);
+        fetch(nxt, min(nb + (it + 1 + DEPTH) * TILE, tlast));
         __syncthreads();
       }
     }
@@ -199,6 +212,38 @@ __device__ __forceinline__ void relu_wide_summary_item(
     }
     __syncthreads();
     if (ntiles > 0 && tid < D) dz = ((zred[tid] + zred[D + tid]) + zred[2 * D + tid]) + zred[3 * D + tid];
+  }
+
+  // A part record holds acc[J][4 i .. 4 i + 3] of thread t as the float4 at
+  // (4 J + i) * 256 + t, then the item's own z entries (accz register 0 at
+  // 32 wave + col, or dz at tid) from float D * D on.
+  if (np > 1) {
+    if (part > 0) {
+      float* rec = parts + ((size_t)bhf * (np - 1) + part - 1) * kReluWideRec;
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          reinterpret_cast<float4*>(rec)[(4 * J + i) * 256 + tid] =
+              make_float4(acc[J][4 * i], acc[J][4 * i + 1], acc[J][4 * i + 2], acc[J][4 * i + 3]);
+      if (!ZROW && !ZV && g == 0) rec[D * D + wave * 32 + col] = accz[0];
+      if (ZV && tid < D) rec[D * D + tid] = dz;
+      publish(&pflags[(size_t)bhf * (np - 1) + part - 1], epoch);
+      return;
+    }
+    wait_all(&pflags[(size_t)bhf * (np - 1)], np - 1, epoch, err);
+    for (int p = 1; p < np; ++p) {
+      const float* rec = parts + ((size_t)bhf * (np - 1) + p - 1) * kReluWideRec;
+#pragma unroll
+      for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 x = reinterpret_cast<const float4*>(rec)[(4 * J + i) * 256 + tid];
+          acc[J][4 * i] += x.x, acc[J][4 * i + 1] += x.y, acc[J][4 * i + 2] += x.z, acc[J][4 * i + 3] += x.w;
+        }
+      if (!ZROW && !ZV) accz[0] += rec[D * D + wave * 32 + col];
+      if (ZV && tid < D) dz += rec[D * D + tid];
+    }
   }
 
   // Add the previous cumulative state.  Lane (col, g), register r of acc[J]

@@ -66,6 +66,8 @@ RELU_CASES = [
     (2, 10, 3, 200, 112, "bf16", 2, True),      # wide path, B*H = 20 (padding items), blocks of 2 frames
     (1, 2, 1, 1, 112, "bf16", 1, True),         # wide path, single token, single frame
     (1, 2, 5, 300, 128, "bf16", 3, True),       # wide path at D = 128 (normaliser by MFMA), ragged block
+    (1, 3, 3, 1000, 112, "bf16", 2, True),      # wide path, each frame's summary in 2 parts (ragged second)
+    (1, 2, 2, 3121, 128, "bf16", 1, True),      # wide path at D = 128, summaries in 8 parts, the last one empty
     (1, 2, 3, 50, 16, "bf16", 1, False),        # generic bf16, D = 16
     (1, 2, 7, 40, 32, "bf16", 3, True),         # blocks of 3 frames (ragged last block)
     (1, 2, 3, 70, 48, "fp32", 2, True),         # generic fp32
@@ -564,6 +566,7 @@ def _weights(H, D, seed):
 
 @pytest.mark.parametrize("H,F,N,D,dt,qw,kw", [(3, 4, 333, 32, "bf16", True, True), (2, 3, 200, 64, "bf16", True, True),
                                               (3, 3, 200, 112, "bf16", True, False), (2, 3, 150, 128, "bf16", False, True),
+                                              (2, 2, 900, 128, "bf16", True, True),  # summaries in 2 parts
                                               (2, 3, 50, 16, "bf16", True, True), (2, 3, 40, 48, "fp32", True, True)])
 def test_relu_prologue_parity(ls, gen, oracle_mod, H, F, N, D, dt, qw, kw):
     x = gen.relu_inputs(1, H, F, N, D, dt, seed=51, part=N)
@@ -689,6 +692,7 @@ def test_gdn_rope_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, qw, kw, relu, l
     (2, 3, 200, 64, "bf16", False, False, 0, 0, 2),    # narrow items, token table only, 2-frame blocks
     (3, 3, 200, 112, "bf16", True, True, 8, 2, 1),     # wide items, head dim 112
     (2, 3, 150, 128, "bf16", False, True, 64, 1, 1),   # wide items, frame table only
+    (2, 2, 900, 112, "bf16", True, True, 8, 1, 1),     # wide items, each frame's summary in 2 parts
     (2, 3, 50, 16, "bf16", True, True, 4, 0, 1),       # generic bf16 kernels
     (2, 3, 40, 48, "fp32", True, True, 8, 0, 2),       # generic fp32 kernels
 ])
