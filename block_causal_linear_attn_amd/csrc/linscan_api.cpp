@@ -255,7 +255,10 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   } else {
     plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);
   }
-  plan_chunks(d.bhf, s->N, 1536, 512, 128, &p.nco, &p.chunko);
+  // output items: wide heads aim at about 1000 (about two per resident slot,
+  // measured best at 20 heads x 10 frames x 3600 tokens) and take chunks down
+  // to 128 tokens when there are few frames (one frame: 52 -> 45 us)
+  plan_chunks(d.bhf, s->N, p.wide ? 1000 : 1536, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
   // wide heads keep one cumulative record per frame, 128 dims wide, then one
   // record per summary part past the first, and no init copy
   const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;

@@ -307,8 +307,12 @@ def test_deterministic(ls, gen):
     y = _dev(gen.gdn_inputs(1, 2, 5, 500, 128, "bf16", seed=24))
     c = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
     d = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    # wide heads, each frame's summary in 2 parts (a fixed order of addition)
+    w = _dev(gen.relu_inputs(1, 4, 3, 1000, 112, "bf16", seed=27))
+    e = ls.ls_relu_block_forward(w["q"], w["k"], w["v"])
+    f = ls.ls_relu_block_forward(w["q"], w["k"], w["v"])
     torch.cuda.synchronize()
-    for s, t in zip(a + c, b + d):
+    for s, t in zip(a + c + e, b + d + f):
         assert torch.equal(s, t)
 
 
@@ -320,10 +324,15 @@ def test_head_isolation(ls, gen):
     y = _dev(gen.gdn_inputs(1, 3, 2, 100, 128, "bf16", seed=26))
     y["v"][0, 1, 1, 7, 0] = float("nan")
     o2, S2 = ls.ls_gdn_frame_forward(y["q"], y["k"], y["v"], y["alpha"], y["beta"])
+    # wide heads with 2 summary parts per frame: the NaN sits in the second part's tokens
+    w = _dev(gen.relu_inputs(1, 3, 2, 800, 128, "bf16", seed=28))
+    w["v"][0, 1, 0, 600, 9] = float("nan")
+    o3, S3, z3 = ls.ls_relu_block_forward(w["q"], w["k"], w["v"])
     torch.cuda.synchronize()
-    for t in (o, S, o2, S2):
+    for t in (o, S, o2, S2, o3, S3):
         assert torch.isfinite(t[:, 0]).all() and torch.isfinite(t[:, 2]).all()
         assert not torch.isfinite(t[:, 1]).all()
+    assert torch.isfinite(z3).all()  # z takes no values
 
 
 # --------------------------------------------------------------------------- carry
