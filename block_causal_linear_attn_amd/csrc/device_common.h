@@ -339,17 +339,25 @@ __device__ __forceinline__ void relu_frame_state(const float* __restrict__ parti
 // ReLU scan: workgroup (frame 0, chunk 0) of each head copies the initial
 // state (or zeros) into the workspace, so that later kernels never read
 // state_in and state_out may alias it.
-template <int D>
+// PAIR: head bh is the pair of heads 2 bh and 2 bh + 1 of dim D / 2, whose
+// states S0 holds one after the other; the pair's state is block-diagonal.
+template <int D, bool PAIR = false>
 __device__ __forceinline__ void relu_copy_init(const float* S0, const float* z0, float* init, long wg,
                                                int F, int nc) {
   constexpr int OUT = D * D + D;
+  constexpr int DH = D / 2;
   if (wg % ((long)F * nc) != 0) return;
   const long bh = wg / ((long)F * nc);
   for (int e = threadIdx.x; e < OUT; e += blockDim.x) {
     float x = 0.0f;
     if (e < D * D) {
-      if (S0) x = S0[(size_t)bh * D * D + e];
-    } else if (z0) {
+      const int m = e / D, n = e % D;
+      if (PAIR) {
+        if (S0 && m / DH == n / DH) x = S0[((size_t)2 * bh + m / DH) * DH * DH + (m % DH) * DH + n % DH];
+      } else if (S0) {
+        x = S0[(size_t)bh * D * D + e];
+      }
+    } else if (z0) {  // (the pair's two normalisers are adjacent: the same index)
       x = z0[(size_t)bh * D + e - D * D];
     }
     init[(size_t)bh * OUT + e] = x;

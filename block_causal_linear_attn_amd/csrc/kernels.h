@@ -48,6 +48,11 @@ struct ScanArgs {
   int nc = 1, chunk = 1;       // token chunks of the summary/gram pass
   int nco = 1, chunko = 1;     // token chunks of the output pass
   int bfr = 1;                 // ReLU frames per causal block
+  // ReLU, head dim 32 with heads interleaved in each token row: heads 2i and
+  // 2i + 1 (one 128-byte row segment) run as one head of dim 64 whose state
+  // is block-diagonal; D, bh, bhf and L then describe the head pairs, while
+  // S0, z0, S_out, z_out keep the per-head layout [B*H][32][32], [B*H][32]
+  bool pair = false;
   TokLayout L;                 // element strides of q, k, v, o
   Prologue P;                  // per-token prologue of q and k
 };

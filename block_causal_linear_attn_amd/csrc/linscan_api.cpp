@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <mutex>
@@ -257,8 +258,10 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   }
   // output items: wide heads aim at about 1000 (about two per resident slot,
   // measured best at 20 heads x 10 frames x 3600 tokens) and take chunks down
-  // to 128 tokens when there are few frames (one frame: 52 -> 45 us)
-  plan_chunks(d.bhf, s->N, p.wide ? 1000 : 1536, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
+  // to 128 tokens when there are few frames (one frame: 52 -> 45 us); head
+  // dim 64 aims at about 512, since each output item sums the partials of
+  // every earlier frame (35 heads x 10 frames x 3600 tokens: 166 -> 153 us)
+  plan_chunks(d.bhf, s->N, p.wide ? 1000 : s->D == 64 ? 512 : 1536, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
   // wide heads keep one cumulative record per frame, 128 dims wide, then one
   // record per summary part past the first, and no init copy
   const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;
@@ -359,6 +362,21 @@ hipError_t timed(const char* name, hipStream_t st, Fn&& launch) {
   return e;
 }
 
+// Head dim 32 in bf16 with an even head count may run as pairs of heads of
+// dim 64 (when the layout puts a pair in one 128-byte row segment): the
+// shape and dims of that launch.
+bool relu_pair_shape(const ls_shape* s) {
+  return s->D == 32 && s->dtype == LS_DTYPE_BF16 && s->H % 2 == 0 && linscan::relu_has_mfma(64, linscan::DT_BF16);
+}
+void relu_pair_dims(const ls_shape* s, const Dims& d, ls_shape* ps, Dims* pd) {
+  *ps = *s;
+  ps->H = s->H / 2;
+  ps->D = 64;
+  *pd = d;
+  pd->bh = d.bh / 2;
+  pd->bhf = d.bhf / 2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -428,7 +446,14 @@ const char* ls_status_string(ls_status st) {
 size_t ls_relu_block_workspace_size(const ls_shape* s, int block_frames) {
   Dims d;
   if (check_shape(s, &d) != LS_OK || block_frames < 1) return 0;
-  return relu_plan(s, d).bytes;
+  size_t bytes = relu_plan(s, d).bytes;
+  if (relu_pair_shape(s)) {  // enough for either launch: the layout is not known here
+    ls_shape ps;
+    Dims pd;
+    relu_pair_dims(s, d, &ps, &pd);
+    bytes = std::max(bytes, relu_plan(&ps, pd).bytes);
+  }
+  return bytes;
 }
 
 size_t ls_gdn_frame_workspace_size(const ls_shape* s) {
@@ -500,15 +525,24 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
       return st;
     return ok();
   }
-  const ReluPlan p = relu_plan(s, d);
-  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", p.bytes);
-  if (workspace_bytes < p.bytes)
-    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  // Heads of dim 32 stored next to each other in every token row share each
+  // 128-byte line in pairs; each pair (2i, 2i + 1) then runs as one head of
+  // dim 64, so that one work item reads the whole line (no prologue).
+  const bool pair = relu_pair_shape(s) && layout.sh == 32 && !prolog.rope() && !prolog.wq && !prolog.wk;
+  ls_shape ps;
+  Dims pd;
+  if (pair) relu_pair_dims(s, d, &ps, &pd);
+  const ReluPlan p = pair ? relu_plan(&ps, pd) : relu_plan(s, d);
+  // the documented size, whichever launch the layout picks
+  const size_t need = ls_relu_block_workspace_size(s, block_frames);
+  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   for (int i = 0; i < 5; ++i)
-    if (overlap(workspace, p.bytes, ins[i], in_n[i]))
+    if (overlap(workspace, need, ins[i], in_n[i]))
       return fail(LS_ERR_ALIASING, "workspace overlaps an input");
-  if (overlap(workspace, p.bytes, o, tok_bytes) || overlap(workspace, p.bytes, state_out, state_out ? state_bytes : 0) ||
-      overlap(workspace, p.bytes, norm_out, norm_out ? norm_bytes : 0))
+  if (overlap(workspace, need, o, tok_bytes) || overlap(workspace, need, state_out, state_out ? state_bytes : 0) ||
+      overlap(workspace, need, norm_out, norm_out ? norm_bytes : 0))
     return fail(LS_ERR_ALIASING, "workspace overlaps an output");
 
   char* ws = (char*)workspace;
@@ -539,8 +573,17 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
   a.bfr = block_frames;
   a.L = layout;
   a.P = prolog;
+  if (pair) {
+    a.pair = true;
+    a.D = 64;
+    a.bh = pd.bh;
+    a.bhf = pd.bhf;
+    a.L.H = ps.H;
+    a.L.sh = 2 * layout.sh;
+    a.L.hg = 1;
+  }
   if (p.fused) {
-    const long bhp = (d.bh + 8 * layout.hg - 1) / (8 * layout.hg) * (8 * layout.hg);
+    const long bhp = (a.bh + 8 * a.L.hg - 1) / (8 * a.L.hg) * (8 * a.L.hg);
     uint64_t* flags = (uint64_t*)(ws + p.flags_off);
     uint32_t* err = (uint32_t*)ws;
     const uint64_t epoch = next_epoch();

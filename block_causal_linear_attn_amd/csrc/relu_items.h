@@ -34,7 +34,9 @@ constexpr int relu_summary_lds_bytes() {
 // (S0, z0) into init[head].
 // PRO: 0 without the per-token prologue, 1 with it, 2 with it and the rotary
 // embedding (separate instantiations keep the registers of the simpler items).
-template <int D, int PRO = 0>
+// PAIR (D = 64, PRO = 0): the head is a pair of heads of dim 32 (dims 0-31
+// and 32-63); only the diagonal blocks of dS are formed, the others stay zero.
+template <int D, int PRO = 0, bool PAIR = false>
 __device__ __forceinline__ void relu_summary_item(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ partial,
     const float* S0, const float* z0, float* __restrict__ init, int F, int N, int nc, int chunk,
@@ -45,6 +47,7 @@ __device__ __forceinline__ void relu_summary_item(
   constexpr int CPR = D / 8;            // 16-byte chunks per token row
   constexpr int LPT = TILE * CPR / 64;  // 16-byte loads per lane per tensor per tile
   constexpr int OUT = D * D + D;
+  static_assert(!PAIR || (D == 64 && PRO == 0), "head pairs: two heads of dim 32, no prologue");
   typedef uint16_t TileT[2][TILE * ROW];
   TileT* lds = reinterpret_cast<TileT*>(lds_raw);  // [4 waves][K, V][TILE * ROW]
 
@@ -158,7 +161,8 @@ __device__ __forceinline__ void relu_summary_item(
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
 #pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
+        for (int i = 0; i < DB; ++i)
+          if (!PAIR || i == j) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
         if (PRO != 2) accz[j] = mfma32x32x16(as_bf16x8(ones), as_bf16x8(bfr[j]), accz[j]);
       }
     }
@@ -199,7 +203,7 @@ __device__ __forceinline__ void relu_summary_item(
   float* dst = partial + (size_t)wg * OUT;
   for (int e = threadIdx.x; e < OUT; e += 256)
     dst[e] = ((red[e] + red[OUT + e]) + red[2 * OUT + e]) + red[3 * OUT + e];
-  relu_copy_init<D>(S0, z0, init, wg, F, nc);
+  relu_copy_init<D, PAIR>(S0, z0, init, wg, F, nc);
 }
 
 // Row pitch (bf16) of the per-wave output staging tile [32 tokens][D + 8].
@@ -213,16 +217,21 @@ constexpr int relu_output_lds_bytes() { return (D * (D + 4) + D) * 4 + 4 * 32 * 
 // Work item `wg` = (frame of one head) * nco + token chunk: the frame's state
 // from init + partials, then o = S phi(q) / (z . phi(q) + eps) for the chunk;
 // the last frame's chunk-0 item writes the final state.
-template <int D, int PRO = 0>
+// PAIR (D = 64, PRO = 0): a pair of heads of dim 32 with a block-diagonal
+// state; each head's rows take its own denominator, and the final state goes
+// out per head.
+template <int D, int PRO = 0, bool PAIR = false>
 __device__ __forceinline__ void relu_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ partial,
     const float* __restrict__ init, float* S_out, float* z_out, float eps, int F, int N, int nc,
     int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
   constexpr int DB = D / 32;  // 32-row blocks of S (output dims)
   constexpr int KS = D / 16;  // 16-dim k-steps over the key dimension
-  // 32-token groups per wave per step (two with the D = 64 prologue: its
-  // fp64 RMSNorm does not fit beside four groups of fragments in registers)
-  constexpr int U = PRO != 0 && D >= 64 ? 2 : 4;
+  static_assert(!PAIR || (D == 64 && PRO == 0), "head pairs: two heads of dim 32, no prologue");
+  // 32-token groups per wave per step: two at D = 64 (with four, the
+  // fragments and the prologue's fp64 RMSNorm do not fit in registers; with
+  // none, 35 heads x 10 frames x 3600 tokens still ran 175 -> 166 us with two)
+  constexpr int U = D >= 64 ? 2 : 4;
   constexpr int STEP = 4 * U * 32;  // tokens per workgroup step
   constexpr int PITCH = D + 4;
   float* Ss = reinterpret_cast<float*>(lds_raw);  // [D][PITCH]
@@ -248,7 +257,14 @@ __device__ __forceinline__ void relu_output_item(
   __syncthreads();
   if (f == F - 1 && wg % nco == 0) {  // the last frame's state is the call's final state
     for (int e = threadIdx.x; e < D * D; e += 256) {
-      if (S_out) S_out[(size_t)bh * D * D + e] = Ss[(e / D) * PITCH + e % D];
+      constexpr int DH = D / 2;
+      const int m = e / D, n = e % D;
+      if (PAIR) {
+        if (S_out && m / DH == n / DH)
+          S_out[((size_t)2 * bh + m / DH) * DH * DH + (m % DH) * DH + n % DH] = Ss[m * PITCH + n];
+      } else if (S_out) {
+        S_out[(size_t)bh * D * D + e] = Ss[m * PITCH + n];
+      }
     }
     if (z_out && threadIdx.x < D) z_out[(size_t)bh * D + threadIdx.x] = zs[threadIdx.x];
   }
@@ -335,7 +351,7 @@ __device__ __forceinline__ void relu_output_item(
                                          (double)bf16hi_to_f32(b[u][s][e]) * (double)wv[2 * e + 1] * inv);
         }
       }
-      float den = 0.0f;
+      float den = 0.0f, inv2 = 0.0f;
       if (PRO == 2) {
         // fp64: RMSNorm (weights), the feature map, the normaliser's dot
         // product on the unrotated features, then the rotation; one rounding
@@ -378,23 +394,32 @@ __device__ __forceinline__ void relu_output_item(
           for (int e = 0; e < 4; ++e) b[u][s][e] = pack_bf16x2_f64(x[2 * e], x[2 * e + 1]);
         }
       } else {
+        // PAIR: den holds the first head's sum (k-steps s < KS / 2), den2 the second's
+        float den2 = 0.0f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
+          float& d = PAIR && s >= KS / 2 ? den2 : den;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             b[u][s][e] = relu_bf16x2(b[u][s][e]);
-            den = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), den);
-            den = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), den);
+            d = fmaf(zr[s][2 * e], bf16lo_to_f32(b[u][s][e]), d);
+            d = fmaf(zr[s][2 * e + 1], bf16hi_to_f32(b[u][s][e]), d);
           }
+        }
+        if (PAIR) {
+          den2 += __shfl_xor(den2, 32);
+          inv2 = 1.0f / (den2 + eps);
         }
       }
       den += __shfl_xor(den, 32);  // the partner lane holds the token's other dims
-      const float inv = 1.0f / (den + eps);
+      const float inv1 = 1.0f / (den + eps);
 #pragma unroll
       for (int I = 0; I < DB; ++I) {
+        const float inv = PAIR && I == 1 ? inv2 : inv1;
         floatx16 acc = {};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
+          if (PAIR && s / (KS / 2) != I) continue;  // the other head's block of S is zero
           acc = mfma32x32x16(as_bf16x8(ahi[I][s]), as_bf16x8(b[u][s]), acc);
           acc = mfma32x32x16(as_bf16x8(alo[I][s]), as_bf16x8(b[u][s]), acc);
         }

@@ -7,7 +7,9 @@
 // head are published; since every item it waits on has a lower block id and
 // block ids dispatch in order, those items are running or done, so the wait
 // ends.  Every item of a head gets block ids equal to the head modulo 8, so
-// they share one XCD and exchange partials through its L2.
+// they share one XCD and exchange partials through its L2.  With PAIR the
+// items run a pair of heads of dim 32 as one head of dim 64 (block-diagonal
+// state), for layouts where the pair shares every 128-byte token segment.
 #include "relu_items.h"
 #include "kernels.h"
 #include "sync.h"
@@ -25,7 +27,7 @@ namespace {
 // keeps every summary an output item waits for at a lower block id.  Within
 // a step items are head-minor with B*H padded to BHp (a multiple of 8);
 // padding items leave at once.
-template <int D, int PRO>
+template <int D, int PRO, bool PAIR = false>
 __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
@@ -59,14 +61,14 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     c = (int)(r % nco);
   }
   if (summary) {
-    relu_summary_item<D, PRO>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L, P);
+    relu_summary_item<D, PRO, PAIR>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L, P);
     publish(&flags[bh * F + f], epoch);
     return;
   }
   const int fend = min(F, (f / bfr + 1) * bfr);
   wait_all(&flags[bh * F], fend, epoch, err);
-  relu_output_item<D, PRO>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
-                      (bh * F + f) * nco + c, lds, L, P);
+  relu_output_item<D, PRO, PAIR>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
+                                 (bh * F + f) * nco + c, lds, L, P);
 }
 
 }  // namespace
@@ -88,6 +90,10 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
                        a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err, a.L, a.P);
     return hipGetLastError();
   };
+  if (a.pair) {  // head pairs of dim 32 as heads of dim 64 (no prologue)
+    if (a.D != 64 || pro != 0) return hipErrorInvalidValue;
+    return run(relu_fused_mfma<64, 0, true>);
+  }
   if (a.D == 32) return run(pick(std::integral_constant<int, 32>{}));
   if (a.D == 64) return run(pick(std::integral_constant<int, 64>{}));
   return hipErrorInvalidValue;

@@ -194,9 +194,10 @@ ls_status ls_relu_block_forward(const ls_shape* shape, int block_frames, float e
 /*
  * ls_relu_block_forward with token tensors in the layout `strides` (NULL:
  * packed [B][H][F][N][D]).  Workspace size and everything else as there.
- * Layouts that interleave heads inside a token row ([B][F][N][H][D]) share
- * 128-byte lines between heads at D = 32, which the kernels read from
- * different work items.
+ * Layouts that interleave heads inside a token row ([B][F][N][H][D], head
+ * stride D) share 128-byte lines between heads at D = 32: with bf16 tokens
+ * and an even head count, heads 2i and 2i + 1 then run in one work item, so
+ * each line is read once (results bit for bit those of the packed call).
  */
 ls_status ls_relu_block_forward_strided(const ls_shape* shape, const ls_strides* strides, int block_frames,
                                         float eps, const void* q, const void* k, const void* v, void* o,

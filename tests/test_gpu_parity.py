@@ -534,6 +534,7 @@ def _bshd(x):
 
 
 @pytest.mark.parametrize("H,F,N,D,dt", [(5, 4, 333, 32, "bf16"), (3, 3, 200, 112, "bf16"), (2, 3, 300, 128, "bf16"),
+                                        (4, 4, 333, 32, "bf16"),  # head dim 32 in pairs (even head count)
                                         (2, 3, 50, 16, "bf16"), (2, 3, 40, 48, "fp32")])
 def test_relu_strided_layout(ls, gen, oracle_mod, H, F, N, D, dt):
     """[B, F, N, H, D] storage matches the oracle and, bit for bit, the packed call."""
@@ -548,6 +549,26 @@ def test_relu_strided_layout(ls, gen, oracle_mod, H, F, N, D, dt):
     tag = "relu strided H%d F%d N%d D%d %s" % (H, F, N, D, dt)
     check(tag + " o", o2, ro, TOL[dt][0], dt)
     check(tag + " S", S2, rS, TOL[dt][1], dt)
+    assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1) and torch.equal(z2, z1)
+
+
+@pytest.mark.parametrize("B,H,F,N,D,bf", [(2, 6, 3, 700, 32, 1), (1, 70, 2, 130, 32, 2), (1, 2, 1, 1, 32, 1)])
+def test_relu_head_pairs_with_state(ls, gen, oracle_mod, B, H, F, N, D, bf):
+    """Head dim 32 stored [B, F, N, H, D] with an even head count runs heads in pairs: the carried state goes in
+    and out per head (in place), and every output equals the packed call's bit for bit."""
+    x = gen.relu_inputs(B, H, F, N, D, "bf16", seed=43, part=N)
+    S0, z0 = _rand_state(B, H, D, 44, scale=4.0, norm=True)
+    xd = _dev(x)
+    o1, S1, z1 = ls.ls_relu_block_forward(xd["q"], xd["k"], xd["v"], S0.to(DEV), z0.to(DEV), block_frames=bf)
+    q, k, v = (_bshd(xd[n]) for n in ("q", "k", "v"))
+    S2, z2 = S0.to(DEV), z0.to(DEV)
+    o2, _, _ = ls.ls_relu_block_forward_strided(q, k, v, S2, z2, block_frames=bf, state_out=S2, norm_out=z2)
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(x["q"], x["k"], x["v"], S0, z0, block_frames=bf)
+    tag = "relu pairs B%d H%d F%d N%d" % (B, H, F, N)
+    check(tag + " o", o2, ro, TOL["bf16"][0], "bf16")
+    check(tag + " S", S2, rS, TOL["bf16"][1], "bf16")
+    check(tag + " z", z2, rz, TOL["bf16"][1], "bf16")
     assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1) and torch.equal(z2, z1)
 
 
