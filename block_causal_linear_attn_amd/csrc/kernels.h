@@ -85,7 +85,7 @@ hipError_t launch_gdn_output(const ScanArgs& a, hipStream_t st);
 // One launch for a whole call (MFMA paths): work items exchange partials,
 // records and states through flags set to `epoch`; `err` is set if a bounded
 // wait timed out.  bhp = B*H rounded up to a multiple of 8.
-//  ReLU: flags[B*H*F]; summary with one chunk per frame (nc = 1).
+//  ReLU: flags[B*H*F*nc], one per summary item (frame, token chunk).
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st);
 //  ReLU, wide heads: `partial` holds the cumulative state of every frame,

@@ -252,6 +252,16 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
     if (p.wide) {
       const long tiles = (s->N + 63) / 64;
       while (p.nc < 8 && (p.nc + 1) * d.bhf <= 512 && tiles >= 6 * (p.nc + 1)) ++p.nc;
+    } else {
+      // narrow heads: up to 4 token chunks of at least 512 tokens per frame
+      // while the summary items stay within one per CU (the rollout's
+      // one-frame calls); output items then sum nc partials per frame
+      while (p.nc < 4 && (p.nc + 1) * d.bhf <= 256 && s->N / (p.nc + 1) >= 512) ++p.nc;
+      if (p.nc > 1) {
+        p.chunk = (s->N + p.nc - 1) / p.nc;
+        p.chunk = (p.chunk + 63) / 64 * 64;
+        p.nc = (s->N + p.chunk - 1) / p.chunk;
+      }
     }
   } else {
     plan_chunks(d.bhf, s->N, 512, 512, 64, &p.nc, &p.chunk);

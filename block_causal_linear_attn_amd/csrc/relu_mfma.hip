@@ -21,8 +21,8 @@ namespace linscan {
 namespace {
 
 // Block ids run over steps j = 0, 1, ...: step j holds the summary items of
-// frame j (one per head, whole frame) and then the output items of frame
-// j - lag (one per head and token chunk), so summaries of later frames
+// frame j (nc per head, one per token chunk of the frame) and then the output
+// items of frame j - lag (one per head and token chunk), so summaries of later frames
 // stream while earlier frames' outputs are written.  lag >= block_frames
 // keeps every summary an output item waits for at a lower block id.  Within
 // a step items are head-minor with B*H padded to BHp (a multiple of 8);
@@ -32,8 +32,8 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
     const float* z0, float* S_out, float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr,
-    int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err, TokLayout L,
-    Prologue P) {
+    int nc, int chunk, int nco, int chunko, int lag, uint64_t* __restrict__ flags, uint64_t epoch, uint32_t* err,
+    TokLayout L, Prologue P) {
   // (each item keeps the prologue's D weights after its own LDS)
   constexpr int LDS = (relu_summary_lds_bytes<D>() > relu_output_lds_bytes<D>() ? relu_summary_lds_bytes<D>()
                                                                                  : relu_output_lds_bytes<D>()) +
@@ -43,17 +43,18 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
   const long bh = L.head_of_slot(b % bhp);
   const long u = b / bhp;  // unit: one item per head
   if (bh >= bh_n) return;
-  const long head_units = lag, mid_units = (long)(F - lag) * (1 + nco);
+  const long head_units = (long)lag * nc, mid_units = (long)(F - lag) * (nc + nco);
   bool summary;
-  int f, c = 0;
+  int f, c;
   if (u < head_units) {
     summary = true;
-    f = (int)u;
+    f = (int)(u / nc);
+    c = (int)(u % nc);
   } else if (u < head_units + mid_units) {
-    const long j = lag + (u - head_units) / (1 + nco), r = (u - head_units) % (1 + nco);
-    summary = r == 0;
+    const long j = lag + (u - head_units) / (nc + nco), r = (u - head_units) % (nc + nco);
+    summary = r < nc;
     f = summary ? (int)j : (int)(j - lag);
-    c = summary ? 0 : (int)(r - 1);
+    c = summary ? (int)r : (int)(r - nc);
   } else {
     const long r = u - head_units - mid_units;
     summary = false;
@@ -61,13 +62,14 @@ __global__ __launch_bounds__(256, 2) void relu_fused_mfma(
     c = (int)(r % nco);
   }
   if (summary) {
-    relu_summary_item<D, PRO, PAIR>(k, v, partial, S0, z0, init, F, N, 1, N, bh * F + f, lds, L, P);
-    publish(&flags[bh * F + f], epoch);
+    relu_summary_item<D, PRO, PAIR>(k, v, partial, S0, z0, init, F, N, nc, chunk, (bh * F + f) * nc + c, lds, L,
+                                    P);
+    publish(&flags[(bh * F + f) * nc + c], epoch);
     return;
   }
   const int fend = min(F, (f / bfr + 1) * bfr);
-  wait_all(&flags[bh * F], fend, epoch, err);
-  relu_output_item<D, PRO, PAIR>(q, o, partial, init, S_out, z_out, eps, F, N, 1, bfr, nco, chunko,
+  wait_all(&flags[bh * F * nc], fend * nc, epoch, err);
+  relu_output_item<D, PRO, PAIR>(q, o, partial, init, S_out, z_out, eps, F, N, nc, bfr, nco, chunko,
                                  (bh * F + f) * nco + c, lds, L, P);
 }
 
@@ -76,7 +78,7 @@ bool relu_has_mfma(int D, int dtype) { return dtype == DT_BF16 && (D == 32 || D 
 
 hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                   uint32_t* err, hipStream_t st) {
-  const long grid = (long)a.F * bhp * (1 + a.nco);
+  const long grid = (long)a.F * bhp * (a.nc + a.nco);
   // the prologue's instantiation: 0 none, 1 RMSNorm, 2 with the rotary embedding
   const int pro = a.P.rope() ? 2 : (a.P.wq != nullptr || a.P.wk != nullptr) ? 1 : 0;
   auto pick = [&](auto d) {
@@ -84,10 +86,11 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
     return pro == 2 ? relu_fused_mfma<D, 2> : pro == 1 ? relu_fused_mfma<D, 1> : relu_fused_mfma<D, 0>;
   };
   auto run = [&](auto kern) {
-    const int lag = fused_lag(device_slots((const void*)kern), bhp * (1 + a.nco), a.bfr, a.F);
+    const int lag = fused_lag(device_slots((const void*)kern), bhp * (a.nc + a.nco), a.bfr, a.F);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0, a.z0, a.S_out, a.z_out, a.eps,
-                       a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, lag, flags, epoch, err, a.L, a.P);
+                       a.bh, bhp, a.F, a.N, a.bfr, a.nc, a.chunk, a.nco, a.chunko, lag, flags, epoch, err, a.L,
+                       a.P);
     return hipGetLastError();
   };
   if (a.pair) {  // head pairs of dim 32 as heads of dim 64 (no prologue)

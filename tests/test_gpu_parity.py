@@ -61,6 +61,8 @@ RELU_CASES = [
     (1, 3, 5, 333, 32, "bf16", 1, True),        # MFMA path, ragged token count
     (2, 2, 3, 700, 32, "bf16", 1, False),       # several token chunks per frame
     (1, 2, 4, 200, 64, "bf16", 1, True),        # MFMA path, D = 64
+    (1, 2, 2, 1500, 32, "bf16", 1, True),       # few items: each frame's summary in 2 token chunks
+    (1, 2, 3, 2100, 64, "bf16", 2, True),       # D = 64, summaries in 4 token chunks, blocks of 2 frames
     (1, 2, 3, 97, 112, "bf16", 1, True),        # wide MFMA path at the pages' head dim (128 dims, zero-padded)
     (1, 2, 4, 2000, 112, "bf16", 1, False),     # wide path, two output chunks per frame, ragged tail
     (2, 10, 3, 200, 112, "bf16", 2, True),      # wide path, B*H = 20 (padding items), blocks of 2 frames
@@ -552,7 +554,8 @@ def test_relu_strided_layout(ls, gen, oracle_mod, H, F, N, D, dt):
     assert torch.equal(o2.contiguous(), o1) and torch.equal(S2, S1) and torch.equal(z2, z1)
 
 
-@pytest.mark.parametrize("B,H,F,N,D,bf", [(2, 6, 3, 700, 32, 1), (1, 70, 2, 130, 32, 2), (1, 2, 1, 1, 32, 1)])
+@pytest.mark.parametrize("B,H,F,N,D,bf", [(2, 6, 3, 700, 32, 1), (1, 70, 2, 130, 32, 2), (1, 2, 1, 1, 32, 1),
+                                          (1, 4, 1, 1100, 32, 1)])  # pairs, summaries in 2 token chunks
 def test_relu_head_pairs_with_state(ls, gen, oracle_mod, B, H, F, N, D, bf):
     """Head dim 32 stored [B, F, N, H, D] with an even head count runs heads in pairs: the carried state goes in
     and out per head (in place), and every output equals the packed call's bit for bit."""
