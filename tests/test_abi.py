@@ -82,6 +82,16 @@ def test_validation_errors_relu(lib):
     assert lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, D=24)), 1) == 0
 
 
+def test_relu_workspace_covers_head_pairs(lib):
+    """Head dim 32 in bf16 with an even head count may run heads in pairs as head dim 64 (a layout the
+    size query does not see), so its workspace covers that launch too; odd head counts never pair."""
+    ws = lambda **kw: lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, **kw)), 1)
+    for H, F, N in ((2, 1, 1), (4, 3, 700), (70, 10, 3600), (6, 1, 1100)):
+        assert ws(H=H, F=F, N=N, D=32) >= ws(H=H // 2, F=F, N=N, D=64) > 0
+    assert ws(H=3, F=3, N=700, D=32) < ws(H=4, F=3, N=700, D=32)
+    assert ws(H=4, F=3, N=700, D=32, dtype=0) > 0  # fp32: generic kernels, no pairs
+
+
 def test_validation_errors_gdn(lib):
     assert _gdn(lib, _shape(lib, D=100)) == 3
     assert _gdn(lib, _shape(lib), scale=float("inf")) == 7
