@@ -308,7 +308,10 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
   } else {
     plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
   }
-  plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
+  // output items: about 2048, except for one-frame phased calls (the chunk
+  // step, B4 H24 N920: 5 chunks of 192 tokens instead of 8 of 128 ran 47.4 ->
+  // 45.6 us, each item loading the frame's 64 KB state once for fewer tokens)
+  plan_chunks(d.bhf, s->N, p.phased && s->F == 1 ? 576 : 2048, 64, 64, &p.nco, &p.chunko);
   // records and per-frame states of the MFMA kernels always cover 128 dims
   const size_t Dw = p.mfma ? 128 : (size_t)s->D;
   const size_t dd = Dw * Dw;
