@@ -108,7 +108,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: the scan has no multi-GPU path in this build "
+        print("bench.py runs on one GPU only: liblinscan has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
