@@ -284,10 +284,11 @@ def test_in_place_state_and_poisoned_outputs(ls, gen, oracle_mod):
     check("gdn in-place S", G, rS, 1e-2)
 
 
-@pytest.mark.parametrize("F,D", [(1, 112), (3, 112), (1, 128)])
-def test_relu_wide_in_place_state(ls, gen, oracle_mod, F, D):
+@pytest.mark.parametrize("F,D,N", [(1, 112, 150), (3, 112, 150), (1, 128, 150),
+                                   (1, 112, 1000), (3, 128, 1000)])  # N = 1000: summaries in 2 parts
+def test_relu_wide_in_place_state(ls, gen, oracle_mod, F, D, N):
     """Wide heads: state_out == state_in, also when one work item reads and writes it (F = 1)."""
-    x = gen.relu_inputs(1, 2, F, 150, D, "bf16", seed=28)
+    x = gen.relu_inputs(1, 2, F, N, D, "bf16", seed=28)
     S0, z0 = _rand_state(1, 2, D, 9, norm=True)
     xd = _dev(x)
     S = S0.to(DEV).clone()
