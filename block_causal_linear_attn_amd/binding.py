@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinscan.so")
 
 LS_OK = 0
+LS_ERR_HIP = 8
 LS_DTYPE_FP32 = 0
 LS_DTYPE_BF16 = 1
 _DT = {torch.float32: LS_DTYPE_FP32, torch.bfloat16: LS_DTYPE_BF16}
@@ -57,7 +58,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     SP = ctypes.POINTER(ls_shape)
-    lib.ls_relu_block_workspace_size.argtypes = [SP, I]
+    lib.ls_relu_block_workspace_size.argtypes = [SP]
     lib.ls_relu_block_workspace_size.restype = Z
     lib.ls_relu_block_forward.argtypes = [SP, I, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_relu_block_forward.restype = I
@@ -167,14 +168,48 @@ _ws_cache: dict = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A cached uint8 device buffer of at least nbytes (per device and stream)."""
+    """A cached uint8 device buffer of at least nbytes (per device and stream).
+
+    A new buffer starts zeroed, so its fault word (the first 4 bytes, which a
+    bounded wait that gives up sets) reads 0; a buffer replaced by a larger
+    one hands its fault word on, so no fault is lost.
+    """
     key = (torch.device(device).index, torch.cuda.current_stream(device).cuda_stream)
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            new = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            if buf is not None:
+                new[:4].copy_(buf[:4])
+            buf = new
             _ws_cache[key] = buf
         return buf
+
+
+def _cached(device=None, ws=None):
+    if ws is not None:
+        return [ws]
+    idx = None if device is None else torch.device(device).index
+    with _ws_lock:
+        return [b for (d, _), b in _ws_cache.items() if idx is None or d == idx]
+
+
+def ls_fault_word(device=None, ws=None) -> int:
+    """The fault word of `ws`, or the OR of the cached workspaces' words (all
+    devices, or `device`'s): nonzero when a bounded wait of a single-launch
+    call gave up, so that call's results are invalid.  Synchronises with the
+    device (it reads device memory)."""
+    word = 0
+    for b in _cached(device, ws):
+        word |= int(b[:4].view(torch.int32).item())
+    return word
+
+
+def ls_clear_fault_word(device=None, ws=None) -> None:
+    """Zero the fault word of `ws`, or of every cached workspace (of `device`);
+    the library only ever sets it."""
+    for b in _cached(device, ws):
+        b[:4].zero_()
 
 
 def _shape(q) -> ls_shape:
@@ -205,7 +240,7 @@ def ls_relu_block_forward(q, k, v, state=None, norm=None, block_frames: int = 1,
     _f32("state_out", so, (B, H, D, D), dev)
     _f32("norm_out", no, (B, H, D), dev)
     shp = _shape(q)
-    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp))
     w = ws if ws is not None else workspace(need, dev)
     _check(lib.ls_relu_block_forward(ctypes.byref(shp), int(block_frames), float(eps), _ptr(q), _ptr(k),
                                      _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so), _ptr(no),
@@ -264,7 +299,7 @@ def ls_relu_block_forward_strided(q, k, v, state=None, norm=None, block_frames: 
     _f32("norm_out", no, (B, H, D), dev)
     shp = _shape(q)
     st = _layout(q)
-    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp))
     w = ws if ws is not None else workspace(need, dev)
     _check(lib.ls_relu_block_forward_strided(ctypes.byref(shp), ctypes.byref(st), int(block_frames), float(eps),
                                              _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so),
@@ -341,7 +376,7 @@ def ls_relu_block_forward_prologue(q, k, v, q_weight=None, k_weight=None, norm_e
     _f32("state_out", so, (B, H, D, D), dev)
     _f32("norm_out", no, (B, H, D), dev)
     shp = _shape(q)
-    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp), int(block_frames))
+    need = lib.ls_relu_block_workspace_size(ctypes.byref(shp))
     w = ws if ws is not None else workspace(need, dev)
     _check(lib.ls_relu_block_forward_prologue(ctypes.byref(shp), ctypes.byref(pr), int(block_frames), float(eps),
                                               _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(norm), _ptr(so),
@@ -483,7 +518,7 @@ def ls_profile_end():
     stats = (ls_kernel_stat * 64)()
     n = lib.ls_profile_end(stats, 64)
     if n < 0:
-        raise LinscanError(9, "profiling events failed")
+        raise LinscanError(LS_ERR_HIP, "profiling events failed")
     return {stats[i].name.decode(): (stats[i].launches, stats[i].total_ms) for i in range(min(n, 64))}
 
 

@@ -11,7 +11,8 @@
 // is either dispatched earlier or, for the scan items, a gram item that can
 // still find a free slot because scan items fill at most a quarter of the
 // device's slots; the library only picks this kernel when that holds
-// (B*H*4 <= 128), which leaves room for other launches running alongside.  All
+// (gdn_fused_fits: 4*B*H within a quarter of the slots the device holds of
+// it), which leaves room for other launches running alongside.  All
 // items of a head share one XCD (block id equal to the head modulo 8), so
 // records and per-frame states are read back from that XCD's L2 shortly
 // after they are written, and the scan's frame-to-frame chain overlaps the
@@ -233,6 +234,26 @@ hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* sta
                        (const uint16_t*)q, (uint16_t*)o, (const uint16_t*)states, N, nco, chunk, L, P);
     return hipGetLastError();
   });
+}
+
+// The fused kernel instance a call with these switches runs (nc > 1: MULTI).
+static const void* gdn_fused_kernel(int D, bool tg, bool pro, int nc) {
+  const void* k = nullptr;
+  with_head_dim(D, [&](auto di) {
+    constexpr int DI = decltype(di)::value;
+    auto kern = nc == 1 ? (tg ? gdn_fused_mfma128<false, DI, true, false>
+                              : (pro ? gdn_fused_mfma128<false, DI, false, true> : gdn_fused_mfma128<false, DI, false, false>))
+                        : (tg ? gdn_fused_mfma128<true, DI, true, false>
+                              : (pro ? gdn_fused_mfma128<true, DI, false, true> : gdn_fused_mfma128<true, DI, false, false>));
+    k = (const void*)kern;
+    return hipSuccess;
+  });
+  return k;
+}
+
+bool gdn_fused_fits(int D, bool tg, bool pro, int nc, long bh) {
+  const void* k = gdn_fused_kernel(D, tg, pro, nc);
+  return k != nullptr && bh * kGdnFusedRowBlocks * 4 <= device_slots(k);
 }
 
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,

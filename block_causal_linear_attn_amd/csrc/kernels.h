@@ -96,9 +96,13 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
 hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, uint64_t epoch,
                                        uint32_t* err, hipStream_t st);
 //  GDN: gflags[B*H*F*nc] (records), sflags[B*H*F*8] (row blocks of states,
-//  kGdnFusedRowBlocks of the 8 used); only for B*H*kGdnFusedRowBlocks <= 128
-//  so that scan items never take more than a quarter of the device's slots.
+//  kGdnFusedRowBlocks of the 8 used); only when gdn_fused_fits, so that scan
+//  items never take more than a quarter of the device's slots.
 constexpr int kGdnFusedRowBlocks = 4;
+// The fused GDN kernel for (head dim D, per-token gates, prologue, nc token
+// chunks per frame) keeps its B*H*kGdnFusedRowBlocks scan items within a
+// quarter of the slots the current device holds of it.
+bool gdn_fused_fits(int D, bool tg, bool pro, int nc, long bh);
 hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                  uint64_t epoch, uint32_t* err, hipStream_t st);
 

@@ -288,15 +288,17 @@ struct GdnPlan {
   size_t partial_off, states_off, gflags_off, sflags_off, bytes;
 };
 
-GdnPlan gdn_plan(const ls_shape* s, const Dims& d) {
+// fused_ok: the device has room for the fused launch's resident scan items
+// (the caller checks gdn_fused_fits; workspace sizes cover both answers).
+GdnPlan gdn_plan(const ls_shape* s, const Dims& d, bool fused_ok) {
   GdnPlan p;
   p.mfma = linscan::gdn_has_mfma(s->D, s->dtype);
   // one launch with the scan items alongside the streaming items when there
   // are frames to overlap and the scan items take at most a quarter of the
-  // device's workgroup slots: they stay resident waiting for gram items that
-  // come later in dispatch order, which need free slots even if calls on
-  // other streams occupy the rest (see the header)
-  p.fused = p.mfma && d.bh * linscan::kGdnFusedRowBlocks <= 128 && s->F >= 2 && s->N > 0;
+  // device's workgroup slots (B*H <= 32 on an MI355X): they stay resident
+  // waiting for gram items that come later in dispatch order, which need
+  // free slots even if calls on other streams occupy the rest (see the header)
+  p.fused = p.mfma && fused_ok && d.bh * linscan::kGdnFusedRowBlocks <= 128 && s->F >= 2 && s->N > 0;
   // every other MFMA call with tokens: gram, scan and output phases in one
   // launch
   p.phased = p.mfma && !p.fused && s->N > 0;
@@ -449,16 +451,16 @@ const char* ls_status_string(ls_status st) {
     case LS_ERR_MISALIGNED: return "pointer not 16-byte aligned";
     case LS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case LS_ERR_BAD_PARAM: return "invalid scalar parameter";
-    case LS_ERR_ALIASING: return "output overlaps an input";
     case LS_ERR_HIP: return "HIP runtime error";
     case LS_ERR_INTERNAL: return "internal error";
+    case LS_ERR_ALIASING: return "output overlaps an input";
   }
   return "unknown status";
 }
 
-size_t ls_relu_block_workspace_size(const ls_shape* s, int block_frames) {
+size_t ls_relu_block_workspace_size(const ls_shape* s) {
   Dims d;
-  if (check_shape(s, &d) != LS_OK || block_frames < 1) return 0;
+  if (check_shape(s, &d) != LS_OK) return 0;
   size_t bytes = relu_plan(s, d).bytes;
   if (relu_pair_shape(s)) {  // enough for either launch: the layout is not known here
     ls_shape ps;
@@ -472,7 +474,8 @@ size_t ls_relu_block_workspace_size(const ls_shape* s, int block_frames) {
 size_t ls_gdn_frame_workspace_size(const ls_shape* s) {
   Dims d;
   if (check_shape(s, &d) != LS_OK) return 0;
-  return gdn_plan(s, d).bytes;
+  // enough for the fused and the phased launch: which one runs depends on the device
+  return std::max(gdn_plan(s, d, true).bytes, gdn_plan(s, d, false).bytes);
 }
 
 // Both ReLU entry points: packed token tensors (strides NULL) or strided ones.
@@ -547,7 +550,7 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
   if (pair) relu_pair_dims(s, d, &ps, &pd);
   const ReluPlan p = pair ? relu_plan(&ps, pd) : relu_plan(s, d);
   // the documented size, whichever launch the layout picks
-  const size_t need = ls_relu_block_workspace_size(s, block_frames);
+  const size_t need = ls_relu_block_workspace_size(s);
   if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", need);
   if (workspace_bytes < need)
     return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
@@ -672,14 +675,17 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const
                                              state_in == nullptr, hs), "state copy");
     return ok();
   }
-  const GdnPlan p = gdn_plan(s, d);
-  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", p.bytes);
-  if (workspace_bytes < p.bytes)
-    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, p.bytes);
+  const size_t need = ls_gdn_frame_workspace_size(s);
+  if (!workspace) return fail(LS_ERR_NULL_POINTER, "workspace is NULL (need %zu bytes)", need);
+  if (workspace_bytes < need)
+    return fail(LS_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   for (int i = 0; i < 6; ++i)
-    if (overlap(workspace, p.bytes, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "workspace overlaps an input");
-  if (overlap(workspace, p.bytes, o, tok_bytes) || overlap(workspace, p.bytes, state_out, state_out ? state_bytes : 0))
+    if (overlap(workspace, need, ins[i], in_n[i])) return fail(LS_ERR_ALIASING, "workspace overlaps an input");
+  if (overlap(workspace, need, o, tok_bytes) || overlap(workspace, need, state_out, state_out ? state_bytes : 0))
     return fail(LS_ERR_ALIASING, "workspace overlaps an output");
+  GdnPlan p = gdn_plan(s, d, true);
+  if (p.fused && !linscan::gdn_fused_fits(D, token_gate, prolog.on_k() || prolog.on_q(), p.nc, d.bh))
+    p = gdn_plan(s, d, false);
 
   // keys are scaled by c = 1/sqrt(D*N) unless the caller gives a scale; with
   // no tokens there is nothing to scale

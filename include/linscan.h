@@ -48,12 +48,13 @@
  *    The library never clears it; callers that check it zero it beforehand.
  *  - Concurrency: every wait of these launches is for work dispatched
  *    earlier in the same launch, with one exception.  A GDN call with
- *    B*H <= 32 and F >= 2 keeps 4*B*H scan work-groups resident for its
- *    whole run, waiting for work-groups of the same launch that still need
- *    free slots; at most a quarter of an MI355X's slots at this kernel's
- *    occupancy.  Up to three such calls may run concurrently on different
- *    streams whatever else runs; a fourth could find every slot taken by
- *    waiting work, and its waits would time out (fault word set).
+ *    F >= 2 and B*H <= 32 whose 4*B*H scan work-groups fit in a quarter of
+ *    the device's slots for that kernel (B*H <= 32 on an MI355X) keeps them
+ *    resident for its whole run, waiting for work-groups of the same launch
+ *    that still need free slots (other calls take a launch whose waits all
+ *    point at earlier work).  Up to three such calls may run concurrently on
+ *    different streams whatever else runs; a fourth could find every slot
+ *    taken by waiting work, and its waits would time out (fault word set).
  *  - The caller owns every buffer, including the workspace.  The library
  *    never allocates device memory and carries nothing from one call to the
  *    next (the optional profiling session below only keeps HIP events).
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define LINSCAN_VERSION 100 /* major*100 + minor */
+#define LINSCAN_VERSION 200 /* major*100 + minor */
 
 typedef enum {
   LS_OK = 0,
@@ -83,9 +84,9 @@ typedef enum {
   LS_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned */
   LS_ERR_WORKSPACE_TOO_SMALL = 6,
   LS_ERR_BAD_PARAM = 7,           /* eps <= 0, block_frames < 1, non-finite scale ... */
-  LS_ERR_ALIASING = 8,            /* an output overlaps an input it must not overlap */
-  LS_ERR_HIP = 9,                 /* a HIP runtime call or kernel launch failed */
-  LS_ERR_INTERNAL = 10
+  LS_ERR_HIP = 8,                 /* a HIP runtime call or kernel launch failed */
+  LS_ERR_INTERNAL = 9,
+  LS_ERR_ALIASING = 10            /* an output overlaps an input it must not overlap */
 } ls_status;
 
 typedef enum { LS_DTYPE_FP32 = 0, LS_DTYPE_BF16 = 1 } ls_dtype;
@@ -159,10 +160,11 @@ typedef struct {
 } ls_prologue;
 
 /*
- * Workspace bytes ls_relu_block_forward needs for `shape` and `block_frames`
- * (0 if the shape is invalid).  The size depends on the shape only.
+ * Workspace bytes ls_relu_block_forward (and its _strided and _prologue
+ * variants) needs for `shape`, 0 if the shape is invalid.  The size depends on
+ * the shape only: it covers every block size and token layout.
  */
-size_t ls_relu_block_workspace_size(const ls_shape* shape, int block_frames);
+size_t ls_relu_block_workspace_size(const ls_shape* shape);
 
 /*
  * ReLU block-causal linear attention over the F frames of one call.

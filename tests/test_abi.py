@@ -40,7 +40,19 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(raw, name), name
     assert set(lib.EXPORTS) == set(declared_functions())
-    assert lib.lib.ls_version() == 100
+    assert lib.lib.ls_version() == 200
+
+
+def test_status_codes_have_their_documented_values():
+    """The status enum keeps the order and values of the boundary's specification (OK .. INTERNAL = 0 .. 9);
+    the aliasing check added beside them takes the next free value."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum \{(.*?)\} ls_status;", text, flags=re.S).group(1)
+    vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"(LS_\w+)\s*=\s*(\d+)", body)}
+    assert vals == {"LS_OK": 0, "LS_ERR_NULL_POINTER": 1, "LS_ERR_BAD_SHAPE": 2, "LS_ERR_UNSUPPORTED_HEAD_DIM": 3,
+                    "LS_ERR_BAD_DTYPE": 4, "LS_ERR_MISALIGNED": 5, "LS_ERR_WORKSPACE_TOO_SMALL": 6,
+                    "LS_ERR_BAD_PARAM": 7, "LS_ERR_HIP": 8, "LS_ERR_INTERNAL": 9, "LS_ERR_ALIASING": 10}
+    assert re.search(r"size_t\s+ls_relu_block_workspace_size\(const ls_shape\* shape\);", text)
 
 
 def _shape(lib, B=1, H=2, F=3, N=64, D=32, dtype=1):
@@ -48,6 +60,7 @@ def _shape(lib, B=1, H=2, F=3, N=64, D=32, dtype=1):
 
 
 A = 1 << 32  # fake 16-byte aligned device addresses, far apart
+ALIASING = 10  # LS_ERR_ALIASING
 P = [ctypes.c_void_p(A * (i + 1)) for i in range(16)]
 
 
@@ -71,21 +84,21 @@ def test_validation_errors_relu(lib):
     assert _relu(lib, _shape(lib), bf=0) == 7
     assert _relu(lib, _shape(lib), q=None) == 1
     assert _relu(lib, _shape(lib), k=ctypes.c_void_p(A + 8)) == 5
-    assert _relu(lib, _shape(lib), o=P[0]) == 8                      # o aliases q
-    assert _relu(lib, _shape(lib), so=P[1]) == 8                     # state_out inside k
+    assert _relu(lib, _shape(lib), o=P[0]) == ALIASING                      # o aliases q
+    assert _relu(lib, _shape(lib), so=P[1]) == ALIASING                     # state_out inside k
     assert _relu(lib, _shape(lib), ws=None) == 1
     shp = _shape(lib)
-    need = lib.lib.ls_relu_block_workspace_size(ctypes.byref(shp), 1)
+    need = lib.lib.ls_relu_block_workspace_size(ctypes.byref(shp))
     assert need > 0
     assert _relu(lib, shp, wsb=need - 1) == 6
     assert "workspace" in lib.lib.ls_last_error().decode()
-    assert lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, D=24)), 1) == 0
+    assert lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, D=24))) == 0
 
 
 def test_relu_workspace_covers_head_pairs(lib):
     """Head dim 32 in bf16 with an even head count may run heads in pairs as head dim 64 (a layout the
     size query does not see), so its workspace covers that launch too; odd head counts never pair."""
-    ws = lambda **kw: lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, **kw)), 1)
+    ws = lambda **kw: lib.lib.ls_relu_block_workspace_size(ctypes.byref(_shape(lib, **kw)))
     for H, F, N in ((2, 1, 1), (4, 3, 700), (70, 10, 3600), (6, 1, 1100)):
         assert ws(H=H, F=F, N=N, D=32) >= ws(H=H // 2, F=F, N=N, D=64) > 0
     assert ws(H=3, F=3, N=700, D=32) < ws(H=4, F=3, N=700, D=32)
@@ -97,8 +110,8 @@ def test_validation_errors_gdn(lib):
     assert _gdn(lib, _shape(lib), scale=float("inf")) == 7
     assert _gdn(lib, _shape(lib), a=None) == 1
     assert _gdn(lib, _shape(lib), b=ctypes.c_void_p(A * 9 + 2)) == 5
-    assert _gdn(lib, _shape(lib), o=P[2]) == 8
-    assert _gdn(lib, _shape(lib), so=P[7]) == 8                      # state_out over alpha
+    assert _gdn(lib, _shape(lib), o=P[2]) == ALIASING
+    assert _gdn(lib, _shape(lib), so=P[7]) == ALIASING                      # state_out over alpha
     shp = _shape(lib, D=128)
     need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
     assert need > 0
@@ -118,7 +131,7 @@ def test_validation_errors_gdn_token_gate(lib):
     # beta holds B*H*F*N gates (1536 bytes here): a state 1 KiB past its start overlaps
     # it, while the per-frame entry point (24 bytes of beta) sees no overlap there
     inside = ctypes.c_void_p(A * 9 + 1024)
-    assert _gdn_tg(lib, _shape(lib), so=inside) == 8
+    assert _gdn_tg(lib, _shape(lib), so=inside) == ALIASING
     assert _gdn(lib, _shape(lib), so=inside, wsb=1) == 6
     shp = _shape(lib, D=112)
     need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
@@ -132,7 +145,7 @@ def test_validation_errors_gdn_reversed(lib):
     assert r(_shape(lib), 0) == 7
     assert r(_shape(lib, D=100), 2) == 3
     assert r(_shape(lib), 2, q=None) == 1
-    assert r(_shape(lib), 2, o=P[1]) == 8
+    assert r(_shape(lib), 2, o=P[1]) == ALIASING
     shp = _shape(lib, D=128)
     need = lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp))
     assert r(shp, 2, wsb=need - 1) == 6
@@ -147,8 +160,8 @@ def test_validation_errors_temporal_conv(lib):
     assert cv(_shape(lib), bf=0) == 7
     assert cv(_shape(lib), w=None) == 1
     assert cv(_shape(lib), x=ctypes.c_void_p(A + 8)) == 5
-    assert cv(_shape(lib), y=P[0]) == 8                # y over x
-    assert cv(_shape(lib), co=P[0]) == 8               # carry_out over x
+    assert cv(_shape(lib), y=P[0]) == ALIASING                # y over x
+    assert cv(_shape(lib), co=P[0]) == ALIASING               # carry_out over x
     assert cv(_shape(lib, B=0)) == 0                   # nothing to do
 
 
@@ -185,7 +198,7 @@ def test_validation_errors_prologue(lib):
     assert gp(Pr(w, None, 0.0, 0, 0)) == 7                                   # eps must be > 0 with weights
     assert gp(Pr(None, None, 0.0, 2, 0)) == 7
     assert gp(Pr(w + 4, None, 1e-6, 0, 0)) == 5                              # misaligned weights
-    assert gp(Pr(P[3].value, None, 1e-6, 0, 0)) == 8                         # weights inside o
+    assert gp(Pr(P[3].value, None, 1e-6, 0, 0)) == ALIASING                         # weights inside o
     # the rotary embedding: D/2 = 16 pairs, F = 3, N = 10
     rf, rt = P[11].value, P[12].value
     def rope(f=rf, t=rt, pf=8, off=0, T=3):
@@ -200,7 +213,7 @@ def test_validation_errors_prologue(lib):
     assert gp(rope(off=1, T=3)) == 7                                         # rows 1..3 of a 3-row table
     assert gp(rope(off=-1)) == 7
     assert gp(rope(t=rt + 8)) == 5                                           # misaligned table
-    assert gp(rope(t=P[3].value)) == 8                                       # table inside o
+    assert gp(rope(t=P[3].value)) == ALIASING                                       # table inside o
 
 
 def test_in_place_state_is_not_an_aliasing_error(lib):
@@ -216,8 +229,37 @@ def test_carry_validation(lib):
     assert c(1, 1, 32, None, None, P[1], None, 0, None) == 1
     assert c(1, 1, 32, P[0], None, None, None, 0, None) == 1
     assert c(1, 1, 32, ctypes.c_void_p(A + 4), None, P[1], None, 0, None) == 5
-    assert c(1, 1, 32, ctypes.c_void_p(A), None, ctypes.c_void_p(A + 16), None, 0, None) == 8
+    assert c(1, 1, 32, ctypes.c_void_p(A), None, ctypes.c_void_p(A + 16), None, 0, None) == ALIASING
     assert c(0, 1, 32, None, None, None, None, 0, None) == 0           # nothing to do
+
+
+def test_empty_shapes_plan_on_the_host(lib):
+    """Frames without tokens, calls without frames and empty batches are planned on the host and, when no
+    output state is asked for, return without any HIP call (fake device addresses are never touched).  The
+    F = 0 path once divided by zero on the host."""
+    for D in (16, 32, 64, 112, 128):
+        for dt in (0, 1):
+            for B, H, F, N in ((1, 2, 0, 64), (1, 2, 3, 0), (1, 2, 0, 0), (0, 3, 4, 64), (2, 0, 4, 64)):
+                shp = _shape(lib, B=B, H=H, F=F, N=N, D=D, dtype=dt)
+                assert lib.lib.ls_relu_block_workspace_size(ctypes.byref(shp)) > 0
+                assert lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(shp)) > 0
+                if F == 0 or B * H == 0:
+                    assert _gdn(lib, shp, si=P[9], so=None, wsb=0, ws=None) == 0
+                    assert lib.lib.ls_gdn_frame_forward_reversed(ctypes.byref(shp), 2, 0.0, P[0], P[1], P[2], P[7],
+                                                                 P[8], P[3], None, 0, None) == 0
+                if F * N == 0 or B * H == 0:
+                    # no tokens: the state would pass through; with no output state nothing is enqueued
+                    assert _relu(lib, shp, si=P[9], ni=P[10], so=None, no=None, wsb=0, ws=None) == 0
+                    st = lib.ls_strides(0, 0, 0, 0)
+                    assert lib.lib.ls_relu_block_forward_strided(ctypes.byref(shp), ctypes.byref(st), 1, 1e-6, P[0],
+                                                                 P[1], P[2], P[3], None, None, None, None, None, 0,
+                                                                 None) == 0
+            # the checks still run first: a bad eps or block size is rejected even without tokens
+            shp = _shape(lib, F=0, D=D, dtype=dt)
+            assert _relu(lib, shp, eps=0.0, so=None, no=None) == 7
+            assert _relu(lib, shp, bf=0, so=None, no=None) == 7
+    cv = lambda shp: lib.lib.ls_temporal_conv3(ctypes.byref(shp), 1, P[0], P[1], None, None, P[2], None, None)
+    assert cv(_shape(lib, F=0)) == 0 and cv(_shape(lib, N=0)) == 0
 
 
 def test_status_strings(lib):

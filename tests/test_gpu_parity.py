@@ -384,11 +384,11 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     if op == "relu":
         x = gen.relu_inputs(1, 11, 9, 777, 32, "bf16", seed=31)   # B*H not a multiple of 8
         shp = ls.ls_shape(1, 11, 9, 777, 32, 1)
-        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
+        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp))
     elif op == "relu_wide":  # head dim 112: chained cumulative states
         x = gen.relu_inputs(1, 11, 9, 777, 112, "bf16", seed=34)
         shp = ls.ls_shape(1, 11, 9, 777, 112, 1)
-        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 2)
+        need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp))
     elif op == "gdn":
         x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=32)
         shp = ls.ls_shape(1, 5, 9, 333, 128, 1)
@@ -458,7 +458,7 @@ def test_concurrent_streams_match_sequential(ls, gen):
         if kind == "gdn":
             need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
         else:
-            need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp), 1)
+            need = ls.lib.ls_relu_block_workspace_size(ls.ctypes.byref(shp))
         return torch.zeros(need, dtype=torch.uint8, device=DEV)
 
     ref = [run(kind, x, workspace(kind, x)) for kind, x in jobs]
