@@ -155,6 +155,10 @@ def main():
         ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], None, out=g_out,
                                 state_out=g_state)
 
+    # the workspaces' fault words (set when a bounded wait of a single-launch
+    # call gives up, which would make that call's results invalid) start at
+    # zero and are read once every measurement is done: the word is sticky
+    ls.ls_clear_fault_word(dev)
     for _ in range(args.warmup):
         part_video()
         part_wm()
@@ -254,6 +258,8 @@ def main():
     pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
+    fault = ls.ls_fault_word(dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, inputs, wv, wg, tokens)
@@ -296,8 +302,13 @@ def main():
                  "sana_wm_720p_60s_reversed_c8": rev, "causal_mix_ffn_temporal_conv": conv,
                  "bshd_layout": strided, "fused_prologue": pro},
         "kernels": kernels,
+        "fault_word": fault,
     }
     print(json.dumps(line), flush=True)
+    if fault != 0:
+        print("a bounded wait gave up (workspace fault word %#x): results of this run are invalid" % fault,
+              file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 def time_480p(torch, ls, inputs, reps=5):

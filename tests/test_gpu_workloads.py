@@ -1,16 +1,19 @@
 """Full-size video workloads on the GPU, in the launch configuration the
-benchmark times, checked against the fp64 oracle on sampled (batch, head)
-pairs (needs an MI355X).
+benchmark times, checked against the fp64 oracle on every (batch, head)
+(needs an MI355X).
 
-Every (batch, head) of the scan is independent, so the oracle recomputes a
-few of them end to end from the same input values and compares every output
-token and the final state of those heads.
+Every (batch, head) of the scan is independent, so the oracle recomputes the
+heads in groups, end to end from the same input values, and every output
+token and the final state of every head are compared.  A group's error floor
+(1e-3 of the group's largest value) is never looser than the whole tensor's.
+After each workload the workspaces' fault words are read: a bounded wait that
+gave up would make the results invalid even where they happen to match.
 """
 import numpy as np
 import pytest
 import torch
 
-from metrics import max_rel_err
+from metrics import max_rel_err, normwise_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 DEV = "cuda"
@@ -20,6 +23,7 @@ DEV = "cuda"
 def ls():
     assert torch.cuda.is_available()
     from block_causal_linear_attn_amd import binding
+    binding.ls_clear_fault_word()
     return binding
 
 
@@ -31,13 +35,43 @@ def gen():
 
 def check(name, got, want, tol):
     err = max_rel_err(got, want)
-    print("%-44s max rel err %.3e (tol %.0e)" % (name, err, tol), flush=True)
+    print("%-52s max rel err %.3e (tol %.0e)" % (name, err, tol), flush=True)
     assert err <= tol, (name, err)
 
 
+def groups(n, size):
+    return [list(range(i, min(n, i + size))) for i in range(0, n, size)]
+
+
 def _heads(t, hs):
-    """[B, H, ...] device tensor -> CPU float32 copy of heads hs (batch 0)."""
+    """[B, H, ...] device tensor -> CPU float32 copy of heads hs (every batch)."""
     return t[:, hs].float().cpu()
+
+
+def no_fault(ls):
+    word = ls.ls_fault_word()
+    assert word == 0, "a bounded wait gave up (fault word %#x)" % word
+
+
+def test_tiny_case_seed0_both_rules(ls, gen, oracle_mod):
+    """The tiny fp32 workload at its own seed: o, S and z of the ReLU scan and o, S of GDN (raw keys)."""
+    w = gen.WORKLOADS["tiny"]
+    t = gen.gdn_inputs(w.B, w.H, w.F, w.N, w.D, "fp32", w.seed, alpha_mu=w.alpha_mu, l2_keys=False)
+    d = {n: x.to(DEV) for n, x in t.items()}
+    o, S, z = ls.ls_relu_block_forward(d["q"], d["k"], d["v"])
+    o2, S2 = ls.ls_gdn_frame_forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+    torch.cuda.synchronize()
+    ro, rS, rz = oracle_mod.relu_block(t["q"], t["k"], t["v"])
+    ro2, rS2 = oracle_mod.gdn_frame(t["q"], t["k"], t["v"], t["alpha"], t["beta"])
+    for name, got, want in (("relu o", o, ro), ("relu S", S, rS), ("relu z", z, rz), ("gdn o", o2, ro2),
+                            ("gdn S", S2, rS2)):
+        nw = normwise_err(got, want)
+        el = max_rel_err(got, want, floor=1e-3)
+        print("tiny seed 0 %-8s normwise %.3e  element-wise (floor 1e-3) %.3e" % (name, nw, el), flush=True)
+        assert nw <= 1e-5, (name, nw)
+        # element-wise with the bf16 floor: what the fp32 path meets on this case (measured ~1e-6)
+        assert el <= 1e-4, (name, el)
+    no_fault(ls)
 
 
 def test_sana_video_480p_5s(ls, gen, oracle_mod):
@@ -45,62 +79,74 @@ def test_sana_video_480p_5s(ls, gen, oracle_mod):
     x = gen.workload_call_inputs(w, 0, device=DEV)
     o, S, z = ls.ls_relu_block_forward(x["q"], x["k"], x["v"])
     torch.cuda.synchronize()
-    hs = [0, 37, 69]
-    ro, rS, rz = oracle_mod.relu_block(_heads(x["q"], hs), _heads(x["k"], hs), _heads(x["v"], hs))
-    check("480p-5s relu o (3 heads)", _heads(o, hs), ro, 2e-2)
-    check("480p-5s relu S", _heads(S, hs), rS, 1e-2)
-    check("480p-5s relu z", _heads(z, hs), rz, 1e-2)
+    no_fault(ls)
+    for hs in groups(w.H, 18):
+        ro, rS, rz = oracle_mod.relu_block(_heads(x["q"], hs), _heads(x["k"], hs), _heads(x["v"], hs))
+        tag = "480p-5s relu heads %d-%d" % (hs[0], hs[-1])
+        check(tag + " o", _heads(o, hs), ro, 2e-2)
+        check(tag + " S", _heads(S, hs), rS, 1e-2)
+        check(tag + " z", _heads(z, hs), rz, 1e-2)
+
+
+def _rollout(ls, gen, oracle_mod, w, group):
+    """241 frames in 25 calls of at most 10 frames chained through ls_state_carry, every head."""
+    cache = torch.zeros((w.B, w.H, w.D, w.D), device=DEV)
+    ncache = torch.zeros((w.B, w.H, w.D), device=DEV)
+    S_blk = torch.empty_like(cache)
+    z_blk = torch.empty_like(ncache)
+    xs, os_ = [], []
+    for call in range(len(w.calls)):
+        x = gen.workload_call_inputs(w, call, device=DEV)
+        o, _, _ = ls.ls_relu_block_forward(x["q"], x["k"], x["v"], cache, ncache, state_out=S_blk, norm_out=z_blk)
+        ls.ls_state_carry(S_blk, cache, z_blk, ncache)
+        xs.append(x)
+        os_.append(o)
+    torch.cuda.synchronize()
+    no_fault(ls)
+    for hs in groups(w.H, group):
+        q, k, v, o = (torch.cat([_heads(t, hs) for t in l], dim=2)
+                      for l in ([x["q"] for x in xs], [x["k"] for x in xs], [x["v"] for x in xs], os_))
+        assert q.shape[2] == w.F
+        ro, rS, rz = oracle_mod.relu_block(q, k, v)
+        del q, k, v
+        tag = "%s relu heads %d-%d" % (w.name, hs[0], hs[-1])
+        check(tag + " o", o, ro, 2e-2)
+        check(tag + " S", _heads(cache, hs), rS, 1e-2)
+        check(tag + " z", _heads(ncache, hs), rz, 1e-2)
+        del o, ro
 
 
 def test_sana_video_720p_minute_rollout(ls, gen, oracle_mod):
-    """241 frames in 25 calls of at most 10 frames chained through ls_state_carry."""
-    w = gen.WORKLOADS["sana_video_720p_minute"]
-    hs = [5, 52]
-    cache = torch.zeros((w.B, w.H, w.D, w.D), device=DEV)
-    ncache = torch.zeros((w.B, w.H, w.D), device=DEV)
-    S_blk = torch.empty_like(cache)
-    z_blk = torch.empty_like(ncache)
-    qs, ks, vs, os_ = [], [], [], []
-    for call in range(len(w.calls)):
-        x = gen.workload_call_inputs(w, call, device=DEV)
-        o, _, _ = ls.ls_relu_block_forward(x["q"], x["k"], x["v"], cache, ncache,
-                                           state_out=S_blk, norm_out=z_blk)
-        ls.ls_state_carry(S_blk, cache, z_blk, ncache)
-        for lst, t in ((qs, x["q"]), (ks, x["k"]), (vs, x["v"]), (os_, o)):
-            lst.append(_heads(t, hs))
-        del x, o
-    torch.cuda.synchronize()
-    q, k, v, o = (torch.cat(l, dim=2) for l in (qs, ks, vs, os_))
-    assert q.shape[2] == 241
-    ro, rS, rz = oracle_mod.relu_block(q, k, v)
-    check("720p-minute relu o (2 heads, 241 frames)", o, ro, 2e-2)
-    check("720p-minute relu S", _heads(cache, hs), rS, 1e-2)
-    check("720p-minute relu z", _heads(ncache, hs), rz, 1e-2)
+    _rollout(ls, gen, oracle_mod, gen.WORKLOADS["sana_video_720p_minute"], 16)
 
 
 def test_sana_video_720p_minute_rollout_d112(ls, gen, oracle_mod):
-    """The rollout at head dim 112 (wide MFMA path), one sampled head over all 241 frames."""
-    w = gen.WORKLOADS["sana_video_720p_minute_d112"]
-    hs = [13]
-    cache = torch.zeros((w.B, w.H, w.D, w.D), device=DEV)
-    ncache = torch.zeros((w.B, w.H, w.D), device=DEV)
-    S_blk = torch.empty_like(cache)
-    z_blk = torch.empty_like(ncache)
-    qs, ks, vs, os_ = [], [], [], []
-    for call in range(len(w.calls)):
-        x = gen.workload_call_inputs(w, call, device=DEV)
-        o, _, _ = ls.ls_relu_block_forward(x["q"], x["k"], x["v"], cache, ncache,
-                                           state_out=S_blk, norm_out=z_blk)
-        ls.ls_state_carry(S_blk, cache, z_blk, ncache)
-        for lst, t in ((qs, x["q"]), (ks, x["k"]), (vs, x["v"]), (os_, o)):
-            lst.append(_heads(t, hs))
-        del x, o
+    """The rollout at head dim 112 (wide MFMA path), every head over all 241 frames."""
+    _rollout(ls, gen, oracle_mod, gen.WORKLOADS["sana_video_720p_minute_d112"], 10)
+
+
+def _gdn_all_heads(ls, oracle_mod, w, x, o, S, tag, group=12, beta=None, rchunk=0):
+    for hs in groups(w.H, group):
+        args = [_heads(x[n], hs) for n in ("q", "k", "v", "alpha")] + [_heads(x["beta"] if beta is None else beta, hs)]
+        t = "%s heads %d-%d" % (tag, hs[0], hs[-1])
+        if rchunk:
+            ro = oracle_mod.gdn_frame_reversed(*args, rchunk)
+        elif beta is not None:
+            ro, rS = oracle_mod.gdn_frame_token_gate(*args)
+        else:
+            ro, rS = oracle_mod.gdn_frame(*args)
+        check(t + " o", _heads(o, hs), ro, 2e-2)
+        if S is not None:
+            check(t + " S", _heads(S, hs), rS, 1e-2)
+
+
+def test_sana_wm_720p_60s(ls, gen, oracle_mod):
+    w = gen.WORKLOADS["sana_wm_720p_60s"]
+    x = gen.workload_call_inputs(w, 0, device=DEV)
+    o, S = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
     torch.cuda.synchronize()
-    q, k, v, o = (torch.cat(l, dim=2) for l in (qs, ks, vs, os_))
-    ro, rS, rz = oracle_mod.relu_block(q, k, v)
-    check("720p-minute D112 relu o (1 head, 241 frames)", o, ro, 2e-2)
-    check("720p-minute D112 relu S", _heads(cache, hs), rS, 1e-2)
-    check("720p-minute D112 relu z", _heads(ncache, hs), rz, 1e-2)
+    no_fault(ls)
+    _gdn_all_heads(ls, oracle_mod, w, x, o, S, "wm-60s gdn")
 
 
 def test_sana_wm_720p_60s_d112(ls, gen, oracle_mod):
@@ -108,10 +154,8 @@ def test_sana_wm_720p_60s_d112(ls, gen, oracle_mod):
     x = gen.workload_call_inputs(w, 0, device=DEV)
     o, S = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
     torch.cuda.synchronize()
-    hs = [0, 27]
-    ro, rS = oracle_mod.gdn_frame(*(_heads(x[n], hs) for n in ("q", "k", "v", "alpha", "beta")))
-    check("wm-60s D112 gdn o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
-    check("wm-60s D112 gdn S", _heads(S, hs), rS, 1e-2)
+    no_fault(ls)
+    _gdn_all_heads(ls, oracle_mod, w, x, o, S, "wm-60s D112 gdn", group=14)
 
 
 def test_sana_wm_720p_60s_token_gate(ls, gen, oracle_mod):
@@ -121,10 +165,8 @@ def test_sana_wm_720p_60s_token_gate(ls, gen, oracle_mod):
     bt = gen.token_gates(w.B, w.H, w.F, w.N, seed=w.seed, device=DEV)
     o, S = ls.ls_gdn_frame_forward_token_gate(x["q"], x["k"], x["v"], x["alpha"], bt)
     torch.cuda.synchronize()
-    hs = [7, 16]
-    ro, rS = oracle_mod.gdn_frame_token_gate(*(_heads(t, hs) for t in (x["q"], x["k"], x["v"], x["alpha"], bt)))
-    check("wm-60s gdn token-gate o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
-    check("wm-60s gdn token-gate S", _heads(S, hs), rS, 1e-2)
+    no_fault(ls)
+    _gdn_all_heads(ls, oracle_mod, w, x, o, S, "wm-60s gdn token-gate", beta=bt)
 
 
 def test_sana_wm_720p_60s_reversed(ls, gen, oracle_mod):
@@ -133,50 +175,34 @@ def test_sana_wm_720p_60s_reversed(ls, gen, oracle_mod):
     x = gen.workload_call_inputs(w, 0, device=DEV)
     o = ls.ls_gdn_frame_forward_reversed(x["q"], x["k"], x["v"], x["alpha"], x["beta"], 8)
     torch.cuda.synchronize()
-    hs = [2, 23]
-    ro = oracle_mod.gdn_frame_reversed(*(_heads(x[n], hs) for n in ("q", "k", "v", "alpha", "beta")), 8)
-    check("wm-60s gdn reversed c8 o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
-
-
-def test_sana_wm_720p_60s(ls, gen, oracle_mod):
-    w = gen.WORKLOADS["sana_wm_720p_60s"]
-    x = gen.workload_call_inputs(w, 0, device=DEV)
-    o, S = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"])
-    torch.cuda.synchronize()
-    hs = [3, 20]
-    ro, rS = oracle_mod.gdn_frame(*(_heads(x[n], hs) for n in ("q", "k", "v", "alpha", "beta")))
-    check("wm-60s gdn o (2 heads, 181 frames)", _heads(o, hs), ro, 2e-2)
-    check("wm-60s gdn S", _heads(S, hs), rS, 1e-2)
+    no_fault(ls)
+    _gdn_all_heads(ls, oracle_mod, w, x, o, None, "wm-60s gdn reversed c8", rchunk=8)
 
 
 def test_sana_wm_chunk_steps(ls, gen, oracle_mod):
     """50 single-frame calls re-reading one carried state built by the oracle
-    from a 60-frame prefix; the cache itself is never written."""
+    from a 60-frame prefix, every (batch, head) of every step; the cache
+    itself is never written."""
     w = gen.WORKLOADS["sana_wm_chunk_step"]
     pre = gen.prefix_inputs(w, device="cpu")
     _, S_pre = oracle_mod.gdn_frame(None, pre["k"], pre["v"], pre["alpha"], pre["beta"], with_output=False)
     del pre
     cache = torch.from_numpy(S_pre.astype(np.float32)).to(DEV)
     cache_copy = cache.clone()
+    cache_cpu = cache.cpu()
     state_out = torch.empty_like(cache)
-    sample = [(0, 0), (3, 17)]
+    worst_o = worst_s = 0.0
     for step in range(w.steps):
         x = gen.workload_call_inputs(w, step, device=DEV)
-        o, _ = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], cache,
-                                       state_out=state_out)
+        o, _ = ls.ls_gdn_frame_forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], cache, state_out=state_out)
         torch.cuda.synchronize()
-        for b, h in sample:
-            sl = lambda t: t[b:b + 1, h:h + 1].float().cpu()
-            ro, rS = oracle_mod.gdn_frame(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["alpha"]),
-                                          sl(x["beta"]), sl(cache))
-            err_o = max_rel_err(sl(o), ro)
-            err_s = max_rel_err(sl(state_out), rS)
-            assert err_o <= 2e-2 and err_s <= 1e-2, (step, b, h, err_o, err_s)
-        if step == w.steps - 1:
-            # every head of the last step
-            ro, rS = oracle_mod.gdn_frame(x["q"].float().cpu(), x["k"].float().cpu(),
-                                          x["v"].float().cpu(), x["alpha"].cpu(), x["beta"].cpu(),
-                                          cache.cpu())
-            check("chunk-step gdn o (all 96 heads)", o, ro, 2e-2)
-            check("chunk-step gdn S (all 96 heads)", state_out, rS, 1e-2)
+        ro, rS = oracle_mod.gdn_frame(x["q"].float().cpu(), x["k"].float().cpu(), x["v"].float().cpu(),
+                                      x["alpha"].cpu(), x["beta"].cpu(), cache_cpu)
+        err_o = max_rel_err(o, ro)
+        err_s = max_rel_err(state_out, rS)
+        worst_o, worst_s = max(worst_o, err_o), max(worst_s, err_s)
+        assert err_o <= 2e-2 and err_s <= 1e-2, (step, err_o, err_s)
+    print("chunk-step gdn, all 96 heads of all %d steps: max rel err o %.3e, S %.3e" % (w.steps, worst_o, worst_s),
+          flush=True)
+    no_fault(ls)
     assert torch.equal(cache, cache_copy)
