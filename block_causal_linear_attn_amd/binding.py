@@ -66,6 +66,8 @@ def _load():
     lib.ls_gdn_frame_workspace_size.restype = Z
     lib.ls_gdn_frame_forward.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.ls_gdn_frame_forward.restype = I
+    lib.ls_gdn_frame_forward_noalloc.argtypes = [SP, F, P, P, P, P, P, P, P, P, P, P]
+    lib.ls_gdn_frame_forward_noalloc.restype = I
     ST = ctypes.POINTER(ls_strides)
     PR = ctypes.POINTER(ls_prologue)
     lib.ls_relu_block_forward_prologue.argtypes = [SP, PR, I, F, P, P, P, P, P, P, P, P, P, Z, P]
@@ -100,7 +102,7 @@ def _load():
 lib = _load()
 
 EXPORTS = ("ls_relu_block_workspace_size", "ls_relu_block_forward", "ls_gdn_frame_workspace_size",
-           "ls_gdn_frame_forward", "ls_gdn_frame_forward_token_gate",
+           "ls_gdn_frame_forward", "ls_gdn_frame_forward_noalloc", "ls_gdn_frame_forward_token_gate",
            "ls_gdn_frame_forward_reversed", "ls_temporal_conv3", "ls_relu_block_forward_strided",
            "ls_gdn_frame_forward_strided", "ls_relu_block_forward_prologue", "ls_gdn_frame_forward_prologue",
            "ls_state_carry", "ls_status_string", "ls_last_error",
@@ -274,6 +276,37 @@ def ls_gdn_frame_forward(q, k, v, alpha, beta, state=None, key_scale=None, out=N
                                     _ptr(beta), _ptr(o), _ptr(state), _ptr(so), _ptr(w), w.numel(),
                                     _stream(dev)))
     return o, so
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LS_NOALLOC_SCRATCH_BYTES
+
+
+def ls_gdn_frame_forward_noalloc(q, k, v, alpha, beta, out, state=None, state_out=None, key_scale=None,
+                                 fault=None):
+    """ls_gdn_frame_forward without a workspace: the library's static device
+    scratch (LS_NOALLOC_SCRATCH_BYTES per GPU) holds it, and nothing is
+    allocated, here or in the library.  The caller passes every output: out
+    like q, state_out [B, H, D, D] fp32 or None (not written), fault a
+    one-element int32 device tensor the kernels set nonzero if a bounded wait
+    gave up, or None.  Calls that overlap in time on one GPU race."""
+    _tokens("q", q)
+    _tokens("k", k, q)
+    _tokens("v", v, q)
+    _tokens("out", out, q)
+    B, H, F, N, D = q.shape
+    dev = q.device
+    _f32("alpha", alpha, (B, H, F), dev)
+    _f32("beta", beta, (B, H, F), dev)
+    _f32("state", state, (B, H, D, D), dev)
+    _f32("state_out", state_out, (B, H, D, D), dev)
+    if fault is not None and (fault.dtype != torch.int32 or fault.numel() < 1 or fault.device != dev):
+        raise ValueError("fault must be an int32 tensor on %s" % dev)
+    shp = _shape(q)
+    scale = 0.0 if key_scale is None else float(key_scale)
+    _check(lib.ls_gdn_frame_forward_noalloc(ctypes.byref(shp), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                            _ptr(beta), _ptr(out), _ptr(state), _ptr(state_out), _ptr(fault),
+                                            _stream(dev)))
+    return out, state_out
 
 
 def ls_relu_block_forward_strided(q, k, v, state=None, norm=None, block_frames: int = 1, eps: float = 1e-6,

@@ -239,7 +239,7 @@ hipError_t launch_gdn_output_mfma(int D, const void* q, void* o, const void* sta
 // The fused kernel instance a call with these switches runs (nc > 1: MULTI).
 static const void* gdn_fused_kernel(int D, bool tg, bool pro, int nc) {
   const void* k = nullptr;
-  with_head_dim(D, [&](auto di) {
+  (void)with_head_dim(D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
     auto kern = nc == 1 ? (tg ? gdn_fused_mfma128<false, DI, true, false>
                               : (pro ? gdn_fused_mfma128<false, DI, false, true> : gdn_fused_mfma128<false, DI, false, false>))

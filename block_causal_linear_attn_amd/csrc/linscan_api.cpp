@@ -394,6 +394,16 @@ void relu_pair_dims(const ls_shape* s, const Dims& d, ls_shape* ps, Dims* pd) {
 
 }  // namespace
 
+namespace linscan {
+
+ls_status set_error(ls_status st, const char* msg) { return fail(st, "%s", msg); }
+
+ls_status gdn_forward_plain(const ls_shape* s, float key_scale, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, void* o, const float* state_in, float* state_out,
+                            void* workspace, size_t workspace_bytes, uint32_t* fault, void* stream);
+
+}  // namespace linscan
+
 extern "C" {
 
 int ls_version(void) { return LINSCAN_VERSION; }
@@ -621,12 +631,13 @@ static ls_status relu_forward(const ls_shape* s, const ls_strides* strides, cons
 
 // The GDN entry points: beta per frame ([B*H*F]) or, with token_gate, per
 // token ([B*H*F][N]); rchunk > 0 runs the reversed scan in chunks of rchunk
-// frames (no state in or out).
+// frames (no state in or out).  `fault` receives the kernels' fault word
+// (nullptr: the workspace's first word).
 static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const ls_prologue* pro, float key_scale,
                              const void* q,
                              const void* k, const void* v, const float* alpha, const float* beta, bool token_gate,
                              int rchunk, void* o, const float* state_in, float* state_out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             size_t workspace_bytes, void* stream, uint32_t* fault = nullptr) {
   g_last_error.clear();
   Dims d;
   ls_status st = check_shape(s, &d);
@@ -725,7 +736,7 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const
     const long bhp = (d.bh + 8 * layout.hg - 1) / (8 * layout.hg) * (8 * layout.hg);
     uint64_t* gflags = (uint64_t*)(ws + p.gflags_off);
     uint64_t* sflags = (uint64_t*)(ws + p.sflags_off);
-    uint32_t* err = (uint32_t*)ws;
+    uint32_t* err = fault ? fault : (uint32_t*)ws;
     const uint64_t epoch = next_epoch();
     if (p.fused)
       return hip_check(timed("gdn_fused", hs, [&] {
@@ -785,6 +796,18 @@ ls_status ls_gdn_frame_forward_prologue(const ls_shape* s, const ls_prologue* pr
   return gdn_forward(s, nullptr, prologue, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out,
                      workspace, workspace_bytes, stream);
 }
+
+}  // extern "C"
+
+ls_status linscan::gdn_forward_plain(const ls_shape* s, float key_scale, const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* beta, void* o, const float* state_in,
+                                     float* state_out, void* workspace, size_t workspace_bytes, uint32_t* fault,
+                                     void* stream) {
+  return gdn_forward(s, nullptr, nullptr, key_scale, q, k, v, alpha, beta, false, 0, o, state_in, state_out, workspace,
+                     workspace_bytes, stream, fault);
+}
+
+extern "C" {
 
 ls_status ls_gdn_frame_forward(const ls_shape* s, float key_scale, const void* q, const void* k,
                                const void* v, const float* alpha, const float* beta, void* o,

@@ -247,6 +247,34 @@ ls_status ls_gdn_frame_forward(const ls_shape* shape, float key_scale,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ls_gdn_frame_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  The scan's records, per-frame states
+ * and flags live in a static device array of LS_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing.  A call whose ls_gdn_frame_workspace_size exceeds
+ * that size is rejected with LS_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued (64 MiB holds, for example, the single-frame step of B4 H24 D128
+ * N920, 19 MB).
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing between calls): calls that overlap
+ * in time on one GPU (concurrent streams, or host threads) race and give
+ * undefined results; serialise them.
+ *
+ * fault_word: a device pointer to 4 bytes (4-byte aligned) that the kernels
+ * OR a nonzero value into if a bounded wait gave up (the results are then
+ * invalid), or NULL (not reported).  The library never clears it.
+ * Everything else, including the error behaviour, as ls_gdn_frame_forward.
+ */
+#define LS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ls_status ls_gdn_frame_forward_noalloc(const ls_shape* shape, float key_scale,
+                                       const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta, void* o,
+                                       const float* state_in, float* state_out,
+                                       unsigned int* fault_word, void* stream);
+
+/*
  * ls_gdn_frame_forward with token tensors in the layout `strides` (NULL:
  * packed [B][H][F][N][D]).  Workspace size and everything else as there.
  */

@@ -262,6 +262,22 @@ def test_empty_shapes_plan_on_the_host(lib):
     assert cv(_shape(lib, F=0)) == 0 and cv(_shape(lib, N=0)) == 0
 
 
+def test_noalloc_checks_its_scratch_size_on_the_host(lib):
+    """The allocation-free GDN entry point rejects a call whose workspace would not fit its static scratch,
+    and a bad shape, before any HIP call."""
+    f = lambda shp: lib.lib.ls_gdn_frame_forward_noalloc(ctypes.byref(shp), 0.0, P[0], P[1], P[2], P[7], P[8], P[3],
+                                                         None, P[4], None, None)
+    big = _shape(lib, B=1, H=24, F=20, N=64, D=128)
+    assert lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(big)) > lib.NOALLOC_SCRATCH_BYTES
+    assert f(big) == 6 and "scratch" in lib.lib.ls_last_error().decode()
+    assert f(_shape(lib, D=24)) == 3
+    assert lib.lib.ls_gdn_frame_forward_noalloc(ctypes.byref(_shape(lib)), 0.0, P[0], P[1], P[2], P[7], P[8], P[3],
+                                                None, P[4], ctypes.c_void_p(A + 2), None) == 5
+    # the chunk step (B4 H24 D128 N920, one frame) fits
+    step = _shape(lib, B=4, H=24, F=1, N=920, D=128)
+    assert lib.lib.ls_gdn_frame_workspace_size(ctypes.byref(step)) <= lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings(lib):
     for st in range(11):
         assert lib.lib.ls_status_string(st).decode()
