@@ -250,51 +250,66 @@ __device__ __forceinline__ void gdn_gram_item(
 // their XCD's L2.
 constexpr int kGramRowsKRow = GD, kGramRowsVRow = 32;  // unpadded; K chunks swizzled by token
 constexpr int kGramRowsDepth = 4;  // tiles in flight per workgroup
-constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;  // (+ kGateLds with TG)
+constexpr int kGramRowsLds = 2 * 64 * (kGramRowsKRow + kGramRowsVRow) * 2;  // RB = 32 (+ kGateLds with TG)
 
 // TG: per-token gates as in gdn_gram_item (the A operands, key and value
 // fragments, scaled and split into hi + lo before each MFMA pair; gates in
 // LDS after the tiles).
-template <int DI = GD, bool TG = false, bool PRO = false>
-__device__ __forceinline__ void gdn_gram_rows_item(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw, TokLayout L,
-    Prologue P) {
+// LDS bytes of the row-split gram accumulation over RB-row blocks: double
+// buffered 64-token tiles of K (all dims) and of the block's RB dims of V.
+template <int RB>
+constexpr int gram_rows_lds() { return 2 * 64 * (GD + RB) * 2; }
+
+// The accumulation of the row-split gram item over rows RB*w .. RB*w + RB - 1
+// (RB = 32 or 64, NB = RB / 32 blocks of 32 rows): wave j of the workgroup
+// ends with G(32 (NB w + b), j) = sum k k_j^T over those rows in accG[b] and
+// U(32 (NB w + b), j) = sum v k_j^T in accU[b] (unscaled), over all N tokens
+// of frame bhf (one head's frame).
+template <int DI = GD, bool TG = false, bool PRO = false, int RB = 32>
+__device__ __forceinline__ void gram_rows_accumulate(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta, int N,
+    long bhf, int w, uint8_t* lds_raw, TokLayout L, Prologue P, floatx16 (&accG)[RB / 32],
+    floatx16 (&accU)[RB / 32]) {
+  static_assert(RB == 32 || RB == 64, "row blocks of 32 or 64 rows");
   constexpr int D = GD;
+  constexpr int NB = RB / 32;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
-  constexpr int KROW = kGramRowsKRow, VROW = kGramRowsVRow;
+  constexpr int KROW = kGramRowsKRow, VROW = RB;
+  constexpr int VCH = RB / 8;                 // 16-byte chunks of a token's V slice
   constexpr int KLPT = TILE * (D / 8) / 256;  // 16-byte K loads per thread per tile (4)
+  constexpr int VLPT = TILE * VCH / 256;      // 16-byte V loads per thread per tile (1 or 2)
   uint16_t* kl[2] = {reinterpret_cast<uint16_t*>(lds_raw),
                      reinterpret_cast<uint16_t*>(lds_raw) + TILE * KROW};
   uint16_t* vl[2] = {reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW,
                      reinterpret_cast<uint16_t*>(lds_raw) + 2 * TILE * KROW + TILE * VROW};
-  float(*gl)[TILE] = reinterpret_cast<float(*)[TILE]>(lds_raw + kGramRowsLds);  // [buffer][token] gates (TG)
+  float(*gl)[TILE] = reinterpret_cast<float(*)[TILE]>(lds_raw + gram_rows_lds<RB>());  // [buffer][token] gates (TG)
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 5, col = lane & 31;
-  const long bhf = item >> 2;
-  const int w = (int)(item & 3);
+  const int g = lane >> 5;
   const uint16_t* kf = k + L.base(bhf);
   const uint16_t* vf = v + L.base(bhf);
-  const int vchunk = 4 * w + (tid & 3);  // this thread's 16-byte chunk of the V rows
   const float* gf = TG ? beta + (size_t)bhf * N : beta;  // token gates of the frame (TG)
-  float* wl = reinterpret_cast<float*>(lds_raw + kGramRowsLds + kGateLds);  // the prologue's key weights
+  float* wl = reinterpret_cast<float*>(lds_raw + gram_rows_lds<RB>() + kGateLds);  // the prologue's key weights
   if (PRO) stage_weights(P.wk, (bhf / L.F) % L.H, DI, wl);
   auto row16 = [](double x) { return group_sum_f64<16>(x); };
 
-  floatx16 accG = {}, accU = {};
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    accG[b] = floatx16{};
+    accU[b] = floatx16{};
+  }
   struct Regs {
-    u32x4 k[KLPT], v;
+    u32x4 k[KLPT], v[VLPT];
     float b;  // gate of token tid % 64 of the tile (TG)
   };
   constexpr int DEPTH = kGramRowsDepth;
   Regs R[DEPTH];
-  // K: token ci >> 4, 16-byte chunk ci & 15; V: token tid >> 2, chunk tid & 3
-  // of the w-th 32 dims.  Every load is issued (rows past the frame re-read
-  // token 0) and such rows are zeroed when staged, so that the compiler can
-  // count the loads in flight instead of waiting for all of them.
+  // K: token ci >> 4, 16-byte chunk ci & 15; V: token ci / VCH, chunk
+  // ci % VCH of the block's RB dims.  Every load is issued (rows past the
+  // frame re-read token 0) and such rows are zeroed when staged, so that the
+  // compiler can count the loads in flight instead of waiting for all of them.
   auto fetch = [&](Regs& R, int t0) {
 #pragma unroll
     for (int r = 0; r < KLPT; ++r) {
@@ -302,11 +317,19 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       const int n = t0 + (ci >> 4);
       R.k[r] = ld16(kf + (size_t)(n < N ? n : 0) * L.sn + ((ci & 15) < CI ? (ci & 15) : CI - 1) * 8);
     }
-    const int n = t0 + (tid >> 2);
-    R.v = ld16(vf + (size_t)(n < N ? n : 0) * L.sn + (vchunk < CI ? vchunk : CI - 1) * 8);
+#pragma unroll
+    for (int r = 0; r < VLPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int n = t0 + ci / VCH, vc = VCH * w + ci % VCH;
+      R.v[r] = ld16(vf + (size_t)(n < N ? n : 0) * L.sn + (vc < CI ? vc : CI - 1) * 8);
+    }
     if (TG) R.b = gf[t0 + (tid & 63) < N ? t0 + (tid & 63) : 0];
   };
   auto stage = [&](const Regs& R, int buf, int t0) {
+    // keep the zeroing of rows past the frame here: hoisted to the top of
+    // the unrolled pass, the selects of every set of the ring made the
+    // compiler wait for all loads in flight (vmcnt(0)) once per pass
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
@@ -323,32 +346,40 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       kd[0] = make_uint2(kk[0], kk[1]);
       kd[1] = make_uint2(kk[2], kk[3]);
     }
-    const u32x4 vv = t0 + (tid >> 2) < N && vchunk < CI ? R.v : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < VLPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci / VCH, ch = ci % VCH;
+      const u32x4 vv = t0 + tok < N && VCH * w + ch < CI ? R.v[r] : u32x4{0u, 0u, 0u, 0u};
+      uint2* vd = reinterpret_cast<uint2*>(vl[buf] + swz_offset<VCH>(tok, ch));
+      vd[0] = make_uint2(vv[0], vv[1]);
+      vd[1] = make_uint2(vv[2], vv[3]);
+    }
     if (TG && tid < TILE) gl[buf][tid] = R.b;
-    uint2* vd = reinterpret_cast<uint2*>(vl[buf] + swz_offset<VROW / 8>(tid >> 2, tid & 3));
-    vd[0] = make_uint2(vv[0], vv[1]);
-    vd[1] = make_uint2(vv[2], vv[3]);
   };
   auto contract = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < TILE / 16; ++s) {
-      const u32x4 kw = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * w, lane);
       const u32x4 kj = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, 32 * wave, lane);
-      const u32x4 vw = gather_tokens_32_swz<VROW / 8>(vl[buf], s * 16, 0, lane);
-      if (TG) {  // gates of this lane's tokens s*16 + 8g + 0..7, hi + lo (see gdn_gram_item)
-        const float4* gb = reinterpret_cast<const float4*>(&gl[buf][s * 16 + 8 * g]);
-        const float4 g0 = gb[0], g1 = gb[1];
-        u32x4 kh, kl2, vh, vl2;
-        scale_split_bf16x8(kw, g0, g1, kh, kl2);
-        scale_split_bf16x8(vw, g0, g1, vh, vl2);
-        accG = mfma32x32x16(as_bf16x8(kh), as_bf16x8(kj), accG);
-        accG = mfma32x32x16(as_bf16x8(kl2), as_bf16x8(kj), accG);
-        accU = mfma32x32x16(as_bf16x8(vh), as_bf16x8(kj), accU);
-        accU = mfma32x32x16(as_bf16x8(vl2), as_bf16x8(kj), accU);
-        continue;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4 kw = gather_tokens_32_swz<KROW / 8>(kl[buf], s * 16, RB * w + 32 * b, lane);
+        const u32x4 vw = gather_tokens_32_swz<VCH>(vl[buf], s * 16, 32 * b, lane);
+        if (TG) {  // gates of this lane's tokens s*16 + 8g + 0..7, hi + lo (see gdn_gram_item)
+          const float4* gb = reinterpret_cast<const float4*>(&gl[buf][s * 16 + 8 * g]);
+          const float4 g0 = gb[0], g1 = gb[1];
+          u32x4 kh, kl2, vh, vl2;
+          scale_split_bf16x8(kw, g0, g1, kh, kl2);
+          scale_split_bf16x8(vw, g0, g1, vh, vl2);
+          accG[b] = mfma32x32x16(as_bf16x8(kh), as_bf16x8(kj), accG[b]);
+          accG[b] = mfma32x32x16(as_bf16x8(kl2), as_bf16x8(kj), accG[b]);
+          accU[b] = mfma32x32x16(as_bf16x8(vh), as_bf16x8(kj), accU[b]);
+          accU[b] = mfma32x32x16(as_bf16x8(vl2), as_bf16x8(kj), accU[b]);
+        } else {
+          accG[b] = mfma32x32x16(as_bf16x8(kw), as_bf16x8(kj), accG[b]);
+          accU[b] = mfma32x32x16(as_bf16x8(vw), as_bf16x8(kj), accU[b]);
+        }
       }
-      accG = mfma32x32x16(as_bf16x8(kw), as_bf16x8(kj), accG);
-      accU = mfma32x32x16(as_bf16x8(vw), as_bf16x8(kj), accU);
     }
   };
 
@@ -379,25 +410,50 @@ __device__ __forceinline__ void gdn_gram_rows_item(
       __syncthreads();
     }
   }
+}
 
-  // block (w, wave) of the record: beta*G hi/lo planes and beta*U (layout as in gdn_gram_item)
-  const float bf = TG ? 1.0f : beta[bhf];
-  const float gs = c2 * bf, us = c * bf;
-  uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)bhf * kRecBytes);
+// Block (rows row0 .. row0 + 31, cols of wave `wave`) of beta*G as bf16 hi/lo
+// planes of a record (row-major, see gdn_gram_item), from the wave's
+// accumulator of that block times gs.
+__device__ __forceinline__ void store_rows_bg(uint16_t* Ghi, int row0, const floatx16& accG, float gs) {
+  constexpr int D = GD;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, col = lane & 31;
   uint16_t* Glo = Ghi + D * D;
-  float* Ud = reinterpret_cast<float*>(Glo + D * D);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int m = w * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+    const int m = row0 + 8 * (r >> 2) + 4 * g + (r & 3);
     uint16_t h, l;
     split_bf16(gs * accG[r], h, l);
     Ghi[m * D + wave * 32 + col] = h;
     Glo[m * D + wave * 32 + col] = l;
   }
+}
+
+template <int DI = GD, bool TG = false, bool PRO = false>
+__device__ __forceinline__ void gdn_gram_rows_item(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    uint8_t* __restrict__ rec, float c, float c2, int N, long item, uint8_t* lds_raw, TokLayout L,
+    Prologue P) {
+  constexpr int D = GD;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  const long bhf = item >> 2;
+  const int w = (int)(item & 3);
+  floatx16 accG[1], accU[1];
+  gram_rows_accumulate<DI, TG, PRO, 32>(k, v, beta, N, bhf, w, lds_raw, L, P, accG, accU);
+
+  // block (w, wave) of the record: beta*G hi/lo planes and beta*U (layout as in gdn_gram_item)
+  const float bf = TG ? 1.0f : beta[bhf];
+  const float gs = c2 * bf, us = c * bf;
+  uint16_t* Ghi = reinterpret_cast<uint16_t*>(rec + (size_t)bhf * kRecBytes);
+  float* Ud = reinterpret_cast<float*>(Ghi + 2 * D * D);
+  store_rows_bg(Ghi, 32 * w, accG[0], gs);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int m0 = w * 32 + 8 * q4 + 4 * g;
-    float4 u4 = make_float4(us * accU[4 * q4], us * accU[4 * q4 + 1], us * accU[4 * q4 + 2], us * accU[4 * q4 + 3]);
+    float4 u4 = make_float4(us * accU[0][4 * q4], us * accU[0][4 * q4 + 1], us * accU[0][4 * q4 + 2],
+                            us * accU[0][4 * q4 + 3]);
     *reinterpret_cast<float4*>(Ud + ((size_t)(m0 >> 2) * D + wave * 32 + col) * 4) = u4;
   }
 }
@@ -647,10 +703,13 @@ constexpr int kOutPitch = GD + 8;
 constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;
 
 // Work item `wg` = (frame of one head) * nco + token chunk: o = S_f q.
+// With wflags, the state is announced by nw flags equal to epoch: the item
+// issues its first query loads, then waits for them, then reads the state.
 template <int DI = GD, bool PRO = false>
 __device__ __forceinline__ void gdn_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const uint16_t* __restrict__ states,
-    int N, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
+    int N, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P,
+    const uint64_t* wflags = nullptr, int nw = 0, uint64_t epoch = 0, uint32_t* err = nullptr) {
   constexpr int D = GD;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -671,12 +730,15 @@ __device__ __forceinline__ void gdn_output_item(
   const uint16_t* hi = states + (size_t)bhf * 2 * D * D;
   const uint16_t* lo = hi + D * D;
   u32x4 ahi[8], alo[8];
+  auto load_state = [&]() {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const size_t off = (size_t)(wave * 32 + col) * D + s * 16 + g * 8;
-    ahi[s] = ld16(hi + off);
-    alo[s] = ld16(lo + off);
-  }
+    for (int s = 0; s < 8; ++s) {
+      const size_t off = (size_t)(wave * 32 + col) * D + s * 16 + g * 8;
+      ahi[s] = ld16(hi + off);
+      alo[s] = ld16(lo + off);
+    }
+  };
+  if (!wflags) load_state();
 
   const uint16_t* qf = q + L.base(bhf);
   uint16_t* of = o + L.base(bhf);
@@ -727,6 +789,10 @@ __device__ __forceinline__ void gdn_output_item(
   Regs R0, R1;
   fetch(R0, n0);
   fetch(R1, min(n0 + TILE, tlast));
+  if (wflags) {  // the state's producers run in this launch: query loads are in flight meanwhile
+    wait_all(wflags, nw, epoch, err);
+    load_state();
+  }
   stage(R0, 0, n0);
   fetch(R0, min(n0 + 2 * TILE, tlast));
   __syncthreads();
@@ -782,6 +848,149 @@ __device__ __forceinline__ void gdn_output_item(
   } else if (it < ntiles) {
     tile(it, R1, false);
   }
+}
+
+
+// Single-frame calls: kStepItems = 2 work items (head, w) per head whose only
+// frame is the call's.  Item w forms rows 64w .. 64w + 63 of the head's new
+// state and the outputs of token chunk w of kStepChunks:
+//  1. G and U rows 64w .. over all tokens (gram_rows_accumulate, two 32-row
+//     blocks per wave);
+//  2. beta G rows 64w .. to the head's record as hi/lo planes; flag
+//     gflags[4 head + w]; S0's rows 64w .. start loading into LDS;
+//  3. once the head's flags are up, S1 rows 64w .. =
+//     alpha (S0 rows - S0 rows . beta G) + beta U rows: wave j forms columns
+//     32j .. 32j + 31 from beta G's rows 32j .. (G is symmetric, so they are
+//     its columns) and its own accumulators U(rows, j);
+//  4. S1 rows 64w .. to S_out (fp32) and to the head's state as hi/lo planes,
+//     whole 16-byte stores through LDS; flag sflags[8 head + w];
+//  5. the output item of token chunk w, which issues its first query loads
+//     before waiting for the head's state flags.
+// The launch adds output-only items for the remaining chunks (gdn_output_item
+// waiting for the state flags), which prefetch their query tiles meanwhile.
+// No separate scan items, and U never leaves registers.  Two items per head
+// read K twice (the second time mostly from L2) and read V in whole 128-byte
+// lines.  The items of a head wait for each other; their block ids lie
+// within 16 of each other, so only items of the (at most 8) heads at the
+// dispatch frontier can wait for a partner not yet dispatched, and every
+// other waiting item's partner is running.  S_out may equal S0: each item
+// reads only its own rows of S0, before writing them.
+constexpr int kStepItems = 2, kStepRows = GD / kStepItems, kStepChunks = 4;
+constexpr int kStepPitch = GD + 4;  // fp32 LDS rows of S0 / S1
+constexpr int kStepLds = gram_rows_lds<kStepRows>() + kGateLds + kPrologueLds;
+static_assert(kStepRows * kStepPitch * 4 <= gram_rows_lds<kStepRows>(), "state rows fit in the tile LDS");
+
+template <int DI, bool TG, bool PRO>
+__device__ __forceinline__ void gdn_step_item(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
+    uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c, float c2,
+    int N, int chunko, long head, int w, uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err,
+    int rchunk, uint8_t* lds_raw, TokLayout L, Prologue P) {
+  constexpr int D = GD, RB = kStepRows, NB = RB / 32, NW = kStepItems, PITCH = kStepPitch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, col = lane & 31;
+  floatx16 accG[NB], accU[NB];
+  gram_rows_accumulate<DI, TG, PRO, RB>(k, v, beta, N, head, w, lds_raw, L, P, accG, accU);
+  const float bf = TG ? 1.0f : beta[head];
+  const uint16_t* Ghi = reinterpret_cast<const uint16_t*>(rec + (size_t)head * kRecBytes);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) store_rows_bg(const_cast<uint16_t*>(Ghi), RB * w + 32 * b, accG[b], c2 * bf);
+  publish(&gflags[head * 4 + w], epoch);  // also: every wave is past the tile loop, LDS is free
+
+  // S rows RB w .. as fp32 in LDS, [RB][PITCH], zero past DI
+  float(*Sl)[PITCH] = reinterpret_cast<float(*)[PITCH]>(lds_raw);
+  const bool with_s0 = S0 && rchunk <= 0;  // a reversed chunk starts from zero
+  const float a = with_s0 ? alpha[head] : 0.0f;
+  const float us = c * bf;
+  floatx16 s1[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s1[b][r] = us * accU[b][r];
+  if (with_s0) {
+    // 16-byte chunks: row i / 32, float4 i % 32 (dims 4 (i % 32) ..), loaded
+    // before the wait so that they arrive meanwhile
+    const float* S0h = S0 + (size_t)head * DI * DI;
+    constexpr int CPT = RB * (D / 4) / 256;  // chunks per thread (8)
+    float4 x[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int i = j * 256 + tid, row = RB * w + i / 32, d0 = 4 * (i % 32);
+      x[j] = *reinterpret_cast<const float4*>(S0h + (size_t)(row < DI ? row : 0) * DI + (d0 < DI ? d0 : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int i = j * 256 + tid, row = RB * w + i / 32, d0 = 4 * (i % 32);
+      *reinterpret_cast<float4*>(&Sl[i / 32][d0]) =
+          row < DI && d0 < DI ? x[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    wait_all(&gflags[head * 4], NW, epoch, err);  // (its barrier also orders the LDS writes)
+    // B operand: beta G(k, 32 wave + (lane & 31)) for k = 16 s + 8 g .. + 7,
+    // i.e. row 32 wave + (lane & 31) of the symmetric beta G
+    const uint16_t* Glo = Ghi + D * D;
+    u32x4 bh[8], bl[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const size_t off = (size_t)(32 * wave + col) * D + 16 * s + 8 * g;
+      bh[s] = ld16(Ghi + off);
+      bl[s] = ld16(Glo + off);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // A operand: S0 row RB w + 32 b + (lane & 31), dims 16 s + 8 g .. + 7, as hi + lo
+      floatx16 acc[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float* src = &Sl[32 * b + col][16 * s + 8 * g];
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+        const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+        const u32x4 ahi = u32x4{p0.x, p1.x, p2.x, p3.x}, alo = u32x4{p0.y, p1.y, p2.y, p3.y};
+        acc[0] = mfma32x32x16(as_bf16x8(ahi), as_bf16x8(bh[s]), acc[0]);
+        acc[1] = mfma32x32x16(as_bf16x8(ahi), as_bf16x8(bl[s]), acc[1]);
+        acc[1] = mfma32x32x16(as_bf16x8(alo), as_bf16x8(bh[s]), acc[1]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float s0 = Sl[32 * b + 8 * (r >> 2) + 4 * g + (r & 3)][32 * wave + col];
+        s1[b][r] = a * (s0 - (acc[0][r] + acc[1][r])) + s1[b][r];
+      }
+    }
+    __syncthreads();  // every wave has read S0's rows: S1 may replace them
+  }
+  // S1 rows through LDS, then whole 16-byte stores: the hi/lo planes of the
+  // state (8 entries per thread and row) and S_out (4 entries, rows and dims below DI)
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Sl[32 * b + 8 * (r >> 2) + 4 * g + (r & 3)][32 * wave + col] = s1[b][r];
+  __syncthreads();
+  uint16_t* Shi = states + (size_t)head * 2 * D * D;
+#pragma unroll
+  for (int j = 0; j < RB * (D / 8) / 256; ++j) {
+    const int i = j * 256 + tid, row = i / 16, c0 = 8 * (i % 16);
+    const float4 x0 = *reinterpret_cast<const float4*>(&Sl[row][c0]);
+    const float4 x1 = *reinterpret_cast<const float4*>(&Sl[row][c0 + 4]);
+    const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+    const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+    uint16_t* hp = Shi + (size_t)(RB * w + row) * D + c0;
+    st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
+    st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+  }
+  if (S_out) {
+    float* So = S_out + (size_t)head * DI * DI;
+#pragma unroll
+    for (int j = 0; j < RB * (D / 4) / 256; ++j) {
+      const int i = j * 256 + tid, row = RB * w + i / 32, d0 = 4 * (i % 32);
+      if (row < DI && d0 < DI)
+        *reinterpret_cast<float4*>(So + (size_t)row * DI + d0) = *reinterpret_cast<const float4*>(&Sl[i / 32][d0]);
+    }
+  }
+  publish(&sflags[head * 8 + w], epoch);  // its barrier: the output item may reuse the LDS
+  gdn_output_item<DI, PRO>(q, o, states, N, kStepChunks, chunko, head * kStepChunks + w, lds_raw, L, P,
+                           &sflags[head * 8], NW, epoch, err);
 }
 
 }  // namespace linscan

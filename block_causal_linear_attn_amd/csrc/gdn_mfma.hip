@@ -163,6 +163,38 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
   gdn_output_item<DI, PRO>(q, o, states, N, nco, chunko, bh * F * nco + r, lds, L, P);
 }
 
+// Single-frame calls (the chunk-causal denoising step): one item per (head,
+// 64-row block) does the gram rows, the state update of its rows and one of
+// the frame's kStepChunks output chunks (gdn_step_item); block id b < 2 bhp
+// serves head slot (b / 16) * 8 + b % 8 and row block (b / 8) % 2, so a head's
+// two items share an XCD and lie 8 block ids apart.  The output-only items of
+// the other chunks follow with the same mapping: they wait for the state
+// items, which have lower block ids.
+template <int DI, bool TG, bool PRO>
+__global__ __launch_bounds__(256, 2) void gdn_step_mfma128(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, uint16_t* __restrict__ o,
+    uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
+    float c2, long bh_n, long bhp, int N, int chunko, uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags,
+    uint64_t epoch, uint32_t* err, int rchunk, TokLayout L, Prologue P) {
+  constexpr int LDS = lds_max(kStepLds, kOutLds, 0);
+  __shared__ __align__(16) uint8_t lds[LDS];
+  constexpr int NO = kStepChunks - kStepItems;  // output-only items per head
+  const long b = blockIdx.x, nstep = bhp * kStepItems;
+  if (b < nstep) {
+    const long head = L.head_of_slot((b / (8 * kStepItems)) * 8 + b % 8);
+    if (head >= bh_n) return;  // a padded slot: its partner is padded too
+    gdn_step_item<DI, TG, PRO>(q, k, v, alpha, beta, o, rec, states, S0, S_out, c, c2, N, chunko, head,
+                               (int)((b / 8) % kStepItems), gflags, sflags, epoch, err, rchunk, lds, L, P);
+    return;
+  }
+  const long bo = b - nstep;
+  const long head = L.head_of_slot((bo / (8 * NO)) * 8 + bo % 8);
+  if (head >= bh_n) return;
+  gdn_output_item<DI, PRO>(q, o, states, N, kStepChunks, chunko, head * kStepChunks + kStepItems + (bo / 8) % NO,
+                           lds, L, P, &sflags[head * 8], kStepItems, epoch, err);
+}
+
 }  // namespace
 // The prologue does some work (the kernels take it as a template switch).
 static bool pro_on(const Prologue& P) { return P.on_k() || P.on_q(); }
@@ -192,6 +224,24 @@ hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nco, a.chunko, gflags,
                        sflags, epoch, err, a.rchunk, a.L, a.P);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_gdn_step_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags, uint64_t epoch,
+                                uint32_t* err, hipStream_t st) {
+  if (a.F != 1 || a.N <= 0 || a.nco != kStepChunks) return hipErrorInvalidValue;
+  const long grid = bhp * kStepChunks;
+  const float* gates = a.tg ? a.gate : a.beta;
+  return with_head_dim(a.D, [&](auto di) {
+    constexpr int DI = decltype(di)::value;
+    if (a.tg && pro_on(a.P)) return hipErrorInvalidValue;  // not instantiated: no entry point combines them
+    auto kern = a.tg ? gdn_step_mfma128<DI, true, false>
+                     : (pro_on(a.P) ? gdn_step_mfma128<DI, false, true> : gdn_step_mfma128<DI, false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
+                       (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.N, a.chunko, gflags, sflags,
+                       epoch, err, a.rchunk, a.L, a.P);
     return hipGetLastError();
   });
 }

@@ -124,6 +124,12 @@ int fused_lag(long slots, long items_per_step, int min_lag, int F);
 hipError_t launch_gdn_phased_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
                                   uint64_t epoch, uint32_t* err, hipStream_t st);
 
+//  GDN, single-frame calls (F = 1, N > 0): two items per head, each the gram
+//  rows, state rows and one output chunk, then two output-only items per
+//  head (nco = 4 chunks of chunko); workspace and flags as the phased launch.
+hipError_t launch_gdn_step_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, uint64_t* sflags,
+                                uint64_t epoch, uint32_t* err, hipStream_t st);
+
 // Generic (VALU) summary and output kernels of either path.
 hipError_t launch_summary_generic(const ScanArgs& a, hipStream_t st);
 hipError_t launch_output_generic(const ScanArgs& a, hipStream_t st);

@@ -283,7 +283,7 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
 }
 
 struct GdnPlan {
-  bool mfma, fused, phased;
+  bool mfma, fused, phased, step;
   int nc, chunk, nco, chunko;
   size_t partial_off, states_off, gflags_off, sflags_off, bytes;
 };
@@ -310,10 +310,14 @@ GdnPlan gdn_plan(const ls_shape* s, const Dims& d, bool fused_ok) {
   } else {
     plan_chunks(d.bhf, s->N, 1024, 1024, 64, &p.nc, &p.chunk);
   }
-  // output items: about 2048, except for one-frame phased calls (the chunk
-  // step, B4 H24 N920: 5 chunks of 192 tokens instead of 8 of 128 ran 47.4 ->
-  // 45.6 us, each item loading the frame's 64 KB state once for fewer tokens)
-  plan_chunks(d.bhf, s->N, p.phased && s->F == 1 ? 576 : 2048, 64, 64, &p.nco, &p.chunko);
+  // output items: about 2048; one-frame calls run the step launch, whose
+  // items output the frame in four chunks
+  plan_chunks(d.bhf, s->N, 2048, 64, 64, &p.nco, &p.chunko);
+  p.step = p.phased && s->F == 1;
+  if (p.step) {
+    p.nco = 4;
+    p.chunko = (s->N + 3) / 4;
+  }
   // records and per-frame states of the MFMA kernels always cover 128 dims
   const size_t Dw = p.mfma ? 128 : (size_t)s->D;
   const size_t dd = Dw * Dw;
@@ -742,6 +746,10 @@ static ls_status gdn_forward(const ls_shape* s, const ls_strides* strides, const
       return hip_check(timed("gdn_fused", hs, [&] {
                          return linscan::launch_gdn_fused_mfma(a, bhp, gflags, sflags, epoch, err, hs);
                        }), "gdn fused");
+    if (p.step)
+      return hip_check(timed("gdn_step", hs, [&] {
+                         return linscan::launch_gdn_step_mfma(a, bhp, gflags, sflags, epoch, err, hs);
+                       }), "gdn step");
     return hip_check(timed("gdn_phased", hs, [&] {
                        return linscan::launch_gdn_phased_mfma(a, bhp, gflags, sflags, epoch, err, hs);
                      }), "gdn phased");

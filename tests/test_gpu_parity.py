@@ -118,6 +118,11 @@ GDN_CASES = [
     (1, 2, 1, 300, 128, "bf16", True, True),    # one frame, two token chunks
     (1, 70, 3, 130, 128, "bf16", True, True),   # 70 heads, a three-frame chain
     (1, 1, 1, 1, 128, "bf16", True, True),      # one token, one frame
+    # single-frame step launch: four items per head swap their rows of beta*G and of the state
+    (1, 37, 1, 257, 128, "bf16", True, True),   # odd head count (padded slots), ragged quarters
+    (1, 5, 1, 3, 128, "bf16", True, True),      # fewer tokens than items: empty output quarters
+    (2, 3, 1, 920, 112, "bf16", True, True),    # head dim 112
+    (1, 9, 1, 130, 128, "bf16", False, True),   # raw keys (beta*G not small beside the identity)
 ]
 
 
@@ -146,6 +151,7 @@ TG_CASES = [
     (1, 2, 3, 80, 64, "bf16", True),        # generic bf16 kernels
     (1, 2, 3, 40, 32, "fp32", True),        # generic fp32 kernels
     (1, 1, 2, 1, 128, "bf16", False),       # one token per frame
+    (1, 11, 1, 333, 128, "bf16", True),     # single-frame step launch, odd head count
 ]
 
 
@@ -193,6 +199,8 @@ RV_CASES = [
     (1, 2, 9, 200, 128, "bf16", 1),     # one-frame chunks: no history
     (1, 2, 5, 64, 64, "bf16", 2),       # generic bf16 kernels
     (1, 2, 5, 40, 32, "fp32", 4),       # generic fp32 kernels
+    (1, 13, 1, 150, 128, "bf16", 1),    # a single frame: the step launch, S = beta U
+    (2, 2, 1, 50, 112, "bf16", 4),      # a single frame shorter than its chunk, head dim 112
 ]
 
 
@@ -377,7 +385,8 @@ def test_chunked_rollout_through_carry_equals_one_call(ls, gen, oracle_mod):
 
 
 # --------------------------------------------------------------------------- single-launch paths
-@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased", "gdn_token_gate", "gdn_reversed"])
+@pytest.mark.parametrize("op", ["relu", "relu_wide", "gdn", "gdn_phased", "gdn_step", "gdn_token_gate",
+                                "gdn_reversed"])
 def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     """The one-launch paths hand data between work items through flags with
     bounded waits; the workspace's fault word must stay zero and results match."""
@@ -396,6 +405,10 @@ def test_single_launch_fault_word_stays_clear(ls, gen, oracle_mod, op):
     elif op == "gdn_phased":  # 80 heads: the phased launch
         x = gen.gdn_inputs(2, 40, 2, 200, 128, "bf16", seed=33)
         shp = ls.ls_shape(2, 40, 2, 200, 128, 1)
+        need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
+    elif op == "gdn_step":  # one frame of 74 heads: the step launch, items waiting for their partners
+        x = gen.gdn_inputs(2, 37, 1, 333, 128, "bf16", seed=37)
+        shp = ls.ls_shape(2, 37, 1, 333, 128, 1)
         need = ls.lib.ls_gdn_frame_workspace_size(ls.ctypes.byref(shp))
     elif op == "gdn_reversed":  # reversed scan in chunks of 4, frame-interleaved launch
         x = gen.gdn_inputs(1, 5, 9, 333, 128, "bf16", seed=36)
@@ -625,6 +638,7 @@ def test_relu_prologue_parity(ls, gen, oracle_mod, H, F, N, D, dt, qw, kw):
     (1, 40, 2, 130, 128, "bf16", True, True, True, False),    # phased launch
     (2, 2, 3, 97, 112, "bf16", False, True, False, True),     # head dim 112: RMSNorm + L2 of keys
     (1, 2, 3, 200, 128, "bf16", False, False, True, False),   # ReLU alone
+    (1, 6, 1, 300, 128, "bf16", True, True, True, True),      # single-frame step launch, whole prologue
     (1, 2, 3, 80, 64, "bf16", True, True, True, True),        # generic bf16 kernels
     (1, 2, 3, 40, 32, "fp32", True, True, True, True),        # generic fp32 kernels
 ])
@@ -692,6 +706,7 @@ def test_gdn_prologue_matches_plain_scan_bitwise(ls, gen, oracle_mod, B, H, F, N
     (1, 3, 4, 300, 128, "bf16", True, True, True, True, 16, 0),      # frame-interleaved launch, whole prologue
     (1, 40, 2, 130, 128, "bf16", False, False, False, False, 0, 0),  # phased launch, token table only
     (1, 2, 3, 200, 128, "bf16", False, True, False, True, 64, 5),    # frame table only, rows from 5
+    (1, 5, 1, 230, 112, "bf16", True, True, True, True, 8, 3),       # single-frame step launch
     (2, 2, 3, 97, 112, "bf16", True, True, False, True, 8, 2),       # head dim 112
     (1, 2, 3, 80, 64, "bf16", True, True, True, True, 8, 1),         # generic bf16 kernels
     (1, 2, 3, 40, 32, "fp32", True, True, True, True, 4, 0),         # generic fp32 kernels
