@@ -698,6 +698,227 @@ __device__ __forceinline__ void gdn_scan_item(
   }
 }
 
+// The scan item of the single launches (fused and phased), rows r0 .. r0 + 31
+// of head `head`'s state over all F frames, with the next frame's record
+// requested while the current frame is computed.  beta G of a frame (hi and
+// lo planes, 64 KB) comes straight from memory into LDS
+// (global_load_lds_dwordx4, no registers), beta U's rows into a second set
+// of registers; each wave checks whether the next frame's record flags are
+// up once it has read the current frame's operands and, if so, requests its
+// quarter of the next record right away, else at the next frame's start.  The
+// frame's compute and state stores then overlap the record's latency, which
+// otherwise sits on the chain once per frame.  Waves decide on their own (no
+// barrier depends on the choice); every wave waits for its own loads and then
+// for all waves before the operands are read.
+//
+// LDS: the state rows, fp32 [32][128] with float4 chunks XOR-swizzled by row
+// (single buffered: read as A operands at a frame's start, rewritten at its
+// end), and one frame's beta G, bf16 [hi, lo][128][128] with 16-byte chunks
+// XOR-swizzled by row so that the 16 rows one quarter-wave reads fall on
+// distinct banks.  80 KB in all: two items per CU.  The decays come from
+// scalar loads one frame ahead.  nfl: gram flags per frame (1, or 4 when the
+// record is written in four parts).  rchunk: as gdn_scan_item.
+constexpr int kScanPfRows = 32;
+constexpr int kScanPfLds = kScanPfRows * GD * 4 + 2 * GD * GD * 2;
+
+template <int DI = GD>
+__device__ __forceinline__ void gdn_scan_item_pf(
+    const uint8_t* __restrict__ rec, const float* __restrict__ alpha, const float* S0,
+    uint16_t* __restrict__ states, float* S_out, long head, int r0, int F, uint8_t* lds_raw,
+    const uint64_t* gflags, uint64_t* sflags, uint64_t epoch, uint32_t* err, int nfl, int rchunk) {
+  constexpr int D = GD, RB = kScanPfRows, SB = RB / 16;
+  float* Ss = reinterpret_cast<float*>(lds_raw);
+  uint8_t* Gl = lds_raw + RB * D * 4;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  // element (m, n) of the LDS state rows
+  auto sidx = [](int m, int n) { return m * D + (((n >> 2) ^ (m & 15)) << 2) + (n & 3); };
+  const size_t hf0 = (size_t)head * F;
+  auto phys = [&](int f) {
+    if (rchunk <= 0) return f;
+    const int c0 = f / rchunk * rchunk;
+    return c0 + min(rchunk, F - c0) - 1 - (f - c0);
+  };
+  // the decay of step f (a reversed chunk's first step starts from zero)
+  auto decay = [&](int f) { return rchunk > 0 && f % rchunk == 0 ? 0.0f : alpha[hf0 + phys(f)]; };
+
+  float s[SB][2][4];
+#pragma unroll
+  for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * sb + 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+        s[sb][nb][r] = S0 && r0 + m < DI && n < DI ? S0[(size_t)head * DI * DI + (size_t)(r0 + m) * DI + n] : 0.0f;
+        Ss[sidx(m, n)] = s[sb][nb][r];
+      }
+
+  typedef float UT[SB][2][4];
+  // this wave's quarter of frame pf's beta G into LDS (chunk P of the 4096
+  // 16-byte chunks: plane P / 2048, row (P / 16) % 128, swizzled chunk P % 16)
+  auto request_bg = [&](int pf) {
+    const uint8_t* base = rec + (hf0 + pf) * kRecBytes;
+    // rolled: the loads write LDS, not registers, so nothing waits on them here
+#pragma unroll 1
+    for (int j = 0; j < 16; ++j) {
+      const int P = wave * 1024 + j * 64 + lane;
+      const int plane = P >> 11, n = (P >> 4) & (D - 1), c = (P & 15) ^ (n & 15);
+      __builtin_amdgcn_global_load_lds(base + (size_t)plane * D * D * 2 + (size_t)n * D * 2 + c * 16,
+                                       (__attribute__((address_space(3))) void*)(Gl + (wave * 1024 + j * 64) * 16),
+                                       16, 0, 0);
+    }
+  };
+  auto request_u = [&](int pf, UT& u) {
+    const float* U = reinterpret_cast<const float*>(rec + (hf0 + pf) * kRecBytes + (size_t)4 * D * D);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = 32 * wave + 16 * nb + lr;
+        const float4 u4 = *reinterpret_cast<const float4*>(U + ((size_t)(((r0 + 16 * sb) >> 2) + lg) * D + n) * 4);
+        u[sb][nb][0] = u4.x;
+        u[sb][nb][1] = u4.y;
+        u[sb][nb][2] = u4.z;
+        u[sb][nb][3] = u4.w;
+      }
+  };
+  // the record flags of frame pf are all up (wave-uniform)
+  auto ready = [&](int pf) {
+    bool ok = true;
+    if (lane < nfl) ok = __hip_atomic_load(&gflags[(hf0 + pf) * nfl + lane], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    return __ballot(!ok) == 0;
+  };
+  auto wave_wait = [&](int pf) {
+    int spins = 0;
+    while (!ready(pf)) {
+      if (++spins > kSpinLimit) {
+        if (lane == 0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  };
+  auto store_state = [&](int pf) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb) {
+      const int row = 16 * sb + (tid >> 4), c0 = 8 * (tid & 15);
+      const float4 x0 = *reinterpret_cast<const float4*>(&Ss[sidx(row, c0)]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&Ss[sidx(row, c0 + 4)]);
+      const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+      const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+      uint16_t* hp = states + (hf0 + pf) * 2 * D * D + (size_t)(r0 + row) * D + c0;
+      st16(hp, u32x4{p0.x, p1.x, p2.x, p3.x});
+      st16(hp + D * D, u32x4{p0.y, p1.y, p2.y, p3.y});
+    }
+  };
+
+  UT U0, U1;
+  bool asked = false;  // this wave has requested the next frame's record
+  float a_next = 0.0f;
+  if (F > 0) {
+    wave_wait(phys(0));
+    request_bg(phys(0));
+    request_u(phys(0), U0);
+    a_next = decay(0);
+  }
+  // step f: its record was requested into LDS and `u`; `un` takes the next one
+  auto frame = [&](int f, UT& u, UT& un) {
+    const int pf = phys(f);
+    const float a = a_next;
+    __builtin_amdgcn_s_waitcnt(0);  // this frame's record, and the previous frame's state stores
+    if (f > 0 && tid == 0)
+      __hip_atomic_store(&sflags[(hf0 + phys(f - 1)) * 8 + r0 / RB], epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    // S_{f-1} (this item's rows) times beta G: per k-step s4, B operands beta
+    // G(k, n) for k = 32 s4 + 8 lg .. + 7, n = 32 wave + 16 nb + lr (G is
+    // symmetric: row n's chunk k / 8) and A operands, the rows of S_{f-1}
+    // split into bf16 hi + lo, straight from LDS
+    floatx4 acc[SB][2][2];
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[sb][nb][0] = acc[sb][nb][1] = floatx4{};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      u32x4 bhi[2], blo[2], ahi[SB], alo[SB];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int n = 32 * wave + 16 * nb + lr, pc = (4 * s4 + lg) ^ (n & 15);
+        bhi[nb] = *reinterpret_cast<const u32x4*>(Gl + (size_t)n * D * 2 + pc * 16);
+        blo[nb] = *reinterpret_cast<const u32x4*>(Gl + (size_t)(D + n) * D * 2 + pc * 16);
+      }
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int m = 16 * sb + lr, n0 = 32 * s4 + 8 * lg;
+        const float4 x0 = *reinterpret_cast<const float4*>(&Ss[sidx(m, n0)]);
+        const float4 x1 = *reinterpret_cast<const float4*>(&Ss[sidx(m, n0 + 4)]);
+        const uint2 p0 = split_bf16x2(x0.x, x0.y), p1 = split_bf16x2(x0.z, x0.w);
+        const uint2 p2 = split_bf16x2(x1.x, x1.y), p3 = split_bf16x2(x1.z, x1.w);
+        ahi[sb] = u32x4{p0.x, p1.x, p2.x, p3.x};
+        alo[sb] = u32x4{p0.y, p1.y, p2.y, p3.y};
+      }
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          acc[sb][nb][0] = mfma16x16x32(as_bf16x8(ahi[sb]), as_bf16x8(bhi[nb]), acc[sb][nb][0]);
+          acc[sb][nb][1] = mfma16x16x32(as_bf16x8(ahi[sb]), as_bf16x8(blo[nb]), acc[sb][nb][1]);
+          acc[sb][nb][1] = mfma16x16x32(as_bf16x8(alo[sb]), as_bf16x8(bhi[nb]), acc[sb][nb][1]);
+        }
+    }
+    __syncthreads();  // every wave is done with beta G's buffer and the state rows
+    if (f + 1 < F) {
+      const int pn = phys(f + 1);
+      asked = ready(pn);
+      if (asked) {
+        request_bg(pn);
+        request_u(pn, un);
+      }
+      a_next = decay(f + 1);
+    }
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * sb + 4 * lg + r, n = 32 * wave + 16 * nb + lr;
+          s[sb][nb][r] = a * (s[sb][nb][r] - (acc[sb][nb][0][r] + acc[sb][nb][1][r])) + u[sb][nb][r];
+          Ss[sidx(m, n)] = s[sb][nb][r];
+        }
+    __syncthreads();
+    store_state(pf);
+    if (f + 1 < F && !asked) {  // the next record was not ready: wait for it now
+      const int pn = phys(f + 1);
+      wave_wait(pn);
+      request_bg(pn);
+      request_u(pn, un);
+    }
+  };
+  int f = 0;
+  for (; f + 2 <= F; f += 2) {
+    frame(f, U0, U1);
+    frame(f + 1, U1, U0);
+  }
+  if (f < F) frame(f, U0, U1);
+  if (F > 0) publish(&sflags[(hf0 + phys(F - 1)) * 8 + r0 / RB], epoch);
+  if (S_out) {
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0 + 16 * sb + 4 * lg + r, cl = 32 * wave + 16 * nb + lr;
+          if (row < DI && cl < DI) S_out[(size_t)head * DI * DI + (size_t)row * DI + cl] = s[sb][nb][r];
+        }
+  }
+}
+
 constexpr int kOutPitch = GD + 8;
 // Q tiles (double buffered) and output staging tiles (double buffered), bf16
 constexpr int kOutLds = 2 * 64 * kOutPitch * 2 + 2 * 64 * kOutPitch * 2;

@@ -68,9 +68,11 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     float c2, long bh_n, long bhp, int F, int N, int nc, int chunk, int nco, int chunko, int lag,
     uint64_t* __restrict__ gflags, uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk,
     TokLayout L, Prologue P) {
-  constexpr int kSL = scan_lds_bytes<kFusedRB>();
+  // one record per frame: the prefetching scan item; several: the chunk-summing one
+  constexpr int kSL = MULTI ? scan_lds_bytes<kFusedRB>() : kScanPfLds;
   constexpr int LDS = lds_max(kGramLds + kGateLds + kPrologueLds, kSL, kOutLds);
   constexpr int NRB = kGdnFusedRowBlocks;
+  static_assert(MULTI || kFusedRB == kScanPfRows, "prefetching scan items cover 32 rows");
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
   const long nscan = (bhp / 8) * 8 * NRB;
@@ -78,8 +80,12 @@ __global__ __launch_bounds__(256, 2) void gdn_fused_mfma128(
     // eight heads x NRB row blocks per group; a head's row blocks keep its XCD
     const long head = L.head_of_slot((b / (8 * NRB)) * 8 + (b % 8));
     if (head >= bh_n) return;
-    gdn_scan_item<MULTI, true, kFusedRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
-                                         F, nc, lds, gflags, sflags, epoch, err, 0, rchunk);
+    if (MULTI)
+      gdn_scan_item<MULTI, true, kFusedRB, DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB,
+                                               F, nc, lds, gflags, sflags, epoch, err, 0, rchunk);
+    else
+      gdn_scan_item_pf<DI>(rec, alpha, S0, states, S_out, head, (int)((b / 8) % NRB) * kFusedRB, F, lds, gflags,
+                           sflags, epoch, err, 1, rchunk);
     return;
   }
   const long s = b - nscan;
@@ -133,9 +139,8 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     uint8_t* __restrict__ rec, uint16_t* __restrict__ states, const float* S0, float* S_out, float c,
     float c2, long bh_n, long bhp, int F, int N, int nco, int chunko, uint64_t* __restrict__ gflags,
     uint64_t* __restrict__ sflags, uint64_t epoch, uint32_t* err, int rchunk, TokLayout L, Prologue P) {
-  constexpr int RB = 32, NRB = GD / RB;
-  constexpr int kSL = scan_lds_bytes<RB>();
-  constexpr int LDS = lds_max(kGramRowsLds + kGateLds + kPrologueLds, kSL, kOutLds);
+  constexpr int RB = kScanPfRows, NRB = GD / RB;
+  constexpr int LDS = lds_max(kGramRowsLds + kGateLds + kPrologueLds, kScanPfLds, kOutLds);
   __shared__ __align__(16) uint8_t lds[LDS];
   const long b = blockIdx.x;
   const long ngram = bhp * F * 4, nscan = bhp * NRB;
@@ -151,8 +156,8 @@ __global__ __launch_bounds__(256, 2) void gdn_phased_mfma128(
     const long bs = b - ngram;
     const long head = L.head_of_slot(bs % bhp);
     if (head >= bh_n) return;
-    gdn_scan_item<false, true, RB, DI>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, 1, lds, gflags,
-                                       sflags, epoch, err, 4, rchunk);
+    gdn_scan_item_pf<DI>(rec, alpha, S0, states, S_out, head, (int)(bs / bhp) * RB, F, lds, gflags, sflags, epoch,
+                         err, 4, rchunk);
     return;
   }
   const long bo = b - ngram - nscan;
