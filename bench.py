@@ -250,12 +250,14 @@ def main():
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
     v480 = None if args.no_480p else time_480p(torch, ls, inputs)
-    d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs)
-    tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg)
-    rev = None if args.no_reversed else time_reversed(torch, ls, g, wg)
+    # GDN side measurements run each timed call right after the rollout, as in
+    # the step: back to back, GDN calls hold the shader clock lower
+    d112 = None if args.no_head_dim_112 else time_head_dim_112(torch, ls, inputs, part_video)
+    tgate = None if args.no_token_gate else time_token_gate(torch, ls, inputs, g, wg, part_video)
+    rev = None if args.no_reversed else time_reversed(torch, ls, g, wg, part_video)
     conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
-    strided = None if args.no_strided else time_strided(torch, ls, calls[0], g)
-    pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g)
+    strided = None if args.no_strided else time_strided(torch, ls, calls[0], g, part_video)
+    pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g, part_video)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     fault = ls.ls_fault_word(dev)
@@ -356,7 +358,7 @@ def device_copy_gbs(torch, nbytes=1 << 30, reps=5):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
-def time_head_dim_112(torch, ls, inputs, reps=3):
+def time_head_dim_112(torch, ls, inputs, prelude, reps=3):
     """Both parts of the step at head dim 112 (not part of the step).
 
     The ReLU rollout (B1 H20 D112 N3600, 25 calls with state carry) and the
@@ -391,6 +393,8 @@ def time_head_dim_112(torch, ls, inputs, reps=3):
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in ev:
+            if fn is wm:
+                prelude()  # the GDN call after a rollout, as in the step
             a.record()
             fn()
             b.record()
@@ -404,9 +408,10 @@ def time_head_dim_112(torch, ls, inputs, reps=3):
     return res
 
 
-def time_token_gate(torch, ls, inputs, g, wg, reps=3):
+def time_token_gate(torch, ls, inputs, g, wg, prelude, reps=3):
     """The GDN part with one update gate per token (same inputs, gates drawn
-    per token), timed over `reps` calls after one warm-up call."""
+    per token), timed over `reps` calls after one warm-up call, each after
+    `prelude` (untimed), as in the step."""
     dev = torch.device("cuda:0")
     bt = inputs.token_gates(wg.B, wg.H, wg.F, wg.N, seed=wg.seed, device=dev)
     out = torch.empty_like(g["q"])
@@ -419,6 +424,7 @@ def time_token_gate(torch, ls, inputs, g, wg, reps=3):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
+        prelude()
         a.record()
         call()
         b.record()
@@ -431,9 +437,9 @@ def time_token_gate(torch, ls, inputs, g, wg, reps=3):
             "workload": "B1 H24 D128 F181 N920 bf16, one update gate per token"}
 
 
-def time_reversed(torch, ls, g, wg, chunk=8, reps=3):
+def time_reversed(torch, ls, g, wg, prelude, chunk=8, reps=3):
     """The GDN part through the reversed scan that resets every `chunk` frames,
-    timed over `reps` calls after one warm-up call."""
+    timed over `reps` calls after one warm-up call, each after `prelude`."""
     out = torch.empty_like(g["q"])
 
     def call():
@@ -443,6 +449,7 @@ def time_reversed(torch, ls, g, wg, chunk=8, reps=3):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
+        prelude()
         a.record()
         call()
         b.record()
@@ -491,42 +498,50 @@ def time_temporal_conv(torch, ls, reps=5):
             "workload": "B1 F10 N3600 C2240 bf16, one block of 10 frames with a carried frame"}
 
 
-def time_strided(torch, ls, relu_call, g, reps=4):
-    """One 10-frame ReLU call of the rollout and the GDN call with q, k, v, o
-    stored [B][F][N][H][D] (heads interleaved in every token row), against
-    the same calls on the packed layout; mean kernel time from the library's
-    per-launch events."""
+def kernel_us(torch, ls, fn, name, reps, prelude=None):
+    """Mean duration of kernel `name` over `reps` calls of fn (after one
+    warm-up call), from the library's per-launch events; with a prelude,
+    each call follows it (untimed), as the GDN call follows the rollout in
+    the step: back-to-back GDN calls run at a lower shader clock."""
+    fn()
+    torch.cuda.synchronize()
+    ls.ls_profile_begin()
+    for _ in range(reps):
+        if prelude is not None:
+            prelude()
+        fn()
+    torch.cuda.synchronize()
+    n, ms = ls.ls_profile_end()[name]
+    return round(1e3 * ms / n, 2)
+
+
+def time_strided(torch, ls, relu_call, g, prelude, reps=4):
+    """One 10-frame ReLU call of the rollout and the GDN call (after the
+    rollout, as in the step) with q, k, v, o stored [B][F][N][H][D] (heads
+    interleaved in every token row), against the same calls on the packed
+    layout; mean kernel time from the library's per-launch events."""
     def bshd(x):
         return x.permute(0, 2, 3, 1, 4).contiguous().permute(0, 3, 1, 2, 4)
-
-    def kernel_us(fn, name):
-        fn()
-        torch.cuda.synchronize()
-        ls.ls_profile_begin()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        n, ms = ls.ls_profile_end()[name]
-        return round(1e3 * ms / n, 2)
 
     res = {}
     r = relu_call
     rs = {n: bshd(r[n]) for n in ("q", "k", "v")}
     res["relu_h70_d32_10_frames_us"] = {
-        "packed": kernel_us(lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused"),
-        "bshd": kernel_us(lambda: ls.ls_relu_block_forward_strided(rs["q"], rs["k"], rs["v"]), "relu_fused")}
+        "packed": kernel_us(torch, ls, lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused", reps),
+        "bshd": kernel_us(torch, ls, lambda: ls.ls_relu_block_forward_strided(rs["q"], rs["k"], rs["v"]),
+                          "relu_fused", reps)}
     del rs
     gs = {n: bshd(g[n]) for n in ("q", "k", "v")}
     res["gdn_h24_d128_181_frames_us"] = {
-        "packed": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"]),
-                            "gdn_fused"),
-        "bshd": kernel_us(lambda: ls.ls_gdn_frame_forward_strided(gs["q"], gs["k"], gs["v"], g["alpha"], g["beta"]),
-                          "gdn_fused")}
+        "packed": kernel_us(torch, ls, lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"]),
+                            "gdn_fused", reps, prelude),
+        "bshd": kernel_us(torch, ls, lambda: ls.ls_gdn_frame_forward_strided(gs["q"], gs["k"], gs["v"], g["alpha"],
+                                                                             g["beta"]), "gdn_fused", reps, prelude)}
     del gs
     return res
 
 
-def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
+def time_prologue(torch, ls, inputs, relu_call, g, prelude, reps=4):
     """The per-token prologue fused into the load stage: one 10-frame ReLU call
     of the rollout with RMSNorm (weights) on q and k, and the GDN call with
     RMSNorm on q and k, ReLU and L2 keys (each once more with a 3D rotary
@@ -538,16 +553,6 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
 
-    def kernel_us(fn, name):
-        fn()
-        torch.cuda.synchronize()
-        ls.ls_profile_begin()
-        for _ in range(reps):
-            fn()
-        torch.cuda.synchronize()
-        n, ms = ls.ls_profile_end()[name]
-        return round(1e3 * ms / n, 2)
-
     res = {}
     r = relu_call
     H, D = r["q"].shape[1], r["q"].shape[-1]
@@ -555,11 +560,11 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
     # 3D rotary embedding: 4 pairs by frame, 12 by the 45 x 80 latent grid
     fr, tr = inputs.rope_tables(r["q"].shape[2], r["q"].shape[3], 80, D, 4, device=dev)
     res["relu_h70_d32_10_frames_rmsnorm_qk_us"] = {
-        "plain": kernel_us(lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused"),
-        "fused_prologue": kernel_us(lambda: ls.ls_relu_block_forward_prologue(r["q"], r["k"], r["v"], wq, wk,
-                                                                               norm_eps=1e-6), "relu_fused"),
-        "fused_prologue_with_3d_rope": kernel_us(lambda: ls.ls_relu_block_forward_prologue(
-            r["q"], r["k"], r["v"], wq, wk, norm_eps=1e-6, rope=(fr, tr, 4, 0)), "relu_fused")}
+        "plain": kernel_us(torch, ls, lambda: ls.ls_relu_block_forward(r["q"], r["k"], r["v"]), "relu_fused", reps),
+        "fused_prologue": kernel_us(torch, ls, lambda: ls.ls_relu_block_forward_prologue(
+            r["q"], r["k"], r["v"], wq, wk, norm_eps=1e-6), "relu_fused", reps),
+        "fused_prologue_with_3d_rope": kernel_us(torch, ls, lambda: ls.ls_relu_block_forward_prologue(
+            r["q"], r["k"], r["v"], wq, wk, norm_eps=1e-6, rope=(fr, tr, 4, 0)), "relu_fused", reps)}
     del fr, tr
     H, D = g["q"].shape[1], g["q"].shape[-1]
     wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
@@ -589,15 +594,17 @@ def time_prologue(torch, ls, inputs, relu_call, g, reps=4):
         ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk, norm_eps=1e-6,
                                          relu=True, l2_keys=True, out=out, rope=(fcs, tcs, 16, 0))
 
-    gdn = {"plain": kernel_us(lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out),
-                              "gdn_fused"),
-           "fused_prologue": kernel_us(fused, "gdn_fused"),
-           "fused_prologue_with_3d_rope": kernel_us(fused_rope, "gdn_fused")}
+    gdn = {"plain": kernel_us(torch, ls, lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"],
+                                                                         g["beta"], out=out),
+                              "gdn_fused", reps, prelude),
+           "fused_prologue": kernel_us(torch, ls, fused, "gdn_fused", reps, prelude),
+           "fused_prologue_with_3d_rope": kernel_us(torch, ls, fused_rope, "gdn_fused", reps, prelude)}
     # the torch variant last: its fp32 temporaries come and go after the library's timings
     unfused()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
+        prelude()
         a.record()
         unfused()
         b.record()
