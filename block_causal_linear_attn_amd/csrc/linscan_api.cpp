@@ -273,12 +273,15 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   // every earlier frame (35 heads x 10 frames x 3600 tokens: 166 -> 153 us)
   plan_chunks(d.bhf, s->N, p.wide ? 1000 : s->D == 64 ? 512 : 1536, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
   // wide heads keep one cumulative record per frame, 128 dims wide, then one
-  // record per summary part past the first, and no init copy
+  // record per summary part, and no init copy; their flags: four row blocks
+  // per cumulative record, then one per part
   const size_t out = p.wide ? (size_t)128 * 128 + 128 : (size_t)s->D * s->D + s->D;
+  const size_t recs = p.wide ? (size_t)d.bhf * (p.nc + 1) : (size_t)d.bhf * p.nc;
+  const size_t nflags = p.wide ? (size_t)d.bhf * (p.nc + 4) : (size_t)d.bhf * p.nc;
   p.partial_off = kHeaderBytes;
-  p.init_off = align_up(p.partial_off + (size_t)d.bhf * p.nc * out * sizeof(float), 256);
+  p.init_off = align_up(p.partial_off + recs * out * sizeof(float), 256);
   p.flags_off = align_up(p.init_off + (p.wide ? 0 : (size_t)d.bh * out * sizeof(float)), 256);
-  p.bytes = align_up(p.flags_off + (p.fused ? (size_t)d.bhf * p.nc * sizeof(uint64_t) : 0), 256);
+  p.bytes = align_up(p.flags_off + (p.fused ? nflags * sizeof(uint64_t) : 0), 256);
   return p;
 }
 
@@ -371,10 +374,10 @@ hipError_t timed(const char* name, hipStream_t st, Fn&& launch) {
       b = prof_event();
     }
   }
-  if (a && b) hipEventRecord(a, st);
+  if (a && b) (void)hipEventRecord(a, st);
   hipError_t e = launch();
   if (a && b) {
-    hipEventRecord(b, st);
+    (void)hipEventRecord(b, st);
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_records.push_back({name, a, b});
   }

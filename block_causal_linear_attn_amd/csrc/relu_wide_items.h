@@ -15,13 +15,14 @@
 // one dimension per MFMA operand with two LDS transpose reads.  dz = 1^T phi(K)
 // comes from a padding row (head dim 112: value dim 112 is set to 1, so row
 // 112 of dS is dz) or, at head dim 128, from one more MFMA with an all-ones
-// A operand.  Part 0 of a frame then adds the other parts' sums and the
-// cumulative state of the previous frame (the initial state for frame 0) and
-// writes the cumulative state of its own frame: the frames of a head form a
-// chain of short hand-offs (about 2 us each), and no later reader has to sum
-// partials.  (A decoupled look-back
-// over earlier frames' own sums was measured slower: every item then reads
-// several 66 KB records from L2 at once.)
+// A operand.  Every part writes its sums as a record.
+//
+// Prefix items, four per head (32 rows of the state each), add the parts of
+// each frame to a running sum held in registers and write the cumulative
+// state of every frame, so no later reader has to sum partials and a frame's
+// hand-off moves 16 KB per item instead of reloading the previous 66 KB
+// state.  (A decoupled look-back over earlier frames' own sums was measured
+// slower: every item then reads several 66 KB records from L2 at once.)
 //
 // Output item, one per (head, frame, token chunk): reads the one cumulative
 // state its frame sees (the last frame of its block), splits S into bf16 hi +
@@ -45,22 +46,15 @@ constexpr int kReluWideOutPitch = kReluWide + 8;
 constexpr int kReluWideOutLds = 4 * 64 * kReluWideOutPitch * 2 + 2 * 64 * 4;
 
 // Summary item `part` (of np) of frame f of head bh.  The frame's tiles of 64
-// tokens are split into np runs of consecutive tiles, one per part.  Part
-// p > 0 writes the sums over its run to parts[(bh * F + f) * (np - 1) + p - 1]
-// (a record in accumulator order) and publishes the flag of the same index in
-// pflags.  Part 0 sums its own run, adds the other parts' records (once all
-// their flags are set) in the order p = 1, 2, ..., then forms
-// cum[bh][f] = cum[bh][f - 1] + (dS, dz), with cum[bh][-1] the initial state
-// (S0, z0; zero where NULL).  The last frame's part 0 also writes the final
-// state to (S_out, z_out), which may alias (S0, z0).  flags[bh * F + f] is
-// published when cum[bh][f] is complete; part 0 waits for
-// flags[bh * F + f - 1] before reading the previous one.
+// tokens are split into np runs of consecutive tiles, one per part; the part
+// writes the sums over its run (dS and dz) to parts[(bh * F + f) * np + part]
+// (a record in accumulator order) and publishes the flag of the same index
+// in pflags.  The prefix items add them up frame by frame.
 template <int DI>
 __device__ __forceinline__ void relu_wide_summary_item(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ cum,
-    const float* S0, const float* z0, float* S_out, float* z_out, int F, int N, long bh, int f, int np,
-    int part, float* __restrict__ parts, uint64_t* __restrict__ pflags, uint64_t* __restrict__ flags,
-    uint64_t epoch, uint32_t* err, uint8_t* lds_raw, TokLayout L, Prologue P) {
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int F, int N, long bh, int f, int np,
+    int part, float* __restrict__ parts, uint64_t* __restrict__ pflags, uint64_t epoch, uint8_t* lds_raw,
+    TokLayout L, Prologue P) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -216,97 +210,124 @@ __device__ __forceinline__ void relu_wide_summary_item(
 
   // A part record holds acc[J][4 i .. 4 i + 3] of thread t as the float4 at
   // (4 J + i) * 256 + t, then the item's own z entries (accz register 0 at
-  // 32 wave + col, or dz at tid) from float D * D on.
-  if (np > 1) {
-    if (part > 0) {
-      float* rec = parts + ((size_t)bhf * (np - 1) + part - 1) * kReluWideRec;
-#pragma unroll
-      for (int J = 0; J < 4; ++J)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          reinterpret_cast<float4*>(rec)[(4 * J + i) * 256 + tid] =
-              make_float4(acc[J][4 * i], acc[J][4 * i + 1], acc[J][4 * i + 2], acc[J][4 * i + 3]);
-      if (!ZROW && !ZV && g == 0) rec[D * D + wave * 32 + col] = accz[0];
-      if (ZV && tid < D) rec[D * D + tid] = dz;
-      publish(&pflags[(size_t)bhf * (np - 1) + part - 1], epoch);
-      return;
-    }
-    wait_all(&pflags[(size_t)bhf * (np - 1)], np - 1, epoch, err);
-    for (int p = 1; p < np; ++p) {
-      const float* rec = parts + ((size_t)bhf * (np - 1) + p - 1) * kReluWideRec;
-#pragma unroll
-      for (int J = 0; J < 4; ++J)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 x = reinterpret_cast<const float4*>(rec)[(4 * J + i) * 256 + tid];
-          acc[J][4 * i] += x.x, acc[J][4 * i + 1] += x.y, acc[J][4 * i + 2] += x.z, acc[J][4 * i + 3] += x.w;
-        }
-      if (!ZROW && !ZV) accz[0] += rec[D * D + wave * 32 + col];
-      if (ZV && tid < D) dz += rec[D * D + tid];
-    }
-  }
-
-  // Add the previous cumulative state.  Lane (col, g), register r of acc[J]
-  // holds S[32 wave + 8 (r / 4) + 4 g + r % 4][32 J + col]; z[n] sits in row
-  // DI, column n (ZROW; the record keeps that row, and a copy of it as its z
-  // part) or in register 0 of accz at n = 32 wave + col.
-  auto row_of = [&](int r) { return wave * 32 + 8 * (r >> 2) + 4 * g + (r & 3); };
-  if (f > 0) {
-    wait_all(&flags[bhf - 1], 1, epoch, err);
-    const float* prv = cum + (size_t)(bhf - 1) * kReluWideRec;
-#pragma unroll
-    for (int J = 0; J < 4; ++J)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[J][r] += prv[row_of(r) * D + J * 32 + col];
-    if (!ZROW) accz[0] += prv[D * D + wave * 32 + col];
-    if (ZV && tid < D) dz += prv[D * D + tid];
-  } else {
-#pragma unroll
-    for (int J = 0; J < 4; ++J)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = row_of(r), n = J * 32 + col;
-        if (S0 && m < DI && n < DI) acc[J][r] += S0[(size_t)bh * DI * DI + m * DI + n];
-        if (ZROW && !ZV && z0 && m == DI && n < DI) acc[J][r] += z0[(size_t)bh * DI + n];
-      }
-    if (!ZROW && z0) accz[0] += z0[(size_t)bh * DI + wave * 32 + col];
-    if (ZV && z0 && tid < DI) dz += z0[(size_t)bh * DI + tid];
-  }
-  float* cur = cum + (size_t)bhf * kReluWideRec;
+  // 32 wave + col, or dz at tid; with ZROW, z is row DI of the S part) from
+  // float D * D on.
+  float* rec = parts + ((size_t)bhf * np + part) * kReluWideRec;
 #pragma unroll
   for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      cur[row_of(r) * D + J * 32 + col] = acc[J][r];
-      if (ZROW && !ZV && row_of(r) == DI) cur[D * D + J * 32 + col] = acc[J][r];
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<float4*>(rec)[(4 * J + i) * 256 + tid] =
+          make_float4(acc[J][4 * i], acc[J][4 * i + 1], acc[J][4 * i + 2], acc[J][4 * i + 3]);
+  if (!ZROW && !ZV && g == 0) rec[D * D + wave * 32 + col] = accz[0];
+  if (ZV && tid < D) rec[D * D + tid] = ntiles > 0 ? dz : 0.0f;
+  publish(&pflags[(size_t)bhf * np + part], epoch);
+}
+
+// Prefix item (head bh, row block w): rows 32w .. 32w + 31 of the head's
+// cumulative state at the end of each block of bfr frames.  The running sum
+// starts from the initial state (S0, z0; zero where NULL) and stays in
+// registers.  Per block it waits once for the part records of all the
+// block's frames (one flag per thread), adds them frame by frame in the order
+// p = 0, 1, ... with the loads of four records in flight at a time, writes
+// the rows to cum[bh][f] for the block's last frame f (row-major S, then z at
+// float D * D) and publishes flags[(bh * F + f) * 4 + w]; the records of
+// other frames are never read.  The last frame's rows also go to (S_out,
+// z_out), which may alias (S0, z0): every element is written by the thread
+// that read it.  Thread T = 64 j + l holds, of each part record, the float4s
+// (4 j + i) * 256 + 64 w + l, i = 0..3: S[32 w + 8 i + 4 (l / 32) + e][32 j +
+// l % 32], e = 0..3 (the accumulator layout of the summary items' wave w),
+// and thread T < 32 the normaliser entry z[32 w + T] where it has its own
+// slot (head dim 128 or the rotary embedding; with the padding row, z is
+// row DI of S and its copy is written from there).  Four items per head
+// shorten each block's hand-off to 16 KB per item, and the records of a
+// head's frames are consecutive, so a block is one run of records.
+template <int DI>
+__device__ __forceinline__ void relu_wide_prefix_item(
+    float* __restrict__ cum, const float* S0, const float* z0, float* S_out, float* z_out, int F, int bfr, long bh,
+    int w, int np, const float* __restrict__ parts, const uint64_t* __restrict__ pflags, uint64_t* __restrict__ flags,
+    uint64_t epoch, uint32_t* err, bool zv) {
+  constexpr int D = kReluWide;
+  constexpr bool ZROW = DI < D;
+  const int T = threadIdx.x, j = T >> 6, l = T & 63;
+  const int g = l >> 5, col = l & 31, n = 32 * j + col;
+  const bool zslot = !ZROW || zv;  // z has its own entries (else it is row DI)
+  auto row = [&](int i, int e) { return 32 * w + 8 * i + 4 * g + e; };
+  float acc[4][4];
+  float z = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = row(i, e);
+      float x = 0.0f;
+      if (S0 && m < DI && n < DI) x = S0[(size_t)bh * DI * DI + (size_t)m * DI + n];
+      if (!zslot && z0 && m == DI && n < DI) x = z0[(size_t)bh * DI + n];
+      acc[i][e] = x;
     }
-  if (!ZROW && !ZV && g == 0) cur[D * D + wave * 32 + col] = accz[0];
-  if (ZV && tid < D) cur[D * D + tid] = dz;
-  if (f == F - 1) {
-    // every element of S_out / z_out is written by the lane that read the
-    // same element of S0 / z0 (frame 0 of this head is this item when F = 1)
+  if (zslot && T < 32 && z0 && 32 * w + T < DI) z = z0[(size_t)bh * DI + 32 * w + T];
+  auto add = [&](const float4 (&x)[4]) {
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+    for (int i = 0; i < 4; ++i) acc[i][0] += x[i].x, acc[i][1] += x[i].y, acc[i][2] += x[i].z, acc[i][3] += x[i].w;
+  };
+  auto load = [&](const float* rec, float4 (&x)[4], float& zx) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = row_of(r), n = J * 32 + col;
-        if (S_out && m < DI && n < DI) S_out[(size_t)bh * DI * DI + m * DI + n] = acc[J][r];
-        if (ZROW && !ZV && z_out && m == DI && n < DI) z_out[(size_t)bh * DI + n] = acc[J][r];
+    for (int i = 0; i < 4; ++i) x[i] = reinterpret_cast<const float4*>(rec)[(4 * j + i) * 256 + 64 * w + l];
+    zx = zslot && T < 32 ? rec[D * D + 32 * w + T] : 0.0f;
+  };
+  for (int f0 = 0; f0 < F; f0 += bfr) {
+    const int f1 = min(F, f0 + bfr);
+    const long r0 = (bh * F + f0) * np, r1 = (bh * F + f1) * np;
+    wait_all(&pflags[r0], (int)(r1 - r0), epoch, err);
+    long r = r0;
+    for (; r + 4 <= r1; r += 4) {  // records r .. r + 3 in the order of the frames and parts
+      float4 x[4][4];
+      float zx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load(parts + (size_t)(r + u) * kReluWideRec, x[u], zx[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(x[u]), z += zx[u];
+    }
+    for (; r < r1; ++r) {
+      float4 x[4];
+      float zx;
+      load(parts + (size_t)r * kReluWideRec, x, zx);
+      add(x), z += zx;
+    }
+    const long bhf = bh * F + f1 - 1;
+    float* cur = cum + (size_t)bhf * kReluWideRec;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cur[(size_t)row(i, e) * D + n] = acc[i][e];
+        if (!zslot && row(i, e) == DI) cur[D * D + n] = acc[i][e];
       }
-    if (!ZROW && !ZV && z_out && g == 0) z_out[(size_t)bh * DI + wave * 32 + col] = accz[0];
-    if (ZV && z_out && tid < DI) z_out[(size_t)bh * DI + tid] = dz;
+    if (zslot && T < 32) cur[D * D + 32 * w + T] = z;
+    if (f1 == F) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row(i, e);
+          if (S_out && m < DI && n < DI) S_out[(size_t)bh * DI * DI + (size_t)m * DI + n] = acc[i][e];
+          if (!zslot && z_out && m == DI && n < DI) z_out[(size_t)bh * DI + n] = acc[i][e];
+        }
+      if (zslot && T < 32 && z_out && 32 * w + T < DI) z_out[(size_t)bh * DI + 32 * w + T] = z;
+    }
+    publish(&flags[(size_t)bhf * 4 + w], epoch);
   }
-  publish(&flags[bhf], epoch);
 }
 
 // Output item `wg` = (frame of one head) * nco + token chunk:
 // o = S phi(q) / (z . phi(q) + eps) with (S, z) = cum[bh][fend - 1], fend the
-// end of the frame's block of bfr frames.  The caller has waited for that
-// record.
+// end of the frame's block of bfr frames.  The record is ready once the four
+// flags at wflags equal epoch (NULL: the caller has waited for it).
 template <int DI>
 __device__ __forceinline__ void relu_wide_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ cum, float eps,
-    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P) {
+    int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P,
+    const uint64_t* wflags, uint64_t epoch, uint32_t* err) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -328,6 +349,32 @@ __device__ __forceinline__ void relu_wide_output_item(
   const int n1 = min(N, n0 + chunk);
   if (n0 >= n1) return;
 
+  const uint16_t* qf = q + L.base(bhf);
+  uint16_t* of = o + L.base(bhf);
+  struct Regs {
+    u32x4 q[LPT];
+  };
+  auto fetch = [&](Regs& X, int t0) {
+#pragma unroll
+    for (int r = 0; r < LPT; ++r) {
+      const int ci = r * 256 + tid;
+      const int tok = ci >> 4, cb = ci & 15;
+      const int n = t0 + tok;
+      // rows past the chunk re-read its first token: their outputs are never
+      // stored; dims past DI re-read a real chunk and are zeroed when staged
+      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
+    }
+  };
+  // the first three query tiles are in flight while the item waits for the
+  // cumulative record of its block (tile t in register set t % 3 until staged)
+  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
+  const int nfull = (n1 - n0) / TILE;
+  const int tlast = n0 + (ntiles - 1) * TILE;
+  Regs R0, R1, R2;
+  fetch(R0, n0);
+  fetch(R1, min(n0 + TILE, tlast));
+  fetch(R2, min(n0 + 2 * TILE, tlast));
+  if (wflags) wait_all(wflags, 4, epoch, err);
   // A operands: S[32 wave + col][16 s + 8 g + e] as bf16 hi and lo terms
   const float* rec = cum + ((size_t)bh * F + fend - 1) * kReluWideRec;
   u32x4 ahi[8], alo[8];
@@ -350,22 +397,6 @@ __device__ __forceinline__ void relu_wide_output_item(
     zr[4] = z1.x, zr[5] = z1.y, zr[6] = z1.z, zr[7] = z1.w;
   }
 
-  const uint16_t* qf = q + L.base(bhf);
-  uint16_t* of = o + L.base(bhf);
-  struct Regs {
-    u32x4 q[LPT];
-  };
-  auto fetch = [&](Regs& X, int t0) {
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int ci = r * 256 + tid;
-      const int tok = ci >> 4, cb = ci & 15;
-      const int n = t0 + tok;
-      // rows past the chunk re-read its first token: their outputs are never
-      // stored; dims past DI re-read a real chunk and are zeroed when staged
-      X.q[r] = ld16_stream(qf + (size_t)(n < n1 ? n : n0) * L.sn + (cb < CI ? cb : CI - 1) * 8);
-    }
-  };
   float wq8[8];  // the prologue's query weights of this thread's channels (chunk tid % 16)
   load_weights8(P.wq, bh % L.H, DI, (tid & 15) * 8, wq8);
   // phi(q) into LDS buffer buf, and each token's denominator into den[buf];
@@ -401,14 +432,10 @@ __device__ __forceinline__ void relu_wide_output_item(
     }
   };
 
-  const int ntiles = (n1 - n0 + TILE - 1) / TILE;
-  const int nfull = (n1 - n0) / TILE;
-  const int tlast = n0 + (ntiles - 1) * TILE;
-  Regs R0, R1;
-  fetch(R0, n0);
-  fetch(R1, min(n0 + TILE, tlast));
+  // query tiles keep coming in through the three register sets, so three
+  // tiles are in flight while one is contracted
   stage(R0, 0, n0);
-  fetch(R0, min(n0 + 2 * TILE, tlast));
+  fetch(R0, min(n0 + 3 * TILE, tlast));
   __syncthreads();
   // a tile's outputs leave as whole rows (16-byte chunks, consecutive lanes on
   // consecutive bytes) from its staging buffer
@@ -422,7 +449,7 @@ __device__ __forceinline__ void relu_wide_output_item(
       if ((full || t0 + tok < n1) && cb < CI) st16_stream(of + (size_t)(t0 + tok) * L.sn + cb * 8, w);
     }
   };
-  // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 3
+  // tile `it` is in LDS buffer it % 2; nxt holds tile it + 1 and is refilled with tile it + 4
   auto tile = [&](int it, Regs& nxt, const bool full) {
     const int buf = it & 1;
 #pragma unroll
@@ -447,21 +474,27 @@ __device__ __forceinline__ void relu_wide_output_item(
       }
     }
     stage(nxt, buf ^ 1, min(n0 + (it + 1) * TILE, tlast));  // the next tile (past the end: a copy of the last, never read)
-    fetch(nxt, min(n0 + (it + 3) * TILE, tlast));
+    fetch(nxt, min(n0 + (it + 4) * TILE, tlast));
     __syncthreads();
     drain(it, full);
   };
-  // Full tiles run in pairs with no branch in the loop body; a last,
+  // Full tiles run in threes with no branch in the loop body; a last,
   // partial tile stores under a token check after the loop.
   int it = 0;
-  for (; it + 2 <= nfull; it += 2) {
+  for (; it + 3 <= nfull; it += 3) {
     tile(it, R1, true);
-    tile(it + 1, R0, true);
+    tile(it + 1, R2, true);
+    tile(it + 2, R0, true);
   }
-  // R1 holds tile it + 1: at most one more full tile, then at most one partial one
-  if (it < nfull) {
+  // R1, R2 and R0 hold tiles it + 1 .. it + 3: at most two more full tiles,
+  // then at most one partial one
+  if (it + 2 <= nfull) {
     tile(it, R1, true);
-    if (it + 1 < ntiles) tile(it + 1, R0, false);
+    tile(it + 1, R2, true);
+    if (it + 2 < ntiles) tile(it + 2, R0, false);
+  } else if (it + 1 <= nfull) {
+    tile(it, R1, true);
+    if (it + 1 < ntiles) tile(it + 1, R2, false);
   } else if (it < ntiles) {
     tile(it, R1, false);
   }

@@ -4,18 +4,18 @@
 // Block ids run over units of B*H padded to a multiple of 8 items, head-minor,
 // so all items of a head share one XCD and hand off through its L2 (padding
 // items leave at once).  Units np f .. np f + np - 1 hold the np summary parts
-// of frame f, part np - 1 first and part 0 last; after the F frames' summary
-// units come the output units, frame by frame, one item per head and token
-// chunk.  Part 0 of a frame waits for the frame's other parts (earlier units
-// of the same frame) and for part 0 of the previous frame (an earlier frame);
-// an output item waits for part 0 of the last frame of its block.  Every
-// item waited on has a lower block id, and block ids dispatch in order, so it
-// is running or done and every wait ends.  All summaries are dispatched
-// before any output item: output items wait for a chain through all earlier
-// frames, so one dispatched early would only hold a slot that a later frame's
-// summary needs to start (measured: at 20 heads x 10 frames x 3600 tokens,
-// head dim 112, 162 us with all summaries first against 190 us with output
-// items of frame f dispatched beside summaries of frame f + 1).
+// of frame f; after the F frames' summary units come four prefix units (one
+// item per 32 rows of a head's state, each walking all frames), then the
+// output units, frame by frame, one item per head and token chunk.  A prefix
+// item waits for the parts of each frame (earlier units); an output item
+// waits for the four prefix items' flags of the last frame of its block.
+// Every item waited on has a lower block id, and block ids dispatch in order,
+// so it is running or done and every wait ends.  All summaries are
+// dispatched before any output item: an output item dispatched early would
+// only hold a slot that a later frame's summary needs to start (measured: at
+// 20 heads x 10 frames x 3600 tokens, head dim 112, 162 us with all summaries
+// first against 190 us with output items of frame f dispatched beside
+// summaries of frame f + 1).
 #include "relu_wide_items.h"
 #include "kernels.h"
 
@@ -40,19 +40,32 @@ __global__ __launch_bounds__(256, 2) void relu_wide_fused_mfma(
   const long u = b / bhp;  // unit: one item per head
   if (bh >= bh_n) return;
   const long bhf_n = bh_n * F;
+  // the parts' records follow the F cumulative records of every head, their
+  // flags the cumulative records' four row-block flags per frame
+  float* parts = cum + (size_t)bhf_n * kReluWideRec;
+  uint64_t* pflags = flags + bhf_n * 4;
+  // which item this unit is: a summary part (frame f, part c), a prefix item
+  // (row block c) or an output item (frame f, chunk c)
+  int kind, f = 0, c;
   if (u < (long)np * F) {
-    // the parts' records follow the F cumulative records of every head, their
-    // flags the frames' flags
-    const int f = (int)(u / np), part = np - 1 - (int)(u % np);
-    relu_wide_summary_item<DI>(k, v, cum, S0, z0, S_out, z_out, F, N, bh, f, np, part,
-                               cum + (size_t)bhf_n * kReluWideRec, flags + bhf_n, flags, epoch, err, lds, L, P);
+    kind = 0, f = (int)(u / np), c = (int)(u % np);
+  } else if (u < (long)np * F + 4) {
+    kind = 1, c = (int)(u - (long)np * F);
+  } else {
+    const long r = u - (long)np * F - 4;
+    kind = 2, f = (int)(r / nco), c = (int)(r % nco);
+  }
+  if (kind == 0) {
+    relu_wide_summary_item<DI>(k, v, F, N, bh, f, np, c, parts, pflags, epoch, lds, L, P);
     return;
   }
-  const long r = u - (long)np * F;
-  const int f = (int)(r / nco), c = (int)(r % nco);
+  if (kind == 1) {
+    relu_wide_prefix_item<DI>(cum, S0, z0, S_out, z_out, F, bfr, bh, c, np, parts, pflags, flags, epoch, err, P.rope());
+    return;
+  }
   const int fend = min(F, (f / bfr + 1) * bfr);
-  wait_all(&flags[bh * F + fend - 1], 1, epoch, err);
-  relu_wide_output_item<DI>(q, o, cum, eps, F, N, bfr, nco, chunko, (bh * F + f) * nco + c, lds, L, P);
+  relu_wide_output_item<DI>(q, o, cum, eps, F, N, bfr, nco, chunko, (bh * F + f) * nco + c, lds, L, P,
+                            &flags[(bh * F + fend - 1) * 4], epoch, err);
 }
 
 template <typename Body>
@@ -70,7 +83,7 @@ hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* fl
                                        uint32_t* err, hipStream_t st) {
   return with_wide_dim(a.D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    const long grid = (long)a.F * bhp * (a.nc + a.nco);
+    const long grid = (long)a.F * bhp * (a.nc + a.nco) + bhp * 4;
     hipLaunchKernelGGL(relu_wide_fused_mfma<DI>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.S0, a.z0, a.S_out,
                        a.z_out, a.eps, a.bh, bhp, a.F, a.N, a.bfr, a.nco, a.chunko, a.nc, flags, epoch, err, a.L,
