@@ -43,6 +43,8 @@ KERNEL_SOURCES = {
     "relu_fused": ["device_common.h", "sync.h", "relu_items.h", "relu_mfma.hip"],
     "gdn_fused": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
     "gdn_phased": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
+    "gdn_step": ["device_common.h", "sync.h", "gdn_items.h", "gdn_mfma.hip"],
+    "relu_wide_fused": ["device_common.h", "sync.h", "relu_wide_items.h", "relu_wide_mfma.hip"],
 }
 
 
@@ -102,6 +104,9 @@ def parse():
                     help="skip the side measurement of the single-frame GDN call latency")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 1 GiB device copy three times (counter calibration)")
+    ap.add_argument("--only", choices=sorted(ONLY_CONFIGS),
+                    help="run only this workload's library calls, --steps passes after one warm-up pass, "
+                         "untimed, and print its algorithmic bytes per pass (for hardware counter runs)")
     return ap.parse_args()
 
 
@@ -128,6 +133,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only:
+        run_only(args, torch, ls, inputs)
+        return
     wv = inputs.WORKLOADS["sana_video_720p_minute"]
     wg = inputs.WORKLOADS["sana_wm_720p_60s"]
 
@@ -655,6 +663,149 @@ def time_chunk_step(torch, ls, inputs):
             "us_p90": round(us[(9 * len(us)) // 10], 2), "tokens_per_s": round(tokens / (med_us * 1e-6), 1),
             "hbm_frac": round(alg / (med_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "workload": "B4 H24 D128 N920, F=1 per call, 50 distinct input sets, one carried state"}
+
+
+def _only_rollout(torch, ls, inputs, name):
+    w = inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    calls = [inputs.workload_call_inputs(w, i, device=dev) for i in range(len(w.calls))]
+    outs = [torch.empty_like(c["q"]) for c in calls]
+    cache = torch.zeros((w.B, w.H, w.D, w.D), device=dev)
+    ncache = torch.zeros((w.B, w.H, w.D), device=dev)
+    S_blk, z_blk = torch.empty_like(cache), torch.empty_like(ncache)
+
+    def run():
+        for i, c in enumerate(calls):
+            ls.ls_relu_block_forward(c["q"], c["k"], c["v"], None if i == 0 else cache, None if i == 0 else ncache,
+                                     out=outs[i], state_out=S_blk, norm_out=z_blk)
+            ls.ls_state_carry(S_blk, cache, z_blk, ncache)
+    # q, k, v in and o out for every call, the carried state read and the new one written
+    return run, 4 * w.B * w.H * w.F * w.N * w.D * 2 + (len(w.calls) - 1) * 2 * w.B * w.H * (w.D * w.D + w.D) * 4
+
+
+def _only_gdn(torch, ls, inputs, name, variant):
+    w = inputs.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    g = inputs.workload_call_inputs(w, 0, device=dev)
+    out = torch.empty_like(g["q"])
+    st = torch.empty((w.B, w.H, w.D, w.D), device=dev)
+    tok = 4 * w.B * w.H * w.F * w.N * w.D * 2
+    if variant == "plain":
+        return (lambda: ls.ls_gdn_frame_forward(g["q"], g["k"], g["v"], g["alpha"], g["beta"], out=out,
+                                                state_out=st)), tok
+    if variant == "token_gate":
+        bt = inputs.token_gates(w.B, w.H, w.F, w.N, seed=w.seed, device=dev)
+        return (lambda: ls.ls_gdn_frame_forward_token_gate(g["q"], g["k"], g["v"], g["alpha"], bt, out=out,
+                                                           state_out=st)), tok + w.B * w.H * w.F * w.N * 4
+    if variant == "reversed_c8":
+        return (lambda: ls.ls_gdn_frame_forward_reversed(g["q"], g["k"], g["v"], g["alpha"], g["beta"], 8,
+                                                         out=out)), tok
+    if variant == "bshd":
+        gs = {n: g[n].permute(0, 2, 3, 1, 4).contiguous().permute(0, 3, 1, 2, 4) for n in ("q", "k", "v")}
+        return (lambda: ls.ls_gdn_frame_forward_strided(gs["q"], gs["k"], gs["v"], g["alpha"], g["beta"])), tok
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    wq, wk = (1.0 + 0.1 * torch.randn((w.H, w.D), generator=gen, device=dev) for _ in range(2))
+    rope = None
+    if variant == "prologue_rope":
+        rope = inputs.rope_tables(w.F, w.N, 40, w.D, 16, device=dev) + (16, 0)
+    return (lambda: ls.ls_gdn_frame_forward_prologue(g["q"], g["k"], g["v"], g["alpha"], g["beta"], wq, wk,
+                                                     norm_eps=1e-6, relu=True, l2_keys=True, out=out,
+                                                     rope=rope)), tok
+
+
+def _only_relu_call(torch, ls, inputs, variant):
+    """The first 10-frame call of the 720p minute-scale rollout (B1 H70 D32 N3600)."""
+    w = inputs.WORKLOADS["sana_video_720p_minute"]
+    dev = torch.device("cuda:0")
+    r = inputs.workload_call_inputs(w, 0, device=dev)
+    out = torch.empty_like(r["q"])
+    tok = 4 * r["q"].numel() * 2
+    if variant == "bshd":
+        rs = {n: r[n].permute(0, 2, 3, 1, 4).contiguous().permute(0, 3, 1, 2, 4) for n in ("q", "k", "v")}
+        return (lambda: ls.ls_relu_block_forward_strided(rs["q"], rs["k"], rs["v"])), tok
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    H, D = r["q"].shape[1], r["q"].shape[-1]
+    wq, wk = (1.0 + 0.1 * torch.randn((H, D), generator=gen, device=dev) for _ in range(2))
+    rope = None
+    if variant == "prologue_rope":
+        rope = inputs.rope_tables(r["q"].shape[2], r["q"].shape[3], 80, D, 4, device=dev) + (4, 0)
+    return (lambda: ls.ls_relu_block_forward_prologue(r["q"], r["k"], r["v"], wq, wk, norm_eps=1e-6, out=out,
+                                                      rope=rope)), tok
+
+
+def _only_480p(torch, ls, inputs):
+    w = inputs.WORKLOADS["sana_video_480p_5s"]
+    x = inputs.relu_inputs(w.B, w.H, w.F, w.N, w.D, "bf16", seed=w.seed, device=torch.device("cuda:0"))
+    out = torch.empty_like(x["q"])
+    return (lambda: ls.ls_relu_block_forward(x["q"], x["k"], x["v"], out=out)), 4 * x["q"].numel() * 2
+
+
+def _only_chunk_step(torch, ls, inputs):
+    w = inputs.WORKLOADS["sana_wm_chunk_step"]
+    dev = torch.device("cuda:0")
+    calls = [inputs.workload_call_inputs(w, i, device=dev) for i in range(w.steps)]
+    state = torch.zeros((w.B, w.H, w.D, w.D), device=dev)
+    outs = [torch.empty_like(c["q"]) for c in calls]
+    s_out = torch.empty_like(state)
+
+    def run():
+        for c, o in zip(calls, outs):
+            ls.ls_gdn_frame_forward(c["q"], c["k"], c["v"], c["alpha"], c["beta"], state, out=o, state_out=s_out)
+    return run, w.steps * (4 * w.B * w.H * w.N * w.D * 2 + 2 * w.B * w.H * w.D * w.D * 4)
+
+
+def _only_temporal_conv(torch, ls, inputs):
+    dev = torch.device("cuda:0")
+    F, N, C = 10, 3600, 2240
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    x = torch.randn((1, 1, F, N, C), generator=g, device=dev).to(torch.bfloat16)
+    w = 0.5 * torch.randn((1, C, 3), generator=g, device=dev)
+    b = 0.1 * torch.randn((1, C), generator=g, device=dev)
+    carry = torch.zeros((1, 1, N, C), dtype=torch.bfloat16, device=dev)
+    y, co = torch.empty_like(x), torch.empty_like(carry)
+    return (lambda: ls.ls_temporal_conv3(x, w, b, carry, block_frames=F, out=y, carry_out=co)), \
+        2 * F * N * C * 2 + 2 * N * C * 2
+
+
+# workloads of --only: name -> f(torch, ls, inputs) -> (one pass, algorithmic HBM bytes per pass)
+ONLY_CONFIGS = {
+    "video_720p_minute": lambda t, l, i: _only_rollout(t, l, i, "sana_video_720p_minute"),
+    "video_720p_minute_d112": lambda t, l, i: _only_rollout(t, l, i, "sana_video_720p_minute_d112"),
+    "video_480p_5s": _only_480p,
+    "video_call_bshd": lambda t, l, i: _only_relu_call(t, l, i, "bshd"),
+    "video_call_prologue": lambda t, l, i: _only_relu_call(t, l, i, "prologue"),
+    "video_call_prologue_rope": lambda t, l, i: _only_relu_call(t, l, i, "prologue_rope"),
+    "wm_720p_60s": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "plain"),
+    "wm_720p_60s_d112": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s_d112", "plain"),
+    "wm_token_gate": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "token_gate"),
+    "wm_reversed_c8": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "reversed_c8"),
+    "wm_bshd": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "bshd"),
+    "wm_prologue": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "prologue"),
+    "wm_prologue_rope": lambda t, l, i: _only_gdn(t, l, i, "sana_wm_720p_60s", "prologue_rope"),
+    "wm_chunk_step": _only_chunk_step,
+    "temporal_conv": _only_temporal_conv,
+}
+
+
+def run_only(args, torch, ls, inputs):
+    """One workload alone: a warm-up pass, then --steps passes (no timing)."""
+    run, alg = ONLY_CONFIGS[args.only](torch, ls, inputs)
+    ls.ls_clear_fault_word()
+    run()
+    torch.cuda.synchronize()
+    ls.ls_profile_begin()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    launches = {k: v[0] // args.steps for k, v in ls.ls_profile_end().items()}
+    fault = ls.ls_fault_word()
+    print(json.dumps({"only": args.only, "passes": args.steps + 1, "alg_bytes_per_pass": int(alg),
+                      "launches_per_pass": launches, "fault_word": fault}), flush=True)
+    if fault:
+        sys.exit(3)
 
 
 def cpu_baseline(args, inputs, wv, wg, tokens):
