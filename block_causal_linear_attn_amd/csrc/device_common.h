@@ -175,7 +175,13 @@ __device__ __forceinline__ u32x4 prologue_bf16x8(u32x4 w, const float (&wt)[8], 
     x[2 * e] = bf16lo_to_f32(w[e]);
     x[2 * e + 1] = bf16hi_to_f32(w[e]);
   }
-  if (norm) {
+  if (norm && is_k && P.l2) {
+    // RMSNorm's factor is positive and the same for every channel of the
+    // token: the ReLU keeps it and the L2 scale below removes it, so only the
+    // weights remain (x * w exact in fp64)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= (double)wt[e];
+  } else if (norm) {
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fma(x[e], x[e], ss);

@@ -110,7 +110,7 @@ __device__ __forceinline__ void gdn_gram_item(
   // zeros (every row fails the token check) and add nothing, and fetches past
   // the chunk re-read its last tile.  A load or stage under a condition would
   // make the compiler wait for every load in flight at every stage.
-  constexpr int DEPTH = kGramDepth;
+  constexpr int DEPTH = PRO ? 1 : kGramDepth;
   struct Regs {
     u32x4 k[LPT], v[LPT];
     float b;  // gate of token tid % 64 of the tile (TG)
@@ -136,17 +136,8 @@ __device__ __forceinline__ void gdn_gram_item(
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
       const bool live = t0 + tok < n1 && cb < CI;
-      u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 kk = live ? X.k[r] : u32x4{0u, 0u, 0u, 0u};
       const u32x4 vv = live ? X.v[r] : u32x4{0u, 0u, 0u, 0u};
-      // the 16 lanes of a DPP row hold the 16 chunks of token `tok`
-      if (PRO && P.on_k()) {
-        float wk8[8];
-        weights8_lds(wl, cb, wk8);
-        // rotary table row of this token (rows past the chunk: a real token's)
-        const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI))
-                                  : Rot8{};
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
-      }
       uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
       uint2* vd = reinterpret_cast<uint2*>(&lds[buf][1][swz_offset<C>(tok, cb)]);
       kd[0] = make_uint2(kk[0], kk[1]);
@@ -155,6 +146,27 @@ __device__ __forceinline__ void gdn_gram_item(
       vd[1] = make_uint2(vv[2], vv[3]);
     }
     if (TG && tid < TILE) gl[buf][tid] = X.b;
+    if (PRO && P.on_k()) {
+      // the prologue on the staged key chunks, in place, one chunk at a time
+      // (each thread reads back only what it wrote; the 16 lanes of a DPP row
+      // hold the 16 chunks of token `tok`)
+#pragma unroll 1
+      for (int r = 0; r < LPT; ++r) {
+        const int ci = r * 256 + tid;
+        const int tok = ci >> 4, cb = ci & 15;
+        uint2* kd = reinterpret_cast<uint2*>(&lds[buf][0][swz_offset<C>(tok, cb)]);
+        const uint2 a = kd[0], b = kd[1];
+        float wk8[8];
+        weights8_lds(wl, cb, wk8);
+        // rotary table row of this token (rows past the chunk: a real token's)
+        const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI))
+                                  : Rot8{};
+        const u32x4 kk =
+            prologue_bf16x8(u32x4{a.x, a.y, b.x, b.y}, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
+        kd[0] = make_uint2(kk[0], kk[1]);
+        kd[1] = make_uint2(kk[2], kk[3]);
+      }
+    }
   };
   auto contract = [&](int buf) {
     const uint16_t* kl = lds[buf][0];
@@ -304,7 +316,7 @@ __device__ __forceinline__ void gram_rows_accumulate(
     u32x4 k[KLPT], v[VLPT];
     float b;  // gate of token tid % 64 of the tile (TG)
   };
-  constexpr int DEPTH = kGramRowsDepth;
+  constexpr int DEPTH = PRO ? 2 : kGramRowsDepth;
   Regs R[DEPTH];
   // K: token ci >> 4, 16-byte chunk ci & 15; V: token ci / VCH, chunk
   // ci % VCH of the block's RB dims.  Every load is issued (rows past the
@@ -333,18 +345,27 @@ __device__ __forceinline__ void gram_rows_accumulate(
 #pragma unroll
     for (int r = 0; r < KLPT; ++r) {
       const int ci = r * 256 + tid;
-      u32x4 kk = t0 + (ci >> 4) < N && (ci & 15) < CI ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
-      if (PRO && P.on_k()) {
+      const u32x4 kk = t0 + (ci >> 4) < N && (ci & 15) < CI ? R.k[r] : u32x4{0u, 0u, 0u, 0u};
+      uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
+      kd[0] = make_uint2(kk[0], kk[1]);
+      kd[1] = make_uint2(kk[2], kk[3]);
+    }
+    if (PRO && P.on_k()) {  // in place on the staged chunks, one at a time (as in gdn_gram_item)
+#pragma unroll 1
+      for (int r = 0; r < KLPT; ++r) {
+        const int ci = r * 256 + tid;
+        uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
+        const uint2 a = kd[0], b = kd[1];
         float wk8[8];
         weights8_lds(wl, ci & 15, wk8);
         const int n = t0 + (ci >> 4);
         const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, n < N ? n : 0, (ci & 15) < CI ? (ci & 15) : 0, DI))
                                   : Rot8{};
-        kk = prologue_bf16x8(kk, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
+        const u32x4 kk =
+            prologue_bf16x8(u32x4{a.x, a.y, b.x, b.y}, wk8, P.wk != nullptr, P, true, 1.0 / DI, row16, P.rope(), rot);
+        kd[0] = make_uint2(kk[0], kk[1]);
+        kd[1] = make_uint2(kk[2], kk[3]);
       }
-      uint2* kd = reinterpret_cast<uint2*>(kl[buf] + swz_offset<KROW / 8>(ci >> 4, ci & 15));
-      kd[0] = make_uint2(kk[0], kk[1]);
-      kd[1] = make_uint2(kk[2], kk[3]);
     }
 #pragma unroll
     for (int r = 0; r < VLPT; ++r) {
@@ -988,14 +1009,21 @@ __device__ __forceinline__ void gdn_output_item(
     for (int r = 0; r < LPT; ++r) {
       const int ci = r * 256 + tid;
       const int tok = ci >> 4, cb = ci & 15;
-      u32x4 qq = X.q[r];
-      if (PRO && P.on_q()) {  // chunks past DI re-read a real chunk: zero them out of the token's sums
-        qq = cb < CI ? qq : u32x4{0u, 0u, 0u, 0u};
+      // with the prologue, chunks past DI (which re-read a real chunk) are
+      // zeroed out of the token's sums
+      const u32x4 qq = PRO && P.on_q() && cb >= CI ? u32x4{0u, 0u, 0u, 0u} : X.q[r];
+      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qq;
+    }
+    if (PRO && P.on_q()) {  // in place on the staged chunks, one at a time (as in gdn_gram_item)
+#pragma unroll 1
+      for (int r = 0; r < LPT; ++r) {
+        const int ci = r * 256 + tid;
+        const int tok = ci >> 4, cb = ci & 15;
+        u32x4* qd = reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]);
         const Rot8 rot = P.rope() ? rot8_load(P.rope8(bhf % L.F, t0 + tok < n1 ? t0 + tok : n0, cb < CI ? cb : 0, DI))
                                   : Rot8{};
-        qq = prologue_bf16x8(qq, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16, P.rope(), rot);
+        *qd = prologue_bf16x8(*qd, wq8, P.wq != nullptr, P, false, 1.0 / DI, row16, P.rope(), rot);
       }
-      *reinterpret_cast<u32x4*>(&lds[buf][tok * ROW + cb * 8]) = qq;
     }
   };
 
