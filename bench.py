@@ -231,6 +231,9 @@ def main():
         "gdn_fused": 6 * wg.B * wg.H * wg.F * wg.N * wg.D ** 2 + 2 * wg.B * wg.H * wg.F * wg.D ** 3,
     }
     copy_gbs = device_copy_gbs(torch)
+    # the ReLU call's own mix (three tensors read, one written, the sizes of a
+    # 10-frame call's tensors) as a second ceiling beside the device copy
+    mix_gbs = stream_mix_gbs(torch, wv.B * wv.H * wv.N * wv.D * 10)
     kernels = {}
     for name, (launches, total_ms) in kstats.items():
         avg_us = 1e3 * total_ms / max(1, launches)
@@ -254,6 +257,8 @@ def main():
                     "traffic": None if traffic is None else int(traffic),
                     "alg_bytes": kernels[dom]["alg_bytes_per_launch"], "traffic_note": note,
                     "copy_GBs": round(copy_gbs, 1), "frac_of_copy": kernels[dom]["copy_frac"],
+                    "read3_write1_GBs": round(mix_gbs, 1),
+                    "frac_of_read3_write1": round(kernels[dom]["achieved_GBs"] / mix_gbs, 4),
                     "mfma_frac": kernels[dom].get("mfma_frac")}
 
     chunk_step = None if args.no_chunk_step else time_chunk_step(torch, ls, inputs)
@@ -364,6 +369,26 @@ def device_copy_gbs(torch, nbytes=1 << 30, reps=5):
     ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
     del src, dst
     return 2 * nbytes / (ms / 1e3) / 1e9
+
+
+def stream_mix_gbs(torch, n, reps=5):
+    """Bytes per second of torch.addcmul over bf16 tensors of n elements
+    (three read, one written: the ReLU call's mix of q, k, v in and o out),
+    median of `reps` calls."""
+    dev = torch.device("cuda:0")
+    a, b, c = (torch.ones(n, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    d = torch.empty_like(a)
+    torch.addcmul(a, b, c, out=d)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        torch.addcmul(a, b, c, out=d)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    del a, b, c, d
+    return 4 * n * 2 / (ms / 1e3) / 1e9
 
 
 def time_head_dim_112(torch, ls, inputs, prelude, reps=3):

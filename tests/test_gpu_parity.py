@@ -141,6 +141,31 @@ def test_gdn_parity(ls, gen, oracle_mod, B, H, F, N, D, dt, l2, with_state):
     check(tag + " S", S, rS, ts, dt)
 
 
+@pytest.mark.parametrize("H,F,N,D,dt", [(3, 4, 150, 128, "bf16"), (2, 3, 97, 112, "bf16"), (2, 3, 60, 64, "bf16")])
+def test_gdn_camera_branch_shares_the_gates(ls, gen, oracle_mod, H, F, N, D, dt):
+    """The coarse camera branch (SANA-WM summary, section 3, Dual-Branch Camera
+    Control) has its own q, k, v and shares the frame-wise GDN gates with the
+    main branch: the same scan with other token tensors.  Both branches stacked
+    on the batch axis with the gates repeated equal the two calls bit for bit,
+    and the camera branch driven by the main branch's alpha and beta matches
+    the oracle."""
+    main = gen.gdn_inputs(1, H, F, N, D, dt, seed=61, part=N, l2_keys=True)
+    cam = gen.gdn_inputs(1, H, F, N, D, dt, seed=62, part=N, l2_keys=True)
+    m, c = _dev(main), _dev(cam)
+    o_m, S_m = ls.ls_gdn_frame_forward(m["q"], m["k"], m["v"], m["alpha"], m["beta"])
+    o_c, S_c = ls.ls_gdn_frame_forward(c["q"], c["k"], c["v"], m["alpha"], m["beta"])
+    st = {n: torch.cat([m[n], c[n]], dim=0) for n in ("q", "k", "v")}
+    ga, gb = torch.cat([m["alpha"], m["alpha"]], dim=0), torch.cat([m["beta"], m["beta"]], dim=0)
+    o_s, S_s = ls.ls_gdn_frame_forward(st["q"], st["k"], st["v"], ga, gb)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s[:1], o_m) and torch.equal(o_s[1:], o_c)
+    assert torch.equal(S_s[:1], S_m) and torch.equal(S_s[1:], S_c)
+    ro, rS = oracle_mod.gdn_frame(cam["q"], cam["k"], cam["v"], main["alpha"], main["beta"])
+    tag = "camera branch H%d F%d N%d D%d" % (H, F, N, D)
+    check(tag + " o", o_c, ro, TOL[dt][0], dt)
+    check(tag + " S", S_c, rS, TOL[dt][1], dt)
+
+
 TG_CASES = [
     # (B, H, F, N, D, dtype, with_state): per-token update gates
     (1, 2, 4, 300, 128, "bf16", True),      # frame-interleaved launch, ragged token count
