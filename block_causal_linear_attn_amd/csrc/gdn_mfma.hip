@@ -327,7 +327,7 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
     // an output item's state needs the records of every frame of its chunk
     // (reversed scan): lag >= rchunk keeps those gram items at lower block ids
     const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco),
-                              a.rchunk > 0 ? a.rchunk : 1, a.F);
+                              a.rchunk > 0 ? a.rchunk : 1, a.F, 1.25);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,

@@ -114,9 +114,9 @@ int device_slots(const void* kernel);
 // Frames by which the consumer items of a fused launch trail their producers
 // so that a consumer is dispatched about when its inputs become ready: the
 // producers of one frame take about as long as the slots need to turn over
-// once, i.e. slots / items_per_step steps of dispatch, with a margin of 1/4
-// and one step.  At least `min_lag`, at most F.
-int fused_lag(long slots, long items_per_step, int min_lag, int F);
+// `rounds` times, i.e. rounds * slots / items_per_step steps of dispatch, plus
+// one step.  At least `min_lag`, at most F.
+int fused_lag(long slots, long items_per_step, int min_lag, int F, double rounds);
 
 //  GDN, any B*H (N > 0): row-split gram items of all frames (four per frame,
 //  one record per frame: nc must be 1), then scan items, then output items,

@@ -86,7 +86,10 @@ hipError_t launch_relu_fused_mfma(const ScanArgs& a, long bhp, uint64_t* flags, 
     return pro == 2 ? relu_fused_mfma<D, 2> : pro == 1 ? relu_fused_mfma<D, 1> : relu_fused_mfma<D, 0>;
   };
   auto run = [&](auto kern) {
-    const int lag = fused_lag(device_slots((const void*)kern), bhp * (a.nc + a.nco), a.bfr, a.F);
+    // three rounds of the resident slots: at B1 H70 D32 N3600 one 10-frame call
+    // 120.9 -> 118.0 us (lag 5 -> 10), 24 heads x 60 frames 266 -> 257 us, the
+    // 480p call (H70 F21 N1560) 117.4 -> 118.6 us, against 1.25 rounds
+    const int lag = fused_lag(device_slots((const void*)kern), bhp * (a.nc + a.nco), a.bfr, a.F, 3.0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.init, a.S0, a.z0, a.S_out, a.z_out, a.eps,
                        a.bh, bhp, a.F, a.N, a.bfr, a.nc, a.chunk, a.nco, a.chunko, lag, flags, epoch, err, a.L,

@@ -11,6 +11,7 @@
 #include "kernels.h"
 
 #include <map>
+#include <cmath>
 #include <mutex>
 #include <utility>
 
@@ -156,8 +157,8 @@ int device_slots(const void* kernel) {
   return slots;
 }
 
-int fused_lag(long slots, long items_per_step, int min_lag, int F) {
-  long lag = items_per_step > 0 ? (5 * slots + 4 * items_per_step - 1) / (4 * items_per_step) + 1 : 1;
+int fused_lag(long slots, long items_per_step, int min_lag, int F, double rounds) {
+  long lag = items_per_step > 0 ? (long)std::ceil(rounds * (double)slots / (double)items_per_step) + 1 : 1;
   if (lag < min_lag) lag = min_lag;
   if (lag > F) lag = F;
   return lag < 1 ? 1 : (int)lag;
