@@ -324,10 +324,13 @@ hipError_t launch_gdn_fused_mfma(const ScanArgs& a, long bhp, uint64_t* gflags, 
                             : (pro ? gdn_fused_mfma128<false, DI, false, true> : gdn_fused_mfma128<false, DI, false, false>))
                     : (a.tg ? gdn_fused_mfma128<true, DI, true, false>
                             : (pro ? gdn_fused_mfma128<true, DI, false, true> : gdn_fused_mfma128<true, DI, false, false>));
-    // an output item's state needs the records of every frame of its chunk
-    // (reversed scan): lag >= rchunk keeps those gram items at lower block ids
+    // gram items lead the output items by three rounds of the resident slots
+    // (as in the ReLU launch): the 720p 60 s call (B1 H24, lag 12 -> 28) ran
+    // 1141 -> 1114 us, against 1.25 rounds.  An output item's state needs the
+    // records of every frame of its chunk (reversed scan): lag >= rchunk
+    // keeps those gram items at lower block ids.
     const int lag = fused_lag(device_slots((const void*)kern) - bhp * kGdnFusedRowBlocks, bhp * (a.nc + a.nco),
-                              a.rchunk > 0 ? a.rchunk : 1, a.F, 1.25);
+                              a.rchunk > 0 ? a.rchunk : 1, a.F, 3.0);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, a.alpha, gates, (uint16_t*)a.o, (uint8_t*)a.partial,
                        (uint16_t*)a.states, a.S0, a.S_out, a.c, a.c2, a.bh, bhp, a.F, a.N, a.nc, a.chunk, a.nco,
