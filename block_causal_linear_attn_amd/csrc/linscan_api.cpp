@@ -270,8 +270,10 @@ ReluPlan relu_plan(const ls_shape* s, const Dims& d) {
   // measured best at 20 heads x 10 frames x 3600 tokens) and take chunks down
   // to 128 tokens when there are few frames (one frame: 52 -> 45 us); head
   // dim 64 aims at about 512, since each output item sums the partials of
-  // every earlier frame (35 heads x 10 frames x 3600 tokens: 166 -> 153 us)
-  plan_chunks(d.bhf, s->N, p.wide ? 1000 : s->D == 64 ? 512 : 1536, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
+  // every earlier frame (35 heads x 10 frames x 3600 tokens: 166 -> 153 us);
+  // head dim 32 at about 2800 (70 heads x 10 frames x 3600 tokens: four
+  // chunks per frame, 118.8 -> 117.7 us against three)
+  plan_chunks(d.bhf, s->N, p.wide ? 1000 : s->D == 64 ? 512 : 2800, p.wide ? 128 : 512, 128, &p.nco, &p.chunko);
   // wide heads keep one cumulative record per frame, 128 dims wide, then one
   // record per summary part, and no init copy; their flags: four row blocks
   // per cumulative record, then one per part
