@@ -227,14 +227,18 @@ __device__ __forceinline__ void relu_wide_summary_item(
 // Prefix item (head bh, row block w): rows 32w .. 32w + 31 of the head's
 // cumulative state at the end of each block of bfr frames.  The running sum
 // starts from the initial state (S0, z0; zero where NULL) and stays in
-// registers.  Per block it waits once for the part records of all the
-// block's frames (one flag per thread), adds them frame by frame in the order
-// p = 0, 1, ... with the loads of four records in flight at a time, writes
-// the rows to cum[bh][f] for the block's last frame f (row-major S, then z at
-// float D * D) and publishes flags[(bh * F + f) * 4 + w]; the records of
-// other frames are never read.  The last frame's rows also go to (S_out,
-// z_out), which may alias (S0, z0): every element is written by the thread
-// that read it.  Thread T = 64 j + l holds, of each part record, the float4s
+// registers.  Frames go in groups of up to kPrefixRecs part records: one
+// wait for the group's records (one flag per thread), all their loads in
+// flight, then the adds frame by frame in the order p = 0, 1, ...; a block's
+// last frame f writes the rows to cum[bh][f] (row-major S, then z at float
+// D * D), and the group's block ends get their flags
+// flags[(bh * F + f) * 4 + w] once its records are complete (with release:
+// all flags at the end, after one agent-scope release, for output items on
+// other XCDs).  Records of other frames are never written.  Ten 1-frame
+// blocks with a wait, a record pair's load and a store each kept the output
+// items waiting about 20 us after the last summary.  The last frame's rows
+// also go to (S_out, z_out), which may alias (S0, z0): every element is
+// written by the thread that read it.  Thread T = 64 j + l holds, of each part record, the float4s
 // (4 j + i) * 256 + 64 w + l, i = 0..3: S[32 w + 8 i + 4 (l / 32) + e][32 j +
 // l % 32], e = 0..3 (the accumulator layout of the summary items' wave w),
 // and thread T < 32 the normaliser entry z[32 w + T] where it has its own
@@ -242,11 +246,12 @@ __device__ __forceinline__ void relu_wide_summary_item(
 // row DI of S and its copy is written from there).  Four items per head
 // shorten each block's hand-off to 16 KB per item, and the records of a
 // head's frames are consecutive, so a block is one run of records.
+constexpr int kPrefixRecs = 8;  // part records in flight per prefix item
 template <int DI>
 __device__ __forceinline__ void relu_wide_prefix_item(
     float* __restrict__ cum, const float* S0, const float* z0, float* S_out, float* z_out, int F, int bfr, long bh,
     int w, int np, const float* __restrict__ parts, const uint64_t* __restrict__ pflags, uint64_t* __restrict__ flags,
-    uint64_t epoch, uint32_t* err, bool zv) {
+    uint64_t epoch, uint32_t* err, bool zv, bool release) {
   constexpr int D = kReluWide;
   constexpr bool ZROW = DI < D;
   const int T = threadIdx.x, j = T >> 6, l = T & 63;
@@ -275,27 +280,10 @@ __device__ __forceinline__ void relu_wide_prefix_item(
     for (int i = 0; i < 4; ++i) x[i] = reinterpret_cast<const float4*>(rec)[(4 * j + i) * 256 + 64 * w + l];
     zx = zslot && T < 32 ? rec[D * D + 32 * w + T] : 0.0f;
   };
-  for (int f0 = 0; f0 < F; f0 += bfr) {
-    const int f1 = min(F, f0 + bfr);
-    const long r0 = (bh * F + f0) * np, r1 = (bh * F + f1) * np;
-    wait_all(&pflags[r0], (int)(r1 - r0), epoch, err);
-    long r = r0;
-    for (; r + 4 <= r1; r += 4) {  // records r .. r + 3 in the order of the frames and parts
-      float4 x[4][4];
-      float zx[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) load(parts + (size_t)(r + u) * kReluWideRec, x[u], zx[u]);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) add(x[u]), z += zx[u];
-    }
-    for (; r < r1; ++r) {
-      float4 x[4];
-      float zx;
-      load(parts + (size_t)r * kReluWideRec, x, zx);
-      add(x), z += zx;
-    }
-    const long bhf = bh * F + f1 - 1;
-    float* cur = cum + (size_t)bhf * kReluWideRec;
+  // the rows of frame f's cumulative state to cum[bh][f] (and the last frame's
+  // to S_out, z_out)
+  auto write_frame = [&](int f) {
+    float* cur = cum + (size_t)(bh * F + f) * kReluWideRec;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -304,7 +292,7 @@ __device__ __forceinline__ void relu_wide_prefix_item(
         if (!zslot && row(i, e) == DI) cur[D * D + n] = acc[i][e];
       }
     if (zslot && T < 32) cur[D * D + 32 * w + T] = z;
-    if (f1 == F) {
+    if (f == F - 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -315,7 +303,46 @@ __device__ __forceinline__ void relu_wide_prefix_item(
         }
       if (zslot && T < 32 && z_out && 32 * w + T < DI) z_out[(size_t)bh * DI + 32 * w + T] = z;
     }
-    publish(&flags[(size_t)bhf * 4 + w], epoch);
+  };
+  auto block_end = [&](int f) { return (f + 1) % bfr == 0 || f == F - 1; };
+  // frames in groups of kPrefixRecs / np: one wait for the group's part
+  // records, all their loads in flight at once (past the group: re-reads of
+  // its last record, not added), then the adds in frame and part order
+  const int gf = np < kPrefixRecs ? kPrefixRecs / np : 1;
+  for (int fa = 0; fa < F; fa += gf) {
+    const int fb = min(F, fa + gf);
+    const long r0 = (bh * F + fa) * np, r1 = (bh * F + fb) * np;
+    wait_all(&pflags[r0], (int)(r1 - r0), epoch, err);
+    float4 x[kPrefixRecs][4];
+    float zx[kPrefixRecs];
+#pragma unroll
+    for (int u = 0; u < kPrefixRecs; ++u)
+      load(parts + (size_t)(r0 + u < r1 ? r0 + u : r1 - 1) * kReluWideRec, x[u], zx[u]);
+#pragma unroll
+    for (int u = 0; u < kPrefixRecs; ++u) {
+      if (r0 + u < r1) {
+        add(x[u]), z += zx[u];
+        if ((u + 1) % np == 0 && block_end(fa + (u + 1) / np - 1)) write_frame(fa + (u + 1) / np - 1);
+      }
+    }
+    if (!release) {  // the group's records are complete: the flags of its block ends
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0)
+        for (int f = fa; f < fb; ++f)
+          if (block_end(f))
+            __hip_atomic_store(&flags[(size_t)(bh * F + f) * 4 + w], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (release) {  // one write-back of the L2 for all records, then every block's flag
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      for (int f0 = 0; f0 < F; f0 += bfr)
+        __hip_atomic_store(&flags[(size_t)(bh * F + min(F, f0 + bfr) - 1) * 4 + w], epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -327,7 +354,7 @@ template <int DI>
 __device__ __forceinline__ void relu_wide_output_item(
     const uint16_t* __restrict__ q, uint16_t* __restrict__ o, const float* __restrict__ cum, float eps,
     int F, int N, int bfr, int nco, int chunk, long wg, uint8_t* lds_raw, TokLayout L, Prologue P,
-    const uint64_t* wflags, uint64_t epoch, uint32_t* err) {
+    const uint64_t* wflags, uint64_t epoch, uint32_t* err, bool acquire) {
   constexpr int D = kReluWide;
   constexpr int CI = DI / 8;  // 16-byte chunks per token row in memory
   constexpr int TILE = 64;
@@ -374,7 +401,12 @@ __device__ __forceinline__ void relu_wide_output_item(
   fetch(R0, n0);
   fetch(R1, min(n0 + TILE, tlast));
   fetch(R2, min(n0 + 2 * TILE, tlast));
-  if (wflags) wait_all(wflags, 4, epoch, err);
+  if (wflags) {
+    if (acquire)
+      wait_all_acquire(wflags, 4, epoch, err);
+    else
+      wait_all(wflags, 4, epoch, err);
+  }
   // A operands: S[32 wave + col][16 s + 8 g + e] as bf16 hi and lo terms
   const float* rec = cum + ((size_t)bh * F + fend - 1) * kReluWideRec;
   u32x4 ahi[8], alo[8];

@@ -65,7 +65,8 @@ RELU_CASES = [
     (1, 2, 3, 2100, 64, "bf16", 2, True),       # D = 64, summaries in 4 token chunks, blocks of 2 frames
     (1, 2, 3, 97, 112, "bf16", 1, True),        # wide MFMA path at the pages' head dim (128 dims, zero-padded)
     (1, 2, 4, 2000, 112, "bf16", 1, False),     # wide path, two output chunks per frame, ragged tail
-    (2, 10, 3, 200, 112, "bf16", 2, True),      # wide path, B*H = 20 (padding items), blocks of 2 frames
+    (2, 10, 3, 200, 112, "bf16", 2, True),      # wide path, B*H = 20 (padding items, outputs spread over XCDs)
+    (2, 8, 3, 300, 112, "bf16", 1, True),       # wide path, B*H = 16: every item on its head's XCD
     (1, 2, 1, 1, 112, "bf16", 1, True),         # wide path, single token, single frame
     (1, 2, 5, 300, 128, "bf16", 3, True),       # wide path at D = 128 (normaliser by MFMA), ragged block
     (1, 3, 3, 1000, 112, "bf16", 2, True),      # wide path, each frame's summary in 2 parts (ragged second)
