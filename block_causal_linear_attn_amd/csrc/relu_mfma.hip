@@ -27,8 +27,12 @@ namespace {
 // keeps every summary an output item waits for at a lower block id.  Within
 // a step items are head-minor with B*H padded to BHp (a multiple of 8);
 // padding items leave at once.
+// Head dim 32 with RMSNorm (PRO 1) is held to three workgroups per CU (at
+// most 168 registers, 164 used), as without the prologue: with two, its
+// fp64 load stage had too few waves to hide behind (10-frame call at H70
+// N3600: 168 -> 143 us, 117 us without the prologue).
 template <int D, int PRO, bool PAIR = false>
-__global__ __launch_bounds__(256, 2) void relu_fused_mfma(
+__global__ __launch_bounds__(256, (D == 32 && PRO == 1) ? 3 : 2) void relu_fused_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ partial, float* __restrict__ init, const float* S0,
     const float* z0, float* S_out, float* z_out, float eps, long bh_n, long bhp, int F, int N, int bfr,
