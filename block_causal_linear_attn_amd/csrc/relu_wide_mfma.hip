@@ -17,7 +17,7 @@
 // first against 190 us with output items of frame f dispatched beside
 // summaries of frame f + 1).
 //
-// When B*H is not a multiple of 8 (spread), one XCD per head would leave
+// When B*H is not a multiple of 8 and F > 1 (spread), one XCD per head would leave
 // some XCDs with a head more than others (20 heads: 3 on XCDs 0-3, 2 on
 // 4-7), and the output phase would end on the busy ones.  The output items
 // then run over consecutive block ids without padding, so every XCD takes
@@ -106,7 +106,10 @@ hipError_t launch_relu_wide_fused_mfma(const ScanArgs& a, long bhp, uint64_t* fl
                                        uint32_t* err, hipStream_t st) {
   return with_wide_dim(a.D, [&](auto di) {
     constexpr int DI = decltype(di)::value;
-    const int spread = a.bh % 8 != 0 && a.L.hg == 1;
+    // (one-frame calls keep every item on its head's XCD: there the prefix
+    // items' write-back sits on the whole call's critical path, 42.7 -> 50.6 us
+    // at 20 heads x 3600 tokens, head dim 112)
+    const int spread = a.bh % 8 != 0 && a.L.hg == 1 && a.F > 1;
     const long grid = (long)a.F * bhp * a.nc + bhp * 4 + (long)a.F * (spread ? a.bh : bhp) * a.nco;
     hipLaunchKernelGGL(relu_wide_fused_mfma<DI>, dim3((unsigned)grid), dim3(256), 0, st, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.partial, a.S0, a.z0, a.S_out,
