@@ -270,7 +270,7 @@ def main():
     rev = None if args.no_reversed else time_reversed(torch, ls, g, wg, part_video)
     conv = None if args.no_temporal_conv else time_temporal_conv(torch, ls)
     strided = None if args.no_strided else time_strided(torch, ls, calls[0], g, part_video)
-    pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g, part_video)
+    pro = None if args.no_prologue else time_prologue(torch, ls, inputs, calls[0], g, part_video, copy_gbs)
 
     # ---- CPU baseline: the fp64 oracle on a sample of the same workload
     fault = ls.ls_fault_word(dev)
@@ -574,14 +574,16 @@ def time_strided(torch, ls, relu_call, g, prelude, reps=4):
     return res
 
 
-def time_prologue(torch, ls, inputs, relu_call, g, prelude, reps=4):
+def time_prologue(torch, ls, inputs, relu_call, g, prelude, copy_gbs, reps=4):
     """The per-token prologue fused into the load stage: one 10-frame ReLU call
     of the rollout with RMSNorm (weights) on q and k, and the GDN call with
     RMSNorm on q and k, ReLU and L2 keys (each once more with a 3D rotary
     embedding), against the same calls without a prologue (mean kernel time
     from the library's per-launch events), and the GDN call after the same
     prologue as separate torch ops (wall time of both, CUDA events), which
-    reads and writes q and k once more."""
+    reads and writes q and k once more; separate_pass_bound_us is what the
+    bytes of such a pass (q and k read and written) take at the device-copy
+    rate copy_gbs, the least any separate pass could cost."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(4242)
@@ -644,6 +646,12 @@ def time_prologue(torch, ls, inputs, relu_call, g, prelude, reps=4):
     torch.cuda.synchronize()
     ms_unfused = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
     gdn["torch_prologue_then_plain_wall"] = round(1e3 * ms_unfused, 2)
+    # what a separate bf16 prologue pass would cost at best: q and k read and
+    # written once more, at the device-copy rate measured in this run
+    for key, t in (("relu", r), ("gdn", g)):
+        sep_bytes = 4 * t["q"].numel() * t["q"].element_size()
+        (res["relu_h70_d32_10_frames_rmsnorm_qk_us"] if key == "relu" else gdn)["separate_pass_bound_us"] = round(
+            sep_bytes / (copy_gbs * 1e9) * 1e6, 2)
     res["gdn_h24_d128_181_frames_rmsnorm_relu_l2_us"] = gdn
     del fcs, tcs
     return res
